@@ -1,0 +1,230 @@
+"""fp64 reference for the paged KV store, in-place append and decode attention.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``): the product path never
+imports this module.
+
+Data format (the pages give a page as "tokens x heads x dims" in fp16 without
+fixing the axis order -- hotelren §3.2, pgsm §3.2; the order below is this
+library's reading):
+
+* ``k_pool``, ``v_pool``: fp16 arrays ``[N][Hkv][P][D]``; one (page, kv head)
+  tile of ``P`` tokens x ``D`` dims is contiguous.
+* ``block_table``: int32 ``[B][max_pages]``; entry ``j`` of row ``b`` is the
+  physical page holding logical tokens ``j*P .. j*P+P-1`` of sequence ``b``
+  (pgsm §3.2 and §4.1: a page table maps each sequence's pages).
+* ``lens``: int32 ``[B]``, tokens of context per sequence *including* the token
+  appended this step.
+* query head ``h`` reads KV head ``h // (Hq // Hkv)`` (grouped-query sharing; the
+  pages only say a layer has H KV heads, dpshk §4.1).
+
+Arithmetic is float64 throughout; fp16 inputs widen exactly.
+"""
+
+import math
+
+import numpy as np
+
+
+# ---------------------------------------------------------------------------
+# sizes
+# ---------------------------------------------------------------------------
+
+def kv_cache_bytes(layers, kv_heads, head_dim, seq_len, dtype_bytes=2, batch=1):
+    """Bytes of K plus V for ``batch`` sequences of ``seq_len`` tokens.
+
+    dpshk §4.1 gives the size as 2 (K and V) x layers x heads x head_dim x
+    tokens x 2 bytes (fp16); pgsm §4.1 states the same product with a batch
+    factor.
+    """
+    return 2 * batch * layers * kv_heads * head_dim * seq_len * dtype_bytes
+
+
+def pages_for_tokens(n_tokens, page_size):
+    """Pages needed to hold ``n_tokens`` tokens: the ceiling of n / P.
+
+    pgsm §4.1 tabulates pages per request against page size for ~2048-token
+    requests (128, 64, 32, 16 pages at P = 16, 32, 64, 128).
+    """
+    if n_tokens < 0 or page_size <= 0:
+        raise ValueError("n_tokens must be >= 0 and page_size > 0")
+    return -(-n_tokens // page_size)
+
+
+def pool_bytes(num_pages, kv_heads, page_size, head_dim, dtype_bytes=2):
+    """Bytes of one layer's K pool plus V pool ``[N][Hkv][P][D]`` each."""
+    return 2 * num_pages * kv_heads * page_size * head_dim * dtype_bytes
+
+
+# ---------------------------------------------------------------------------
+# paging
+# ---------------------------------------------------------------------------
+
+def token_slot(block_table_row, t, page_size):
+    """Physical (page, offset-in-page) of logical token ``t``.
+
+    The page table lookup of pgsm §3.2: logical page ``t // P`` is looked up in
+    the sequence's table; the token sits at ``t % P`` inside that page.
+    """
+    page = int(block_table_row[t // page_size])
+    return page, t % page_size
+
+
+def gather_sequence(pool, block_table_row, length, kv_head, page_size):
+    """Contiguous float64 ``[length][D]`` copy of one sequence's K (or V).
+
+    Token ``t`` is read from page ``block_table_row[t // P]`` at offset
+    ``t % P`` (``token_slot``), so the result is exactly the contiguous cache a
+    non-paged implementation would hold.
+    """
+    t = np.arange(length)
+    pages = np.asarray(block_table_row, dtype=np.int64)[t // page_size]
+    if length and (pages.min() < 0 or pages.max() >= pool.shape[0]):
+        raise IndexError("block table entry out of range")
+    return pool[pages, kv_head, t % page_size, :].astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# decode attention
+# ---------------------------------------------------------------------------
+
+def _scale64(scale):
+    # the scale reaches the library as a 32-bit float; widen that exact value
+    return float(np.float32(scale))
+
+
+def _check_heads(hq, hkv):
+    if hkv <= 0 or hq % hkv != 0:
+        raise ValueError("query heads must be a multiple of KV heads")
+    return hq // hkv
+
+
+def decode_attention(q, k_pool, v_pool, block_table, lens, scale, page_size):
+    """One decode step of attention for every sequence and query head.
+
+    For sequence ``b`` and query head ``h`` (KV head ``h // g``):
+    gather the ``lens[b]`` past keys/values through the page table, score
+    ``s_t = scale * <q, k_t>``, normalise with a softmax, and return the
+    softmax-weighted sum of the values (pgsm §4.2: a decode step reads all
+    past KV, scores them, normalises and takes the weighted sum).
+
+    ``lens[b] == 0`` yields a zero row (there is nothing to attend to).
+    Returns float64 ``[B][Hq][D]``.
+    """
+    b_count, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    g = _check_heads(hq, hkv)
+    s64 = _scale64(scale)
+    out = np.zeros((b_count, hq, d), dtype=np.float64)
+    for b in range(b_count):
+        n = int(lens[b])
+        if n == 0:
+            continue
+        for kvh in range(hkv):
+            keys = gather_sequence(k_pool, block_table[b], n, kvh, page_size)
+            vals = gather_sequence(v_pool, block_table[b], n, kvh, page_size)
+            for i in range(g):
+                h = kvh * g + i
+                qh = q[b, h].astype(np.float64)
+                s = s64 * (keys @ qh)
+                p = np.exp(s - s.max())
+                out[b, h] = (p @ vals) / p.sum()
+    return out
+
+
+def kv_append(k_pool, v_pool, k_new, v_new, block_table, pos, page_size):
+    """Return copies of the pools with each sequence's new token written.
+
+    Decode only appends the new token's K and V (one ``D``-vector per KV head
+    each) at position ``pos[b]`` and never rewrites older entries (pgsm §3.2 and
+    §4.3; hotelren §3.1 appends into preallocated storage instead of
+    reallocating). The write lands at the slot the page table gives for
+    ``pos[b]``.
+    """
+    k_out = k_pool.copy()
+    v_out = v_pool.copy()
+    b_count, hkv, _ = k_new.shape
+    for b in range(b_count):
+        page, off = token_slot(block_table[b], int(pos[b]), page_size)
+        for kvh in range(hkv):
+            k_out[page, kvh, off, :] = k_new[b, kvh, :]
+            v_out[page, kvh, off, :] = v_new[b, kvh, :]
+    return k_out, v_out
+
+
+# ---------------------------------------------------------------------------
+# split context
+# ---------------------------------------------------------------------------
+
+def decode_partials(q, k_pool, v_pool, block_table, lens, scale, page_size,
+                    partition_tokens):
+    """Per-partition softmax statistics for split-context decode.
+
+    The context of sequence ``b`` is cut into consecutive partitions of
+    ``partition_tokens`` tokens (the last may be shorter). For partition ``j``
+    and head ``h`` this returns the partition's score maximum ``m``, the sum
+    ``l = sum_t exp(s_t - m)`` and the unnormalised ``o = sum_t exp(s_t - m) v_t``.
+    The pages do not describe split context; this is the plain reading of the
+    standard log-sum-exp decomposition of a softmax.
+
+    Returns a list over ``b`` of tuples ``(m [Hq][n], l [Hq][n], o [Hq][n][D])``.
+    """
+    if partition_tokens <= 0:
+        raise ValueError("partition_tokens must be positive")
+    b_count, hq, d = q.shape
+    hkv = k_pool.shape[1]
+    g = _check_heads(hq, hkv)
+    s64 = _scale64(scale)
+    result = []
+    for b in range(b_count):
+        n = int(lens[b])
+        n_parts = pages_for_tokens(n, partition_tokens)
+        m = np.full((hq, n_parts), -np.inf)
+        l = np.zeros((hq, n_parts))
+        o = np.zeros((hq, n_parts, d))
+        for kvh in range(hkv):
+            keys = gather_sequence(k_pool, block_table[b], n, kvh, page_size)
+            vals = gather_sequence(v_pool, block_table[b], n, kvh, page_size)
+            for i in range(g):
+                h = kvh * g + i
+                s = s64 * (keys @ q[b, h].astype(np.float64))
+                for j in range(n_parts):
+                    lo, hi = j * partition_tokens, min(n, (j + 1) * partition_tokens)
+                    sj = s[lo:hi]
+                    mj = sj.max()
+                    pj = np.exp(sj - mj)
+                    m[h, j] = mj
+                    l[h, j] = pj.sum()
+                    o[h, j] = pj @ vals[lo:hi]
+        result.append((m, l, o))
+    return result
+
+
+def lse_merge(m, l, o):
+    """Merge per-partition statistics of one head into the softmax output.
+
+    With ``M = max_j m_j`` and weights ``w_j = exp(m_j - M)``:
+    ``out = sum_j w_j o_j / sum_j w_j l_j``. Exact rearrangement of the
+    softmax over the union of the partitions. Empty input gives zeros.
+    """
+    m = np.asarray(m, dtype=np.float64)
+    l = np.asarray(l, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
+    if m.size == 0:
+        return np.zeros(o.shape[-1])
+    big = m.max()
+    w = np.exp(m - big)
+    return (w @ o) / float(w @ l)
+
+
+def fp16_round(x):
+    """Round float64 values to the nearest fp16 (ties to even), back as float64."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16).astype(np.float64)
+
+
+def max_abs_error(a, b):
+    return float(np.max(np.abs(np.asarray(a, np.float64) - np.asarray(b, np.float64)))) if np.size(a) else 0.0
+
+
+def rms_error(a, b):
+    diff = np.asarray(a, np.float64) - np.asarray(b, np.float64)
+    return math.sqrt(float(np.mean(diff * diff))) if diff.size else 0.0

@@ -1,0 +1,116 @@
+"""Pins for the allocator reference model and the block-table checker.
+
+The model's policy (FIFO free list, all-or-nothing reserve, reference-counted
+shared prefixes) is a reading of the pages; these tests pin it to invariants
+that any correct page allocator must keep, to the page-count table the pages
+print, and to a brute-force re-count of ownership after random operation
+sequences.
+"""
+
+import numpy as np
+import pytest
+from hypothesis import given, settings, strategies as st
+
+import oracle
+from oracle import PageAllocatorModel, OutOfPages, validate_tables
+
+
+def test_reserve_takes_pages_in_free_order():
+    a = PageAllocatorModel(8, 16, free_order=[5, 2, 7, 0, 1, 3, 4, 6])
+    assert a.reserve(0, 33) == [5, 2, 7]           # ceil(33/16) = 3 pages
+    assert a.reserve(1, 16) == [0]
+    assert a.reserve(0, 48) == [5, 2, 7]           # already enough
+    assert a.reserve(0, 49) == [5, 2, 7, 1]
+    assert a.free_count() == 3
+
+
+def test_page_count_table_via_reserve():
+    # pgsm §4.1 table: a 2048-token request needs 128/64/32/16 pages
+    for P, pages in ((16, 128), (32, 64), (64, 32), (128, 16)):
+        a = PageAllocatorModel(200, P)
+        assert len(a.reserve(0, 2048)) == pages
+
+
+def test_reserve_is_all_or_nothing():
+    a = PageAllocatorModel(4, 16)
+    a.reserve(0, 40)                                 # 3 pages
+    before = (list(a.free_list), dict(a.tables), list(a.refcount))
+    with pytest.raises(OutOfPages):
+        a.reserve(1, 40)
+    with pytest.raises(OutOfPages):
+        a.reserve(0, 80)                             # needs 2 more, 1 free
+    assert (list(a.free_list), dict(a.tables), list(a.refcount)) == before
+
+
+def test_free_returns_pages_to_the_back():
+    a = PageAllocatorModel(4, 16, free_order=[3, 2, 1, 0])
+    a.reserve(0, 32)                                 # [3, 2]
+    a.reserve(1, 16)                                 # [1]
+    a.free(0)
+    assert list(a.free_list) == [0, 3, 2]
+    a.free(0)                                        # unknown: no-op
+    assert a.reserve(2, 48) == [0, 3, 2]
+
+
+def test_shared_prefix_refcounts():
+    a = PageAllocatorModel(10, 16)
+    prefix = a.reserve(100, 32)                      # owner of the prefix: pages [0, 1]
+    a.share_prefix(0, prefix)
+    a.share_prefix(1, prefix)
+    assert a.reserve(0, 40) == [0, 1, 2]
+    assert a.reserve(1, 33) == [0, 1, 3]
+    a.free(100)
+    a.free(0)
+    assert 0 not in a.free_list and 1 not in a.free_list
+    a.free(1)
+    assert set(a.free_list) == set(range(10))
+    with pytest.raises(ValueError):
+        a.share_prefix(5, [9])                        # not allocated
+
+
+OPS = st.lists(
+    st.tuples(st.sampled_from(["reserve", "free", "share"]), st.integers(0, 5), st.integers(0, 120)),
+    max_size=60)
+
+
+@settings(max_examples=200, deadline=None)
+@given(OPS, st.integers(1, 40), st.sampled_from([1, 4, 16]))
+def test_random_operation_sequences_keep_invariants(ops, n_pages, P):
+    a = PageAllocatorModel(n_pages, P, free_order=list(np.random.default_rng(n_pages).permutation(n_pages)))
+    for kind, seq, n in ops:
+        if kind == "reserve":
+            before = (list(a.free_list), {k: list(v) for k, v in a.tables.items()})
+            try:
+                row = a.reserve(seq, n)
+                assert len(row) >= oracle.pages_for_tokens(n, P)
+            except OutOfPages:
+                assert (list(a.free_list), {k: list(v) for k, v in a.tables.items()}) == before
+        elif kind == "free":
+            a.free(seq)
+        else:
+            donor = a.tables.get((seq + 1) % 6)
+            if donor and not a.tables.get(seq):
+                a.share_prefix(seq, donor[: max(1, len(donor) // 2)])
+        # brute-force recount of ownership
+        count = [0] * n_pages
+        for pages in a.tables.values():
+            assert len(set(pages)) == len(pages)
+            for p in pages:
+                count[p] += 1
+        assert count == a.refcount
+        assert sorted(list(a.free_list) + [p for p in range(n_pages) if count[p] > 0]) == list(range(n_pages))
+        assert all(count[p] == 0 for p in a.free_list)
+
+
+def test_validate_tables_detects_problems():
+    bt = np.array([[3, 1, -1], [0, 2, -1]], np.int32)
+    assert validate_tables(bt, [20, 17], 16, 4) == []
+    assert validate_tables(bt, [20, 40], 16, 4) == [("page_out_of_range", 1, 2)]
+    assert validate_tables(bt, [20, 49], 16, 4) == [("length_exceeds_table", 1, -1)]
+    assert validate_tables(bt, [-1, 3], 16, 4) == [("negative_length", 0, -1)]
+    assert validate_tables(np.array([[3, 3]], np.int32), [20], 16, 4) == [("duplicate_in_row", 0, 1)]
+    assert validate_tables(np.array([[9]], np.int32), [1], 16, 4) == [("page_out_of_range", 0, 0)]
+    shared = np.array([[0, 1], [0, 2]], np.int32)
+    assert validate_tables(shared, [20, 20], 16, 3, exclusive_tail=True) == []
+    assert validate_tables(shared, [16, 20], 16, 3, exclusive_tail=True) == [("shared_tail_page", 0, 0)]
+    assert validate_tables(shared, [16, 20], 16, 3) == []
