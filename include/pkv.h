@@ -1,0 +1,246 @@
+/*
+ * pkv.h -- C ABI of libpkv.so: paged KV-cache decode attention for gfx950.
+ *
+ * Sources (the three pages on LLM-inference optimisation this library
+ * follows; cited by key and section):
+ *   hotelren = www.hotelren.com/news/4669576
+ *   dpshk    = www.dpshk.com/news/5622214
+ *   pgsm     = www.pgsm.cn/news/396587
+ *              (LLM推理优化：从硬件瓶颈到KV Cache的工程实践)
+ *
+ * Data layout shared by every device entry point
+ * ----------------------------------------------
+ *   K pool, V pool : fp16 [N][Hkv][P][D], row-major. The P x D tile of one
+ *                    (page, KV head) is contiguous. A page holds P tokens of
+ *                    every KV head (hotelren §3.2 and pgsm §3.2 describe a page
+ *                    as tokens x heads x dims in fp16; the axis order is this
+ *                    library's choice).
+ *   block table    : int32 [B][max_pages], row-major. Entry j of row b is the
+ *                    physical page of logical tokens j*P .. j*P+P-1 of
+ *                    sequence b (the page table of pgsm §3.2 and §4.1).
+ *                    Unused entries may hold anything (the allocator writes -1).
+ *   token t of sequence b lives at page bt[b][t / P], row t % P of its tile.
+ *   query head h reads KV head h / (Hq / Hkv).
+ *
+ * Conventions
+ * -----------
+ *   - Every function returns a pkv_status (0 = PKV_OK). Nothing throws, aborts
+ *     or keeps global error state.
+ *   - Device pointers are caller-owned device memory. fp16 tensors must be
+ *     16-byte aligned; int32 tensors 4-byte aligned. Nothing is allocated,
+ *     freed or synchronised inside a device entry point: work is enqueued on
+ *     `stream` (a hipStream_t; NULL is the default stream) and the call returns.
+ *   - Argument checks run on the host before any launch; a failed check
+ *     launches nothing. PKV_ERR_HIP is returned only when a launch fails.
+ *   - Device-resident contents (block-table entries, lengths, positions) are
+ *     not validated per call, which would need a synchronisation. Kernels never
+ *     read or write outside the buffers described by the sizes passed in:
+ *     a page id outside [0, N) or a length beyond the table width /
+ *     max_context turns the affected output row into NaN, and an append whose
+ *     slot is out of range is skipped. pkv_validate_tables checks host copies.
+ *   - Supported: D in {64, 128}; P in {16, 32, 64, 128}; Hq / Hkv in
+ *     {1, 2, 4, 8}. Other values return PKV_ERR_UNSUPPORTED.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum pkv_status {
+  PKV_OK = 0,
+  PKV_ERR_INVALID_ARG = 1,          /* null/misaligned pointer, bad size or shape */
+  PKV_ERR_UNSUPPORTED = 2,          /* valid but not built: D, P or group size */
+  PKV_ERR_OUT_OF_PAGES = 3,         /* allocator cannot cover a reservation */
+  PKV_ERR_WORKSPACE_TOO_SMALL = 4,  /* split decode given too little workspace */
+  PKV_ERR_HIP = 5,                  /* a kernel launch failed */
+  PKV_ERR_INVALID_TABLE = 6         /* pkv_validate_tables found a bad entry */
+} pkv_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* pkv_status_string(int status);
+
+/* ABI version of this header: 1. */
+int pkv_abi_version(void);
+
+/* ------------------------------------------------------------------------ */
+/* Device entry points                                                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * pkv_kv_append -- write each sequence's new-token K and V into its page slot.
+ *
+ * Decode appends the new token's K and V (one D-vector per KV head each) to
+ * the cache and never recomputes older entries (pgsm §3.2 and §4.3); the write
+ * goes in place into preallocated storage instead of growing a tensor
+ * (hotelren §3.1, pgsm §4.3).
+ *
+ *   k_new, v_new : fp16 [B][Hkv][D] device, read.
+ *   k_pool, v_pool: fp16 [N][Hkv][P][D] device, written only at
+ *                  (bt[b][pos[b] / P], kvh, pos[b] % P, :) for every b, kvh.
+ *   block_table  : int32 [B][max_pages] device, read.
+ *   pos          : int32 [B] device: position of the new token (the length
+ *                  of the context before the append).
+ * The copy is bit-exact. A position outside [0, max_pages * P) or a page id
+ * outside [0, N) skips that sequence. B == 0 is a no-op.
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED, PKV_ERR_HIP.
+ */
+int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                  const int32_t* block_table, int32_t max_pages, const int32_t* pos,
+                  int32_t B, int32_t Hkv, int32_t D, int32_t P, int32_t N, void* stream);
+
+/*
+ * pkv_decode_workspace_bytes -- workspace size split-context decode needs.
+ *
+ * With partition_tokens > 0 the context of every sequence is cut into
+ * partitions of that many tokens and each partition's softmax statistics go
+ * to the workspace: per (b, query head, partition) a float max, a float sum
+ * and D floats of unnormalised output, ceil(max_context / partition_tokens)
+ * partitions per sequence. partition_tokens == 0 needs no workspace (*bytes
+ * = 0). Errors: PKV_ERR_INVALID_ARG (negative sizes, partition_tokens not a
+ * multiple of 16, null `bytes`).
+ */
+int pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context,
+                               int32_t partition_tokens, size_t* bytes);
+
+/*
+ * pkv_paged_decode_attention -- single-token decode attention through the
+ * page table.
+ *
+ * For every sequence b and query head h: read the lens[b] cached keys and
+ * values of KV head h / (Hq / Hkv) through the block table, score
+ * s_t = scale * <q[b][h], k_t>, softmax over t, and write the weighted sum of
+ * the values (pgsm §4.2 describes exactly these four steps of a decode step:
+ * read all past KV, score, normalise, weighted sum). Accumulation is fp32
+ * (dpshk §3.3 keeps high-precision accumulation on the critical path); the
+ * result is rounded to fp16 (round to nearest even).
+ *
+ *   out          : fp16 [B][Hq][D] device, written.
+ *   q            : fp16 [B][Hq][D] device, read.
+ *   k_pool/v_pool: fp16 [N][Hkv][P][D] device, read.
+ *   block_table  : int32 [B][max_pages] device, read.
+ *   lens         : int32 [B] device: tokens to attend (the new token
+ *                  included). lens[b] == 0 writes a zero row.
+ *   max_context  : host upper bound on every lens[b]; sizes the launch and
+ *                  the workspace; must be <= max_pages * P.
+ *   scale        : softmax scale, normally 1/sqrt(D).
+ *   partition_tokens: 0 = one workgroup per (sequence, KV head) over the whole
+ *                  context; otherwise a positive multiple of 16: the context is
+ *                  split into partitions of that many tokens, processed in
+ *                  parallel, then merged by a log-sum-exp reduction kernel.
+ *   workspace    : device buffer of at least pkv_decode_workspace_bytes bytes
+ *                  (ignored when partition_tokens == 0), 256-byte aligned.
+ * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED,
+ * PKV_ERR_WORKSPACE_TOO_SMALL, PKV_ERR_HIP.
+ */
+int pkv_paged_decode_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
+                               const int32_t* block_table, int32_t max_pages, const int32_t* lens,
+                               int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                               int32_t max_context, float scale, int32_t partition_tokens,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_append_paged_decode_attention -- append then attend, in one launch.
+ *
+ * Same result as pkv_kv_append(k_new, v_new, ..., pos = lens - 1) followed by
+ * pkv_paged_decode_attention(...): the new token is part of the context it
+ * attends to (hotelren §3.1: write the new K/V at the end, then attend). The
+ * workgroup that owns the last partition of (b, KV head) writes the new K/V
+ * into the pool and uses them from registers, saving a launch per step.
+ * lens[b] >= 1 is the context after the append; lens[b] == 0 writes a zero
+ * row and appends nothing. Arguments as in the two calls above.
+ */
+int pkv_append_paged_decode_attention(void* out, const void* q, const void* k_new, const void* v_new,
+                                      void* k_pool, void* v_pool, const int32_t* block_table,
+                                      int32_t max_pages, const int32_t* lens, int32_t B, int32_t Hq,
+                                      int32_t Hkv, int32_t D, int32_t P, int32_t N, int32_t max_context,
+                                      float scale, int32_t partition_tokens, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host page allocator (CPU only; no device calls)                           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * A pool of N fixed-size pages handed to sequences on demand (dpshk §4.2:
+ * allocate in fixed blocks, give pages back as soon as a request ends or
+ * fails; shared system-prompt prefixes are stored once). Policy:
+ *   - the free list is FIFO: pages leave from the front, in `free_order`
+ *     (NULL = 0, 1, ..., N-1), and return to the back;
+ *   - reservations are all-or-nothing: on failure nothing changes;
+ *   - shared pages are reference counted; a page returns to the free list
+ *     when its count reaches zero.
+ * Sequence ids are caller-chosen non-negative int32. One allocator may be used
+ * from several threads (calls are serialised internally).
+ */
+typedef struct pkv_allocator pkv_allocator;
+
+/* Create an allocator over num_pages pages of page_size tokens.
+ * free_order: NULL or a permutation of [0, num_pages) (host, copied).
+ * Errors: PKV_ERR_INVALID_ARG (bad sizes, not a permutation, null out). */
+int pkv_alloc_create(int32_t num_pages, int32_t page_size, const int32_t* free_order,
+                     pkv_allocator** out);
+
+/* Destroy an allocator (NULL is a no-op). */
+void pkv_alloc_destroy(pkv_allocator* alloc);
+
+/* Grow sequence `seq` to hold at least n_tokens tokens (ceil(n_tokens / P)
+ * pages), taking new pages from the free list. On success, if bt_row is not
+ * NULL, writes the sequence's whole table into bt_row[0 .. max_pages) (-1
+ * past the end) and, if n_pages is not NULL, its page count.
+ * Errors: PKV_ERR_INVALID_ARG (negative seq/n_tokens, table wider than
+ * max_pages), PKV_ERR_OUT_OF_PAGES. On error nothing changes. */
+int pkv_alloc_reserve(pkv_allocator* alloc, int32_t seq, int32_t n_tokens, int32_t* bt_row,
+                      int32_t max_pages, int32_t* n_pages);
+
+/* Reserve for B sequences at once, all-or-nothing over the whole batch:
+ * seqs[i] grows to n_tokens[i] tokens; block_table [B][max_pages] (host) gets
+ * every row. Used once per decode step to add a page to the sequences whose
+ * next token starts one. Errors as pkv_alloc_reserve. */
+int pkv_alloc_reserve_batch(pkv_allocator* alloc, int32_t B, const int32_t* seqs,
+                            const int32_t* n_tokens, int32_t* block_table, int32_t max_pages);
+
+/* Start the (empty) sequence `seq` with n already-allocated pages (their
+ * reference counts go up by one), e.g. a shared system-prompt prefix.
+ * Errors: PKV_ERR_INVALID_ARG (seq not empty, page not allocated, duplicate). */
+int pkv_alloc_share_prefix(pkv_allocator* alloc, int32_t seq, const int32_t* pages, int32_t n);
+
+/* Release all pages of `seq` in table order (reference count - 1; back to the
+ * free list at zero). Unknown sequences are a no-op. Call it on completion
+ * and on failure of a request alike. */
+int pkv_alloc_free(pkv_allocator* alloc, int32_t seq);
+
+/* Pages currently free (-1 if alloc is NULL). */
+int32_t pkv_alloc_free_count(const pkv_allocator* alloc);
+
+/* Copy `seq`'s table into bt_row[0 .. max_pages) (-1 padded) and its page
+ * count into *n_pages (0 for an unknown sequence). */
+int pkv_alloc_table(const pkv_allocator* alloc, int32_t seq, int32_t* bt_row, int32_t max_pages,
+                    int32_t* n_pages);
+
+/* Reference count of `page` into *count. */
+int pkv_alloc_refcount(const pkv_allocator* alloc, int32_t page, int32_t* count);
+
+/*
+ * pkv_validate_tables -- check host copies of a block table and lengths.
+ * Rules: lens[b] >= 0; ceil(lens[b] / P) <= max_pages; every entry a token
+ * reaches is in [0, N); no page twice within a row; with exclusive_tail != 0
+ * the page of each sequence's last token (where an append writes) appears in
+ * no other row. Returns PKV_OK or PKV_ERR_INVALID_TABLE with the first
+ * offending row and entry in *bad_row / *bad_entry (entry -1 for a length
+ * problem) and the rule number (1..5, in the order above) in *rule.
+ * Errors: PKV_ERR_INVALID_ARG for null pointers or bad sizes.
+ */
+int pkv_validate_tables(const int32_t* block_table, const int32_t* lens, int32_t B, int32_t max_pages,
+                        int32_t P, int32_t N, int32_t exclusive_tail, int32_t* bad_row,
+                        int32_t* bad_entry, int32_t* rule);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

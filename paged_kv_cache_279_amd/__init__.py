@@ -1,0 +1,25 @@
+"""Paged KV-cache single-token decode attention for AMD MI355X (gfx950).
+
+The kernels and the page allocator live in ``libpkv.so`` (C ABI, ``include/pkv.h``);
+this package is its Python binding. Build it with
+``python -m paged_kv_cache_279_amd.build``.
+"""
+
+from .binding import (  # noqa: F401
+    PKV_OK,
+    PKV_ERR_INVALID_ARG,
+    PKV_ERR_UNSUPPORTED,
+    PKV_ERR_OUT_OF_PAGES,
+    PKV_ERR_WORKSPACE_TOO_SMALL,
+    PKV_ERR_HIP,
+    PKV_ERR_INVALID_TABLE,
+    PkvError,
+    PageAllocator,
+    append_paged_decode_attention,
+    decode_workspace_bytes,
+    kv_append,
+    lib,
+    paged_decode_attention,
+    status_string,
+    validate_tables,
+)

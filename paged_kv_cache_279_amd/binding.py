@@ -1,0 +1,273 @@
+"""ctypes binding over libpkv.so: argument marshalling only.
+
+Every function mirrors the C entry point of the same name in ``include/pkv.h``
+(without the ``pkv_`` prefix). Tensors are torch tensors: device tensors for
+the device entry points, host int32 arrays (numpy or torch) for the allocator.
+torch is used for device memory and streams; all arithmetic of the decode path
+runs in the library's HIP kernels. There is no fallback: if ``libpkv.so`` is
+missing or fails to load, every call raises.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+import torch  # loaded before libpkv.so so both share torch's HIP runtime
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_OK = 0
+PKV_ERR_INVALID_ARG = 1
+PKV_ERR_UNSUPPORTED = 2
+PKV_ERR_OUT_OF_PAGES = 3
+PKV_ERR_WORKSPACE_TOO_SMALL = 4
+PKV_ERR_HIP = 5
+PKV_ERR_INVALID_TABLE = 6
+
+_i32 = ctypes.c_int32
+_vp = ctypes.c_void_p
+_ip = ctypes.POINTER(ctypes.c_int32)
+
+_SIGNATURES = {
+    "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pkv_abi_version": (ctypes.c_int, []),
+    "pkv_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_decode_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
+    "pkv_paged_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                  _i32, _i32, ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]),
+    "pkv_append_paged_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                                         _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _vp,
+                                                         ctypes.c_size_t, _vp]),
+    "pkv_alloc_create": (ctypes.c_int, [_i32, _i32, _ip, ctypes.POINTER(_vp)]),
+    "pkv_alloc_destroy": (None, [_vp]),
+    "pkv_alloc_reserve": (ctypes.c_int, [_vp, _i32, _i32, _ip, _i32, _ip]),
+    "pkv_alloc_reserve_batch": (ctypes.c_int, [_vp, _i32, _ip, _ip, _ip, _i32]),
+    "pkv_alloc_share_prefix": (ctypes.c_int, [_vp, _i32, _ip, _i32]),
+    "pkv_alloc_free": (ctypes.c_int, [_vp, _i32]),
+    "pkv_alloc_free_count": (ctypes.c_int32, [_vp]),
+    "pkv_alloc_table": (ctypes.c_int, [_vp, _i32, _ip, _i32, _ip]),
+    "pkv_alloc_refcount": (ctypes.c_int, [_vp, _i32, _ip]),
+    "pkv_validate_tables": (ctypes.c_int, [_ip, _ip, _i32, _i32, _i32, _i32, _i32, _ip, _ip, _ip]),
+}
+
+_LIB = None
+
+
+class PkvError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s" % (where, status_string(status)))
+
+
+def lib():
+    """Load libpkv.so once; raise if it is not built."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libpkv.so is not built; run `python -m paged_kv_cache_279_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = handle
+    return _LIB
+
+
+def status_string(status):
+    return lib().pkv_status_string(int(status)).decode()
+
+
+def _check(status, where):
+    if status != PKV_OK:
+        raise PkvError(status, where)
+
+
+def _dev_ptr(t, dtype, name, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch tensor" % name)
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError("%s must have %d dims, got %d" % (name, ndim, t.dim()))
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+# ---------------------------------------------------------------------------
+# device entry points
+# ---------------------------------------------------------------------------
+
+def kv_append(k_new, v_new, k_pool, v_pool, block_table, pos, stream=None):
+    """pkv_kv_append: write k_new/v_new [B][Hkv][D] at slot pos[b] of each sequence."""
+    N, Hkv, P, D = k_pool.shape
+    B, max_pages = block_table.shape
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D) or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("shape mismatch")
+    if tuple(pos.shape) != (B,):
+        raise ValueError("pos must be [B]")
+    rc = lib().pkv_kv_append(_dev_ptr(k_new, torch.float16, "k_new"), _dev_ptr(v_new, torch.float16, "v_new"),
+                             _dev_ptr(k_pool, torch.float16, "k_pool"), _dev_ptr(v_pool, torch.float16, "v_pool"),
+                             _dev_ptr(block_table, torch.int32, "block_table"), max_pages,
+                             _dev_ptr(pos, torch.int32, "pos"), B, Hkv, D, P, N, _stream(stream))
+    _check(rc, "pkv_kv_append")
+
+
+def decode_workspace_bytes(B, Hq, D, max_context, partition_tokens):
+    """pkv_decode_workspace_bytes."""
+    out = ctypes.c_size_t(0)
+    _check(lib().pkv_decode_workspace_bytes(B, Hq, D, max_context, partition_tokens, ctypes.byref(out)),
+           "pkv_decode_workspace_bytes")
+    return out.value
+
+
+def _decode_args(out, q, k_pool, v_pool, block_table, lens, max_context, partition_tokens, workspace):
+    N, Hkv, P, D = k_pool.shape
+    B, Hq, Dq = q.shape
+    _, max_pages = block_table.shape
+    if Dq != D or tuple(v_pool.shape) != tuple(k_pool.shape) or block_table.shape[0] != B or tuple(lens.shape) != (B,):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B][Hq][D]")
+    ws_bytes = decode_workspace_bytes(B, Hq, D, max_context, partition_tokens)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    return out, (N, Hkv, P, D, B, Hq, max_pages), ws_ptr, ws_len
+
+
+def paged_decode_attention(q, k_pool, v_pool, block_table, lens, max_context, scale, partition_tokens=0,
+                           out=None, workspace=None, stream=None):
+    """pkv_paged_decode_attention; returns ``out`` (fp16 [B][Hq][D])."""
+    out, (N, Hkv, P, D, B, Hq, max_pages), ws_ptr, ws_len = _decode_args(
+        out, q, k_pool, v_pool, block_table, lens, max_context, partition_tokens, workspace)
+    rc = lib().pkv_paged_decode_attention(
+        _dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"),
+        _dev_ptr(k_pool, torch.float16, "k_pool"), _dev_ptr(v_pool, torch.float16, "v_pool"),
+        _dev_ptr(block_table, torch.int32, "block_table"), max_pages, _dev_ptr(lens, torch.int32, "lens"),
+        B, Hq, Hkv, D, P, N, int(max_context), float(scale), int(partition_tokens), ws_ptr, ws_len, _stream(stream))
+    _check(rc, "pkv_paged_decode_attention")
+    return out
+
+
+def append_paged_decode_attention(q, k_new, v_new, k_pool, v_pool, block_table, lens, max_context, scale,
+                                  partition_tokens=0, out=None, workspace=None, stream=None):
+    """pkv_append_paged_decode_attention: append at lens-1, then attend; returns ``out``."""
+    out, (N, Hkv, P, D, B, Hq, max_pages), ws_ptr, ws_len = _decode_args(
+        out, q, k_pool, v_pool, block_table, lens, max_context, partition_tokens, workspace)
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new/v_new must be [B][Hkv][D]")
+    rc = lib().pkv_append_paged_decode_attention(
+        _dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"),
+        _dev_ptr(k_new, torch.float16, "k_new"), _dev_ptr(v_new, torch.float16, "v_new"),
+        _dev_ptr(k_pool, torch.float16, "k_pool"), _dev_ptr(v_pool, torch.float16, "v_pool"),
+        _dev_ptr(block_table, torch.int32, "block_table"), max_pages, _dev_ptr(lens, torch.int32, "lens"),
+        B, Hq, Hkv, D, P, N, int(max_context), float(scale), int(partition_tokens), ws_ptr, ws_len, _stream(stream))
+    _check(rc, "pkv_append_paged_decode_attention")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# host allocator
+# ---------------------------------------------------------------------------
+
+def _host_i32(a, name):
+    arr = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    return arr, arr.ctypes.data_as(_ip)
+
+
+class PageAllocator:
+    """Host page allocator (pkv_alloc_*): FIFO free list, all-or-nothing
+    reservations, reference-counted shared prefixes."""
+
+    def __init__(self, num_pages, page_size, free_order=None):
+        self._h = ctypes.c_void_p(0)
+        if free_order is None:
+            rc = lib().pkv_alloc_create(num_pages, page_size, None, ctypes.byref(self._h))
+        else:
+            arr, ptr = _host_i32(free_order, "free_order")
+            if arr.shape != (num_pages,):
+                raise ValueError("free_order must have num_pages entries")
+            rc = lib().pkv_alloc_create(num_pages, page_size, ptr, ctypes.byref(self._h))
+        _check(rc, "pkv_alloc_create")
+        self.num_pages = num_pages
+        self.page_size = page_size
+
+    def close(self):
+        if self._h:
+            lib().pkv_alloc_destroy(self._h)
+            self._h = ctypes.c_void_p(0)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def reserve(self, seq, n_tokens, max_pages=None):
+        """Grow ``seq`` to ``n_tokens`` tokens; returns its table (list of page ids)."""
+        width = max_pages if max_pages is not None else max(1, -(-n_tokens // self.page_size) + 1)
+        row = np.full(width, -1, np.int32)
+        n = ctypes.c_int32(0)
+        _check(lib().pkv_alloc_reserve(self._h, seq, n_tokens, row.ctypes.data_as(_ip), width, ctypes.byref(n)),
+               "pkv_alloc_reserve")
+        if max_pages is None:
+            return self.table(seq)
+        return row[:n.value].tolist()
+
+    def reserve_batch(self, seqs, n_tokens, block_table):
+        """All-or-nothing reservation for a batch; fills ``block_table`` [B][max_pages] (int32 numpy)."""
+        s, sp = _host_i32(seqs, "seqs")
+        t, tp = _host_i32(n_tokens, "n_tokens")
+        if block_table.dtype != np.int32 or not block_table.flags.c_contiguous:
+            raise ValueError("block_table must be a C-contiguous int32 array")
+        _check(lib().pkv_alloc_reserve_batch(self._h, len(s), sp, tp, block_table.ctypes.data_as(_ip),
+                                             block_table.shape[1]), "pkv_alloc_reserve_batch")
+        return block_table
+
+    def share_prefix(self, seq, pages):
+        arr, ptr = _host_i32(pages, "pages")
+        _check(lib().pkv_alloc_share_prefix(self._h, seq, ptr, len(arr)), "pkv_alloc_share_prefix")
+
+    def free(self, seq):
+        _check(lib().pkv_alloc_free(self._h, seq), "pkv_alloc_free")
+
+    def free_count(self):
+        return int(lib().pkv_alloc_free_count(self._h))
+
+    def table(self, seq):
+        n = ctypes.c_int32(0)
+        _check(lib().pkv_alloc_table(self._h, seq, None, 0, ctypes.byref(n)), "pkv_alloc_table")
+        row = np.full(max(1, n.value), -1, np.int32)
+        _check(lib().pkv_alloc_table(self._h, seq, row.ctypes.data_as(_ip), len(row), ctypes.byref(n)),
+               "pkv_alloc_table")
+        return row[:n.value].tolist()
+
+    def refcount(self, page):
+        c = ctypes.c_int32(0)
+        _check(lib().pkv_alloc_refcount(self._h, page, ctypes.byref(c)), "pkv_alloc_refcount")
+        return c.value
+
+
+def validate_tables(block_table, lens, page_size, num_pages, exclusive_tail=False):
+    """pkv_validate_tables on host copies; returns ``(status, row, entry, rule)``."""
+    bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+    ln, lp = _host_i32(lens, "lens")
+    row, entry, rule = ctypes.c_int32(-1), ctypes.c_int32(-1), ctypes.c_int32(0)
+    rc = lib().pkv_validate_tables(bt.ctypes.data_as(_ip), lp, bt.shape[0], bt.shape[1], page_size, num_pages,
+                                   1 if exclusive_tail else 0, ctypes.byref(row), ctypes.byref(entry),
+                                   ctypes.byref(rule))
+    return rc, row.value, entry.value, rule.value
