@@ -1,0 +1,362 @@
+"""Benchmark: paged-KV decode steps on one MI355X.
+
+One timed step is one decode step of the whole batch through ``--layers``
+attention layers (distinct K/V pools per layer, one block table shared by all
+layers, as a model's layers share page ids):
+
+  host   : the page allocator grows every sequence by one token
+           (pkv_alloc_reserve_batch); when a sequence starts a new page, the
+           block table is copied to the device (async, pinned);
+  device : per layer, append the new token's K/V and run paged decode
+           attention (fused append + partition kernel + log-sum-exp reduce,
+           or separate append with ``--separate-append``).
+
+Positions advance every step, so the context grows and sequences cross page
+boundaries as they do in serving. Inputs are seeded synthetic data
+(``workloads``): layer 0 is the workload as drawn, the other layers get their
+own random pools drawn on the device. The first step of layer 0 is checked
+against the fp64 oracle on sampled sequences.
+
+Output: one JSON line on stdout (rank 0, N = 1).
+"""
+
+import argparse
+import json
+import math
+import os
+import platform
+import subprocess
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E, published
+
+
+def parse_args():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=3, help="workload number (3 = Llama-3-8B GQA, shared prefix)")
+    ap.add_argument("--page-size", type=int, default=None, help="page size (workload 5 only)")
+    ap.add_argument("--layers", type=int, default=8, help="distinct layer pools per step (working set >> 256 MB MALL)")
+    ap.add_argument("--partition", type=int, default=None, help="partition tokens (0 = unsplit)")
+    ap.add_argument("--separate-append", action="store_true", help="kv_append launch + decode instead of fused")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
+    ap.add_argument("--check-sequences", type=int, default=8)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device-to-device copy of this many MiB (3 times) so HBM counters can be "
+                         "scaled against a kernel of known traffic")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def git_sha():
+    try:
+        return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
+                              text=True).stdout.strip() or None
+    except Exception:
+        return None
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return platform.processor() or None
+
+
+def algorithmic_bytes(lens, B, Hq, Hkv, D, P, shared_tokens):
+    """Unique bytes one layer-step must move: every attended K/V byte once
+    (shared-prefix tokens once for the whole batch), q in, out, new K/V in and
+    written, the block-table entries and lengths."""
+    lens = np.asarray(lens, dtype=np.int64)
+    kv_tokens = int(lens.sum()) - shared_tokens * (len(lens) - 1)
+    kv = kv_tokens * Hkv * D * 2 * 2
+    q_out = 2 * B * Hq * D * 2
+    new_kv = 2 * 2 * B * Hkv * D * 2          # read k_new/v_new, write them to the pool
+    table = int(sum(-(-int(n) // P) for n in lens)) * 4 + B * 4
+    return kv + q_out + new_kv + table, kv
+
+
+def cpu_baseline(w, seconds):
+    """Time the oracle (as it stands) on layer 0 of the workload: append then
+    decode for every sequence, repeated until ``seconds`` have passed."""
+    import oracle
+    from threadpoolctl import threadpool_limits
+    step = 0
+    lens = w.lens(step)
+    passes = 0
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        while True:
+            kp, vp = oracle.kv_append(w.k_pool, w.v_pool, w.k_new[step], w.v_new[step], w.block_table,
+                                      w.pos(step), w.P)
+            oracle.decode_attention(w.q, kp, vp, w.block_table, lens, w.scale, w.P)
+            passes += 1
+            if time.perf_counter() - t0 >= seconds:
+                break
+        dt = time.perf_counter() - t0
+    return {
+        "value": passes * w.B / dt,
+        "unit": "tokens/s",
+        "cores": 1,
+        "kind": "oracle",
+        "sample": "%d pass(es) of append + decode over layer 0 of workload '%s' (%d sequences, %d cached tokens), "
+                  "numpy fp64, one thread; %.1f s" % (passes, w.name, w.B, int(lens.sum()), dt),
+        "cpu_model": cpu_model(),
+        "host_cores_available": len(os.sched_getaffinity(0)),
+        "numpy": np.__version__,
+    }
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import oracle
+    import paged_kv_cache_279_amd as pkv
+    from workloads import workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    pkv.lib()
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+
+    w = workload(args.workload, page_size=args.page_size)
+    B, Hq, Hkv, D, P = w.B, w.Hq, w.Hkv, w.D, w.P
+    part = w.partition_tokens if args.partition is None else args.partition
+    R = args.layers
+    total_steps = args.warmup + args.steps
+    fused = not args.separate_append
+    if w.steps == 0:
+        raise SystemExit("workload %d has no append; pick 2-5" % args.workload)
+    log("workload %s: B=%d Hq=%d Hkv=%d D=%d P=%d part=%d layers=%d fused=%s" % (w.name, B, Hq, Hkv, D, P, part, R,
+                                                                                  fused))
+
+    # ---- a1: page allocator (host). Pages for every step are drawn on demand.
+    prefix_pages = w.shared_prefix_pages
+    final_ctx = w.context.astype(np.int64) + max(total_steps, w.steps)   # tokens after the last step
+    need = prefix_pages + sum(-(-int(n) // P) - prefix_pages for n in final_ctx)
+    N = max(need, w.N)
+    free_order = np.concatenate([w.perm, np.arange(w.N, N, dtype=np.int32)]).astype(np.int32)
+    max_pages = max(-(-int(n) // P) for n in final_ctx)
+    alloc = pkv.PageAllocator(N, P, free_order=free_order)
+    seqs = np.arange(B, dtype=np.int32)
+    if prefix_pages:
+        owner = B
+        alloc.reserve(owner, prefix_pages * P)
+        for b in range(B):
+            alloc.share_prefix(b, alloc.table(owner))
+    bt_host = torch.full((B, max_pages), -1, dtype=torch.int32).pin_memory()
+    bt_np = bt_host.numpy()
+    # the workload reserves pages for all of its own steps up front (page-sweep: 64 steps)
+    alloc.reserve_batch(seqs, w.context + w.steps, bt_np)
+    assert np.array_equal(bt_np[:, :w.max_pages], w.block_table), "allocator layout differs from the workload"
+
+    # ---- device buffers
+    def put(a):
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1000 + args.workload)
+    k_pools, v_pools = [], []
+    for layer in range(R):
+        kp = torch.empty((N, Hkv, P, D), dtype=torch.float16, device=dev)
+        vp = torch.empty((N, Hkv, P, D), dtype=torch.float16, device=dev)
+        if layer == 0:
+            kp[:w.N].copy_(put(w.k_pool))
+            vp[:w.N].copy_(put(w.v_pool))
+            if N > w.N:
+                kp[w.N:].normal_(generator=gen)
+                vp[w.N:].normal_(generator=gen)
+        else:
+            kp.normal_(generator=gen)
+            vp.normal_(generator=gen)
+        k_pools.append(kp)
+        v_pools.append(vp)
+    q = put(w.q)
+    knew = torch.empty((total_steps, B, Hkv, D), dtype=torch.float16, device=dev)
+    vnew = torch.empty_like(knew)
+    knew.normal_(generator=gen)
+    vnew.normal_(generator=gen)
+    knew[0].copy_(put(w.k_new[0]))
+    vnew[0].copy_(put(w.v_new[0]))
+    bt_dev = torch.empty((B, max_pages), dtype=torch.int32, device=dev)
+    bt_dev.copy_(bt_host)
+    lens_all = torch.from_numpy((w.context[None, :] + 1 + np.arange(total_steps)[:, None]).astype(np.int32)).to(dev)
+    pos_all = lens_all - 1
+    max_context = int(final_ctx.max())
+    ws_bytes = pkv.decode_workspace_bytes(B, Hq, D, max_context, part)
+    workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
+    torch.cuda.synchronize()
+    mem_gb = (2 * R * N * Hkv * P * D * 2) / 1e9
+    log("pools: N=%d pages/layer, %.2f GB over %d layers" % (N, mem_gb, R))
+
+    scale = w.scale
+
+    def layer_step(step, layer):
+        if fused:
+            pkv.append_paged_decode_attention(q, knew[step], vnew[step], k_pools[layer], v_pools[layer], bt_dev,
+                                              lens_all[step], max_context, scale, part, out=out,
+                                              workspace=workspace, stream=stream)
+        else:
+            pkv.kv_append(knew[step], vnew[step], k_pools[layer], v_pools[layer], bt_dev, pos_all[step],
+                          stream=stream)
+            pkv.paged_decode_attention(q, k_pools[layer], v_pools[layer], bt_dev, lens_all[step], max_context,
+                                       scale, part, out=out, workspace=workspace, stream=stream)
+
+    last_bt = bt_np.copy()
+
+    def host_step(step):
+        # a1: grow every sequence to hold this step's token; upload the table if it changed
+        nonlocal last_bt
+        alloc.reserve_batch(seqs, w.context + step + 1, bt_np)
+        if not np.array_equal(bt_np, last_bt):
+            bt_dev.copy_(bt_host, non_blocking=True)
+            last_bt = bt_np.copy()
+
+    # ---- parity check: step 0, layer 0, sampled sequences, against the oracle
+    host_step(0)
+    layer_step(0, 0)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy().astype(np.float64)
+    sample = np.linspace(0, B - 1, min(B, args.check_sequences)).astype(int)
+    kp0, vp0 = oracle.kv_append(w.k_pool, w.v_pool, w.k_new[0], w.v_new[0], w.block_table, w.pos(0), P)
+    ref = oracle.decode_attention(w.q[sample], kp0, vp0, w.block_table[sample], w.lens(0)[sample], scale, P)
+    max_err = float(np.abs(got[sample] - ref).max())
+    log("parity (layer 0, step 0, %d sequences): max_abs_err=%.3e" % (len(sample), max_err))
+    if not max_err <= 4e-3:
+        raise SystemExit("parity check failed: %.3e" % max_err)
+    # the check ran step 0 on layer 0 already; restore its pools so every layer starts alike
+    k_pools[0][:w.N].copy_(put(w.k_pool))
+    v_pools[0][:w.N].copy_(put(w.v_pool))
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of %d MiB (read %d B + write %d B each)" % (args.copy_calibration_mib, n, n))
+        del src, dst
+
+    # ---- warmup
+    for step in range(args.warmup):
+        host_step(step)
+        for layer in range(R):
+            layer_step(step, layer)
+    torch.cuda.synchronize()
+
+    # ---- timed: HIP events on the launch stream around every decode call
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps * R)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step = args.warmup + i
+        host_step(step)
+        for layer in range(R):
+            e0, e1 = ev[i * R + layer]
+            e0.record(stream)
+            layer_step(step, layer)
+            e1.record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms_per_step = total_ms / args.steps
+    ms_per_layer = ms_per_step / R
+
+    # algorithmic bytes of the timed steps (lengths grow by one per step)
+    bytes_steps = []
+    kv_steps = []
+    for i in range(args.steps):
+        step = args.warmup + i
+        tot, kv = algorithmic_bytes(w.context + step + 1, B, Hq, Hkv, D, P, prefix_pages * P)
+        bytes_steps.append(tot)
+        kv_steps.append(kv)
+    bytes_per_call = float(np.mean(bytes_steps))
+    kv_per_call = float(np.mean(kv_steps))
+    call_avg_s = float(call_ms.mean()) / 1e3
+    achieved = bytes_per_call / call_avg_s / 1e9
+    tokens_per_s = B / (ms_per_layer / 1e3)
+
+    result = {
+        "metric": "decode tokens/s and effective KV-read HBM GB/s (% of peak), GQA 32/8, d=128",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": P,
+            "kv_dtype": "f16", "accumulate": "f32",
+            "mean_context": float(np.mean(w.context + args.warmup + 1 + (args.steps - 1) / 2)),
+            "shared_prefix_tokens": prefix_pages * P,
+            "partition_tokens": part,
+            "layers_per_step": R,
+            "append": "fused" if fused else "separate",
+            "tokens_per_s_definition": "batch / (time of one attention layer-step: append + decode), "
+                                       "i.e. sequences advanced per second through one layer",
+            "tokens_per_s_32_layers": round(tokens_per_s / 32, 1),
+            "ms_per_layer_step": round(ms_per_layer, 5),
+            "kv_gbps": round(kv_per_call / (ms_per_layer / 1e3) / 1e9, 1),
+            "kv_frac_of_peak": round(kv_per_call / (ms_per_layer / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
+            "parity_max_abs_err": max_err,
+            "working_set_gb": round(mem_gb, 2),
+            "wall_s": round(wall, 3),
+            "git": git_sha(),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "paged decode call (partition kernel%s + log-sum-exp reduce)" % (" with fused append" if fused else ""),
+            "achieved": round(achieved, 1),
+            "peak": PEAK_HBM_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBPS, 4),
+            "traffic": None,
+            "bytes_per_launch": round(bytes_per_call),
+            "avg_launch_us": round(call_avg_s * 1e6, 3),
+        },
+    }
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (>= %.0f s)" % args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -10,16 +10,24 @@
  *
  * Data layout shared by every device entry point
  * ----------------------------------------------
- *   K pool, V pool : fp16 [N][Hkv][P][D], row-major. The P x D tile of one
- *                    (page, KV head) is contiguous. A page holds P tokens of
- *                    every KV head (hotelren §3.2 and pgsm §3.2 describe a page
- *                    as tokens x heads x dims in fp16; the axis order is this
- *                    library's choice).
+ *   K pool, V pool : fp16, N pages x Hkv KV heads x one tile of P*D halves;
+ *                    the tile of (page, KV head) is contiguous. A page holds P
+ *                    tokens of every KV head (hotelren §3.2 and pgsm §3.2
+ *                    describe a page as tokens x heads x dims in fp16; the
+ *                    order inside a tile is this library's choice). A tile is
+ *                    P/16 sub-blocks of 16 tokens (16*D halves each); token
+ *                    u = t % 16 of sub-block t / 16, dim d, sits at
+ *                      K: ((d / 8) * 16 + u) * 8 + d % 8
+ *                      V: (((d / 32) * 4 + u / 4) * 16 + d % 16) * 8
+ *                         + ((d / 16) % 2) * 4 + u % 4
+ *                    inside its sub-block, so that consecutive 16-byte runs are
+ *                    the matrix-core operands of the decode kernel. Use
+ *                    pkv_kv_append (or the same formulas) to write tokens.
  *   block table    : int32 [B][max_pages], row-major. Entry j of row b is the
  *                    physical page of logical tokens j*P .. j*P+P-1 of
  *                    sequence b (the page table of pgsm §3.2 and §4.1).
  *                    Unused entries may hold anything (the allocator writes -1).
- *   token t of sequence b lives at page bt[b][t / P], row t % P of its tile.
+ *   token t of sequence b is token t % P of page bt[b][t / P].
  *   query head h reads KV head h / (Hq / Hkv).
  *
  * Conventions
@@ -39,7 +47,7 @@
  *     max_context turns the affected output row into NaN, and an append whose
  *     slot is out of range is skipped. pkv_validate_tables checks host copies.
  *   - Supported: D in {64, 128}; P in {16, 32, 64, 128}; Hq / Hkv in
- *     {1, 2, 4, 8}. Other values return PKV_ERR_UNSUPPORTED.
+ *     {1, 2, 4, 8, 16}. Other values return PKV_ERR_UNSUPPORTED.
  */
 #ifndef PKV_H_
 #define PKV_H_
@@ -80,8 +88,9 @@ int pkv_abi_version(void);
  * (hotelren §3.1, pgsm §4.3).
  *
  *   k_new, v_new : fp16 [B][Hkv][D] device, read.
- *   k_pool, v_pool: fp16 [N][Hkv][P][D] device, written only at
- *                  (bt[b][pos[b] / P], kvh, pos[b] % P, :) for every b, kvh.
+ *   k_pool, v_pool: fp16 pools (layout above) device, written only at the
+ *                  D halves of token pos[b] % P of page bt[b][pos[b] / P],
+ *                  KV head kvh, for every b, kvh.
  *   block_table  : int32 [B][max_pages] device, read.
  *   pos          : int32 [B] device: position of the new token (the length
  *                  of the context before the append).
@@ -121,7 +130,7 @@ int pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_con
  *
  *   out          : fp16 [B][Hq][D] device, written.
  *   q            : fp16 [B][Hq][D] device, read.
- *   k_pool/v_pool: fp16 [N][Hkv][P][D] device, read.
+ *   k_pool/v_pool: fp16 pools (layout above) device, read.
  *   block_table  : int32 [B][max_pages] device, read.
  *   lens         : int32 [B] device: tokens to attend (the new token
  *                  included). lens[b] == 0 writes a zero row.

@@ -24,6 +24,10 @@ from .paged_decode import (  # noqa: F401
     pages_for_tokens,
     pool_bytes,
     token_slot,
+    k_tile_offset,
+    v_tile_offset,
+    read_token,
+    write_token,
     gather_sequence,
     decode_attention,
     kv_append,

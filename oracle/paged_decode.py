@@ -7,8 +7,12 @@ Data format (the pages give a page as "tokens x heads x dims" in fp16 without
 fixing the axis order -- hotelren §3.2, pgsm §3.2; the order below is this
 library's reading):
 
-* ``k_pool``, ``v_pool``: fp16 arrays ``[N][Hkv][P][D]``; one (page, kv head)
-  tile of ``P`` tokens x ``D`` dims is contiguous.
+* ``k_pool``, ``v_pool``: fp16 arrays of shape ``[N][Hkv][P][D]``; the ``P*D``
+  halves of one (page, kv head) tile are contiguous. Inside a tile, token ``t``
+  and dim ``d`` sit at the offset given by ``k_tile_offset`` / ``v_tile_offset``
+  (the tile is cut into 16-token sub-blocks; K keeps 8-dim chunks with the
+  token index minor, V keeps 4-token groups with the token index minor). The
+  pool's two last axes are therefore storage, not (token, dim).
 * ``block_table``: int32 ``[B][max_pages]``; entry ``j`` of row ``b`` is the
   physical page holding logical tokens ``j*P .. j*P+P-1`` of sequence ``b``
   (pgsm §3.2 and §4.1: a page table maps each sequence's pages).
@@ -60,27 +64,89 @@ def pool_bytes(num_pages, kv_heads, page_size, head_dim, dtype_bytes=2):
 # ---------------------------------------------------------------------------
 
 def token_slot(block_table_row, t, page_size):
-    """Physical (page, offset-in-page) of logical token ``t``.
+    """Physical (page, token-in-page) of logical token ``t``.
 
     The page table lookup of pgsm §3.2: logical page ``t // P`` is looked up in
-    the sequence's table; the token sits at ``t % P`` inside that page.
+    the sequence's table; the token is number ``t % P`` inside that page.
     """
     page = int(block_table_row[t // page_size])
     return page, t % page_size
 
 
-def gather_sequence(pool, block_table_row, length, kv_head, page_size):
-    """Contiguous float64 ``[length][D]`` copy of one sequence's K (or V).
+def _check_tile(page_size, head_dim):
+    if page_size % 16 or head_dim % 32 or page_size <= 0 or head_dim <= 0:
+        raise ValueError("tile layout needs page_size % 16 == 0 and head_dim % 32 == 0")
 
-    Token ``t`` is read from page ``block_table_row[t // P]`` at offset
-    ``t % P`` (``token_slot``), so the result is exactly the contiguous cache a
-    non-paged implementation would hold.
+
+def k_tile_offset(t, d, page_size, head_dim):
+    """Offset (in halves) of token ``t`` (within its page), dim ``d`` in a K tile.
+
+    16-token sub-block ``t // 16``; inside it, dim chunk ``d // 8`` is a run of
+    16 tokens x 8 dims: offset ``((d // 8) * 16 + t % 16) * 8 + d % 8``.
     """
+    _check_tile(page_size, head_dim)
+    t = np.asarray(t)
+    d = np.asarray(d)
+    return (t // 16) * 16 * head_dim + ((d // 8) * 16 + t % 16) * 8 + d % 8
+
+
+def v_tile_offset(t, d, page_size, head_dim):
+    """Offset (in halves) of token ``t`` (within its page), dim ``d`` in a V tile.
+
+    16-token sub-block ``t // 16``; inside it the 4-token group ``(t % 16) // 4``
+    of 32-dim slice ``d // 32`` holds, for each of 16 dims ``d % 16``, the two
+    16-dim halves of the slice (``(d // 16) % 2``) with 4 tokens each.
+    """
+    _check_tile(page_size, head_dim)
+    t = np.asarray(t)
+    d = np.asarray(d)
+    u = t % 16
+    return ((t // 16) * 16 * head_dim
+            + (((d // 32) * 4 + u // 4) * 16 + d % 16) * 8 + ((d // 16) % 2) * 4 + u % 4)
+
+
+def _tile_offset(kind, t, d, page_size, head_dim):
+    if kind == "k":
+        return k_tile_offset(t, d, page_size, head_dim)
+    if kind == "v":
+        return v_tile_offset(t, d, page_size, head_dim)
+    raise ValueError("kind must be 'k' or 'v'")
+
+
+def _tiles(pool):
+    n, hkv, p, d = pool.shape
+    return pool.reshape(n, hkv, p * d)
+
+
+def read_token(pool, page, kv_head, t, kind):
+    """The ``D`` halves of token ``t`` (within ``page``) of one KV head."""
+    n, hkv, p, dim = pool.shape
+    return _tiles(pool)[page, kv_head, _tile_offset(kind, t, np.arange(dim), p, dim)]
+
+
+def write_token(pool, page, kv_head, t, vec, kind):
+    """Store the ``D`` halves ``vec`` as token ``t`` of ``page`` (in place)."""
+    n, hkv, p, dim = pool.shape
+    _tiles(pool)[page, kv_head, _tile_offset(kind, t, np.arange(dim), p, dim)] = vec
+
+
+def gather_sequence(pool, block_table_row, length, kv_head, page_size, kind):
+    """Contiguous float64 ``[length][D]`` copy of one sequence's K or V.
+
+    Token ``t`` is read from page ``block_table_row[t // P]`` as token
+    ``t % P`` of that page (``token_slot``), through the tile layout of
+    ``kind``, so the result is exactly the contiguous cache a non-paged
+    implementation would hold.
+    """
+    n, hkv, p, dim = pool.shape
+    if p != page_size:
+        raise ValueError("pool page size differs from page_size")
     t = np.arange(length)
     pages = np.asarray(block_table_row, dtype=np.int64)[t // page_size]
-    if length and (pages.min() < 0 or pages.max() >= pool.shape[0]):
+    if length and (pages.min() < 0 or pages.max() >= n):
         raise IndexError("block table entry out of range")
-    return pool[pages, kv_head, t % page_size, :].astype(np.float64)
+    off = _tile_offset(kind, (t % page_size)[:, None], np.arange(dim)[None, :], page_size, dim)
+    return _tiles(pool)[pages[:, None], kv_head, off].astype(np.float64)
 
 
 # ---------------------------------------------------------------------------
@@ -120,8 +186,8 @@ def decode_attention(q, k_pool, v_pool, block_table, lens, scale, page_size):
         if n == 0:
             continue
         for kvh in range(hkv):
-            keys = gather_sequence(k_pool, block_table[b], n, kvh, page_size)
-            vals = gather_sequence(v_pool, block_table[b], n, kvh, page_size)
+            keys = gather_sequence(k_pool, block_table[b], n, kvh, page_size, "k")
+            vals = gather_sequence(v_pool, block_table[b], n, kvh, page_size, "v")
             for i in range(g):
                 h = kvh * g + i
                 qh = q[b, h].astype(np.float64)
@@ -146,8 +212,8 @@ def kv_append(k_pool, v_pool, k_new, v_new, block_table, pos, page_size):
     for b in range(b_count):
         page, off = token_slot(block_table[b], int(pos[b]), page_size)
         for kvh in range(hkv):
-            k_out[page, kvh, off, :] = k_new[b, kvh, :]
-            v_out[page, kvh, off, :] = v_new[b, kvh, :]
+            write_token(k_out, page, kvh, off, k_new[b, kvh, :], "k")
+            write_token(v_out, page, kvh, off, v_new[b, kvh, :], "v")
     return k_out, v_out
 
 
@@ -182,8 +248,8 @@ def decode_partials(q, k_pool, v_pool, block_table, lens, scale, page_size,
         l = np.zeros((hq, n_parts))
         o = np.zeros((hq, n_parts, d))
         for kvh in range(hkv):
-            keys = gather_sequence(k_pool, block_table[b], n, kvh, page_size)
-            vals = gather_sequence(v_pool, block_table[b], n, kvh, page_size)
+            keys = gather_sequence(k_pool, block_table[b], n, kvh, page_size, "k")
+            vals = gather_sequence(v_pool, block_table[b], n, kvh, page_size, "v")
             for i in range(g):
                 h = kvh * g + i
                 s = s64 * (keys @ q[b, h].astype(np.float64))

@@ -25,6 +25,8 @@ HIP_FLAGS = [
     "-Wall",
     # never let the compiler form packed fp32 arithmetic
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the softmax rescales them with VALU ops
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

@@ -8,23 +8,29 @@
 // say that reading the KV dominates a decode step (pgsm §4.2, dpshk §2.2), so
 // every kernel here is organised around streaming the pool from HBM once.
 //
-// Decode kernel organisation (one workgroup = 4 waves per (sequence, KV head,
-// partition)):
-//   * a wave owns 16-token blocks blk = wave, wave + 4, ... of the partition;
-//     each block is one contiguous 16 x D fp16 run inside a page tile, read
-//     with fully coalesced 16-byte loads (lane l reads bytes 16 l .. 16 l + 15
-//     of each 1 KiB slice), the next block's loads issued before the current
-//     block is consumed;
-//   * a lane holds 8 dims of NL tokens (D = 128: 16 lanes per token, 4 tokens
-//     per load; D = 64: 8 lanes, 8 tokens); all G = Hq / Hkv query heads of the
-//     group are served from the same K/V registers, so each K/V byte is read
-//     from memory once per step;
-//   * q.k uses v_dot2_f32_f16 (fp16 products, fp32 accumulation) and a DPP
-//     reduction inside the lane group; the softmax is online (running max and
-//     sum per lane group, fp32, base-2 exponent with the scale folded in);
-//   * at the end the lane groups of a wave merge through cross-lane shuffles
-//     and the 4 waves through LDS; the result is either the final fp16 row or
-//     a (max, sum, unnormalised output) partial for the reduce kernel.
+// Tile layout (per (page, KV head) tile of P x D halves, 16-token sub-blocks):
+//   K: sub-block offset ((d / 8) * 16 + u) * 8 + d % 8        (u = token % 16)
+//   V: sub-block offset (((d / 32) * 4 + u / 4) * 16 + d % 16) * 8
+//                        + ((d / 16) % 2) * 4 + u % 4
+// Both are chosen so that one 16-byte load per lane, lanes reading consecutive
+// 16-byte runs, delivers exactly the MFMA operand a lane needs:
+//   * scores S = K . Q^T with v_mfma_f32_16x16x32_f16: A = K (row = token
+//     lane % 16, 8 dims), B = Q^T (column = query head lane % 16 of the GQA
+//     group, padded with zero heads); one MFMA per 32 dims;
+//   * the score tile comes out as lane (head h = lane % 16, q = lane / 16)
+//     holding tokens 4q .. 4q+3, which is exactly the A operand layout of
+//     O += P . V with v_mfma_f32_16x16x16f16 (A = P, row = head), so the
+//     softmax runs in registers and feeds the second MFMA with no shuffle;
+//     B = V (column = dim, 4 tokens per lane), one MFMA per 16 dims.
+// The group of G = Hq / Hkv query heads shares every K/V byte (G <= 16 fills
+// the 16 MFMA columns); each K/V byte is read from memory once per step.
+//
+// Decode kernel organisation: one workgroup of 4 waves per (sequence, KV head,
+// partition). A wave owns 16-token blocks blk = wave, wave + 4, ... of the
+// partition and keeps its own online-softmax state (running max per head,
+// partial sums, fp32 output tile); the next block's loads are in flight while
+// the current one is consumed. At the end the 4 waves merge through LDS into
+// either the final fp16 row or a (max, sum, unnormalised output) partial.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -35,18 +41,45 @@ namespace {
 
 typedef _Float16 half_t;
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float float4_t __attribute__((ext_vector_type(4)));
+
+// Tuning knobs (compile-time; the defaults are the measured best on MI355X).
+#ifndef PKV_PREFETCH_DEPTH
+#define PKV_PREFETCH_DEPTH 3
+#endif
+#ifndef PKV_KV_LOAD_POLICY
+#define PKV_KV_LOAD_POLICY 2
+#endif
+// Order of the (partition, sequence) work items in the grid: 0 = partition
+// major (every sequence's first partition first), 1 = sequence major.
+#ifndef PKV_GRID_ORDER
+#define PKV_GRID_ORDER 0
+#endif
 
 constexpr int kWave = 64;
 constexpr int kWaves = 4;
 constexpr int kThreads = kWave * kWaves;
-constexpr int kBlk = 16;                   // tokens per block
+constexpr int kBlk = 16;                   // tokens per block (= one sub-block)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr size_t kWsAlign = 256;
+constexpr int32_t kMaxPartitions = 4096;   // partitions per sequence (reduce kernel LDS)
+// Online-softmax rescaling is deferred until a head's block maximum exceeds
+// the running reference by this much (base-2 exponent units): probabilities
+// then stay below 2^8 and fp16/fp32 ranges are never approached.
+constexpr float kRescaleSlack = 8.0f;
+// Blocks each wave keeps in flight ahead of the one it is consuming.
+constexpr int kDepth = PKV_PREFETCH_DEPTH;
+// Word 3 of a raw gfx9 buffer descriptor (32-bit data format, no swizzle).
+constexpr int32_t kBufferFlags = 0x00020000;
+// Cache policy of the K/V loads: 2 = non-temporal (streamed once per step).
+constexpr int32_t kKvLoadPolicy = PKV_KV_LOAD_POLICY;
 
 struct DecodeParams {
   half_t* out;               // [B][Hq][D]
   const half_t* q;           // [B][Hq][D]
-  const half_t* k_pool;      // [N][Hkv][P][D]
+  const half_t* k_pool;      // [N][Hkv][P*D] tiles
   const half_t* v_pool;
   half_t* k_pool_w;          // same pools, written by the fused append
   half_t* v_pool_w;
@@ -68,62 +101,63 @@ struct DecodeParams {
 
 __device__ __forceinline__ float kNegInf() { return -__builtin_huge_valf(); }
 
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the LPT consecutive lanes that hold one token (LPT = 16 or 8);
-// every lane of the group receives the total.
-template <int LPT>
-__device__ __forceinline__ float group_sum(float x) {
-  if constexpr (LPT == 16) {
-    x += dpp<0x128>(x);   // row_ror:8
-    x += dpp<0x124>(x);   // row_ror:4
-  } else {
-    static_assert(LPT == 8, "lanes per token must be 8 or 16");
-    x += dpp<0x141>(x);   // row_half_mirror
-  }
-  x += dpp<0x4E>(x);      // quad_perm [2,3,0,1]
-  x += dpp<0xB1>(x);      // quad_perm [1,0,3,2]
-  return x;
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
+__device__ __forceinline__ half8_t as_h8(const uint4& v) { return __builtin_bit_cast(half8_t, v); }
 
-__device__ __forceinline__ void unpack8(const uint4& v, float f[8]) {
-  const half2_t a = as_h2(v.x), b = as_h2(v.y), c = as_h2(v.z), d = as_h2(v.w);
-  f[0] = (float)a.x; f[1] = (float)a.y; f[2] = (float)b.x; f[3] = (float)b.y;
-  f[4] = (float)c.x; f[5] = (float)c.y; f[6] = (float)d.x; f[7] = (float)d.y;
+__device__ __forceinline__ half4_t lo4(const uint4& v) {
+  return __builtin_bit_cast(half4_t, make_uint2(v.x, v.y));
+}
+
+__device__ __forceinline__ half4_t hi4(const uint4& v) {
+  return __builtin_bit_cast(half4_t, make_uint2(v.z, v.w));
+}
+
+// Offsets (halves) inside a 16-token sub-block of D dims; see the layout note.
+template <int D>
+__device__ __forceinline__ int32_t k_sub_off(int32_t u, int32_t d) {
+  return ((d >> 3) * 16 + u) * 8 + (d & 7);
+}
+
+template <int D>
+__device__ __forceinline__ int32_t v_sub_off(int32_t u, int32_t d) {
+  return (((d >> 5) * 4 + (u >> 2)) * 16 + (d & 15)) * 8 + ((d >> 4) & 1) * 4 + (u & 3);
+}
+
+// Write one token's K (D/8 chunks of 16 bytes) and V (D halves) into its slot.
+// Threads 0 .. D-1 of the caller participate (thread i: V dim i; i < D/8 also
+// the K chunk i). `sub` points at the token's 16-token sub-block (K or V pool).
+template <int D>
+__device__ __forceinline__ void store_token(half_t* k_sub, half_t* v_sub, int32_t u, const half_t* k_src,
+                                            const half_t* v_src, int i) {
+  if (i < D / 8) {
+    *reinterpret_cast<uint4*>(k_sub + k_sub_off<D>(u, i * 8)) = reinterpret_cast<const uint4*>(k_src)[i];
+  }
+  if (i < D) v_sub[v_sub_off<D>(u, i)] = v_src[i];
 }
 
 // -------------------------------------------------------------------------
 // append
 // -------------------------------------------------------------------------
 
-// One thread per 16-byte chunk of (b, kvh, d/8): copies the new token's K and
-// V chunk into slot (bt[b][pos/P], kvh, pos % P).
-__global__ __launch_bounds__(256) void kv_append_kernel(const uint4* __restrict__ k_new,
-                                                        const uint4* __restrict__ v_new,
-                                                        uint4* __restrict__ k_pool, uint4* __restrict__ v_pool,
-                                                        const int32_t* __restrict__ bt, int32_t max_pages,
-                                                        const int32_t* __restrict__ pos, int32_t B, int32_t Hkv,
-                                                        int32_t d8, int32_t p_shift, int32_t N) {
-  const int32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
-  if (idx >= B * Hkv * d8) return;
-  const int32_t c = idx % d8;
-  const int32_t r = idx / d8;
-  const int32_t kvh = r % Hkv;
-  const int32_t b = r / Hkv;
+// One workgroup of D threads per (b, kvh): writes the new token's K and V
+// into slot (bt[b][pos / P], kvh, pos % P) of the tile layout.
+template <int D>
+__global__ __launch_bounds__(D) void kv_append_kernel(const half_t* __restrict__ k_new,
+                                                      const half_t* __restrict__ v_new, half_t* __restrict__ k_pool,
+                                                      half_t* __restrict__ v_pool, const int32_t* __restrict__ bt,
+                                                      int32_t max_pages, const int32_t* __restrict__ pos, int32_t Hkv,
+                                                      int32_t p_shift, int32_t N) {
+  const int32_t kvh = blockIdx.x % Hkv;
+  const int32_t b = blockIdx.x / Hkv;
   const int32_t t = pos[b];
   if (t < 0 || (t >> p_shift) >= max_pages) return;
   const int32_t page = bt[(int64_t)b * max_pages + (t >> p_shift)];
   if (page < 0 || page >= N) return;
-  const int64_t slot = ((((int64_t)page * Hkv + kvh) << p_shift) + (t & ((1 << p_shift) - 1))) * d8 + c;
-  k_pool[slot] = k_new[idx];
-  v_pool[slot] = v_new[idx];
+  const int64_t tile = (((int64_t)page * Hkv + kvh) * D) << p_shift;
+  const int64_t sub = tile + (int64_t)((t & ((1 << p_shift) - 1)) >> 4) * (kBlk * D);
+  const int64_t src = ((int64_t)b * Hkv + kvh) * D;
+  store_token<D>(k_pool + sub, v_pool + sub, t & 15, k_new + src, v_new + src, threadIdx.x);
 }
 
 // -------------------------------------------------------------------------
@@ -132,9 +166,9 @@ __global__ __launch_bounds__(256) void kv_append_kernel(const uint4* __restrict_
 
 template <int D, int G, bool SPLIT, bool FUSED>
 __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams p) {
-  constexpr int LPT = D / 8;           // lanes per token
-  constexpr int TPI = kWave / LPT;     // tokens per 16-byte-per-lane load
-  constexpr int NL = kBlk / TPI;       // loads per pool per block
+  static_assert(D % 32 == 0 && G >= 1 && G <= 16, "shape");
+  constexpr int KL = D / 32;           // 16-byte loads per lane per block, for K and for V
+  constexpr int NT = D / 16;           // 16-dim output tiles
 
   __shared__ float sm_o[kWaves][G][D];
   __shared__ float sm_m[kWaves][G];
@@ -143,13 +177,18 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   const int32_t id = blockIdx.x;
   const int32_t kvh = id % p.Hkv;      // consecutive ids -> consecutive KV heads (XCD round robin)
   const int32_t rest = id / p.Hkv;
+#if PKV_GRID_ORDER == 0
   const int32_t b = rest % p.B;
   const int32_t part = rest / p.B;
+#else
+  const int32_t part = rest % p.n_parts;
+  const int32_t b = rest / p.n_parts;
+#endif
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int grp = lane / LPT;
-  const int dc = lane % LPT;
+  const int col = lane & 15;           // MFMA column: query head of the group / output dim
+  const int quad = lane >> 4;          // MFMA k-group: tokens 4 quad .. 4 quad + 3
 
   const int32_t L = p.lens[b];
   const bool bad_len = L < 0 || L > p.max_context || L > (p.max_pages << p.p_shift);
@@ -171,177 +210,151 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
   const int32_t pmask = (1 << p.p_shift) - 1;
   const int64_t tile_elems = (int64_t)D << p.p_shift;       // one (page, kvh) tile
 
-  // fused append: the workgroup owning the new token writes it to the pool
-  uint4 knew = {0, 0, 0, 0}, vnew = {0, 0, 0, 0};
-  const bool owns_new = FUSED && (start <= Lc - 1) && (Lc - 1 < end);
   if constexpr (FUSED) {
-    if (owns_new) {
-      const int64_t src = (((int64_t)b * p.Hkv + kvh) * D) / 8 + dc;
-      knew = reinterpret_cast<const uint4*>(p.k_new)[src];
-      vnew = reinterpret_cast<const uint4*>(p.v_new)[src];
+    // the workgroup owning the new token writes it to the pool; the barrier
+    // makes the stores visible to this workgroup's loads below
+    if (start <= Lc - 1 && Lc - 1 < end) {
       const int32_t t = Lc - 1;
       const int32_t page = bt_row[t >> p.p_shift];
-      if (wave == 0 && grp == 0 && page >= 0 && page < p.N) {
-        const int64_t dst = ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)(t & pmask) * D + dc * 8;
-        *reinterpret_cast<uint4*>(p.k_pool_w + dst) = knew;
-        *reinterpret_cast<uint4*>(p.v_pool_w + dst) = vnew;
+      if (page >= 0 && page < p.N) {
+        const int64_t sub = ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)((t & pmask) >> 4) * (kBlk * D);
+        const int64_t src = ((int64_t)b * p.Hkv + kvh) * D;
+        store_token<D>(p.k_pool_w + sub, p.v_pool_w + sub, t & 15, p.k_new + src, p.v_new + src, threadIdx.x);
       }
+      __syncthreads();
     }
   }
 
-  // the group's query rows, 8 dims per lane, kept as packed fp16 pairs
-  half2_t qv[G][4];
+  // B operand of the score MFMA: lane (head col, quad) holds q[col][32 j + 8 quad .. + 8]
+  half8_t qb[KL];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const uint4 t = *reinterpret_cast<const uint4*>(p.q + (head_row0 + h) * D + dc * 8);
-    qv[h][0] = as_h2(t.x); qv[h][1] = as_h2(t.y); qv[h][2] = as_h2(t.z); qv[h][3] = as_h2(t.w);
+  for (int j = 0; j < KL; ++j) {
+    uint4 t = {0, 0, 0, 0};
+    if (col < G) t = *reinterpret_cast<const uint4*>(p.q + (head_row0 + col) * D + j * 32 + quad * 8);
+    qb[j] = as_h8(t);
   }
 
-  float o[G][8];
-  float m[G], l[G];
+  float4_t o[NT];
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    m[h] = kNegInf();
-    l[h] = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) o[h][e] = 0.f;
-  }
+  for (int nt = 0; nt < NT; ++nt) o[nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  float m_ref = kNegInf();     // running reference max of head `col` (base-2 units)
+  float l_part = 0.f;          // this lane's share of the softmax denominator
   bool bad_page = false;
   const float c = p.scale_log2;
 
   const int32_t nblocks = (end - start + kBlk - 1) / kBlk;
 
-  auto tile_offset = [&](int32_t blk) -> int64_t {
-    const int32_t t0 = start + blk * kBlk;
+  // Loads go through buffer descriptors built per 16-token block (base = the
+  // block's sub-block, size 16 * D halves). Past the last block the size is 0:
+  // the loads return zeros without touching memory, so the prefetch below is
+  // unconditional and the compiler keeps exactly one block's loads in flight.
+  auto load_block = [&](int32_t blk, uint4 kr[KL], uint4 vr[KL]) {
+    const bool live = blk < nblocks;
+    const int32_t t0 = start + (live ? blk : 0) * kBlk;
     int32_t page = bt_row[t0 >> p.p_shift];
     if (page < 0 || page >= p.N) {
-      bad_page = true;
+      bad_page = bad_page || live;
       page = 0;                         // stay in bounds; the row becomes NaN below
     }
-    return ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)(t0 & pmask) * D;
+    const int64_t off = ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)(t0 & pmask) * D;
+    const int32_t bytes = live ? kBlk * D * 2 : 0;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_pool + off), (short)0, bytes, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(p.v_pool + off), (short)0, bytes, kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < KL; ++j)
+      kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, lane * 16 + j * 1024, 0, kKvLoadPolicy));
+#pragma unroll
+    for (int j = 0; j < KL; ++j)
+      vr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, lane * 16 + j * 1024, 0, kKvLoadPolicy));
   };
 
-  auto load_block = [&](int32_t blk, uint4 kr[NL], uint4 vr[NL]) {
-    const int64_t off = tile_offset(blk);
-    const uint4* kp = reinterpret_cast<const uint4*>(p.k_pool + off) + lane;
-    const uint4* vp = reinterpret_cast<const uint4*>(p.v_pool + off) + lane;
-#pragma unroll
-    for (int j = 0; j < NL; ++j) kr[j] = kp[j * kWave];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) vr[j] = vp[j * kWave];
-  };
-
-  auto consume = [&](int32_t blk, uint4 kr[NL], uint4 vr[NL]) {
+  auto consume = [&](int32_t blk, uint4 kr[KL], uint4 vr[KL]) {
     const int32_t t0 = start + blk * kBlk;
-    const bool tail = t0 + kBlk >= end;        // last block of the partition: mask / substitute
-    if (tail) {
+    // scores of tokens 4 quad + i for head col
+    float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        const int32_t tok = t0 + j * TPI + grp;
-        if (FUSED && owns_new && tok == Lc - 1) {
-          kr[j] = knew;
-          vr[j] = vnew;
-        }
-        if (tok >= end) vr[j] = uint4{0, 0, 0, 0};     // never multiply unowned slots
+    for (int j = 0; j < KL; ++j) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kr[j]), qb[j], s, 0, 0, 0);
+    const int32_t rem = end - t0;      // valid tokens in this block (>= 1)
+    if (rem < kBlk) {
+      // tail: mask scores of absent tokens and zero their values (never 0 * NaN)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) s[i] = 4 * quad + i < rem ? s[i] : kNegInf();
+      const uint32_t m0 = (4 * quad + 0 < rem ? 0x0000FFFFu : 0u) | (4 * quad + 1 < rem ? 0xFFFF0000u : 0u);
+      const uint32_t m1 = (4 * quad + 2 < rem ? 0x0000FFFFu : 0u) | (4 * quad + 3 < rem ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int j = 0; j < KL; ++j) {
+        vr[j].x &= m0;
+        vr[j].y &= m1;
+        vr[j].z &= m0;
+        vr[j].w &= m1;
       }
     }
-    float s[NL][G];
+    float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
+    bm = fmaxf(bm, __shfl_xor(bm, 16));
+    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    bm *= c;                            // block max of head col, base-2 units (c > 0)
+    if (__builtin_amdgcn_ballot_w64(bm > m_ref + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_ref, bm);
+      const float alpha = fast_exp2(m_ref - m_new);            // 0 on the first block
+      l_part *= alpha;
+      // output row 4 quad + i belongs to head 4 quad + i, whose alpha sits in lane 4 quad + i
 #pragma unroll
-    for (int j = 0; j < NL; ++j) {
+      for (int i = 0; i < 4; ++i) {
+        const float a = __shfl(alpha, 4 * quad + i);
 #pragma unroll
-      for (int h = 0; h < G; ++h) {
-        float acc = 0.f;
-        acc = __builtin_amdgcn_fdot2(qv[h][0], as_h2(kr[j].x), acc, false);
-        acc = __builtin_amdgcn_fdot2(qv[h][1], as_h2(kr[j].y), acc, false);
-        acc = __builtin_amdgcn_fdot2(qv[h][2], as_h2(kr[j].z), acc, false);
-        acc = __builtin_amdgcn_fdot2(qv[h][3], as_h2(kr[j].w), acc, false);
-        s[j][h] = group_sum<LPT>(acc);
+        for (int nt = 0; nt < NT; ++nt) o[nt][i] *= a;
       }
+      m_ref = m_new;
     }
-    if (tail) {
+    float pr[4];
 #pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        const int32_t tok = t0 + j * TPI + grp;
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(s[i], c, -m_ref));
+    l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    const half4_t pa = {(half_t)pr[0], (half_t)pr[1], (half_t)pr[2], (half_t)pr[3]};
 #pragma unroll
-        for (int h = 0; h < G; ++h) s[j][h] = tok < end ? s[j][h] : kNegInf();
-      }
-    }
-    float vf[NL][8];
-#pragma unroll
-    for (int j = 0; j < NL; ++j) unpack8(vr[j], vf[j]);
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      float bm = s[0][h];
-#pragma unroll
-      for (int j = 1; j < NL; ++j) bm = fmaxf(bm, s[j][h]);
-      const float mn = fmaxf(m[h], bm * c);
-      const float ms = mn == kNegInf() ? 0.f : mn;
-      const float alpha = fast_exp2(m[h] - ms);
-      float pj[NL];
-      float ps = 0.f;
-#pragma unroll
-      for (int j = 0; j < NL; ++j) {
-        pj[j] = fast_exp2(fmaf(s[j][h], c, -ms));
-        ps += pj[j];
-      }
-      l[h] = fmaf(l[h], alpha, ps);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        float acc = o[h][e] * alpha;
-#pragma unroll
-        for (int j = 0; j < NL; ++j) acc = fmaf(pj[j], vf[j][e], acc);
-        o[h][e] = acc;
-      }
-      m[h] = mn;
+    for (int j = 0; j < KL; ++j) {
+      o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, lo4(vr[j]), o[2 * j], 0, 0, 0);
+      o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, hi4(vr[j]), o[2 * j + 1], 0, 0, 0);
     }
   };
 
-  // software pipeline: next block's loads are in flight while this one is consumed
-  uint4 ka[NL], va[NL], kb[NL], vb[NL];
+  // software pipeline over a ring of kDepth + 1 block buffers: while block i is
+  // consumed, blocks i + 1 .. i + kDepth (of this wave) are in flight. The
+  // scheduling barriers keep the compiler from sinking a prefetch below the
+  // first use of the current block.
+  uint4 kr[kDepth + 1][KL], vr[kDepth + 1][KL];
+#pragma unroll
+  for (int r = 0; r < kDepth; ++r) load_block(wave + r * kWaves, kr[r], vr[r]);
   int32_t blk = wave;
-  if (blk < nblocks) load_block(blk, ka, va);
-  while (blk < nblocks) {
-    const int32_t nxt = blk + kWaves;
-    if (nxt < nblocks) load_block(nxt, kb, vb);
-    consume(blk, ka, va);
-    blk = nxt;
-    if (blk >= nblocks) break;
-    const int32_t nxt2 = blk + kWaves;
-    if (nxt2 < nblocks) load_block(nxt2, ka, va);
-    consume(blk, kb, vb);
-    blk = nxt2;
-  }
-
-  // merge the lane groups of this wave (they saw disjoint tokens)
+  while (true) {
 #pragma unroll
-  for (int off = LPT; off < kWave; off <<= 1) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mo = __shfl_xor(m[h], off);
-      const float lo = __shfl_xor(l[h], off);
-      const float mn = fmaxf(m[h], mo);
-      const float ms = mn == kNegInf() ? 0.f : mn;
-      const float wa = fast_exp2(m[h] - ms);
-      const float wb = fast_exp2(mo - ms);
-      l[h] = l[h] * wa + lo * wb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) o[h][e] = o[h][e] * wa + __shfl_xor(o[h][e], off) * wb;
-      m[h] = mn;
+    for (int r = 0; r <= kDepth; ++r) {
+      if (blk >= nblocks) goto done;
+      load_block(blk + kDepth * kWaves, kr[(r + kDepth) % (kDepth + 1)], vr[(r + kDepth) % (kDepth + 1)]);
+      __builtin_amdgcn_sched_barrier(0);
+      consume(blk, kr[r], vr[r]);
+      blk += kWaves;
     }
   }
-  if (bad_page) {
-#pragma unroll
-    for (int h = 0; h < G; ++h) l[h] = __builtin_nanf("");
+done:
+
+  // per-head denominators of this wave: sum the 4 quads of column col
+  l_part += __shfl_xor(l_part, 16);
+  l_part += __shfl_xor(l_part, 32);
+  if (bad_page) l_part = __builtin_nanf("");
+  if (quad == 0 && col < G) {
+    sm_m[wave][col] = m_ref;
+    sm_l[wave][col] = l_part;
   }
-  if (grp == 0) {
+  // output tile: lane holds rows (heads) 4 quad + i of dims 16 nt + col
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
+  for (int i = 0; i < 4; ++i) {
+    const int h = 4 * quad + i;
+    if (h < G) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sm_o[wave][h][dc * 8 + e] = o[h][e];
-      if (dc == 0) {
-        sm_m[wave][h] = m[h];
-        sm_l[wave][h] = l[h];
-      }
+      for (int nt = 0; nt < NT; ++nt) sm_o[wave][h][16 * nt + col] = o[nt][i];
     }
   }
   __syncthreads();
@@ -379,10 +392,15 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
 // decode: log-sum-exp reduce over partitions
 // -------------------------------------------------------------------------
 
-// One workgroup of D threads per (sequence, query head); thread d merges
-// output dim d over the sequence's ceil(L / part_tokens) partitions.
+// One workgroup of D threads per (sequence, query head). The partition maxima
+// and sums are loaded in parallel (one partition per thread) into LDS, the
+// merge weights exp2(m_j - M) computed once, and thread d then sums output dim
+// d over the partitions with independent loads.
 template <int D>
 __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
+  constexpr int kMaxParts = kMaxPartitions;
+  __shared__ float sm_w[kMaxParts];
+  __shared__ float sm_red[D / kWave];
   const int64_t bh = blockIdx.x;
   const int32_t b = (int32_t)(bh / p.Hq);
   const int d = threadIdx.x;
@@ -392,15 +410,46 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
   const float* pm = p.part_m + bh * p.n_parts;
   const float* pl = p.part_l + bh * p.n_parts;
   const float* po = p.part_o + bh * p.n_parts * D + d;
+
+  // M = max_j m_j
   float M = kNegInf();
-  for (int32_t j = 0; j < np; ++j) M = fmaxf(M, pm[j]);
-  const float Ms = M == kNegInf() ? 0.f : M;
-  float Ls = 0.f, O = 0.f;
-  for (int32_t j = 0; j < np; ++j) {
-    const float wt = fast_exp2(pm[j] - Ms);
-    Ls = fmaf(wt, pl[j], Ls);
-    O = fmaf(wt, po[(int64_t)j * D], O);
+  for (int32_t j = d; j < np; j += D) {
+    const float mj = pm[j];
+    sm_w[j] = mj;
+    M = fmaxf(M, mj);
   }
+  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  if ((d & (kWave - 1)) == 0) sm_red[d / kWave] = M;
+  __syncthreads();
+  M = sm_red[0];
+#pragma unroll
+  for (int w = 1; w < D / kWave; ++w) M = fmaxf(M, sm_red[w]);
+  const float Ms = M == kNegInf() ? 0.f : M;
+  __syncthreads();
+  // weights and the denominator
+  float Lp = 0.f;
+  for (int32_t j = d; j < np; j += D) {
+    const float wj = fast_exp2(sm_w[j] - Ms);
+    sm_w[j] = wj;
+    Lp = fmaf(wj, pl[j], Lp);
+  }
+  for (int off = 32; off > 0; off >>= 1) Lp += __shfl_xor(Lp, off);
+  if ((d & (kWave - 1)) == 0) sm_red[d / kWave] = Lp;
+  __syncthreads();
+  float Ls = 0.f;
+#pragma unroll
+  for (int w = 0; w < D / kWave; ++w) Ls += sm_red[w];
+  // numerator of dim d, four independent partial sums
+  float O0 = 0.f, O1 = 0.f, O2 = 0.f, O3 = 0.f;
+  int32_t j = 0;
+  for (; j + 4 <= np; j += 4) {
+    O0 = fmaf(sm_w[j + 0], po[(int64_t)(j + 0) * D], O0);
+    O1 = fmaf(sm_w[j + 1], po[(int64_t)(j + 1) * D], O1);
+    O2 = fmaf(sm_w[j + 2], po[(int64_t)(j + 2) * D], O2);
+    O3 = fmaf(sm_w[j + 3], po[(int64_t)(j + 3) * D], O3);
+  }
+  for (; j < np; ++j) O0 = fmaf(sm_w[j], po[(int64_t)j * D], O0);
+  const float O = (O0 + O1) + (O2 + O3);
   float r = Ls > 0.f ? O / Ls : 0.f;
   if (bad_len || Ls != Ls) r = __builtin_nanf("");
   p.out[bh * D + d] = (half_t)r;
@@ -451,7 +500,8 @@ hipError_t dispatch_g(int G, const DecodeParams& p, hipStream_t s, int64_t grid)
     case 1: return launch_partition<D, 1, SPLIT, FUSED>(p, s, grid);
     case 2: return launch_partition<D, 2, SPLIT, FUSED>(p, s, grid);
     case 4: return launch_partition<D, 4, SPLIT, FUSED>(p, s, grid);
-    default: return launch_partition<D, 8, SPLIT, FUSED>(p, s, grid);
+    case 8: return launch_partition<D, 8, SPLIT, FUSED>(p, s, grid);
+    default: return launch_partition<D, 16, SPLIT, FUSED>(p, s, grid);
   }
 }
 
@@ -475,7 +525,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
   const int p_shift = log2_page(P);
   if (p_shift < 0) return PKV_ERR_UNSUPPORTED;
-  if (G != 1 && G != 2 && G != 4 && G != 8) return PKV_ERR_UNSUPPORTED;
+  if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PKV_ERR_UNSUPPORTED;
   if (partition_tokens % kBlk != 0) return PKV_ERR_INVALID_ARG;
   if (static_cast<int64_t>(max_context) > (static_cast<int64_t>(max_pages) << p_shift)) return PKV_ERR_INVALID_ARG;
   if (B == 0) return PKV_OK;
@@ -491,6 +541,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
 
   const bool split = partition_tokens > 0;
   const int32_t n_parts = parts_for(max_context, partition_tokens);
+  if (split && n_parts > kMaxPartitions) return PKV_ERR_INVALID_ARG;
   const int64_t grid = static_cast<int64_t>(n_parts) * B * Hkv;
   if (grid > 0x7fffffffLL || static_cast<int64_t>(B) * Hq > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
 
@@ -560,14 +611,21 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_po
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
       !aligned(block_table, 4) || !aligned(pos, 4))
     return PKV_ERR_INVALID_ARG;
-  const int64_t threads = static_cast<int64_t>(B) * Hkv * (D / 8);
-  if (threads > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
+  const int64_t rows = static_cast<int64_t>(B) * Hkv;
+  if (rows > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
   const int64_t pool_elems = static_cast<int64_t>(N) * Hkv * P * D;
   if (pool_elems / N / Hkv / P != D) return PKV_ERR_INVALID_ARG;
-  const uint32_t blocks = static_cast<uint32_t>((threads + 255) / 256);
-  hipLaunchKernelGGL(kv_append_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
-                     static_cast<const uint4*>(k_new), static_cast<const uint4*>(v_new), static_cast<uint4*>(k_pool),
-                     static_cast<uint4*>(v_pool), block_table, max_pages, pos, B, Hkv, D / 8, p_shift, N);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const half_t* kn = static_cast<const half_t*>(k_new);
+  const half_t* vn = static_cast<const half_t*>(v_new);
+  half_t* kp = static_cast<half_t*>(k_pool);
+  half_t* vp = static_cast<half_t*>(v_pool);
+  if (D == 64)
+    hipLaunchKernelGGL(kv_append_kernel<64>, dim3(static_cast<uint32_t>(rows)), dim3(64), 0, s, kn, vn, kp, vp,
+                       block_table, max_pages, pos, Hkv, p_shift, N);
+  else
+    hipLaunchKernelGGL(kv_append_kernel<128>, dim3(static_cast<uint32_t>(rows)), dim3(128), 0, s, kn, vn, kp, vp,
+                       block_table, max_pages, pos, Hkv, p_shift, N);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 

@@ -24,7 +24,8 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 import oracle  # noqa: E402
-from workloads import workload, poison_unused  # noqa: E402
+from workloads import workload  # noqa: E402
+from _helpers import poison_unused, fill_tokens, set_dims  # noqa: E402
 
 TOL = 4e-3
 
@@ -208,7 +209,7 @@ def _marked_tokens(L, P, part, D):
 
 
 @pytest.mark.parametrize("P,part,D,G", [(16, 512, 128, 4), (16, 0, 128, 1), (64, 512, 128, 4), (128, 256, 64, 2),
-                                        (32, 0, 64, 8)])
+                                        (32, 0, 64, 8), (16, 256, 128, 16)])
 def test_count_probe_reads_every_token_once(P, part, D, G):
     rng = np.random.default_rng(31 + P + D)
     Hkv = 2
@@ -222,10 +223,11 @@ def test_count_probe_reads_every_token_once(P, part, D, G):
     for b in range(B):
         L = int(lens[b])
         t = np.arange(L)
-        kp[bt[b, t // P], :, t % P, :] = rng.standard_normal((L, Hkv, D)).astype(np.float16)
-        vp[bt[b, t // P], :, t % P, :] = 0
+        fill_tokens(kp, bt[b], t, rng.standard_normal((Hkv, L, D)).astype(np.float16), "k")
+        fill_tokens(vp, bt[b], t, np.zeros((Hkv, L, D), np.float16), "v")
         for d, tok in enumerate(_marked_tokens(L, P, part, D)):
-            vp[bt[b, tok // P], :, tok % P, d] = 1
+            for kvh in range(Hkv):
+                set_dims(vp, bt[b], tok, kvh, [d], 1, "v")
             expect[b, :, d] = 1.0
     q = np.zeros((B, Hq, D), np.float16)
     say("count probe P=%d part=%d D=%d G=%d" % (P, part, D, G))
@@ -252,18 +254,18 @@ def test_spike_probe_selects_each_boundary_token(P, part):
     q = rng.standard_normal((B, Hq, D)).astype(np.float16)
     t = np.arange(L)
     for b in range(B):
-        kp[bt[b, t // P], :, t % P, :] = (0.05 * rng.standard_normal((L, Hkv, D))).astype(np.float16)
-        vp[bt[b, t // P], :, t % P, :] = rng.standard_normal((L, Hkv, D)).astype(np.float16)
+        fill_tokens(kp, bt[b], t, (0.05 * rng.standard_normal((Hkv, L, D))).astype(np.float16), "k")
+        fill_tokens(vp, bt[b], t, rng.standard_normal((Hkv, L, D)).astype(np.float16), "v")
         s = spikes[b]
-        for kvh in range(Hkv):
-            # the spike key is 4x the group's first query head
-            kp[bt[b, s // P], kvh, s % P, :] = (4.0 * q[b, kvh * G].astype(np.float32)).astype(np.float16)
+        # the spike key is 4x the group's first query head
+        spike = np.stack([(4.0 * q[b, kvh * G].astype(np.float32)).astype(np.float16) for kvh in range(Hkv)])
+        fill_tokens(kp, bt[b], np.array([s]), spike[:, None, :], "k")
     say("spike probe P=%d part=%d" % (P, part))
     got = host(gpu_decode(q, dev(kp), dev(vp), bt, lens, L, 1 / math.sqrt(D), part)).astype(np.float64)
     for b in range(B):
         s = spikes[b]
         for kvh in range(Hkv):
-            v = vp[bt[b, s // P], kvh, s % P, :].astype(np.float64)
+            v = oracle.read_token(vp, bt[b, s // P], kvh, s % P, "v").astype(np.float64)
             np.testing.assert_allclose(got[b, kvh * G], v, rtol=0, atol=TOL)
 
 

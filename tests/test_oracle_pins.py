@@ -112,20 +112,21 @@ def make_paged_case(rng, B, Hq, Hkv, D, P, lens, spare_pages=3, poison=True):
         bt[b, :npg] = perm[cur:cur + npg]
         cur += npg
         for t in range(n):
-            k_pool[bt[b, t // P], :, t % P, :] = kb[:, t, :]
-            v_pool[bt[b, t // P], :, t % P, :] = vb[:, t, :]
+            for kvh in range(Hkv):
+                oracle.write_token(k_pool, bt[b, t // P], kvh, t % P, kb[kvh, t], "k")
+                oracle.write_token(v_pool, bt[b, t // P], kvh, t % P, vb[kvh, t], "v")
     q = rng.standard_normal((B, Hq, D)).astype(np.float16)
     return q, k_pool, v_pool, bt, K, V
 
 
 CASES = [
     # B, Hq, Hkv, D, P, lens
-    (1, 1, 1, 8, 1, [1]),
-    (2, 2, 2, 8, 2, [5, 3]),
-    (3, 4, 2, 8, 4, [17, 1, 40]),
+    (1, 1, 1, 32, 16, [1]),
+    (2, 2, 2, 32, 16, [5, 3]),
+    (3, 4, 2, 32, 16, [17, 1, 40]),
     (2, 4, 1, 64, 16, [33, 16]),
-    (3, 4, 4, 8, 16, [1, 15, 40]),
-    (2, 2, 1, 64, 4, [9, 38]),
+    (3, 4, 4, 32, 32, [1, 15, 40]),
+    (2, 2, 1, 64, 32, [9, 70]),
 ]
 
 
@@ -165,7 +166,7 @@ def test_library_attention_agrees():
 # special cases with exact answers
 # ---------------------------------------------------------------------------
 
-def _one_seq(rng, n, D=16, P=4, Hkv=1, Hq=1):
+def _one_seq(rng, n, D=32, P=16, Hkv=1, Hq=1):
     return make_paged_case(rng, 1, Hq, Hkv, D, P, [n])
 
 
@@ -179,47 +180,47 @@ def test_single_token_returns_its_value():
 
 def test_zero_query_gives_mean_of_values():
     rng = np.random.default_rng(6)
-    q, kp, vp, bt, K, V = _one_seq(rng, 29, D=16, P=4)
+    q, kp, vp, bt, K, V = _one_seq(rng, 29)
     q[:] = 0
-    got = oracle.decode_attention(q, kp, vp, bt, np.array([29], np.int32), 0.25, 4)
+    got = oracle.decode_attention(q, kp, vp, bt, np.array([29], np.int32), 0.25, 16)
     np.testing.assert_allclose(got[0, 0], V[0][0].astype(np.float64).mean(axis=0), rtol=0, atol=1e-13)
 
 
 def test_zero_keys_give_mean_of_values():
     rng = np.random.default_rng(7)
-    q, kp, vp, bt, K, V = _one_seq(rng, 23, D=16, P=4)
+    q, kp, vp, bt, K, V = _one_seq(rng, 23)
     kp[np.isfinite(kp)] = 0
-    got = oracle.decode_attention(q, kp, vp, bt, np.array([23], np.int32), 0.25, 4)
+    got = oracle.decode_attention(q, kp, vp, bt, np.array([23], np.int32), 0.25, 16)
     np.testing.assert_allclose(got[0, 0], V[0][0].astype(np.float64).mean(axis=0), rtol=0, atol=1e-13)
 
 
 def test_constant_values_give_the_constant():
     rng = np.random.default_rng(8)
-    q, kp, vp, bt, K, V = _one_seq(rng, 31, D=16, P=4)
+    q, kp, vp, bt, K, V = _one_seq(rng, 31)
     vp[np.isfinite(vp)] = 1.5
-    got = oracle.decode_attention(q, kp, vp, bt, np.array([31], np.int32), 0.25, 4)
+    got = oracle.decode_attention(q, kp, vp, bt, np.array([31], np.int32), 0.25, 16)
     np.testing.assert_allclose(got[0, 0], 1.5, rtol=0, atol=1e-13)
 
 
-@pytest.mark.parametrize("spike", [0, 3, 4, 30])
+@pytest.mark.parametrize("spike", [0, 3, 15, 16, 30])
 def test_spike_key_selects_its_value(spike):
     rng = np.random.default_rng(9)
-    n, D, P = 31, 16, 4
+    n, D, P = 31, 32, 16
     q, kp, vp, bt, K, V = _one_seq(rng, n, D=D, P=P)
     q[0, 0] = np.float16(1.0)
-    # every other key orthogonal-ish small, the spike aligned with q and large
+    # every other key zero, the spike a large constant vector
     for t in range(n):
-        kp[bt[0, t // P], 0, t % P, :] = 0
-    kp[bt[0, spike // P], 0, spike % P, :] = np.float16(64.0)
+        oracle.write_token(kp, bt[0, t // P], 0, t % P, np.zeros(D, np.float16), "k")
+    oracle.write_token(kp, bt[0, spike // P], 0, spike % P, np.full(D, 64.0, np.float16), "k")
     got = oracle.decode_attention(q, kp, vp, bt, np.array([n], np.int32), 1.0, P)
-    # score gap 64*16 = 1024 -> other weights below exp(-1000)
+    # the spike's score exceeds the others' by 64 * sum(q) with q >= 0 here
     assert np.array_equal(got[0, 0], V[0][0][spike].astype(np.float64))
 
 
 def test_empty_sequence_gives_zeros():
     rng = np.random.default_rng(10)
-    q, kp, vp, bt, K, V = make_paged_case(rng, 2, 2, 2, 8, 4, [0, 3])
-    got = oracle.decode_attention(q, kp, vp, bt, np.array([0, 3], np.int32), 0.5, 4)
+    q, kp, vp, bt, K, V = make_paged_case(rng, 2, 2, 2, 32, 16, [0, 3])
+    got = oracle.decode_attention(q, kp, vp, bt, np.array([0, 3], np.int32), 0.5, 16)
     assert np.all(got[0] == 0)
     assert np.all(np.isfinite(got[1]))
 
@@ -230,8 +231,8 @@ def test_empty_sequence_gives_zeros():
 
 def test_physical_page_permutation_is_invisible():
     rng = np.random.default_rng(11)
-    B, Hq, Hkv, D, P = 3, 4, 2, 16, 4
-    lens = np.array([13, 29, 8], np.int32)
+    B, Hq, Hkv, D, P = 3, 4, 2, 32, 16
+    lens = np.array([13, 49, 8], np.int32)
     q, kp, vp, bt, K, V = make_paged_case(rng, B, Hq, Hkv, D, P, lens)
     base = oracle.decode_attention(q, kp, vp, bt, lens, 0.25, P)
     sigma = rng.permutation(kp.shape[0])          # new page id of old page i
@@ -246,13 +247,13 @@ def test_physical_page_permutation_is_invisible():
 
 def test_page_size_is_invisible():
     rng = np.random.default_rng(12)
-    B, Hq, Hkv, D = 2, 4, 2, 16
-    lens = [100, 37]
+    B, Hq, Hkv, D = 2, 4, 2, 32
+    lens = [300, 37]
     q = rng.standard_normal((B, Hq, D)).astype(np.float16)
     K = [rng.standard_normal((Hkv, n, D)).astype(np.float16) for n in lens]
     V = [rng.standard_normal((Hkv, n, D)).astype(np.float16) for n in lens]
     outs = []
-    for P in (1, 2, 16, 32, 64, 128):
+    for P in (16, 32, 64, 128):
         npg = [-(-n // P) for n in lens]
         N = sum(npg) + 1
         perm = np.random.default_rng(P).permutation(N)
@@ -264,11 +265,44 @@ def test_page_size_is_invisible():
             bt[b, :npg[b]] = perm[cur:cur + npg[b]]
             cur += npg[b]
             for t in range(n):
-                kp[bt[b, t // P], :, t % P] = K[b][:, t]
-                vp[bt[b, t // P], :, t % P] = V[b][:, t]
+                for kvh in range(Hkv):
+                    oracle.write_token(kp, bt[b, t // P], kvh, t % P, K[b][kvh, t], "k")
+                    oracle.write_token(vp, bt[b, t // P], kvh, t % P, V[b][kvh, t], "v")
         outs.append(oracle.decode_attention(q, kp, vp, bt, np.array(lens, np.int32), 0.25, P))
     for o in outs[1:]:
         assert np.array_equal(outs[0], o)
+
+
+@pytest.mark.parametrize("P,D", [(16, 32), (16, 64), (16, 128), (32, 64), (64, 128), (128, 128)])
+def test_tile_layouts_are_bijections(P, D):
+    t, d = np.meshgrid(np.arange(P), np.arange(D), indexing="ij")
+    for f in (oracle.k_tile_offset, oracle.v_tile_offset):
+        off = f(t, d, P, D).ravel()
+        assert sorted(off.tolist()) == list(range(P * D))
+
+
+def test_tile_layout_keeps_16_byte_runs():
+    # K: 8 consecutive dims of one token are one 16-byte run; V: 4 consecutive
+    # tokens (same 4-group) of one dim are one 8-byte run
+    P, D = 32, 128
+    for tt in range(P):
+        for c in range(D // 8):
+            off = oracle.k_tile_offset(tt, np.arange(c * 8, c * 8 + 8), P, D)
+            assert off[0] % 8 == 0 and np.all(np.diff(off) == 1)
+    for g in range(P // 4):
+        for dd in range(D):
+            off = oracle.v_tile_offset(np.arange(g * 4, g * 4 + 4), dd, P, D)
+            assert off[0] % 4 == 0 and np.all(np.diff(off) == 1)
+
+
+def test_write_then_read_token_roundtrip():
+    rng = np.random.default_rng(3)
+    pool = np.zeros((3, 2, 32, 64), np.float16)
+    vec = rng.standard_normal(64).astype(np.float16)
+    for kind in ("k", "v"):
+        oracle.write_token(pool, 2, 1, 17, vec, kind)
+        assert np.array_equal(oracle.read_token(pool, 2, 1, 17, kind), vec)
+        assert (pool.view(np.uint16) != 0).sum() <= 64 * (2 if kind == "v" else 1)
 
 
 # ---------------------------------------------------------------------------
@@ -277,8 +311,8 @@ def test_page_size_is_invisible():
 
 def test_append_writes_exactly_one_token_per_sequence():
     rng = np.random.default_rng(13)
-    B, Hkv, D, P = 3, 2, 16, 4
-    lens = np.array([7, 8, 1], np.int32)      # appended positions 7, 8, 1
+    B, Hkv, D, P = 3, 2, 32, 16
+    lens = np.array([15, 16, 1], np.int32)    # appended positions 15, 16, 1
     q, kp, vp, bt, K, V = make_paged_case(rng, B, 2, Hkv, D, P, lens + 1, poison=False)
     k_new = rng.standard_normal((B, Hkv, D)).astype(np.float16)
     v_new = rng.standard_normal((B, Hkv, D)).astype(np.float16)
@@ -287,7 +321,7 @@ def test_append_writes_exactly_one_token_per_sequence():
     assert changed <= 2 * B * Hkv * D
     assert changed >= 2 * B * Hkv * D - 8      # random fp16 collisions are rare
     for b in range(B):
-        keys = oracle.gather_sequence(k2, bt[b], int(lens[b]) + 1, 1, P)
+        keys = oracle.gather_sequence(k2, bt[b], int(lens[b]) + 1, 1, P, "k")
         assert np.array_equal(keys[-1], k_new[b, 1].astype(np.float64))
         assert np.array_equal(keys[:-1], K[b][1][:lens[b]].astype(np.float64))
     assert np.array_equal(kp, kp)  # inputs untouched
@@ -301,7 +335,7 @@ def test_append_writes_exactly_one_token_per_sequence():
 @pytest.mark.parametrize("part", [1, 4, 7, 16, 64, 1000])
 def test_split_merge_equals_unsplit(part):
     rng = np.random.default_rng(14)
-    B, Hq, Hkv, D, P = 3, 4, 2, 16, 4
+    B, Hq, Hkv, D, P = 3, 4, 2, 32, 16
     lens = np.array([1, 33, 64], np.int32)
     q, kp, vp, bt, K, V = make_paged_case(rng, B, Hq, Hkv, D, P, lens)
     full = oracle.decode_attention(q, kp, vp, bt, lens, 0.3, P)
@@ -332,11 +366,14 @@ MUTANTS = [
     ("p = np.exp(s - s.max())", "p = np.exp(s.max() - s)"),        # sign
     ("out[b, h] = (p @ vals) / p.sum()", "out[b, h] = (p @ keys) / p.sum()"),   # K/V swapped
     ("out[b, h] = (p @ vals) / p.sum()", "out[b, h] = (p @ vals) / n"),         # wrong normaliser
-    ("[t // page_size]", "[t // page_size - (t % page_size == 0) * (t > 0)]"),  # page off by one
-    ("t % page_size, :]", "(t + 1) % page_size, :]"),              # slot off by one
+    ("[t // page_size]\n", "[t // page_size - (t % page_size == 0) * (t > 0)]\n"),  # page off by one
+    ("(t % page_size)[:, None]", "((t + 1) % page_size)[:, None]"),  # slot off by one
     ("return float(np.float32(scale))", "return float(np.float16(scale))"),    # scale precision
-    ("keys = gather_sequence(k_pool, block_table[b], n, kvh, page_size)\n            vals",
-     "keys = gather_sequence(k_pool, block_table[b], n - 1, kvh, page_size)\n            keys = np.vstack([keys, keys[-1:]])\n            vals"),  # last token dropped
+    ('keys = gather_sequence(k_pool, block_table[b], n, kvh, page_size, "k")\n            vals',
+     'keys = gather_sequence(k_pool, block_table[b], n - 1, kvh, page_size, "k")\n'
+     '            keys = np.vstack([keys, keys[-1:]])\n            vals'),  # last token dropped
+    ('vals = gather_sequence(v_pool, block_table[b], n, kvh, page_size, "v")\n            for i',
+     'vals = gather_sequence(v_pool, block_table[b], n, kvh, page_size, "k")\n            for i'),  # V read as K
 ]
 
 

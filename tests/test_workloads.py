@@ -4,7 +4,8 @@ import numpy as np
 import pytest
 
 import oracle
-from workloads import workload, poison_unused
+from workloads import workload
+from _helpers import poison_unused
 
 
 def test_deterministic():
@@ -58,6 +59,8 @@ def test_poison_marks_only_unused_slots():
     lens = w.lens(0)
     k, v = poison_unused(w, lens)
     for b in range(w.B):
-        keys = oracle.gather_sequence(k, w.block_table[b], int(lens[b]), 0, w.P)
+        keys = oracle.gather_sequence(k, w.block_table[b], int(lens[b]), 0, w.P, "k")
+        vals = oracle.gather_sequence(v, w.block_table[b], int(lens[b]), 0, w.P, "v")
+        assert np.all(np.isfinite(vals))
         assert np.all(np.isfinite(keys))
     assert np.isnan(k.astype(np.float32)).sum() == w.N * w.P * w.Hkv * w.D - sum(int(n) for n in lens) * w.Hkv * w.D

@@ -1,2 +1,2 @@
 """Seeded synthetic inputs for the paged decode workloads (no method arithmetic)."""
-from .synthetic import DecodeWorkload, workload, poison_unused  # noqa: F401
+from .synthetic import DecodeWorkload, workload  # noqa: F401

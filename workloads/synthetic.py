@@ -180,24 +180,3 @@ def workload(number, page_size=None, seed=None, batch=None):
         return _build("page-sweep-p%d" % P, rng, seed, B, 32, 8, 128, P, ctx, ctx + steps, steps,
                       1.0 / math.sqrt(128), partition_tokens=512)
     raise ValueError("workload number must be 1..5")
-
-
-def poison_unused(w, lens, fill=np.nan):
-    """Copy of the pools with every slot no sequence attends to set to ``fill``.
-
-    ``lens`` is the per-sequence context that will be attended; slots past it
-    in a sequence's last page, and pages no sequence uses, become NaN, so any
-    read of them shows in the output.
-    """
-    live = np.zeros((w.N, w.P), dtype=bool)
-    for b in range(w.B):
-        n = int(lens[b])
-        for j in range(_ceil_div(n, w.P)):
-            page = int(w.block_table[b, j])
-            live[page, :min(w.P, n - j * w.P)] = True
-    k = w.k_pool.copy()
-    v = w.v_pool.copy()
-    dead = ~live
-    k.transpose(0, 2, 1, 3)[dead] = fill
-    v.transpose(0, 2, 1, 3)[dead] = fill
-    return k, v
