@@ -170,6 +170,50 @@ int pkv_append_paged_decode_attention(void* out, const void* q, const void* k_ne
                                       float scale, int32_t partition_tokens, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/*
+ * pkv_decode_workspace_bytes_shared_prefix -- workspace size for
+ * pkv_paged_decode_attention_shared_prefix. Per (b, query head) it holds one
+ * partial per 256-token chunk of the shared prefix plus one per private
+ * partition (ceil((max_context - prefix_tokens) / partition_tokens)).
+ * Errors: PKV_ERR_INVALID_ARG (as pkv_decode_workspace_bytes; prefix_tokens
+ * negative, not a multiple of 16, above max_context, or > 0 with
+ * partition_tokens == 0).
+ */
+int pkv_decode_workspace_bytes_shared_prefix(int32_t B, int32_t Hq, int32_t D, int32_t max_context,
+                                             int32_t partition_tokens, int32_t prefix_tokens, size_t* bytes);
+
+/*
+ * pkv_paged_decode_attention_shared_prefix -- decode for a batch whose
+ * sequences all begin with the same prefix_tokens tokens held in the same
+ * physical pages (a system prompt stored once and shared by every request:
+ * dpshk §4.2, pgsm §3.2 and §4.3).
+ *
+ * Same result as pkv_paged_decode_attention (after the append, if k_new and
+ * v_new are given), computed so that the shared pages are read once per KV
+ * head instead of once per sequence: each 256-token chunk of the prefix is
+ * scored against all B * Hq / Hkv query rows of a KV head together on the
+ * matrix cores, each sequence's private tokens are processed as in the split
+ * path, and the log-sum-exp reduction merges both.
+ *
+ *   prefix_tokens: multiple of P, 0 <= prefix_tokens <= max_context; entries
+ *                  0 .. prefix_tokens / P - 1 of every block-table row must be
+ *                  identical (they are read from row 0). lens[b] <
+ *                  prefix_tokens makes row b NaN.
+ *   k_new, v_new : both NULL (no append) or both fp16 [B][Hkv][D]: append
+ *                  each sequence's new token at lens[b] - 1 first, as in
+ *                  pkv_append_paged_decode_attention (that position must lie
+ *                  after the prefix).
+ *   partition_tokens: > 0 (this path always splits).
+ *   workspace    : at least pkv_decode_workspace_bytes_shared_prefix bytes.
+ * Other arguments and errors as pkv_paged_decode_attention.
+ */
+int pkv_paged_decode_attention_shared_prefix(void* out, const void* q, const void* k_new, const void* v_new,
+                                             void* k_pool, void* v_pool, const int32_t* block_table,
+                                             int32_t max_pages, const int32_t* lens, int32_t B, int32_t Hq,
+                                             int32_t Hkv, int32_t D, int32_t P, int32_t N, int32_t max_context,
+                                             float scale, int32_t partition_tokens, int32_t prefix_tokens,
+                                             void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host page allocator (CPU only; no device calls)                           */
 /* ------------------------------------------------------------------------ */
@@ -207,9 +251,10 @@ int pkv_alloc_reserve(pkv_allocator* alloc, int32_t seq, int32_t n_tokens, int32
                       int32_t max_pages, int32_t* n_pages);
 
 /* Reserve for B sequences at once, all-or-nothing over the whole batch:
- * seqs[i] grows to n_tokens[i] tokens; block_table [B][max_pages] (host) gets
- * every row. Used once per decode step to add a page to the sequences whose
- * next token starts one. Errors as pkv_alloc_reserve. */
+ * seqs[i] grows to n_tokens[i] tokens, pages taken in batch order;
+ * block_table [B][max_pages] (host) gets every row. Used once per decode step
+ * to add a page to the sequences whose next token starts one. Errors as
+ * pkv_alloc_reserve, plus PKV_ERR_INVALID_ARG for a sequence listed twice. */
 int pkv_alloc_reserve_batch(pkv_allocator* alloc, int32_t B, const int32_t* seqs,
                             const int32_t* n_tokens, int32_t* block_table, int32_t max_pages);
 

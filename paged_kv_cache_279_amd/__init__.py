@@ -20,6 +20,7 @@ from .binding import (  # noqa: F401
     kv_append,
     lib,
     paged_decode_attention,
+    paged_decode_attention_shared_prefix,
     status_string,
     validate_tables,
 )

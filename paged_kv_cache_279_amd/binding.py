@@ -39,6 +39,11 @@ _SIGNATURES = {
     "pkv_append_paged_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                                          _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _vp,
                                                          ctypes.c_size_t, _vp]),
+    "pkv_decode_workspace_bytes_shared_prefix": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32,
+                                                                 ctypes.POINTER(ctypes.c_size_t)]),
+    "pkv_paged_decode_attention_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
+                                                                _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
+                                                                _i32, _i32, _vp, ctypes.c_size_t, _vp]),
     "pkv_alloc_create": (ctypes.c_int, [_i32, _i32, _ip, ctypes.POINTER(_vp)]),
     "pkv_alloc_destroy": (None, [_vp]),
     "pkv_alloc_reserve": (ctypes.c_int, [_vp, _i32, _i32, _ip, _i32, _ip]),
@@ -123,15 +128,20 @@ def kv_append(k_new, v_new, k_pool, v_pool, block_table, pos, stream=None):
     _check(rc, "pkv_kv_append")
 
 
-def decode_workspace_bytes(B, Hq, D, max_context, partition_tokens):
-    """pkv_decode_workspace_bytes."""
+def decode_workspace_bytes(B, Hq, D, max_context, partition_tokens, prefix_tokens=0):
+    """pkv_decode_workspace_bytes (or the shared-prefix variant when prefix_tokens > 0)."""
     out = ctypes.c_size_t(0)
-    _check(lib().pkv_decode_workspace_bytes(B, Hq, D, max_context, partition_tokens, ctypes.byref(out)),
-           "pkv_decode_workspace_bytes")
+    if prefix_tokens:
+        rc = lib().pkv_decode_workspace_bytes_shared_prefix(B, Hq, D, max_context, partition_tokens, prefix_tokens,
+                                                            ctypes.byref(out))
+    else:
+        rc = lib().pkv_decode_workspace_bytes(B, Hq, D, max_context, partition_tokens, ctypes.byref(out))
+    _check(rc, "pkv_decode_workspace_bytes")
     return out.value
 
 
-def _decode_args(out, q, k_pool, v_pool, block_table, lens, max_context, partition_tokens, workspace):
+def _decode_args(out, q, k_pool, v_pool, block_table, lens, max_context, partition_tokens, workspace,
+                 prefix_tokens=0):
     N, Hkv, P, D = k_pool.shape
     B, Hq, Dq = q.shape
     _, max_pages = block_table.shape
@@ -141,7 +151,7 @@ def _decode_args(out, q, k_pool, v_pool, block_table, lens, max_context, partiti
         out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
     if tuple(out.shape) != (B, Hq, D):
         raise ValueError("out must be [B][Hq][D]")
-    ws_bytes = decode_workspace_bytes(B, Hq, D, max_context, partition_tokens)
+    ws_bytes = decode_workspace_bytes(B, Hq, D, max_context, partition_tokens, prefix_tokens)
     if workspace is None and ws_bytes > 0:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
@@ -177,6 +187,31 @@ def append_paged_decode_attention(q, k_new, v_new, k_pool, v_pool, block_table, 
         _dev_ptr(block_table, torch.int32, "block_table"), max_pages, _dev_ptr(lens, torch.int32, "lens"),
         B, Hq, Hkv, D, P, N, int(max_context), float(scale), int(partition_tokens), ws_ptr, ws_len, _stream(stream))
     _check(rc, "pkv_append_paged_decode_attention")
+    return out
+
+
+def paged_decode_attention_shared_prefix(q, k_pool, v_pool, block_table, lens, max_context, scale,
+                                         partition_tokens, prefix_tokens, k_new=None, v_new=None, out=None,
+                                         workspace=None, stream=None):
+    """pkv_paged_decode_attention_shared_prefix: every sequence starts with the
+    same ``prefix_tokens`` tokens in the same pages; optional fused append."""
+    out, (N, Hkv, P, D, B, Hq, max_pages), ws_ptr, ws_len = _decode_args(
+        out, q, k_pool, v_pool, block_table, lens, max_context, partition_tokens, workspace, prefix_tokens)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+            raise ValueError("k_new/v_new must be [B][Hkv][D]")
+        kn, vn = _dev_ptr(k_new, torch.float16, "k_new"), _dev_ptr(v_new, torch.float16, "v_new")
+    else:
+        kn, vn = ctypes.c_void_p(0), ctypes.c_void_p(0)
+    rc = lib().pkv_paged_decode_attention_shared_prefix(
+        _dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"), kn, vn,
+        _dev_ptr(k_pool, torch.float16, "k_pool"), _dev_ptr(v_pool, torch.float16, "v_pool"),
+        _dev_ptr(block_table, torch.int32, "block_table"), max_pages, _dev_ptr(lens, torch.int32, "lens"),
+        B, Hq, Hkv, D, P, N, int(max_context), float(scale), int(partition_tokens), int(prefix_tokens),
+        ws_ptr, ws_len, _stream(stream))
+    _check(rc, "pkv_paged_decode_attention_shared_prefix")
     return out
 
 

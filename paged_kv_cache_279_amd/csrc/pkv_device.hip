@@ -64,7 +64,8 @@ constexpr int kThreads = kWave * kWaves;
 constexpr int kBlk = 16;                   // tokens per block (= one sub-block)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr size_t kWsAlign = 256;
-constexpr int32_t kMaxPartitions = 4096;   // partitions per sequence (reduce kernel LDS)
+constexpr int32_t kMaxPartitions = 4096;   // partial slots per (sequence, head) (reduce kernel LDS)
+constexpr int32_t kPrefixChunk = 256;      // shared-prefix tokens per prefix work item
 // Online-softmax rescaling is deferred until a head's block maximum exceeds
 // the running reference by this much (base-2 exponent units): probabilities
 // then stay below 2^8 and fp16/fp32 ranges are never approached.
@@ -94,8 +95,14 @@ struct DecodeParams {
   int32_t B, Hq, Hkv, N;
   int32_t p_shift;           // log2(P)
   int32_t max_context;
-  int32_t part_tokens;       // multiple of 16
-  int32_t n_parts;           // partitions per sequence in this launch
+  int32_t part_tokens;       // private partition size, multiple of 16
+  int32_t priv_parts;        // private partitions per sequence in the grid
+  int32_t prefix_tokens;     // shared leading tokens (0 = none)
+  int32_t prefix_chunk;      // tokens per prefix work item
+  int32_t n_chunks;          // prefix chunks (partial slots 0 .. n_chunks - 1)
+  int32_t n_tilegroups;      // prefix workgroups per (chunk, KV head)
+  int32_t n_prefix_wgs;      // prefix workgroups at the front of the grid
+  int32_t n_parts;           // partial slots per (sequence, query head)
   float scale_log2;          // scale * log2(e)
 };
 
@@ -164,97 +171,43 @@ __global__ __launch_bounds__(D) void kv_append_kernel(const half_t* __restrict__
 // decode: partition kernel
 // -------------------------------------------------------------------------
 
-template <int D, int G, bool SPLIT, bool FUSED>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams p) {
-  static_assert(D % 32 == 0 && G >= 1 && G <= 16, "shape");
+// Streaming state of one wave over a run of 16-token blocks: online softmax of
+// the 16 MFMA columns (query rows) and their fp32 output tile.
+template <int D>
+struct WaveState {
+  float4_t o[D / 16];
+  float m_ref;     // running reference max of this lane's column (base-2 units)
+  float l_part;    // this lane's share of the column's softmax denominator
+  bool bad_page;   // a page id outside [0, N) was met
+};
+
+// Streams blocks first, first + stride, ... (< nblocks) of the token range
+// [start, end) of the tiles reached through bt_row / kvh, for the query rows
+// held in qb (B operand of the score MFMA: lane (col, quad) holds query row
+// col, dims 32 j + 8 quad .. + 8). Shared by the prefix and the private roles.
+template <int D>
+__device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32_t* bt_row, int32_t kvh,
+                                              int32_t start, int32_t end, int32_t first, int32_t stride,
+                                              const half8_t (&qb)[D / 32], WaveState<D>& st, int lane) {
   constexpr int KL = D / 32;           // 16-byte loads per lane per block, for K and for V
   constexpr int NT = D / 16;           // 16-dim output tiles
-
-  __shared__ float sm_o[kWaves][G][D];
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
-
-  const int32_t id = blockIdx.x;
-  const int32_t kvh = id % p.Hkv;      // consecutive ids -> consecutive KV heads (XCD round robin)
-  const int32_t rest = id / p.Hkv;
-#if PKV_GRID_ORDER == 0
-  const int32_t b = rest % p.B;
-  const int32_t part = rest / p.B;
-#else
-  const int32_t part = rest % p.n_parts;
-  const int32_t b = rest / p.n_parts;
-#endif
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15;           // MFMA column: query head of the group / output dim
   const int quad = lane >> 4;          // MFMA k-group: tokens 4 quad .. 4 quad + 3
-
-  const int32_t L = p.lens[b];
-  const bool bad_len = L < 0 || L > p.max_context || L > (p.max_pages << p.p_shift);
-  const int32_t Lc = bad_len ? 0 : L;
-  const int32_t start = part * p.part_tokens;
-  const int32_t end = min(Lc, start + p.part_tokens);
-  const int64_t head_row0 = (int64_t)b * p.Hq + (int64_t)kvh * G;   // first query head of the group
-
-  if (start >= end) {
-    // nothing to attend in this partition; the unsplit kernel still owns the output row
-    if (!SPLIT && part == 0) {
-      const half_t fill = bad_len ? (half_t)__builtin_nanf("") : (half_t)0.0f;
-      for (int i = threadIdx.x; i < G * D; i += kThreads) p.out[head_row0 * D + i] = fill;
-    }
-    return;
-  }
-
-  const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
   const int32_t pmask = (1 << p.p_shift) - 1;
   const int64_t tile_elems = (int64_t)D << p.p_shift;       // one (page, kvh) tile
-
-  if constexpr (FUSED) {
-    // the workgroup owning the new token writes it to the pool; the barrier
-    // makes the stores visible to this workgroup's loads below
-    if (start <= Lc - 1 && Lc - 1 < end) {
-      const int32_t t = Lc - 1;
-      const int32_t page = bt_row[t >> p.p_shift];
-      if (page >= 0 && page < p.N) {
-        const int64_t sub = ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)((t & pmask) >> 4) * (kBlk * D);
-        const int64_t src = ((int64_t)b * p.Hkv + kvh) * D;
-        store_token<D>(p.k_pool_w + sub, p.v_pool_w + sub, t & 15, p.k_new + src, p.v_new + src, threadIdx.x);
-      }
-      __syncthreads();
-    }
-  }
-
-  // B operand of the score MFMA: lane (head col, quad) holds q[col][32 j + 8 quad .. + 8]
-  half8_t qb[KL];
-#pragma unroll
-  for (int j = 0; j < KL; ++j) {
-    uint4 t = {0, 0, 0, 0};
-    if (col < G) t = *reinterpret_cast<const uint4*>(p.q + (head_row0 + col) * D + j * 32 + quad * 8);
-    qb[j] = as_h8(t);
-  }
-
-  float4_t o[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) o[nt] = float4_t{0.f, 0.f, 0.f, 0.f};
-  float m_ref = kNegInf();     // running reference max of head `col` (base-2 units)
-  float l_part = 0.f;          // this lane's share of the softmax denominator
-  bool bad_page = false;
-  const float c = p.scale_log2;
-
   const int32_t nblocks = (end - start + kBlk - 1) / kBlk;
+  const float c = p.scale_log2;
 
   // Loads go through buffer descriptors built per 16-token block (base = the
   // block's sub-block, size 16 * D halves). Past the last block the size is 0:
   // the loads return zeros without touching memory, so the prefetch below is
-  // unconditional and the compiler keeps exactly one block's loads in flight.
+  // unconditional and the compiler keeps exactly kDepth blocks in flight.
   auto load_block = [&](int32_t blk, uint4 kr[KL], uint4 vr[KL]) {
     const bool live = blk < nblocks;
     const int32_t t0 = start + (live ? blk : 0) * kBlk;
     int32_t page = bt_row[t0 >> p.p_shift];
     if (page < 0 || page >= p.N) {
-      bad_page = bad_page || live;
-      page = 0;                         // stay in bounds; the row becomes NaN below
+      st.bad_page = st.bad_page || live;
+      page = 0;                         // stay in bounds; the row becomes NaN later
     }
     const int64_t off = ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)(t0 & pmask) * D;
     const int32_t bytes = live ? kBlk * D * 2 : 0;
@@ -264,15 +217,17 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.v_pool + off), (short)0, bytes, kBufferFlags);
 #pragma unroll
     for (int j = 0; j < KL; ++j)
-      kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, lane * 16 + j * 1024, 0, kKvLoadPolicy));
+      kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, lane * 16 + j * 1024, 0,
+                                                                             kKvLoadPolicy));
 #pragma unroll
     for (int j = 0; j < KL; ++j)
-      vr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, lane * 16 + j * 1024, 0, kKvLoadPolicy));
+      vr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, lane * 16 + j * 1024, 0,
+                                                                             kKvLoadPolicy));
   };
 
   auto consume = [&](int32_t blk, uint4 kr[KL], uint4 vr[KL]) {
     const int32_t t0 = start + blk * kBlk;
-    // scores of tokens 4 quad + i for head col
+    // scores of tokens 4 quad + i for query row col
     float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KL; ++j) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kr[j]), qb[j], s, 0, 0, 0);
@@ -294,59 +249,203 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
     float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
     bm = fmaxf(bm, __shfl_xor(bm, 16));
     bm = fmaxf(bm, __shfl_xor(bm, 32));
-    bm *= c;                            // block max of head col, base-2 units (c > 0)
-    if (__builtin_amdgcn_ballot_w64(bm > m_ref + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_ref, bm);
-      const float alpha = fast_exp2(m_ref - m_new);            // 0 on the first block
-      l_part *= alpha;
-      // output row 4 quad + i belongs to head 4 quad + i, whose alpha sits in lane 4 quad + i
+    bm *= c;                            // block max of column col, base-2 units (c > 0)
+    if (__builtin_amdgcn_ballot_w64(bm > st.m_ref + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(st.m_ref, bm);
+      const float alpha = fast_exp2(st.m_ref - m_new);         // 0 on the first block
+      st.l_part *= alpha;
+      // output row 4 quad + i belongs to column 4 quad + i, whose alpha sits in lane 4 quad + i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float a = __shfl(alpha, 4 * quad + i);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) o[nt][i] *= a;
+        for (int nt = 0; nt < NT; ++nt) st.o[nt][i] *= a;
       }
-      m_ref = m_new;
+      st.m_ref = m_new;
     }
     float pr[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(s[i], c, -m_ref));
-    l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(s[i], c, -st.m_ref));
+    st.l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     const half4_t pa = {(half_t)pr[0], (half_t)pr[1], (half_t)pr[2], (half_t)pr[3]};
 #pragma unroll
     for (int j = 0; j < KL; ++j) {
-      o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, lo4(vr[j]), o[2 * j], 0, 0, 0);
-      o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, hi4(vr[j]), o[2 * j + 1], 0, 0, 0);
+      st.o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, lo4(vr[j]), st.o[2 * j], 0, 0, 0);
+      st.o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, hi4(vr[j]), st.o[2 * j + 1], 0, 0, 0);
     }
   };
 
   // software pipeline over a ring of kDepth + 1 block buffers: while block i is
-  // consumed, blocks i + 1 .. i + kDepth (of this wave) are in flight. The
-  // scheduling barriers keep the compiler from sinking a prefetch below the
-  // first use of the current block.
+  // consumed, the next kDepth blocks of this wave are in flight. The scheduling
+  // barriers keep the compiler from sinking a prefetch below the first use of
+  // the current block.
   uint4 kr[kDepth + 1][KL], vr[kDepth + 1][KL];
 #pragma unroll
-  for (int r = 0; r < kDepth; ++r) load_block(wave + r * kWaves, kr[r], vr[r]);
-  int32_t blk = wave;
+  for (int r = 0; r < kDepth; ++r) load_block(first + r * stride, kr[r], vr[r]);
+  int32_t blk = first;
   while (true) {
 #pragma unroll
     for (int r = 0; r <= kDepth; ++r) {
-      if (blk >= nblocks) goto done;
-      load_block(blk + kDepth * kWaves, kr[(r + kDepth) % (kDepth + 1)], vr[(r + kDepth) % (kDepth + 1)]);
+      if (blk >= nblocks) return;
+      load_block(blk + kDepth * stride, kr[(r + kDepth) % (kDepth + 1)], vr[(r + kDepth) % (kDepth + 1)]);
       __builtin_amdgcn_sched_barrier(0);
       consume(blk, kr[r], vr[r]);
-      blk += kWaves;
+      blk += stride;
     }
   }
-done:
+}
+
+template <int D>
+__device__ __forceinline__ void init_state(WaveState<D>& st) {
+#pragma unroll
+  for (int nt = 0; nt < D / 16; ++nt) st.o[nt] = float4_t{0.f, 0.f, 0.f, 0.f};
+  st.m_ref = kNegInf();
+  st.l_part = 0.f;
+  st.bad_page = false;
+}
+
+// Grid: the shared-prefix workgroups (if any) first, then one workgroup per
+// (KV head, sequence, private partition).
+//
+// Prefix role (only with a shared prefix): workgroup (chunk c, tile group tg,
+// KV head). Wave w takes the 16 query rows tg * 64 + 16 w .. + 15 of the
+// B * G rows that read this KV head (row r = sequence r / G, head
+// kvh * G + r % G), streams every block of prefix chunk c once for all 16 of
+// them and writes their partials to slot c.
+//
+// Private role: workgroup (KV head, sequence b, partition). Its 4 waves split
+// the partition's blocks; columns are the G query heads of the group (padded
+// to 16 with zero heads); the waves merge through LDS into the final fp16 row
+// (unsplit) or the partial of slot n_chunks + partition.
+template <int D, int G, bool SPLIT, bool FUSED>
+__global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams p) {
+  static_assert(D % 32 == 0 && G >= 1 && G <= 16, "shape");
+  constexpr int KL = D / 32;
+  constexpr int NT = D / 16;
+
+  __shared__ float sm_o[kWaves][G][D];
+  __shared__ float sm_m[kWaves][G];
+  __shared__ float sm_l[kWaves][G];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int col = lane & 15;           // MFMA column: query row / output dim
+  const int quad = lane >> 4;
+
+  if constexpr (SPLIT) {
+    if ((int32_t)blockIdx.x < p.n_prefix_wgs) {
+      // ---------------- prefix role ----------------
+      const int32_t id = blockIdx.x;
+      const int32_t kvh = id % p.Hkv;
+      const int32_t rest = id / p.Hkv;
+      const int32_t tg = rest % p.n_tilegroups;
+      const int32_t chunk = rest / p.n_tilegroups;
+      const int32_t row = (tg * kWaves + wave) * 16 + col;    // this lane's query row
+      const bool live_col = row < p.B * G;
+      const int32_t rb = live_col ? row / G : 0;
+      const int64_t qrow = (int64_t)rb * p.Hq + (int64_t)kvh * G + row % G;
+      const int32_t start = chunk * p.prefix_chunk;
+      const int32_t end = min(p.prefix_tokens, start + p.prefix_chunk);
+      half8_t qb[KL];
+#pragma unroll
+      for (int j = 0; j < KL; ++j) {
+        uint4 t = {0, 0, 0, 0};
+        if (live_col) t = *reinterpret_cast<const uint4*>(p.q + qrow * D + j * 32 + quad * 8);
+        qb[j] = as_h8(t);
+      }
+      WaveState<D> st;
+      init_state<D>(st);
+      // the prefix pages are the same in every row of the table: read row 0
+      stream_blocks<D>(p, p.bt, kvh, start, end, 0, 1, qb, st, lane);
+      st.l_part += __shfl_xor(st.l_part, 16);
+      st.l_part += __shfl_xor(st.l_part, 32);
+      if (st.bad_page) st.l_part = __builtin_nanf("");
+      if (quad == 0 && live_col) {
+        const int64_t slot = qrow * p.n_parts + chunk;
+        p.part_m[slot] = st.m_ref;
+        p.part_l[slot] = st.l_part;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int32_t r = (tg * kWaves + wave) * 16 + 4 * quad + i;
+        if (r < p.B * G) {
+          const int64_t qr = (int64_t)(r / G) * p.Hq + (int64_t)kvh * G + r % G;
+          float* dst = p.part_o + (qr * p.n_parts + chunk) * D + col;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) dst[16 * nt] = st.o[nt][i];
+        }
+      }
+      return;
+    }
+  }
+
+  // ---------------- private role ----------------
+  const int32_t id = blockIdx.x - p.n_prefix_wgs;
+  const int32_t kvh = id % p.Hkv;      // consecutive ids -> consecutive KV heads (XCD round robin)
+  const int32_t rest = id / p.Hkv;
+#if PKV_GRID_ORDER == 0
+  const int32_t b = rest % p.B;
+  const int32_t part = rest / p.B;
+#else
+  const int32_t part = rest % p.priv_parts;
+  const int32_t b = rest / p.priv_parts;
+#endif
+
+  const int32_t L = p.lens[b];
+  const bool bad_len = L < p.prefix_tokens || L > p.max_context || L > (p.max_pages << p.p_shift);
+  const int32_t Lc = bad_len ? 0 : L;
+  const int32_t start = p.prefix_tokens + part * p.part_tokens;
+  const int32_t end = min(Lc, start + p.part_tokens);
+  const int64_t head_row0 = (int64_t)b * p.Hq + (int64_t)kvh * G;   // first query head of the group
+
+  if (start >= end) {
+    // nothing to attend in this partition; the unsplit kernel still owns the output row
+    if (!SPLIT && part == 0) {
+      const half_t fill = bad_len ? (half_t)__builtin_nanf("") : (half_t)0.0f;
+      for (int i = threadIdx.x; i < G * D; i += kThreads) p.out[head_row0 * D + i] = fill;
+    }
+    return;
+  }
+
+  const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
+
+  if constexpr (FUSED) {
+    // the workgroup owning the new token writes it to the pool; the barrier
+    // makes the stores visible to this workgroup's loads below
+    if (start <= Lc - 1 && Lc - 1 < end) {
+      const int32_t t = Lc - 1;
+      const int32_t page = bt_row[t >> p.p_shift];
+      if (page >= 0 && page < p.N) {
+        const int64_t tile_elems = (int64_t)D << p.p_shift;
+        const int32_t pmask = (1 << p.p_shift) - 1;
+        const int64_t sub = ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)((t & pmask) >> 4) * (kBlk * D);
+        const int64_t src = ((int64_t)b * p.Hkv + kvh) * D;
+        store_token<D>(p.k_pool_w + sub, p.v_pool_w + sub, t & 15, p.k_new + src, p.v_new + src, threadIdx.x);
+      }
+      __syncthreads();
+    }
+  }
+
+  // B operand of the score MFMA: lane (head col, quad) holds q[col][32 j + 8 quad .. + 8]
+  half8_t qb[KL];
+#pragma unroll
+  for (int j = 0; j < KL; ++j) {
+    uint4 t = {0, 0, 0, 0};
+    if (col < G) t = *reinterpret_cast<const uint4*>(p.q + (head_row0 + col) * D + j * 32 + quad * 8);
+    qb[j] = as_h8(t);
+  }
+
+  WaveState<D> st;
+  init_state<D>(st);
+  stream_blocks<D>(p, bt_row, kvh, start, end, wave, kWaves, qb, st, lane);
 
   // per-head denominators of this wave: sum the 4 quads of column col
-  l_part += __shfl_xor(l_part, 16);
-  l_part += __shfl_xor(l_part, 32);
-  if (bad_page) l_part = __builtin_nanf("");
+  st.l_part += __shfl_xor(st.l_part, 16);
+  st.l_part += __shfl_xor(st.l_part, 32);
+  if (st.bad_page) st.l_part = __builtin_nanf("");
   if (quad == 0 && col < G) {
-    sm_m[wave][col] = m_ref;
-    sm_l[wave][col] = l_part;
+    sm_m[wave][col] = st.m_ref;
+    sm_l[wave][col] = st.l_part;
   }
   // output tile: lane holds rows (heads) 4 quad + i of dims 16 nt + col
 #pragma unroll
@@ -354,7 +453,7 @@ done:
     const int h = 4 * quad + i;
     if (h < G) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sm_o[wave][h][16 * nt + col] = o[nt][i];
+      for (int nt = 0; nt < NT; ++nt) sm_o[wave][h][16 * nt + col] = st.o[nt][i];
     }
   }
   __syncthreads();
@@ -375,7 +474,7 @@ done:
       O = fmaf(wt, sm_o[w][h][d], O);
     }
     if constexpr (SPLIT) {
-      const int64_t slot = (head_row0 + h) * p.n_parts + part;
+      const int64_t slot = (head_row0 + h) * p.n_parts + p.n_chunks + part;
       p.part_o[slot * D + d] = O;
       if (d == 0) {
         p.part_m[slot] = M;
@@ -405,8 +504,9 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
   const int32_t b = (int32_t)(bh / p.Hq);
   const int d = threadIdx.x;
   const int32_t L = p.lens[b];
-  const bool bad_len = L < 0 || L > p.max_context || L > (p.max_pages << p.p_shift);
-  const int32_t np = bad_len ? 0 : (L + p.part_tokens - 1) / p.part_tokens;
+  const bool bad_len = L < p.prefix_tokens || L > p.max_context || L > (p.max_pages << p.p_shift);
+  // slots 0 .. n_chunks - 1: shared-prefix chunks; then the private partitions
+  const int32_t np = bad_len ? 0 : p.n_chunks + (L - p.prefix_tokens + p.part_tokens - 1) / p.part_tokens;
   const float* pm = p.part_m + bh * p.n_parts;
   const float* pl = p.part_l + bh * p.n_parts;
   const float* po = p.part_o + bh * p.n_parts * D + d;
@@ -483,8 +583,40 @@ WsLayout ws_layout(int64_t B, int64_t Hq, int64_t D, int64_t n_parts) {
   return WsLayout{0, stats, 2 * stats, 2 * stats + outs};
 }
 
-int32_t parts_for(int32_t max_context, int32_t partition_tokens) {
-  return partition_tokens > 0 ? (max_context + partition_tokens - 1) / partition_tokens : 1;
+// Work decomposition of one decode call.
+struct Plan {
+  bool split;
+  int32_t part_tokens;     // private partition size (unsplit: covers any admissible length)
+  int32_t priv_parts;      // private partitions per sequence in the grid
+  int32_t n_chunks;        // shared-prefix chunks
+  int32_t n_tilegroups;    // prefix workgroups per (chunk, KV head)
+  int32_t n_prefix_wgs;
+  int32_t n_parts;         // partial slots per (sequence, query head)
+  int64_t grid;
+};
+
+int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_context, int32_t partition_tokens,
+              int32_t prefix_tokens, Plan* pl) {
+  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_context < 0 || partition_tokens < 0 ||
+      partition_tokens % kBlk != 0 || prefix_tokens < 0 || prefix_tokens % kBlk != 0 || prefix_tokens > max_context)
+    return PKV_ERR_INVALID_ARG;
+  if (prefix_tokens > 0 && partition_tokens == 0) return PKV_ERR_INVALID_ARG;
+  Plan p{};
+  p.split = partition_tokens > 0;
+  p.part_tokens = p.split ? partition_tokens : ((max_context + kBlk - 1) / kBlk) * kBlk + kBlk;
+  p.priv_parts = p.split ? (max_context - prefix_tokens + partition_tokens - 1) / partition_tokens : 1;
+  p.n_chunks = (prefix_tokens + kPrefixChunk - 1) / kPrefixChunk;
+  const int64_t rows = static_cast<int64_t>(B) * (Hq / Hkv);
+  const int64_t tiles = (rows + 15) / 16;
+  p.n_tilegroups = p.n_chunks > 0 ? static_cast<int32_t>((tiles + kWaves - 1) / kWaves) : 0;
+  const int64_t n_prefix = static_cast<int64_t>(p.n_chunks) * p.n_tilegroups * Hkv;
+  p.n_parts = p.n_chunks + p.priv_parts;
+  if (p.split && p.n_parts > kMaxPartitions) return PKV_ERR_INVALID_ARG;
+  p.grid = n_prefix + static_cast<int64_t>(p.priv_parts) * B * Hkv;
+  if (p.grid > 0x7fffffffLL || static_cast<int64_t>(B) * Hq > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
+  p.n_prefix_wgs = static_cast<int32_t>(n_prefix);
+  *pl = p;
+  return PKV_OK;
 }
 
 template <int D, int G, bool SPLIT, bool FUSED>
@@ -513,10 +645,10 @@ hipError_t dispatch_d(int D, int G, const DecodeParams& p, hipStream_t s, int64_
 int decode_common(void* out, const void* q, const void* k_new, const void* v_new, const void* k_pool,
                   const void* v_pool, void* k_pool_w, void* v_pool_w, const int32_t* bt, int32_t max_pages,
                   const int32_t* lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
-                  int32_t max_context, float scale, int32_t partition_tokens, void* workspace,
-                  size_t workspace_bytes, void* stream, bool fused) {
+                  int32_t max_context, float scale, int32_t partition_tokens, int32_t prefix_tokens,
+                  void* workspace, size_t workspace_bytes, void* stream, bool fused) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || N <= 0 || max_pages <= 0 || max_context < 0 ||
-      partition_tokens < 0)
+      partition_tokens < 0 || prefix_tokens < 0)
     return PKV_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return PKV_ERR_INVALID_ARG;
   if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
@@ -526,24 +658,21 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   const int p_shift = log2_page(P);
   if (p_shift < 0) return PKV_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PKV_ERR_UNSUPPORTED;
-  if (partition_tokens % kBlk != 0) return PKV_ERR_INVALID_ARG;
+  if (prefix_tokens % P != 0) return PKV_ERR_INVALID_ARG;       // shared pages hold prefix tokens only
   if (static_cast<int64_t>(max_context) > (static_cast<int64_t>(max_pages) << p_shift)) return PKV_ERR_INVALID_ARG;
+  Plan plan;
+  const int rc = make_plan(B, Hq, Hkv, max_context, partition_tokens, prefix_tokens, &plan);
+  if (rc != PKV_OK) return rc;
   if (B == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !bt || !lens) return PKV_ERR_INVALID_ARG;
   if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(bt, 4) ||
       !aligned(lens, 4))
     return PKV_ERR_INVALID_ARG;
   if (fused && (!k_new || !v_new || !aligned(k_new, 16) || !aligned(v_new, 16))) return PKV_ERR_INVALID_ARG;
-  // every index the kernels form must fit in 64-bit arithmetic and the grid in 31 bits
+  // every index the kernels form must fit in 64-bit arithmetic
   const int64_t pool_elems = static_cast<int64_t>(N) * Hkv * P * D;
   if (pool_elems / N / Hkv / P != D) return PKV_ERR_INVALID_ARG;
   if (static_cast<int64_t>(B) * max_pages > (int64_t{1} << 40)) return PKV_ERR_INVALID_ARG;
-
-  const bool split = partition_tokens > 0;
-  const int32_t n_parts = parts_for(max_context, partition_tokens);
-  if (split && n_parts > kMaxPartitions) return PKV_ERR_INVALID_ARG;
-  const int64_t grid = static_cast<int64_t>(n_parts) * B * Hkv;
-  if (grid > 0x7fffffffLL || static_cast<int64_t>(B) * Hq > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
 
   DecodeParams prm{};
   prm.out = static_cast<half_t*>(out);
@@ -563,13 +692,18 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   prm.N = N;
   prm.p_shift = p_shift;
   prm.max_context = max_context;
-  // unsplit: one partition covering any admissible length
-  prm.part_tokens = split ? partition_tokens : ((max_context + kBlk - 1) / kBlk) * kBlk + kBlk;
-  prm.n_parts = n_parts;
+  prm.part_tokens = plan.part_tokens;
+  prm.priv_parts = plan.priv_parts;
+  prm.prefix_tokens = prefix_tokens;
+  prm.prefix_chunk = kPrefixChunk;
+  prm.n_chunks = plan.n_chunks;
+  prm.n_tilegroups = plan.n_tilegroups;
+  prm.n_prefix_wgs = plan.n_prefix_wgs;
+  prm.n_parts = plan.n_parts;
   prm.scale_log2 = scale * kLog2e;
 
-  if (split) {
-    const WsLayout ws = ws_layout(B, Hq, D, n_parts);
+  if (plan.split) {
+    const WsLayout ws = ws_layout(B, Hq, D, plan.n_parts);
     if (!workspace) return PKV_ERR_INVALID_ARG;
     if (!aligned(workspace, kWsAlign)) return PKV_ERR_INVALID_ARG;
     if (workspace_bytes < ws.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
@@ -580,18 +714,30 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t grid = plan.grid;
   hipError_t e = hipSuccess;
   if (grid > 0) {
-    if (split) e = fused ? dispatch_d<true, true>(D, G, prm, s, grid) : dispatch_d<true, false>(D, G, prm, s, grid);
+    if (plan.split) e = fused ? dispatch_d<true, true>(D, G, prm, s, grid) : dispatch_d<true, false>(D, G, prm, s, grid);
     else e = fused ? dispatch_d<false, true>(D, G, prm, s, grid) : dispatch_d<false, false>(D, G, prm, s, grid);
     if (e != hipSuccess) return PKV_ERR_HIP;
   }
-  if (split) {
+  if (plan.split) {
     const uint32_t rows = static_cast<uint32_t>(static_cast<int64_t>(B) * Hq);
     if (D == 64) hipLaunchKernelGGL(lse_reduce_kernel<64>, dim3(rows), dim3(64), 0, s, prm);
     else hipLaunchKernelGGL(lse_reduce_kernel<128>, dim3(rows), dim3(128), 0, s, prm);
     if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   }
+  return PKV_OK;
+}
+
+int workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context, int32_t partition_tokens,
+                    int32_t prefix_tokens, size_t* bytes) {
+  if (!bytes || D <= 0) return PKV_ERR_INVALID_ARG;
+  Plan plan;
+  // Hkv does not change the slot count; any divisor of Hq gives the same plan sizes
+  const int rc = make_plan(B, Hq, Hq, max_context, partition_tokens, prefix_tokens, &plan);
+  if (rc != PKV_OK) return rc;
+  *bytes = plan.split ? ws_layout(B, Hq, D, plan.n_parts).total : 0;
   return PKV_OK;
 }
 
@@ -631,11 +777,12 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_po
 
 int pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context, int32_t partition_tokens,
                                size_t* bytes) {
-  if (!bytes || B < 0 || Hq <= 0 || D <= 0 || max_context < 0 || partition_tokens < 0 ||
-      partition_tokens % kBlk != 0)
-    return PKV_ERR_INVALID_ARG;
-  *bytes = partition_tokens == 0 ? 0 : ws_layout(B, Hq, D, parts_for(max_context, partition_tokens)).total;
-  return PKV_OK;
+  return workspace_bytes(B, Hq, D, max_context, partition_tokens, 0, bytes);
+}
+
+int pkv_decode_workspace_bytes_shared_prefix(int32_t B, int32_t Hq, int32_t D, int32_t max_context,
+                                             int32_t partition_tokens, int32_t prefix_tokens, size_t* bytes) {
+  return workspace_bytes(B, Hq, D, max_context, partition_tokens, prefix_tokens, bytes);
 }
 
 int pkv_paged_decode_attention(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -644,7 +791,7 @@ int pkv_paged_decode_attention(void* out, const void* q, const void* k_pool, con
                                float scale, int32_t partition_tokens, void* workspace, size_t workspace_bytes,
                                void* stream) {
   return decode_common(out, q, nullptr, nullptr, k_pool, v_pool, nullptr, nullptr, block_table, max_pages, lens, B,
-                       Hq, Hkv, D, P, N, max_context, scale, partition_tokens, workspace, workspace_bytes, stream,
+                       Hq, Hkv, D, P, N, max_context, scale, partition_tokens, 0, workspace, workspace_bytes, stream,
                        false);
 }
 
@@ -654,7 +801,20 @@ int pkv_append_paged_decode_attention(void* out, const void* q, const void* k_ne
                                       int32_t N, int32_t max_context, float scale, int32_t partition_tokens,
                                       void* workspace, size_t workspace_bytes, void* stream) {
   return decode_common(out, q, k_new, v_new, k_pool, v_pool, k_pool, v_pool, block_table, max_pages, lens, B, Hq,
-                       Hkv, D, P, N, max_context, scale, partition_tokens, workspace, workspace_bytes, stream, true);
+                       Hkv, D, P, N, max_context, scale, partition_tokens, 0, workspace, workspace_bytes, stream, true);
+}
+
+int pkv_paged_decode_attention_shared_prefix(void* out, const void* q, const void* k_new, const void* v_new,
+                                             void* k_pool, void* v_pool, const int32_t* block_table,
+                                             int32_t max_pages, const int32_t* lens, int32_t B, int32_t Hq,
+                                             int32_t Hkv, int32_t D, int32_t P, int32_t N, int32_t max_context,
+                                             float scale, int32_t partition_tokens, int32_t prefix_tokens,
+                                             void* workspace, size_t workspace_bytes, void* stream) {
+  if ((k_new == nullptr) != (v_new == nullptr)) return PKV_ERR_INVALID_ARG;
+  const bool fused = k_new != nullptr;
+  return decode_common(out, q, k_new, v_new, k_pool, v_pool, k_pool, v_pool, block_table, max_pages, lens, B, Hq,
+                       Hkv, D, P, N, max_context, scale, partition_tokens, prefix_tokens, workspace, workspace_bytes,
+                       stream, fused);
 }
 
 }  // extern "C"

@@ -330,3 +330,90 @@ def test_invalid_arguments_return_status_codes():
     with pytest.raises(m.PkvError) as e:
         m.paged_decode_attention(q, kp, vp, bt, lens, 256, w.scale, partition_tokens=64, workspace=ws)
     assert e.value.status == m.PKV_ERR_WORKSPACE_TOO_SMALL
+
+
+# ---------------------------------------------------------------------------
+# shared-prefix path
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("batch,part,fused", [(6, 512, False), (6, 1024, True), (3, 512, True), (None, 1024, True)])
+def test_shared_prefix_matches_oracle(batch, part, fused):
+    w = wl(3, None, batch)
+    step = 0
+    lens = w.lens(step)
+    prefix = w.shared_prefix_pages * w.P
+    say("shared prefix B=%d part=%d fused=%s" % (w.B, part, fused))
+    if fused:
+        k0, v0 = poison_unused(w, lens - 1)
+        kp, vp = dev(k0), dev(v0)
+        got = pkv().paged_decode_attention_shared_prefix(dev(w.q), kp, vp, dev(w.block_table), dev(lens),
+                                                         int(lens.max()), w.scale, part, prefix,
+                                                         k_new=dev(w.k_new[step]), v_new=dev(w.v_new[step]))
+        torch.cuda.synchronize()
+        rk, rv = oracle.kv_append(k0, v0, w.k_new[step], w.v_new[step], w.block_table, w.pos(step), w.P)
+        assert np.array_equal(host(kp).view(np.uint16), rk.view(np.uint16))
+        assert np.array_equal(host(vp).view(np.uint16), rv.view(np.uint16))
+    else:
+        rk, rv, lens = _prepared(w, step)
+        got = pkv().paged_decode_attention_shared_prefix(dev(w.q), dev(rk), dev(rv), dev(w.block_table), dev(lens),
+                                                         int(lens.max()), w.scale, part, prefix)
+        torch.cuda.synchronize()
+    ref = oracle.decode_attention(w.q, rk, rv, w.block_table, lens, w.scale, w.P)
+    check_close(got, ref, "shared prefix B=%d" % w.B)
+
+
+def _prefix_case(rng, B, Hkv, G, D, P, prefix_pages, lens):
+    """Every row starts with the same prefix pages; private pages follow."""
+    Hq = Hkv * G
+    npg = [max(prefix_pages, -(-int(n) // P)) for n in lens]
+    N = prefix_pages + sum(n - prefix_pages for n in npg) + 2
+    perm = rng.permutation(N).astype(np.int32)
+    bt = np.full((B, max(npg)), -1, np.int32)
+    cur = prefix_pages
+    for b in range(B):
+        bt[b, :prefix_pages] = perm[:prefix_pages]
+        bt[b, prefix_pages:npg[b]] = perm[cur:cur + npg[b] - prefix_pages]
+        cur += npg[b] - prefix_pages
+    kp = rng.standard_normal((N, Hkv, P, D)).astype(np.float16)
+    vp = rng.standard_normal((N, Hkv, P, D)).astype(np.float16)
+    q = rng.standard_normal((B, Hq, D)).astype(np.float16)
+    return q, kp, vp, bt
+
+
+@pytest.mark.parametrize("B,Hkv,G,D,P,prefix_pages,part", [
+    (5, 2, 4, 128, 16, 20, 256),     # 20 rows: last column tile partly empty
+    (3, 2, 1, 64, 64, 5, 512),       # MHA, prefix chunk boundary inside a page
+    (9, 1, 8, 128, 32, 9, 1024),
+    (2, 2, 16, 64, 16, 17, 16),      # G = 16 fills a whole column tile per sequence
+])
+def test_shared_prefix_shapes_and_edges(B, Hkv, G, D, P, prefix_pages, part):
+    rng = np.random.default_rng(61 + B + G)
+    prefix = prefix_pages * P
+    lens = np.array([prefix + int(x) for x in rng.integers(1, 700, size=B)], np.int32)
+    lens[0] = prefix                       # nothing private
+    if B > 2:
+        lens[1] = prefix + 1
+    q, kp, vp, bt = _prefix_case(rng, B, Hkv, G, D, P, prefix_pages, lens)
+    say("prefix shapes B=%d Hkv=%d G=%d D=%d P=%d prefix=%d part=%d" % (B, Hkv, G, D, P, prefix, part))
+    ref = oracle.decode_attention(q, kp, vp, bt, lens, 1 / math.sqrt(D), P)
+    got = pkv().paged_decode_attention_shared_prefix(dev(q), dev(kp), dev(vp), dev(bt), dev(lens), int(lens.max()),
+                                                     1 / math.sqrt(D), part, prefix)
+    torch.cuda.synchronize()
+    check_close(got, ref, "prefix shapes")
+    # a sequence shorter than the declared prefix is flagged, the others are unchanged
+    short = lens.copy()
+    short[-1] = prefix - 1
+    got2 = host(pkv().paged_decode_attention_shared_prefix(dev(q), dev(kp), dev(vp), dev(bt), dev(short),
+                                                           int(lens.max()), 1 / math.sqrt(D), part, prefix))
+    assert np.all(np.isnan(got2[-1].astype(np.float64)))
+    assert np.array_equal(got2[:-1].view(np.uint16), host(got)[:-1].view(np.uint16))
+
+
+def test_shared_prefix_argument_checks():
+    m = pkv()
+    w = wl(3, None, 3)
+    args = (dev(w.q), dev(w.k_pool), dev(w.v_pool), dev(w.block_table), dev(w.lens(0)), int(w.lens(0).max()), w.scale)
+    for part, prefix in [(0, 2048), (512, 2040), (512, 24)]:      # unsplit; not a multiple of 16; not a multiple of P
+        with pytest.raises(m.PkvError) as e:
+            m.paged_decode_attention_shared_prefix(*args, part, prefix)
+        assert e.value.status == m.PKV_ERR_INVALID_ARG

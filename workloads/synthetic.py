@@ -23,12 +23,13 @@ few thousand tokens as on dpshk §2.1):
    pool sized to the demand, append one token then attend over context+1.
 3. llama3-8b-gqa-prefix: B=64, Hq=32, Hkv=8, D=128, P=16; every sequence starts
    with the same 128 pages (a 2048-token system prefix); private context
-   ~ round(LogNormal(ln 1024, ln 2)) clipped to [128, 8192]; append one token.
+   ~ round(LogNormal(ln 1024, ln 2)) clipped to [128, 8192]; append one token;
+   1024-token partitions.
 4. long-context: B=4, Hq=32, Hkv=8, D=128, 32767 cached tokens + 1 appended
    = 32768, P=16, split into 512-token partitions.
 5. page-sweep: B=32, Hq=32, Hkv=8, D=128, cached context ~ U{200..4000},
    P in {16, 32, 64, 128}, 64 consecutive append+decode steps; pages for all 64
-   steps reserved up front.
+   steps reserved up front; 512-token partitions.
 """
 
 import math
@@ -166,7 +167,7 @@ def workload(number, page_size=None, seed=None, batch=None):
         private = np.clip(np.rint(rng.lognormal(math.log(1024.0), math.log(2.0), size=B)), 128, 8192).astype(np.int64)
         ctx = PREFIX_PAGES_W3 * 16 + private
         return _build("llama3-8b-gqa-prefix", rng, seed, B, 32, 8, 128, 16, ctx, ctx + 1, 1, 1.0 / math.sqrt(128),
-                      prefix_pages=PREFIX_PAGES_W3, partition_tokens=512)
+                      prefix_pages=PREFIX_PAGES_W3, partition_tokens=1024)
     if number == 4:
         B = batch or 4
         ctx = np.full(B, 32767, dtype=np.int64)
