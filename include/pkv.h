@@ -105,13 +105,14 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_po
 /*
  * pkv_decode_workspace_bytes -- workspace size split-context decode needs.
  *
- * With partition_tokens > 0 the context of every sequence is cut into
- * partitions of that many tokens and each partition's softmax statistics go
- * to the workspace: per (b, query head, partition) a float max, a float sum
- * and D floats of unnormalised output, ceil(max_context / partition_tokens)
- * partitions per sequence. partition_tokens == 0 needs no workspace (*bytes
- * = 0). Errors: PKV_ERR_INVALID_ARG (negative sizes, partition_tokens not a
- * multiple of 16, null `bytes`).
+ * In split mode the private tokens of every sequence are divided among a
+ * fixed set of workgroups (see pkv_paged_decode_attention); each piece a
+ * workgroup takes of a (sequence, KV head) leaves, per query head, a float
+ * max, a float sum and D floats of unnormalised output, plus a small header
+ * and one int per sequence. The size does not depend on max_context.
+ * partition_tokens == 0 needs no workspace (*bytes = 0).
+ * Errors: PKV_ERR_INVALID_ARG (negative sizes, partition_tokens not a
+ * multiple of 16, B > 4096 with partition_tokens > 0, null `bytes`).
  */
 int pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context,
                                int32_t partition_tokens, size_t* bytes);
@@ -138,9 +139,14 @@ int pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_con
  *                  the workspace; must be <= max_pages * P.
  *   scale        : softmax scale, normally 1/sqrt(D).
  *   partition_tokens: 0 = one workgroup per (sequence, KV head) over the whole
- *                  context; otherwise a positive multiple of 16: the context is
- *                  split into partitions of that many tokens, processed in
- *                  parallel, then merged by a log-sum-exp reduction kernel.
+ *                  context, writing the output directly. Otherwise a positive
+ *                  multiple of 16 (split mode, at most 4096 sequences): the
+ *                  16-token blocks of all (KV head, sequence) contexts form
+ *                  one list that is divided evenly among a fixed set of
+ *                  workgroups, each taking at least partition_tokens tokens
+ *                  (pieces may cross from one sequence into the next); a
+ *                  log-sum-exp reduction kernel then merges the pieces of
+ *                  every sequence. This balances batches of mixed lengths.
  *   workspace    : device buffer of at least pkv_decode_workspace_bytes bytes
  *                  (ignored when partition_tokens == 0), 256-byte aligned.
  * Errors: PKV_ERR_INVALID_ARG, PKV_ERR_UNSUPPORTED,
@@ -172,9 +178,10 @@ int pkv_append_paged_decode_attention(void* out, const void* q, const void* k_ne
 
 /*
  * pkv_decode_workspace_bytes_shared_prefix -- workspace size for
- * pkv_paged_decode_attention_shared_prefix. Per (b, query head) it holds one
- * partial per 256-token chunk of the shared prefix plus one per private
- * partition (ceil((max_context - prefix_tokens) / partition_tokens)).
+ * pkv_paged_decode_attention_shared_prefix: the split path's per-sequence
+ * block counts and per-piece partials (score max, denominator, D outputs for
+ * 16 query rows), with one extra segment per 16 query rows of a KV head for
+ * the shared prefix.
  * Errors: PKV_ERR_INVALID_ARG (as pkv_decode_workspace_bytes; prefix_tokens
  * negative, not a multiple of 16, above max_context, or > 0 with
  * partition_tokens == 0).
@@ -190,10 +197,11 @@ int pkv_decode_workspace_bytes_shared_prefix(int32_t B, int32_t Hq, int32_t D, i
  *
  * Same result as pkv_paged_decode_attention (after the append, if k_new and
  * v_new are given), computed so that the shared pages are read once per KV
- * head instead of once per sequence: each 256-token chunk of the prefix is
- * scored against all B * Hq / Hkv query rows of a KV head together on the
- * matrix cores, each sequence's private tokens are processed as in the split
- * path, and the log-sum-exp reduction merges both.
+ * head and 16 query rows instead of once per sequence: the prefix blocks are
+ * scored against 16 query rows of a KV head at a time (a full matrix-core
+ * tile), and these prefix pieces and every sequence's private blocks form one
+ * work list per KV head, cut evenly among the split path's workgroups; the
+ * log-sum-exp reduction merges both.
  *
  *   prefix_tokens: multiple of P, 0 <= prefix_tokens <= max_context; entries
  *                  0 .. prefix_tokens / P - 1 of every block-table row must be
@@ -201,8 +209,9 @@ int pkv_decode_workspace_bytes_shared_prefix(int32_t B, int32_t Hq, int32_t D, i
  *                  prefix_tokens makes row b NaN.
  *   k_new, v_new : both NULL (no append) or both fp16 [B][Hkv][D]: append
  *                  each sequence's new token at lens[b] - 1 first, as in
- *                  pkv_append_paged_decode_attention (that position must lie
- *                  after the prefix).
+ *                  pkv_append_paged_decode_attention. That position must lie
+ *                  after the prefix: with prefix_tokens > 0, a row with
+ *                  lens[b] <= prefix_tokens is NaN and appends nothing.
  *   partition_tokens: > 0 (this path always splits).
  *   workspace    : at least pkv_decode_workspace_bytes_shared_prefix bytes.
  * Other arguments and errors as pkv_paged_decode_attention.

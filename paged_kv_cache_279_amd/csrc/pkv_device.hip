@@ -47,15 +47,16 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X).
 #ifndef PKV_PREFETCH_DEPTH
-#define PKV_PREFETCH_DEPTH 3
+#define PKV_PREFETCH_DEPTH 2
 #endif
 #ifndef PKV_KV_LOAD_POLICY
 #define PKV_KV_LOAD_POLICY 2
 #endif
 // Order of the (partition, sequence) work items in the grid: 0 = partition
 // major (every sequence's first partition first), 1 = sequence major.
-#ifndef PKV_GRID_ORDER
-#define PKV_GRID_ORDER 0
+// Private workgroups of the balanced split schedule (2 per CU on 256 CUs).
+#ifndef PKV_FLAT_WORKGROUPS
+#define PKV_FLAT_WORKGROUPS 512
 #endif
 
 constexpr int kWave = 64;
@@ -65,7 +66,7 @@ constexpr int kBlk = 16;                   // tokens per block (= one sub-block)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr size_t kWsAlign = 256;
 constexpr int32_t kMaxPartitions = 4096;   // partial slots per (sequence, head) (reduce kernel LDS)
-constexpr int32_t kPrefixChunk = 256;      // shared-prefix tokens per prefix work item
+constexpr int32_t kMaxFlatBatch = 4096;    // sequences per split call (LDS prefix sums)
 // Online-softmax rescaling is deferred until a head's block maximum exceeds
 // the running reference by this much (base-2 exponent units): probabilities
 // then stay below 2^8 and fp16/fp32 ranges are never approached.
@@ -74,8 +75,13 @@ constexpr float kRescaleSlack = 8.0f;
 constexpr int kDepth = PKV_PREFETCH_DEPTH;
 // Word 3 of a raw gfx9 buffer descriptor (32-bit data format, no swizzle).
 constexpr int32_t kBufferFlags = 0x00020000;
-// Cache policy of the K/V loads: 2 = non-temporal (streamed once per step).
+// Cache policy of the K/V loads: 2 = non-temporal (private pages are streamed
+// once per step); shared-prefix pages use the default policy so they stay in L2.
 constexpr int32_t kKvLoadPolicy = PKV_KV_LOAD_POLICY;
+#ifndef PKV_PREFIX_LOAD_POLICY
+#define PKV_PREFIX_LOAD_POLICY 0
+#endif
+constexpr int32_t kPrefixLoadPolicy = PKV_PREFIX_LOAD_POLICY;
 
 struct DecodeParams {
   half_t* out;               // [B][Hq][D]
@@ -88,21 +94,20 @@ struct DecodeParams {
   const half_t* v_new;
   const int32_t* bt;         // [B][max_pages]
   const int32_t* lens;       // [B]
-  float* part_m;             // [B][Hq][n_parts], base-2 scaled score max
-  float* part_l;             // [B][Hq][n_parts]
-  float* part_o;             // [B][Hq][n_parts][D], unnormalised
   int32_t max_pages;
   int32_t B, Hq, Hkv, N;
   int32_t p_shift;           // log2(P)
   int32_t max_context;
-  int32_t part_tokens;       // private partition size, multiple of 16
-  int32_t priv_parts;        // private partitions per sequence in the grid
-  int32_t prefix_tokens;     // shared leading tokens (0 = none)
-  int32_t prefix_chunk;      // tokens per prefix work item
-  int32_t n_chunks;          // prefix chunks (partial slots 0 .. n_chunks - 1)
-  int32_t n_tilegroups;      // prefix workgroups per (chunk, KV head)
-  int32_t n_prefix_wgs;      // prefix workgroups at the front of the grid
-  int32_t n_parts;           // partial slots per (sequence, query head)
+  int32_t prefix_tokens;     // shared leading tokens (0 = none), multiple of P
+  int32_t min_len;           // split mode: shorter sequences are invalid (NaN rows)
+  int32_t n_tiles;           // 16-row query tiles per KV head that read the prefix (0 = none)
+  int32_t n_flat_wgs;        // workgroups of the balanced split schedule
+  int32_t min_piece;         // minimum blocks per piece
+  int32_t* flat_hdr;         // [2]: private blocks per KV head, units per workgroup
+  int32_t* flat_cum;         // [B]: inclusive prefix sums of private blocks
+  float* flat_m;             // [slots][16]: piece partials, base-2 scaled score max
+  float* flat_l;             // [slots][16]: softmax denominators
+  float* flat_o;             // [slots][16][D]: unnormalised outputs
   float scale_log2;          // scale * log2(e)
 };
 
@@ -185,7 +190,7 @@ struct WaveState {
 // [start, end) of the tiles reached through bt_row / kvh, for the query rows
 // held in qb (B operand of the score MFMA: lane (col, quad) holds query row
 // col, dims 32 j + 8 quad .. + 8). Shared by the prefix and the private roles.
-template <int D>
+template <int D, int32_t kPolicy>
 __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32_t* bt_row, int32_t kvh,
                                               int32_t start, int32_t end, int32_t first, int32_t stride,
                                               const half8_t (&qb)[D / 32], WaveState<D>& st, int lane) {
@@ -197,18 +202,36 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
   const int32_t nblocks = (end - start + kBlk - 1) / kBlk;
   const float c = p.scale_log2;
 
+  // Page ids come 64 blocks at a time: lane l of the wave holds the page of
+  // its block kb + l, read back with a uniform readlane. A page-table load per
+  // block would be a vector load whose use waits for every load issued before
+  // it (the counter is in order), draining the prefetch ring each block.
+  int32_t pg = 0;
+  int32_t kb = -64;
+  auto fetch_pages = [&](int32_t k0) {
+    const int32_t blk = first + (k0 + lane) * stride;
+    int32_t page = 0;
+    bool bad = false;
+    if (blk < nblocks) {
+      page = bt_row[(start + blk * kBlk) >> p.p_shift];
+      bad = page < 0 || page >= p.N;
+    }
+    if (__builtin_amdgcn_ballot_w64(bad) != 0) st.bad_page = true;   // the row becomes NaN later
+    pg = bad ? 0 : page;                                                // stay in bounds
+    kb = k0;
+  };
+
   // Loads go through buffer descriptors built per 16-token block (base = the
   // block's sub-block, size 16 * D halves). Past the last block the size is 0:
   // the loads return zeros without touching memory, so the prefetch below is
   // unconditional and the compiler keeps exactly kDepth blocks in flight.
-  auto load_block = [&](int32_t blk, uint4 kr[KL], uint4 vr[KL]) {
+  // k counts this wave's blocks: block first + k * stride.
+  auto load_block = [&](int32_t k, uint4 kr[KL], uint4 vr[KL]) {
+    if (k - kb >= kWave) fetch_pages(k);
+    const int32_t blk = first + k * stride;
     const bool live = blk < nblocks;
     const int32_t t0 = start + (live ? blk : 0) * kBlk;
-    int32_t page = bt_row[t0 >> p.p_shift];
-    if (page < 0 || page >= p.N) {
-      st.bad_page = st.bad_page || live;
-      page = 0;                         // stay in bounds; the row becomes NaN later
-    }
+    const int32_t page = __builtin_amdgcn_readlane(pg, k - kb);
     const int64_t off = ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)(t0 & pmask) * D;
     const int32_t bytes = live ? kBlk * D * 2 : 0;
     const __amdgpu_buffer_rsrc_t krs =
@@ -217,12 +240,10 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.v_pool + off), (short)0, bytes, kBufferFlags);
 #pragma unroll
     for (int j = 0; j < KL; ++j)
-      kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, lane * 16 + j * 1024, 0,
-                                                                             kKvLoadPolicy));
+      kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, lane * 16 + j * 1024, 0, kPolicy));
 #pragma unroll
     for (int j = 0; j < KL; ++j)
-      vr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, lane * 16 + j * 1024, 0,
-                                                                             kKvLoadPolicy));
+      vr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, lane * 16 + j * 1024, 0, kPolicy));
   };
 
   auto consume = [&](int32_t blk, uint4 kr[KL], uint4 vr[KL]) {
@@ -281,16 +302,17 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
   // the current block.
   uint4 kr[kDepth + 1][KL], vr[kDepth + 1][KL];
 #pragma unroll
-  for (int r = 0; r < kDepth; ++r) load_block(first + r * stride, kr[r], vr[r]);
-  int32_t blk = first;
+  for (int r = 0; r < kDepth; ++r) load_block(r, kr[r], vr[r]);
+  int32_t k = 0;
   while (true) {
 #pragma unroll
     for (int r = 0; r <= kDepth; ++r) {
+      const int32_t blk = first + k * stride;
       if (blk >= nblocks) return;
-      load_block(blk + kDepth * stride, kr[(r + kDepth) % (kDepth + 1)], vr[(r + kDepth) % (kDepth + 1)]);
+      load_block(k + kDepth, kr[(r + kDepth) % (kDepth + 1)], vr[(r + kDepth) % (kDepth + 1)]);
       __builtin_amdgcn_sched_barrier(0);
       consume(blk, kr[r], vr[r]);
-      blk += stride;
+      ++k;
     }
   }
 }
@@ -304,185 +326,274 @@ __device__ __forceinline__ void init_state(WaveState<D>& st) {
   st.bad_page = false;
 }
 
-// Grid: the shared-prefix workgroups (if any) first, then one workgroup per
-// (KV head, sequence, private partition).
-//
-// Prefix role (only with a shared prefix): workgroup (chunk c, tile group tg,
-// KV head). Wave w takes the 16 query rows tg * 64 + 16 w .. + 15 of the
-// B * G rows that read this KV head (row r = sequence r / G, head
-// kvh * G + r % G), streams every block of prefix chunk c once for all 16 of
-// them and writes their partials to slot c.
-//
-// Private role: workgroup (KV head, sequence b, partition). Its 4 waves split
-// the partition's blocks; columns are the G query heads of the group (padded
-// to 16 with zero heads); the waves merge through LDS into the final fp16 row
-// (unsplit) or the partial of slot n_chunks + partition.
-template <int D, int G, bool SPLIT, bool FUSED>
-__global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams p) {
-  static_assert(D % 32 == 0 && G >= 1 && G <= 16, "shape");
+// LDS of one workgroup: per-wave softmax state of up to 16 columns.
+template <int D, int NC>
+struct WgShared {
+  float o[kWaves][NC][D];
+  float m[kWaves][NC];
+  float l[kWaves][NC];
+};
+
+// LDS of the partition kernel: the merge area of one range (16 columns for a
+// prefix tile, G for a private segment; one at a time) and the per-sequence
+// block prefix sums of the split schedule.
+template <int D, int G>
+struct KernelShared {
+  union {
+    WgShared<D, 16> prefix;
+    WgShared<D, G> priv;
+  } tile;
+  int32_t cum[kMaxFlatBatch];    // inclusive prefix sums of private blocks per sequence
+  int32_t wsum[kWaves];
+};
+
+// The 4 waves of a workgroup stream tokens [start, end) of KV head kvh through
+// block-table row bt_row (wave w takes blocks w, w + 4, ...), for NC query
+// rows: column c < NC reads q row qrow(c) (< 0: no row, zero query). The
+// waves merge through LDS and every (column c, dim d) goes to
+// emit(c, d, M, Ls, O): the column's base-2 score max, softmax denominator
+// and unnormalised output. Callers must be workgroup-uniform.
+template <int D, int NC, int32_t kPolicy, class RowFn, class EmitFn>
+__device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>& sh, const int32_t* bt_row,
+                                          int32_t kvh, int32_t start, int32_t end, RowFn qrow, EmitFn emit,
+                                          int lane, int wave) {
   constexpr int KL = D / 32;
   constexpr int NT = D / 16;
-
-  __shared__ float sm_o[kWaves][G][D];
-  __shared__ float sm_m[kWaves][G];
-  __shared__ float sm_l[kWaves][G];
-
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int col = lane & 15;           // MFMA column: query row / output dim
+  const int col = lane & 15;
   const int quad = lane >> 4;
-
-  if constexpr (SPLIT) {
-    if ((int32_t)blockIdx.x < p.n_prefix_wgs) {
-      // ---------------- prefix role ----------------
-      const int32_t id = blockIdx.x;
-      const int32_t kvh = id % p.Hkv;
-      const int32_t rest = id / p.Hkv;
-      const int32_t tg = rest % p.n_tilegroups;
-      const int32_t chunk = rest / p.n_tilegroups;
-      const int32_t row = (tg * kWaves + wave) * 16 + col;    // this lane's query row
-      const bool live_col = row < p.B * G;
-      const int32_t rb = live_col ? row / G : 0;
-      const int64_t qrow = (int64_t)rb * p.Hq + (int64_t)kvh * G + row % G;
-      const int32_t start = chunk * p.prefix_chunk;
-      const int32_t end = min(p.prefix_tokens, start + p.prefix_chunk);
-      half8_t qb[KL];
-#pragma unroll
-      for (int j = 0; j < KL; ++j) {
-        uint4 t = {0, 0, 0, 0};
-        if (live_col) t = *reinterpret_cast<const uint4*>(p.q + qrow * D + j * 32 + quad * 8);
-        qb[j] = as_h8(t);
-      }
-      WaveState<D> st;
-      init_state<D>(st);
-      // the prefix pages are the same in every row of the table: read row 0
-      stream_blocks<D>(p, p.bt, kvh, start, end, 0, 1, qb, st, lane);
-      st.l_part += __shfl_xor(st.l_part, 16);
-      st.l_part += __shfl_xor(st.l_part, 32);
-      if (st.bad_page) st.l_part = __builtin_nanf("");
-      if (quad == 0 && live_col) {
-        const int64_t slot = qrow * p.n_parts + chunk;
-        p.part_m[slot] = st.m_ref;
-        p.part_l[slot] = st.l_part;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int32_t r = (tg * kWaves + wave) * 16 + 4 * quad + i;
-        if (r < p.B * G) {
-          const int64_t qr = (int64_t)(r / G) * p.Hq + (int64_t)kvh * G + r % G;
-          float* dst = p.part_o + (qr * p.n_parts + chunk) * D + col;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) dst[16 * nt] = st.o[nt][i];
-        }
-      }
-      return;
-    }
-  }
-
-  // ---------------- private role ----------------
-  const int32_t id = blockIdx.x - p.n_prefix_wgs;
-  const int32_t kvh = id % p.Hkv;      // consecutive ids -> consecutive KV heads (XCD round robin)
-  const int32_t rest = id / p.Hkv;
-#if PKV_GRID_ORDER == 0
-  const int32_t b = rest % p.B;
-  const int32_t part = rest / p.B;
-#else
-  const int32_t part = rest % p.priv_parts;
-  const int32_t b = rest / p.priv_parts;
-#endif
-
-  const int32_t L = p.lens[b];
-  const bool bad_len = L < p.prefix_tokens || L > p.max_context || L > (p.max_pages << p.p_shift);
-  const int32_t Lc = bad_len ? 0 : L;
-  const int32_t start = p.prefix_tokens + part * p.part_tokens;
-  const int32_t end = min(Lc, start + p.part_tokens);
-  const int64_t head_row0 = (int64_t)b * p.Hq + (int64_t)kvh * G;   // first query head of the group
-
-  if (start >= end) {
-    // nothing to attend in this partition; the unsplit kernel still owns the output row
-    if (!SPLIT && part == 0) {
-      const half_t fill = bad_len ? (half_t)__builtin_nanf("") : (half_t)0.0f;
-      for (int i = threadIdx.x; i < G * D; i += kThreads) p.out[head_row0 * D + i] = fill;
-    }
-    return;
-  }
-
-  const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
-
-  if constexpr (FUSED) {
-    // the workgroup owning the new token writes it to the pool; the barrier
-    // makes the stores visible to this workgroup's loads below
-    if (start <= Lc - 1 && Lc - 1 < end) {
-      const int32_t t = Lc - 1;
-      const int32_t page = bt_row[t >> p.p_shift];
-      if (page >= 0 && page < p.N) {
-        const int64_t tile_elems = (int64_t)D << p.p_shift;
-        const int32_t pmask = (1 << p.p_shift) - 1;
-        const int64_t sub = ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)((t & pmask) >> 4) * (kBlk * D);
-        const int64_t src = ((int64_t)b * p.Hkv + kvh) * D;
-        store_token<D>(p.k_pool_w + sub, p.v_pool_w + sub, t & 15, p.k_new + src, p.v_new + src, threadIdx.x);
-      }
-      __syncthreads();
-    }
-  }
-
-  // B operand of the score MFMA: lane (head col, quad) holds q[col][32 j + 8 quad .. + 8]
+  // B operand of the score MFMA: lane (column col, quad) holds q[row][32 j + 8 quad .. + 8]
+  const int64_t row = col < NC ? qrow(col) : -1;
   half8_t qb[KL];
 #pragma unroll
   for (int j = 0; j < KL; ++j) {
     uint4 t = {0, 0, 0, 0};
-    if (col < G) t = *reinterpret_cast<const uint4*>(p.q + (head_row0 + col) * D + j * 32 + quad * 8);
+    if (row >= 0) t = *reinterpret_cast<const uint4*>(p.q + row * D + j * 32 + quad * 8);
     qb[j] = as_h8(t);
   }
-
   WaveState<D> st;
   init_state<D>(st);
-  stream_blocks<D>(p, bt_row, kvh, start, end, wave, kWaves, qb, st, lane);
-
-  // per-head denominators of this wave: sum the 4 quads of column col
+  stream_blocks<D, kPolicy>(p, bt_row, kvh, start, end, wave, kWaves, qb, st, lane);
+  // per-column denominators of this wave: sum the 4 quads of column col
   st.l_part += __shfl_xor(st.l_part, 16);
   st.l_part += __shfl_xor(st.l_part, 32);
   if (st.bad_page) st.l_part = __builtin_nanf("");
-  if (quad == 0 && col < G) {
-    sm_m[wave][col] = st.m_ref;
-    sm_l[wave][col] = st.l_part;
+  if (quad == 0 && col < NC) {
+    sh.m[wave][col] = st.m_ref;
+    sh.l[wave][col] = st.l_part;
   }
-  // output tile: lane holds rows (heads) 4 quad + i of dims 16 nt + col
+  // output tile: lane holds rows (columns) 4 quad + i of dims 16 nt + col
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int h = 4 * quad + i;
-    if (h < G) {
+    const int c = 4 * quad + i;
+    if (c < NC) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) sm_o[wave][h][16 * nt + col] = st.o[nt][i];
+      for (int nt = 0; nt < NT; ++nt) sh.o[wave][c][16 * nt + col] = st.o[nt][i];
     }
   }
   __syncthreads();
-
-  // merge the waves and write
-  for (int i = threadIdx.x; i < G * D; i += kThreads) {
-    const int h = i / D;
+  for (int i = threadIdx.x; i < NC * D; i += kThreads) {
+    const int c = i / D;
     const int d = i % D;
-    float M = sm_m[0][h];
+    float M = sh.m[0][c];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sm_m[w][h]);
+    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.m[w][c]);
     const float Ms = M == kNegInf() ? 0.f : M;
     float Ls = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float wt = fast_exp2(sm_m[w][h] - Ms);
-      Ls = fmaf(wt, sm_l[w][h], Ls);
-      O = fmaf(wt, sm_o[w][h][d], O);
+      const float wt = fast_exp2(sh.m[w][c] - Ms);
+      Ls = fmaf(wt, sh.l[w][c], Ls);
+      O = fmaf(wt, sh.o[w][c][d], O);
     }
-    if constexpr (SPLIT) {
-      const int64_t slot = (head_row0 + h) * p.n_parts + p.n_chunks + part;
-      p.part_o[slot * D + d] = O;
-      if (d == 0) {
-        p.part_m[slot] = M;
-        p.part_l[slot] = Ls;
+    emit(c, d, M, Ls, O);
+  }
+  // the LDS is reused by the caller's next range
+  __syncthreads();
+}
+
+// Writes the new token of sequence b, KV head kvh (position t) into its slot;
+// threads 0 .. D - 1 take part.
+template <int D>
+__device__ __forceinline__ void append_token(const DecodeParams& p, const int32_t* bt_row, int32_t b, int32_t kvh,
+                                             int32_t t) {
+  const int32_t page = bt_row[t >> p.p_shift];
+  if (page >= 0 && page < p.N) {
+    const int64_t tile_elems = (int64_t)D << p.p_shift;
+    const int32_t pmask = (1 << p.p_shift) - 1;
+    const int64_t sub = ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)((t & pmask) >> 4) * (kBlk * D);
+    const int64_t src = ((int64_t)b * p.Hkv + kvh) * D;
+    store_token<D>(p.k_pool_w + sub, p.v_pool_w + sub, t & 15, p.k_new + src, p.v_new + src, threadIdx.x);
+  }
+}
+
+// Unsplit (partition_tokens == 0): workgroup (KV head, sequence) over the
+// whole context; columns are the G heads of the group (zero-padded to 16);
+// fp16 output.
+//
+// Split: one balanced schedule per KV head. The head's work list is
+//   [tile 0 prefix blocks] ... [tile NT-1 prefix blocks] [seq 0 private] ...
+// where a prefix segment is the PB = prefix_tokens / 16 shared blocks read for
+// one tile of 16 query rows (row r = sequence r / G, head kvh * G + r % G; a
+// full 16-column MFMA tile, read once for all 16) and a private segment is a
+// sequence's own blocks after the prefix, read for its G heads. Every block
+// costs the same matrix-core work, so the list is cut evenly: private
+// workgroup w serves KV head w % Hkv (one XCD keeps to the same heads under
+// round-robin dispatch, so shared pages stay in its L2) and takes units
+// [j Q, (j + 1) Q), j = w / Hkv, Q = max(ceil(units / Wk), minimum piece),
+// Wk = W / Hkv. Pieces cross segment boundaries. The piece of (segment s,
+// local workgroup j) writes slot kvh * (S + Wk) + s + j (S segments per head):
+// walking the pieces in order increases s or j (or both) by one each step, so
+// the slots are distinct; each slot holds 16 columns.
+template <int D, int G, bool SPLIT, bool FUSED>
+__global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodeParams p) {
+  static_assert(D % 32 == 0 && G >= 1 && G <= 16, "shape");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __shared__ KernelShared<D, G> smem;
+
+  if constexpr (!SPLIT) {
+    WgShared<D, G>& sh = smem.tile.priv;
+    const int32_t kvh = blockIdx.x % p.Hkv;
+    const int32_t b = blockIdx.x / p.Hkv;
+    const int32_t L = p.lens[b];
+    const bool bad_len = L < 0 || L > p.max_context || L > (p.max_pages << p.p_shift);
+    const int32_t Lc = bad_len ? 0 : L;
+    const int64_t head_row0 = (int64_t)b * p.Hq + (int64_t)kvh * G;
+    if (Lc == 0) {
+      const half_t fill = bad_len ? (half_t)__builtin_nanf("") : (half_t)0.0f;
+      for (int i = threadIdx.x; i < G * D; i += kThreads) p.out[head_row0 * D + i] = fill;
+      return;
+    }
+    const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
+    if constexpr (FUSED) {
+      append_token<D>(p, bt_row, b, kvh, Lc - 1);
+      __syncthreads();   // the stores are visible to this workgroup's loads below
+    }
+    run_range<D, G, kKvLoadPolicy>(p, sh, bt_row, kvh, 0, Lc, [&](int c) -> int64_t { return head_row0 + c; },
+                    [&](int c, int d, float, float Ls, float O) {
+                      const float r = Ls > 0.f ? O / Ls : (Ls == 0.f ? 0.f : __builtin_nanf(""));
+                      p.out[(head_row0 + c) * D + d] = (half_t)(Ls != Ls ? __builtin_nanf("") : r);
+                    },
+                    lane, wave);
+  } else {
+    int32_t* sm_cum = smem.cum;
+    int32_t* sm_wsum = smem.wsum;
+    const int32_t wg = blockIdx.x;
+    const int32_t per = (p.B + kThreads - 1) / kThreads;
+    const int32_t b0 = threadIdx.x * per;
+    auto priv_blocks = [&](int32_t bb) -> int32_t {
+      const int32_t L = p.lens[bb];
+      const bool bad = L < p.min_len || L > p.max_context || L > (p.max_pages << p.p_shift);
+      return bad ? 0 : (L - p.prefix_tokens + kBlk - 1) / kBlk;
+    };
+    int32_t local = 0;
+    for (int32_t i = 0; i < per; ++i) {
+      const int32_t bb = b0 + i;
+      if (bb < p.B) {
+        const int32_t nb = priv_blocks(bb);
+        sm_cum[bb] = nb;
+        local += nb;
       }
-    } else {
-      const float r = Ls > 0.f ? O / Ls : (Ls == 0.f ? 0.f : __builtin_nanf(""));
-      p.out[(head_row0 + h) * D + d] = (half_t)(Ls != Ls ? __builtin_nanf("") : r);
+    }
+    int32_t incl = local;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int32_t y = __shfl_up(incl, off);
+      if (lane >= off) incl += y;
+    }
+    if (lane == kWave - 1) sm_wsum[wave] = incl;
+    __syncthreads();
+    int32_t run = incl - local;
+    for (int w = 0; w < wave; ++w) run += sm_wsum[w];
+    for (int32_t i = 0; i < per; ++i) {
+      const int32_t bb = b0 + i;
+      if (bb < p.B) {
+        run += sm_cum[bb];
+        sm_cum[bb] = run;
+      }
+    }
+    __syncthreads();
+    const int32_t NB = sm_cum[p.B - 1];               // private blocks per KV head
+    const int32_t PB = p.prefix_tokens / kBlk;        // prefix blocks per tile
+    const int32_t NTP = p.n_tiles * PB;               // prefix units per KV head
+    const int32_t units = NTP + NB;
+    const int32_t Wk = p.n_flat_wgs / p.Hkv;          // workgroups per KV head
+    const int32_t Q = max(max((units + Wk - 1) / Wk, p.min_piece), 1);
+    if (wg == 0) {
+      // the reduce kernel locates the pieces from these
+      if (threadIdx.x == 0) {
+        p.flat_hdr[0] = NB;
+        p.flat_hdr[1] = Q;
+      }
+      for (int32_t bb = threadIdx.x; bb < p.B; bb += kThreads) p.flat_cum[bb] = sm_cum[bb];
+    }
+    const int32_t kvh = wg % p.Hkv;
+    const int32_t jw = wg / p.Hkv;
+    const int64_t slot_base = (int64_t)kvh * (p.n_tiles + p.B + Wk) + jw;
+    int32_t g = jw < Wk ? jw * Q : units;
+    const int32_t ge = min(g + Q, units);
+    while (g < ge) {
+      if (g < NTP) {
+        // shared prefix, 16 query rows of tile rt
+        const int32_t rt = g / PB;
+        const int32_t blk0 = g - rt * PB;
+        const int32_t piece_n = min(ge - g, PB - blk0);
+        const int32_t rows = p.B * G;
+        auto qrow = [&](int c) -> int64_t {
+          const int32_t r = rt * 16 + c;
+          return r < rows ? (int64_t)(r / G) * p.Hq + (int64_t)kvh * G + r % G : -1;
+        };
+        const int64_t slot = slot_base + rt;
+        // the prefix pages are the same in every row of the table: read row 0
+        run_range<D, 16, kPrefixLoadPolicy>(p, smem.tile.prefix, p.bt, kvh, blk0 * kBlk, (blk0 + piece_n) * kBlk, qrow,
+                                            [&](int c, int d, float M, float Ls, float O) {
+                                              const int64_t ps = slot * 16 + c;
+                                              p.flat_o[ps * D + d] = O;
+                                              if (d == 0) {
+                                                p.flat_m[ps] = M;
+                                                p.flat_l[ps] = Ls;
+                                              }
+                                            },
+                                            lane, wave);
+        g += piece_n;
+      } else {
+        const int32_t r = g - NTP;
+        // first sequence whose inclusive prefix exceeds r
+        int32_t lo = 0, hi = p.B - 1;
+        while (lo < hi) {
+          const int32_t mid = (lo + hi) >> 1;
+          if (sm_cum[mid] > r) hi = mid;
+          else lo = mid + 1;
+        }
+        const int32_t b = lo;
+        const int32_t seg_first = b > 0 ? sm_cum[b - 1] : 0;
+        const int32_t seg_n = sm_cum[b] - seg_first;
+        const int32_t blk0 = r - seg_first;
+        const int32_t piece_n = min(ge - g, seg_n - blk0);
+        const int32_t L = p.lens[b];
+        const int32_t start = p.prefix_tokens + blk0 * kBlk;
+        const int32_t end = min(L, p.prefix_tokens + (blk0 + piece_n) * kBlk);
+        const int64_t head_row0 = (int64_t)b * p.Hq + (int64_t)kvh * G;
+        const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
+        if constexpr (FUSED) {
+          // the piece holding the sequence's last block owns its new token
+          if (blk0 + piece_n == seg_n) append_token<D>(p, bt_row, b, kvh, end - 1);
+          __syncthreads();   // the stores are visible to this workgroup's loads below
+        }
+        const int64_t slot = slot_base + p.n_tiles + b;
+        run_range<D, G, kKvLoadPolicy>(p, smem.tile.priv, bt_row, kvh, start, end,
+                                       [&](int c) -> int64_t { return c < G ? head_row0 + c : -1; },
+                                       [&](int c, int d, float M, float Ls, float O) {
+                                         const int64_t ps = slot * 16 + c;
+                                         p.flat_o[ps * D + d] = O;
+                                         if (d == 0) {
+                                           p.flat_m[ps] = M;
+                                           p.flat_l[ps] = Ls;
+                                         }
+                                       },
+                                       lane, wave);
+        g += piece_n;
+      }
     }
   }
 }
@@ -491,30 +602,58 @@ __global__ __launch_bounds__(kThreads) void decode_partition_kernel(DecodeParams
 // decode: log-sum-exp reduce over partitions
 // -------------------------------------------------------------------------
 
-// One workgroup of D threads per (sequence, query head). The partition maxima
-// and sums are loaded in parallel (one partition per thread) into LDS, the
-// merge weights exp2(m_j - M) computed once, and thread d then sums output dim
-// d over the partitions with independent loads.
+// One workgroup of D threads per (sequence, query head). Its partials are the
+// pieces of the head's prefix tile segment (column = its row within the tile)
+// and of its private segment, made by KV head kvh's workgroups j0 .. j1 of the
+// balanced schedule (slot kvh * (S + Wk) + segment + j). Maxima are loaded in
+// parallel into LDS, the merge weights exp2(m_j - M) computed once, and thread
+// d sums output dim d over the partials with independent loads.
 template <int D>
 __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
-  constexpr int kMaxParts = kMaxPartitions;
-  __shared__ float sm_w[kMaxParts];
+  __shared__ float sm_w[kMaxPartitions];
   __shared__ float sm_red[D / kWave];
   const int64_t bh = blockIdx.x;
   const int32_t b = (int32_t)(bh / p.Hq);
+  const int32_t h = (int32_t)(bh % p.Hq);
+  const int32_t G = p.Hq / p.Hkv;
+  const int32_t kvh = h / G;
+  const int32_t hg = h % G;
   const int d = threadIdx.x;
   const int32_t L = p.lens[b];
-  const bool bad_len = L < p.prefix_tokens || L > p.max_context || L > (p.max_pages << p.p_shift);
-  // slots 0 .. n_chunks - 1: shared-prefix chunks; then the private partitions
-  const int32_t np = bad_len ? 0 : p.n_chunks + (L - p.prefix_tokens + p.part_tokens - 1) / p.part_tokens;
-  const float* pm = p.part_m + bh * p.n_parts;
-  const float* pl = p.part_l + bh * p.n_parts;
-  const float* po = p.part_o + bh * p.n_parts * D + d;
+  const bool bad_len = L < p.min_len || L > p.max_context || L > (p.max_pages << p.p_shift);
+  const int32_t Q = p.flat_hdr[1];
+  const int32_t Wk = p.n_flat_wgs / p.Hkv;
+  const int32_t PB = p.prefix_tokens / kBlk;
+  const int32_t NTP = p.n_tiles * PB;
+  const int64_t slot_base = (int64_t)kvh * (p.n_tiles + p.B + Wk);
+  // prefix tile segment of row r = b * G + hg
+  const int32_t r = b * G + hg;
+  const int32_t rt = r / 16;
+  const int32_t ct = r % 16;
+  int32_t np1 = 0, ja = 0;
+  if (PB > 0) {
+    const int32_t u0 = rt * PB;
+    ja = u0 / Q;
+    np1 = (u0 + PB - 1) / Q - ja + 1;
+  }
+  // private segment
+  const int32_t prev = b > 0 ? p.flat_cum[b - 1] : 0;
+  const int32_t nblk = p.flat_cum[b] - prev;
+  int32_t np2 = 0, jb = 0;
+  if (nblk > 0) {
+    const int32_t u0 = NTP + prev;
+    jb = u0 / Q;
+    np2 = (u0 + nblk - 1) / Q - jb + 1;
+  }
+  const int32_t np = bad_len ? 0 : np1 + np2;
+  auto idx = [&](int32_t j) -> int64_t {
+    return j < np1 ? (slot_base + rt + ja + j) * 16 + ct : (slot_base + p.n_tiles + b + jb + (j - np1)) * 16 + hg;
+  };
 
   // M = max_j m_j
   float M = kNegInf();
   for (int32_t j = d; j < np; j += D) {
-    const float mj = pm[j];
+    const float mj = p.flat_m[idx(j)];
     sm_w[j] = mj;
     M = fmaxf(M, mj);
   }
@@ -531,7 +670,7 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
   for (int32_t j = d; j < np; j += D) {
     const float wj = fast_exp2(sm_w[j] - Ms);
     sm_w[j] = wj;
-    Lp = fmaf(wj, pl[j], Lp);
+    Lp = fmaf(wj, p.flat_l[idx(j)], Lp);
   }
   for (int off = 32; off > 0; off >>= 1) Lp += __shfl_xor(Lp, off);
   if ((d & (kWave - 1)) == 0) sm_red[d / kWave] = Lp;
@@ -540,19 +679,20 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
 #pragma unroll
   for (int w = 0; w < D / kWave; ++w) Ls += sm_red[w];
   // numerator of dim d, four independent partial sums
+  const float* po = p.flat_o + d;
   float O0 = 0.f, O1 = 0.f, O2 = 0.f, O3 = 0.f;
   int32_t j = 0;
   for (; j + 4 <= np; j += 4) {
-    O0 = fmaf(sm_w[j + 0], po[(int64_t)(j + 0) * D], O0);
-    O1 = fmaf(sm_w[j + 1], po[(int64_t)(j + 1) * D], O1);
-    O2 = fmaf(sm_w[j + 2], po[(int64_t)(j + 2) * D], O2);
-    O3 = fmaf(sm_w[j + 3], po[(int64_t)(j + 3) * D], O3);
+    O0 = fmaf(sm_w[j + 0], po[idx(j + 0) * D], O0);
+    O1 = fmaf(sm_w[j + 1], po[idx(j + 1) * D], O1);
+    O2 = fmaf(sm_w[j + 2], po[idx(j + 2) * D], O2);
+    O3 = fmaf(sm_w[j + 3], po[idx(j + 3) * D], O3);
   }
-  for (; j < np; ++j) O0 = fmaf(sm_w[j], po[(int64_t)j * D], O0);
+  for (; j < np; ++j) O0 = fmaf(sm_w[j], po[idx(j) * D], O0);
   const float O = (O0 + O1) + (O2 + O3);
-  float r = Ls > 0.f ? O / Ls : 0.f;
-  if (bad_len || Ls != Ls) r = __builtin_nanf("");
-  p.out[bh * D + d] = (half_t)r;
+  float res = Ls > 0.f ? O / Ls : 0.f;
+  if (bad_len || Ls != Ls) res = __builtin_nanf("");
+  p.out[bh * D + d] = (half_t)res;
 }
 
 // -------------------------------------------------------------------------
@@ -573,25 +713,36 @@ int log2_page(int32_t P) {
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
+// Workspace of a split call: a 256-byte header, the per-sequence prefix sums,
+// then the piece partials [slots][16] (max, sum) and [slots][16][D] (output).
 struct WsLayout {
-  size_t m_off, l_off, o_off, total;
+  size_t hdr_off, cum_off, fm_off, fl_off, fo_off, total;
 };
 
-WsLayout ws_layout(int64_t B, int64_t Hq, int64_t D, int64_t n_parts) {
-  const size_t stats = align_up(static_cast<size_t>(B * Hq * n_parts) * sizeof(float));
-  const size_t outs = align_up(static_cast<size_t>(B * Hq * n_parts * D) * sizeof(float));
-  return WsLayout{0, stats, 2 * stats, 2 * stats + outs};
+WsLayout ws_layout(int64_t B, int64_t D, int64_t slots) {
+  WsLayout w{};
+  size_t at = 0;
+  auto take = [&](size_t bytes) {
+    const size_t off = at;
+    at += align_up(bytes);
+    return off;
+  };
+  w.hdr_off = take(2 * sizeof(int32_t));
+  w.cum_off = take(static_cast<size_t>(B) * sizeof(int32_t));
+  w.fm_off = take(static_cast<size_t>(slots * 16) * sizeof(float));
+  w.fl_off = take(static_cast<size_t>(slots * 16) * sizeof(float));
+  w.fo_off = take(static_cast<size_t>(slots * 16 * D) * sizeof(float));
+  w.total = at;
+  return w;
 }
 
 // Work decomposition of one decode call.
 struct Plan {
   bool split;
-  int32_t part_tokens;     // private partition size (unsplit: covers any admissible length)
-  int32_t priv_parts;      // private partitions per sequence in the grid
-  int32_t n_chunks;        // shared-prefix chunks
-  int32_t n_tilegroups;    // prefix workgroups per (chunk, KV head)
-  int32_t n_prefix_wgs;
-  int32_t n_parts;         // partial slots per (sequence, query head)
+  int32_t n_tiles;         // 16-row query tiles per KV head reading the shared prefix
+  int32_t n_flat_wgs;      // workgroups of the split schedule (a multiple of Hkv)
+  int32_t min_piece;       // minimum blocks per piece
+  int64_t slots;           // piece slots: Hkv * (n_tiles + B + n_flat_wgs / Hkv)
   int64_t grid;
 };
 
@@ -603,20 +754,26 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_context, int32_t p
   if (prefix_tokens > 0 && partition_tokens == 0) return PKV_ERR_INVALID_ARG;
   Plan p{};
   p.split = partition_tokens > 0;
-  p.part_tokens = p.split ? partition_tokens : ((max_context + kBlk - 1) / kBlk) * kBlk + kBlk;
-  p.priv_parts = p.split ? (max_context - prefix_tokens + partition_tokens - 1) / partition_tokens : 1;
-  p.n_chunks = (prefix_tokens + kPrefixChunk - 1) / kPrefixChunk;
+  if (p.split && B > kMaxFlatBatch) return PKV_ERR_INVALID_ARG;
   const int64_t rows = static_cast<int64_t>(B) * (Hq / Hkv);
-  const int64_t tiles = (rows + 15) / 16;
-  p.n_tilegroups = p.n_chunks > 0 ? static_cast<int32_t>((tiles + kWaves - 1) / kWaves) : 0;
-  const int64_t n_prefix = static_cast<int64_t>(p.n_chunks) * p.n_tilegroups * Hkv;
-  p.n_parts = p.n_chunks + p.priv_parts;
-  if (p.split && p.n_parts > kMaxPartitions) return PKV_ERR_INVALID_ARG;
-  p.grid = n_prefix + static_cast<int64_t>(p.priv_parts) * B * Hkv;
+  p.n_tiles = prefix_tokens > 0 ? static_cast<int32_t>((rows + 15) / 16) : 0;
+  // a whole number of workgroups per KV head, at least one
+  p.n_flat_wgs = p.split ? max(PKV_FLAT_WORKGROUPS / Hkv, 1) * Hkv : 0;
+  if (p.split && 2 * (p.n_flat_wgs / Hkv) > kMaxPartitions) return PKV_ERR_INVALID_ARG;
+  p.min_piece = partition_tokens / kBlk;
+  p.slots = p.split ? static_cast<int64_t>(Hkv) * (p.n_tiles + B + p.n_flat_wgs / Hkv) : 0;
+  p.grid = p.split ? p.n_flat_wgs : static_cast<int64_t>(B) * Hkv;
   if (p.grid > 0x7fffffffLL || static_cast<int64_t>(B) * Hq > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
-  p.n_prefix_wgs = static_cast<int32_t>(n_prefix);
   *pl = p;
   return PKV_OK;
+}
+
+// Upper bound of Plan::slots over every Hkv that divides Hq (the workspace
+// query does not take Hkv): Hkv * n_tiles <= B * Hq / 16 + Hkv,
+// Hkv * B <= Hq * B, Hkv * (W / Hkv) <= max(W, Hkv).
+int64_t max_slots(int32_t B, int32_t Hq, bool prefix) {
+  return (prefix ? static_cast<int64_t>(B) * Hq / 16 + Hq : 0) + static_cast<int64_t>(B) * Hq + PKV_FLAT_WORKGROUPS +
+         Hq;
 }
 
 template <int D, int G, bool SPLIT, bool FUSED>
@@ -692,25 +849,25 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   prm.N = N;
   prm.p_shift = p_shift;
   prm.max_context = max_context;
-  prm.part_tokens = plan.part_tokens;
-  prm.priv_parts = plan.priv_parts;
   prm.prefix_tokens = prefix_tokens;
-  prm.prefix_chunk = kPrefixChunk;
-  prm.n_chunks = plan.n_chunks;
-  prm.n_tilegroups = plan.n_tilegroups;
-  prm.n_prefix_wgs = plan.n_prefix_wgs;
-  prm.n_parts = plan.n_parts;
+  // an appended token must land in a private page
+  prm.min_len = prefix_tokens + (fused && prefix_tokens > 0 ? 1 : 0);
+  prm.n_tiles = plan.n_tiles;
+  prm.n_flat_wgs = plan.n_flat_wgs;
+  prm.min_piece = plan.min_piece;
   prm.scale_log2 = scale * kLog2e;
 
   if (plan.split) {
-    const WsLayout ws = ws_layout(B, Hq, D, plan.n_parts);
+    const WsLayout ws = ws_layout(B, D, plan.slots);
     if (!workspace) return PKV_ERR_INVALID_ARG;
     if (!aligned(workspace, kWsAlign)) return PKV_ERR_INVALID_ARG;
     if (workspace_bytes < ws.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
     char* base = static_cast<char*>(workspace);
-    prm.part_m = reinterpret_cast<float*>(base + ws.m_off);
-    prm.part_l = reinterpret_cast<float*>(base + ws.l_off);
-    prm.part_o = reinterpret_cast<float*>(base + ws.o_off);
+    prm.flat_hdr = reinterpret_cast<int32_t*>(base + ws.hdr_off);
+    prm.flat_cum = reinterpret_cast<int32_t*>(base + ws.cum_off);
+    prm.flat_m = reinterpret_cast<float*>(base + ws.fm_off);
+    prm.flat_l = reinterpret_cast<float*>(base + ws.fl_off);
+    prm.flat_o = reinterpret_cast<float*>(base + ws.fo_off);
   }
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -737,7 +894,7 @@ int workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context, int32
   // Hkv does not change the slot count; any divisor of Hq gives the same plan sizes
   const int rc = make_plan(B, Hq, Hq, max_context, partition_tokens, prefix_tokens, &plan);
   if (rc != PKV_OK) return rc;
-  *bytes = plan.split ? ws_layout(B, Hq, D, plan.n_parts).total : 0;
+  *bytes = plan.split ? ws_layout(B, D, max_slots(B, Hq, prefix_tokens > 0)).total : 0;
   return PKV_OK;
 }
 

@@ -82,10 +82,18 @@ def test_append_argument_checks(pkv):
 def test_workspace_size(pkv):
     assert pkv.decode_workspace_bytes(4, 32, 128, 32768, 0) == 0
     n = pkv.decode_workspace_bytes(4, 32, 128, 32768, 512)
-    # per (b, head, partition): max + sum + D floats, 64 partitions, 256-byte aligned sections
-    assert n >= 4 * 32 * 64 * (128 + 2) * 4 and n % 256 == 0
+    # piece slots of 16 rows x (max, sum, D floats): at least one per (sequence, KV head) and one per
+    # workgroup (512) for any Hkv; 256-byte aligned sections
+    assert n >= (4 + 512) * 16 * (128 + 2) * 4 and n % 256 == 0
+    m = pkv.decode_workspace_bytes(4, 32, 128, 32768, 512, prefix_tokens=2048)
+    # plus one prefix segment per 16 query rows
+    assert m >= n + (4 * 32 // 16) * 16 * (128 + 2) * 4
     with pytest.raises(pkv.PkvError):
         pkv.decode_workspace_bytes(4, 32, 128, 32768, 500)
+    with pytest.raises(pkv.PkvError):
+        pkv.decode_workspace_bytes(5000, 32, 128, 32768, 512)        # split path holds at most 4096 sequences
+    with pytest.raises(pkv.PkvError):
+        pkv.decode_workspace_bytes(4, 32, 128, 2000, 0, prefix_tokens=1024)   # prefix needs the split path
 
 
 # ---------------------------------------------------------------------------

@@ -407,6 +407,22 @@ def test_shared_prefix_shapes_and_edges(B, Hkv, G, D, P, prefix_pages, part):
                                                            int(lens.max()), 1 / math.sqrt(D), part, prefix))
     assert np.all(np.isnan(got2[-1].astype(np.float64)))
     assert np.array_equal(got2[:-1].view(np.uint16), host(got)[:-1].view(np.uint16))
+    # with an append every new token lands after the prefix; row 0 has nothing private, so it is NaN and
+    # appends nothing (its position would fall in a shared page)
+    kn = rng.standard_normal((B, Hkv, D)).astype(np.float16)
+    vn = rng.standard_normal((B, Hkv, D)).astype(np.float16)
+    live = lens > prefix
+    rk, rv = oracle.kv_append(kp, vp, kn[live], vn[live], bt[live], (lens - 1)[live], P)
+    dk, dv = dev(kp), dev(vp)
+    got3 = pkv().paged_decode_attention_shared_prefix(dev(q), dk, dv, dev(bt), dev(lens), int(lens.max()),
+                                                      1 / math.sqrt(D), part, prefix, k_new=dev(kn), v_new=dev(vn))
+    torch.cuda.synchronize()
+    assert np.array_equal(host(dk).view(np.uint16), rk.view(np.uint16))
+    assert np.array_equal(host(dv).view(np.uint16), rv.view(np.uint16))
+    got3 = host(got3)
+    assert np.all(np.isnan(got3[0].astype(np.float64)))
+    ref3 = oracle.decode_attention(q, rk, rv, bt, lens, 1 / math.sqrt(D), P)
+    check_close(torch.from_numpy(got3[live]), ref3[live], "prefix shapes, fused")
 
 
 def test_shared_prefix_argument_checks():
