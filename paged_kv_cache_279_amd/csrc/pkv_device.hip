@@ -55,6 +55,10 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 // Order of the (partition, sequence) work items in the grid: 0 = partition
 // major (every sequence's first partition first), 1 = sequence major.
 // Private workgroups of the balanced split schedule (2 per CU on 256 CUs).
+#ifndef PKV_PRIO_BALANCE
+#define PKV_PRIO_BALANCE 1
+#endif
+constexpr bool kPrioBalance = PKV_PRIO_BALANCE != 0;   // level workgroups sharing a CU by issue priority
 #ifndef PKV_FLAT_WORKGROUPS
 #define PKV_FLAT_WORKGROUPS 512
 #endif
@@ -103,7 +107,7 @@ struct DecodeParams {
   int32_t n_tiles;           // 16-row query tiles per KV head that read the prefix (0 = none)
   int32_t n_flat_wgs;        // workgroups of the balanced split schedule
   int32_t min_piece;         // minimum blocks per piece
-  int32_t* flat_hdr;         // [2]: private blocks per KV head, units per workgroup
+  int32_t* flat_hdr;         // [3]: private blocks per KV head, private and prefix units per workgroup
   int32_t* flat_cum;         // [B]: inclusive prefix sums of private blocks
   float* flat_m;             // [slots][16]: piece partials, base-2 scaled score max
   float* flat_l;             // [slots][16]: softmax denominators
@@ -186,13 +190,29 @@ struct WaveState {
   bool bad_page;   // a page id outside [0, N) was met
 };
 
+// Issue priority from the share of the workgroup's work still ahead of it.
+// Waves of the same priority issue oldest first, so of two workgroups that
+// stream side by side on a CU the one dispatched first would take most of the
+// memory pipe and the other would finish long after it; raising the priority
+// of whichever has more left keeps them level (four levels: quarters of the
+// quota).
+__device__ __forceinline__ void set_priority(int32_t remaining, int32_t quota) {
+  if (remaining * 4 > quota * 3) __builtin_amdgcn_s_setprio(3);
+  else if (remaining * 2 > quota) __builtin_amdgcn_s_setprio(2);
+  else if (remaining * 4 > quota) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
 // Streams blocks first, first + stride, ... (< nblocks) of the token range
 // [start, end) of the tiles reached through bt_row / kvh, for the query rows
 // held in qb (B operand of the score MFMA: lane (col, quad) holds query row
 // col, dims 32 j + 8 quad .. + 8). Shared by the prefix and the private roles.
+// quota > 0: the range is part of a workgroup share of quota blocks with
+// `after` blocks following it; the wave's priority follows what is left.
 template <int D, int32_t kPolicy>
 __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32_t* bt_row, int32_t kvh,
                                               int32_t start, int32_t end, int32_t first, int32_t stride,
+                                              int32_t quota, int32_t after,
                                               const half8_t (&qb)[D / 32], WaveState<D>& st, int lane) {
   constexpr int KL = D / 32;           // 16-byte loads per lane per block, for K and for V
   constexpr int NT = D / 16;           // 16-dim output tiles
@@ -309,6 +329,7 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     for (int r = 0; r <= kDepth; ++r) {
       const int32_t blk = first + k * stride;
       if (blk >= nblocks) return;
+      if (kPrioBalance && quota > 0) set_priority(after + nblocks - blk, quota);
       load_block(k + kDepth, kr[(r + kDepth) % (kDepth + 1)], vr[(r + kDepth) % (kDepth + 1)]);
       __builtin_amdgcn_sched_barrier(0);
       consume(blk, kr[r], vr[r]);
@@ -355,8 +376,8 @@ struct KernelShared {
 // and unnormalised output. Callers must be workgroup-uniform.
 template <int D, int NC, int32_t kPolicy, class RowFn, class EmitFn>
 __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>& sh, const int32_t* bt_row,
-                                          int32_t kvh, int32_t start, int32_t end, RowFn qrow, EmitFn emit,
-                                          int lane, int wave) {
+                                          int32_t kvh, int32_t start, int32_t end, int32_t quota, int32_t after,
+                                          RowFn qrow, EmitFn emit, int lane, int wave) {
   constexpr int KL = D / 32;
   constexpr int NT = D / 16;
   const int col = lane & 15;
@@ -372,7 +393,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
   }
   WaveState<D> st;
   init_state<D>(st);
-  stream_blocks<D, kPolicy>(p, bt_row, kvh, start, end, wave, kWaves, qb, st, lane);
+  stream_blocks<D, kPolicy>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, qb, st, lane);
   // per-column denominators of this wave: sum the 4 quads of column col
   st.l_part += __shfl_xor(st.l_part, 16);
   st.l_part += __shfl_xor(st.l_part, 32);
@@ -430,20 +451,23 @@ __device__ __forceinline__ void append_token(const DecodeParams& p, const int32_
 // whole context; columns are the G heads of the group (zero-padded to 16);
 // fp16 output.
 //
-// Split: one balanced schedule per KV head. The head's work list is
-//   [tile 0 prefix blocks] ... [tile NT-1 prefix blocks] [seq 0 private] ...
-// where a prefix segment is the PB = prefix_tokens / 16 shared blocks read for
-// one tile of 16 query rows (row r = sequence r / G, head kvh * G + r % G; a
-// full 16-column MFMA tile, read once for all 16) and a private segment is a
-// sequence's own blocks after the prefix, read for its G heads. Every block
-// costs the same matrix-core work, so the list is cut evenly: private
-// workgroup w serves KV head w % Hkv (one XCD keeps to the same heads under
-// round-robin dispatch, so shared pages stay in its L2) and takes units
-// [j Q, (j + 1) Q), j = w / Hkv, Q = max(ceil(units / Wk), minimum piece),
-// Wk = W / Hkv. Pieces cross segment boundaries. The piece of (segment s,
-// local workgroup j) writes slot kvh * (S + Wk) + s + j (S segments per head):
-// walking the pieces in order increases s or j (or both) by one each step, so
-// the slots are distinct; each slot holds 16 columns.
+// Split: a balanced schedule per KV head over two work lists,
+//   prefix:  [tile 0: PB blocks] ... [tile NT-1: PB blocks]
+//   private: [seq 0 private blocks] ... [seq B-1 private blocks]
+// A prefix segment is the PB = prefix_tokens / 16 shared blocks read for one
+// tile of 16 query rows (row r = sequence r / G, head kvh * G + r % G: a full
+// 16-column MFMA tile, the shared pages read once for all 16); a private
+// segment is a sequence's own blocks after the prefix, read for its G heads.
+// Workgroup w serves KV head w % Hkv (under round-robin dispatch an XCD keeps
+// to the same heads, so their shared pages stay in its L2); its index j =
+// w / Hkv among the head's Wk = W / Hkv workgroups selects units
+// [j Qp, (j + 1) Qp) of the prefix list and [j Qv, (j + 1) Qv) of the private
+// list, Qx = max(ceil(list length / Wk), minimum piece). Every workgroup thus
+// gets the same mix of L2-resident prefix reads and HBM-bound private reads;
+// pieces cross segment boundaries. The piece of (segment s, workgroup j)
+// writes slot kvh * (NT + B + 2 Wk) + s + j, private segments numbered after
+// NT + Wk: walking a list in order increases s or j (or both) by one each
+// step, so the slots are distinct; each slot holds 16 columns.
 template <int D, int G, bool SPLIT, bool FUSED>
 __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodeParams p) {
   static_assert(D % 32 == 0 && G >= 1 && G <= 16, "shape");
@@ -469,7 +493,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
       append_token<D>(p, bt_row, b, kvh, Lc - 1);
       __syncthreads();   // the stores are visible to this workgroup's loads below
     }
-    run_range<D, G, kKvLoadPolicy>(p, sh, bt_row, kvh, 0, Lc, [&](int c) -> int64_t { return head_row0 + c; },
+    run_range<D, G, kKvLoadPolicy>(p, sh, bt_row, kvh, 0, Lc, 0, 0, [&](int c) -> int64_t { return head_row0 + c; },
                     [&](int c, int d, float, float Ls, float O) {
                       const float r = Ls > 0.f ? O / Ls : (Ls == 0.f ? 0.f : __builtin_nanf(""));
                       p.out[(head_row0 + c) * D + d] = (half_t)(Ls != Ls ? __builtin_nanf("") : r);
@@ -516,28 +540,31 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
     const int32_t NB = sm_cum[p.B - 1];               // private blocks per KV head
     const int32_t PB = p.prefix_tokens / kBlk;        // prefix blocks per tile
     const int32_t NTP = p.n_tiles * PB;               // prefix units per KV head
-    const int32_t units = NTP + NB;
     const int32_t Wk = p.n_flat_wgs / p.Hkv;          // workgroups per KV head
-    const int32_t Q = max(max((units + Wk - 1) / Wk, p.min_piece), 1);
+    const int32_t Qv = max(max((NB + Wk - 1) / Wk, p.min_piece), 1);
+    const int32_t Qp = max(max((NTP + Wk - 1) / Wk, p.min_piece), 1);
     if (wg == 0) {
       // the reduce kernel locates the pieces from these
       if (threadIdx.x == 0) {
         p.flat_hdr[0] = NB;
-        p.flat_hdr[1] = Q;
+        p.flat_hdr[1] = Qv;
+        p.flat_hdr[2] = Qp;
       }
       for (int32_t bb = threadIdx.x; bb < p.B; bb += kThreads) p.flat_cum[bb] = sm_cum[bb];
     }
     const int32_t kvh = wg % p.Hkv;
     const int32_t jw = wg / p.Hkv;
-    const int64_t slot_base = (int64_t)kvh * (p.n_tiles + p.B + Wk) + jw;
-    int32_t g = jw < Wk ? jw * Q : units;
-    const int32_t ge = min(g + Q, units);
-    while (g < ge) {
-      if (g < NTP) {
-        // shared prefix, 16 query rows of tile rt
+    const int64_t slot_base = (int64_t)kvh * (p.n_tiles + p.B + 2 * Wk) + jw;
+    const int32_t gp0 = min(jw * Qp, NTP), gp1 = min(gp0 + Qp, NTP);
+    const int32_t gv0 = min(jw * Qv, NB), gv1 = min(gv0 + Qv, NB);
+    const int32_t quota = (gp1 - gp0) + (gv1 - gv0);
+
+    // shared prefix, units [g0, g1): 16 query rows of tile rt per piece
+    auto prefix_part = [&](int32_t g0, int32_t g1, int32_t after) {
+      for (int32_t g = g0; g < g1;) {
         const int32_t rt = g / PB;
         const int32_t blk0 = g - rt * PB;
-        const int32_t piece_n = min(ge - g, PB - blk0);
+        const int32_t piece_n = min(g1 - g, PB - blk0);
         const int32_t rows = p.B * G;
         auto qrow = [&](int c) -> int64_t {
           const int32_t r = rt * 16 + c;
@@ -545,7 +572,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
         };
         const int64_t slot = slot_base + rt;
         // the prefix pages are the same in every row of the table: read row 0
-        run_range<D, 16, kPrefixLoadPolicy>(p, smem.tile.prefix, p.bt, kvh, blk0 * kBlk, (blk0 + piece_n) * kBlk, qrow,
+        run_range<D, 16, kPrefixLoadPolicy>(p, smem.tile.prefix, p.bt, kvh, blk0 * kBlk, (blk0 + piece_n) * kBlk, quota,
+                                            after + g1 - g - piece_n, qrow,
                                             [&](int c, int d, float M, float Ls, float O) {
                                               const int64_t ps = slot * 16 + c;
                                               p.flat_o[ps * D + d] = O;
@@ -556,20 +584,23 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
                                             },
                                             lane, wave);
         g += piece_n;
-      } else {
-        const int32_t r = g - NTP;
-        // first sequence whose inclusive prefix exceeds r
+      }
+    };
+    // private blocks, units [g0, g1) of the concatenated per-sequence lists
+    auto private_part = [&](int32_t g0, int32_t g1, int32_t after) {
+      for (int32_t g = g0; g < g1;) {
+        // first sequence whose inclusive prefix exceeds g
         int32_t lo = 0, hi = p.B - 1;
         while (lo < hi) {
           const int32_t mid = (lo + hi) >> 1;
-          if (sm_cum[mid] > r) hi = mid;
+          if (sm_cum[mid] > g) hi = mid;
           else lo = mid + 1;
         }
         const int32_t b = lo;
         const int32_t seg_first = b > 0 ? sm_cum[b - 1] : 0;
         const int32_t seg_n = sm_cum[b] - seg_first;
-        const int32_t blk0 = r - seg_first;
-        const int32_t piece_n = min(ge - g, seg_n - blk0);
+        const int32_t blk0 = g - seg_first;
+        const int32_t piece_n = min(g1 - g, seg_n - blk0);
         const int32_t L = p.lens[b];
         const int32_t start = p.prefix_tokens + blk0 * kBlk;
         const int32_t end = min(L, p.prefix_tokens + (blk0 + piece_n) * kBlk);
@@ -580,8 +611,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
           if (blk0 + piece_n == seg_n) append_token<D>(p, bt_row, b, kvh, end - 1);
           __syncthreads();   // the stores are visible to this workgroup's loads below
         }
-        const int64_t slot = slot_base + p.n_tiles + b;
-        run_range<D, G, kKvLoadPolicy>(p, smem.tile.priv, bt_row, kvh, start, end,
+        const int64_t slot = slot_base + p.n_tiles + Wk + b;
+        run_range<D, G, kKvLoadPolicy>(p, smem.tile.priv, bt_row, kvh, start, end, quota, after + g1 - g - piece_n,
                                        [&](int c) -> int64_t { return c < G ? head_row0 + c : -1; },
                                        [&](int c, int d, float M, float Ls, float O) {
                                          const int64_t ps = slot * 16 + c;
@@ -594,6 +625,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
                                        lane, wave);
         g += piece_n;
       }
+    };
+    // half of the workgroups start on the prefix, half on private blocks, so
+    // L2-resident and HBM-bound reads overlap throughout
+    if (jw & 1) {
+      prefix_part(gp0, gp1, gv1 - gv0);
+      private_part(gv0, gv1, 0);
+    } else {
+      private_part(gv0, gv1, gp1 - gp0);
+      prefix_part(gp0, gp1, 0);
     }
   }
 }
@@ -605,7 +645,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
 // One workgroup of D threads per (sequence, query head). Its partials are the
 // pieces of the head's prefix tile segment (column = its row within the tile)
 // and of its private segment, made by KV head kvh's workgroups j0 .. j1 of the
-// balanced schedule (slot kvh * (S + Wk) + segment + j). Maxima are loaded in
+// balanced schedule (slot segment + j of each list). Maxima are loaded in
 // parallel into LDS, the merge weights exp2(m_j - M) computed once, and thread
 // d sums output dim d over the partials with independent loads.
 template <int D>
@@ -621,11 +661,11 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
   const int d = threadIdx.x;
   const int32_t L = p.lens[b];
   const bool bad_len = L < p.min_len || L > p.max_context || L > (p.max_pages << p.p_shift);
-  const int32_t Q = p.flat_hdr[1];
+  const int32_t Qv = p.flat_hdr[1];
+  const int32_t Qp = p.flat_hdr[2];
   const int32_t Wk = p.n_flat_wgs / p.Hkv;
   const int32_t PB = p.prefix_tokens / kBlk;
-  const int32_t NTP = p.n_tiles * PB;
-  const int64_t slot_base = (int64_t)kvh * (p.n_tiles + p.B + Wk);
+  const int64_t slot_base = (int64_t)kvh * (p.n_tiles + p.B + 2 * Wk);
   // prefix tile segment of row r = b * G + hg
   const int32_t r = b * G + hg;
   const int32_t rt = r / 16;
@@ -633,21 +673,21 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
   int32_t np1 = 0, ja = 0;
   if (PB > 0) {
     const int32_t u0 = rt * PB;
-    ja = u0 / Q;
-    np1 = (u0 + PB - 1) / Q - ja + 1;
+    ja = u0 / Qp;
+    np1 = (u0 + PB - 1) / Qp - ja + 1;
   }
   // private segment
   const int32_t prev = b > 0 ? p.flat_cum[b - 1] : 0;
   const int32_t nblk = p.flat_cum[b] - prev;
   int32_t np2 = 0, jb = 0;
   if (nblk > 0) {
-    const int32_t u0 = NTP + prev;
-    jb = u0 / Q;
-    np2 = (u0 + nblk - 1) / Q - jb + 1;
+    jb = prev / Qv;
+    np2 = (prev + nblk - 1) / Qv - jb + 1;
   }
   const int32_t np = bad_len ? 0 : np1 + np2;
   auto idx = [&](int32_t j) -> int64_t {
-    return j < np1 ? (slot_base + rt + ja + j) * 16 + ct : (slot_base + p.n_tiles + b + jb + (j - np1)) * 16 + hg;
+    return j < np1 ? (slot_base + rt + ja + j) * 16 + ct
+                   : (slot_base + p.n_tiles + Wk + b + jb + (j - np1)) * 16 + hg;
   };
 
   // M = max_j m_j
@@ -727,7 +767,7 @@ WsLayout ws_layout(int64_t B, int64_t D, int64_t slots) {
     at += align_up(bytes);
     return off;
   };
-  w.hdr_off = take(2 * sizeof(int32_t));
+  w.hdr_off = take(3 * sizeof(int32_t));
   w.cum_off = take(static_cast<size_t>(B) * sizeof(int32_t));
   w.fm_off = take(static_cast<size_t>(slots * 16) * sizeof(float));
   w.fl_off = take(static_cast<size_t>(slots * 16) * sizeof(float));
@@ -742,7 +782,7 @@ struct Plan {
   int32_t n_tiles;         // 16-row query tiles per KV head reading the shared prefix
   int32_t n_flat_wgs;      // workgroups of the split schedule (a multiple of Hkv)
   int32_t min_piece;       // minimum blocks per piece
-  int64_t slots;           // piece slots: Hkv * (n_tiles + B + n_flat_wgs / Hkv)
+  int64_t slots;           // piece slots: Hkv * (n_tiles + B + 2 * n_flat_wgs / Hkv)
   int64_t grid;
 };
 
@@ -761,7 +801,7 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_context, int32_t p
   p.n_flat_wgs = p.split ? max(PKV_FLAT_WORKGROUPS / Hkv, 1) * Hkv : 0;
   if (p.split && 2 * (p.n_flat_wgs / Hkv) > kMaxPartitions) return PKV_ERR_INVALID_ARG;
   p.min_piece = partition_tokens / kBlk;
-  p.slots = p.split ? static_cast<int64_t>(Hkv) * (p.n_tiles + B + p.n_flat_wgs / Hkv) : 0;
+  p.slots = p.split ? static_cast<int64_t>(Hkv) * (p.n_tiles + B + 2 * (p.n_flat_wgs / Hkv)) : 0;
   p.grid = p.split ? p.n_flat_wgs : static_cast<int64_t>(B) * Hkv;
   if (p.grid > 0x7fffffffLL || static_cast<int64_t>(B) * Hq > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
   *pl = p;
@@ -772,8 +812,8 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_context, int32_t p
 // query does not take Hkv): Hkv * n_tiles <= B * Hq / 16 + Hkv,
 // Hkv * B <= Hq * B, Hkv * (W / Hkv) <= max(W, Hkv).
 int64_t max_slots(int32_t B, int32_t Hq, bool prefix) {
-  return (prefix ? static_cast<int64_t>(B) * Hq / 16 + Hq : 0) + static_cast<int64_t>(B) * Hq + PKV_FLAT_WORKGROUPS +
-         Hq;
+  return (prefix ? static_cast<int64_t>(B) * Hq / 16 + Hq : 0) + static_cast<int64_t>(B) * Hq +
+         2 * (static_cast<int64_t>(PKV_FLAT_WORKGROUPS) + Hq);
 }
 
 template <int D, int G, bool SPLIT, bool FUSED>
