@@ -17,6 +17,11 @@ boundaries as they do in serving. Inputs are seeded synthetic data
 own random pools drawn on the device. The first step of layer 0 is checked
 against the fp64 oracle on sampled sequences.
 
+Timing: HIP events on the launch stream bracket the whole timed region
+(``ms_per_step``, ``value``) and one decode call per step, the layer rotating
+with the step (``roofline.avg_launch_us``); an event record costs a few
+microseconds of GPU time, so not every call is bracketed.
+
 Output: one JSON line on stdout (rank 0, N = 1).
 """
 
@@ -49,6 +54,11 @@ def parse_args():
     ap.add_argument("--separate-append", action="store_true", help="kv_append launch + decode instead of fused")
     ap.add_argument("--no-shared-prefix", action="store_true",
                     help="treat a shared prefix like private tokens (read once per sequence)")
+    ap.add_argument("--graph", action="store_true",
+                    help="replay a captured HIP graph of each step's layer calls instead of launching them from "
+                         "Python (slower on this stack: graph launch costs more than it saves)")
+    ap.add_argument("--patch-max", type=int, default=1024,
+                    help="table changes per step applied in place by pkv_block_table_patch; more -> full upload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--check-sequences", type=int, default=8)
@@ -197,8 +207,7 @@ def main():
         alloc.reserve(owner, prefix_pages * P)
         for b in range(B):
             alloc.share_prefix(b, alloc.table(owner))
-    bt_host = torch.full((B, max_pages), -1, dtype=torch.int32).pin_memory()
-    bt_np = bt_host.numpy()
+    bt_np = np.full((B, max_pages), -1, dtype=np.int32)          # the allocator's table (host)
     # the workload reserves pages for all of its own steps up front (page-sweep: 64 steps)
     alloc.reserve_batch(seqs, w.context + w.steps, bt_np)
     assert np.array_equal(bt_np[:, :w.max_pages], w.block_table), "allocator layout differs from the workload"
@@ -231,8 +240,7 @@ def main():
     vnew.normal_(generator=gen)
     knew[0].copy_(put(w.k_new[0]))
     vnew[0].copy_(put(w.v_new[0]))
-    bt_dev = torch.empty((B, max_pages), dtype=torch.int32, device=dev)
-    bt_dev.copy_(bt_host)
+    bt_dev = torch.from_numpy(bt_np).to(dev)
     lens_all = torch.from_numpy((w.context[None, :] + 1 + np.arange(total_steps)[:, None]).astype(np.int32)).to(dev)
     pos_all = lens_all - 1
     max_context = int(final_ctx.max())
@@ -245,33 +253,58 @@ def main():
 
     scale = w.scale
 
-    def layer_step(step, layer):
+    def layer_call(layer, lens, pos, kn, vn, s):
         if prefix_tokens:
-            pkv.paged_decode_attention_shared_prefix(
-                q, k_pools[layer], v_pools[layer], bt_dev, lens_all[step], max_context, scale, part, prefix_tokens,
-                k_new=knew[step] if fused else None, v_new=vnew[step] if fused else None, out=out,
-                workspace=workspace, stream=stream)
             if not fused:
                 raise SystemExit("the shared-prefix bench path runs with the fused append")
+            pkv.paged_decode_attention_shared_prefix(
+                q, k_pools[layer], v_pools[layer], bt_dev, lens, max_context, scale, part, prefix_tokens,
+                k_new=kn, v_new=vn, out=out, workspace=workspace, stream=s)
         elif fused:
-            pkv.append_paged_decode_attention(q, knew[step], vnew[step], k_pools[layer], v_pools[layer], bt_dev,
-                                              lens_all[step], max_context, scale, part, out=out,
-                                              workspace=workspace, stream=stream)
+            pkv.append_paged_decode_attention(q, kn, vn, k_pools[layer], v_pools[layer], bt_dev, lens, max_context,
+                                              scale, part, out=out, workspace=workspace, stream=s)
         else:
-            pkv.kv_append(knew[step], vnew[step], k_pools[layer], v_pools[layer], bt_dev, pos_all[step],
-                          stream=stream)
-            pkv.paged_decode_attention(q, k_pools[layer], v_pools[layer], bt_dev, lens_all[step], max_context,
-                                       scale, part, out=out, workspace=workspace, stream=stream)
+            pkv.kv_append(kn, vn, k_pools[layer], v_pools[layer], bt_dev, pos, stream=s)
+            pkv.paged_decode_attention(q, k_pools[layer], v_pools[layer], bt_dev, lens, max_context, scale, part,
+                                       out=out, workspace=workspace, stream=s)
+
+    def layer_step(step, layer):
+        layer_call(layer, lens_all[step], pos_all[step], knew[step], vnew[step], stream)
 
     last_bt = bt_np.copy()
+    host_t = {"alloc": 0.0, "upload": 0.0}
+    # table uploads go through a ring of pinned staging buffers; a buffer is
+    # refilled only once the stream has finished the copy that last used it
+    n_stage = 4
+    stage = [torch.empty((B, max_pages), dtype=torch.int32).pin_memory() for _ in range(n_stage)]
+    stage_ev = [torch.cuda.Event() for _ in range(n_stage)]
+    stage_used = [False] * n_stage
+    n_upload = 0
 
     def host_step(step):
         # a1: grow every sequence to hold this step's token; upload the table if it changed
-        nonlocal last_bt
+        nonlocal last_bt, n_upload
+        t0 = time.perf_counter()
         alloc.reserve_batch(seqs, w.context + step + 1, bt_np)
-        if not np.array_equal(bt_np, last_bt):
-            bt_dev.copy_(bt_host, non_blocking=True)
+        changed = not np.array_equal(bt_np, last_bt)
+        t1 = time.perf_counter()
+        if changed:
+            rows, cols = np.nonzero(bt_np != last_bt)
+            if len(rows) <= args.patch_max:
+                # a few new pages: patch the device table in place (entries in the kernel arguments)
+                pkv.block_table_patch(bt_dev, rows, cols, bt_np[rows, cols], stream=stream)
+            else:
+                i = n_upload % n_stage
+                if stage_used[i]:
+                    stage_ev[i].synchronize()
+                stage[i].numpy()[...] = bt_np
+                bt_dev.copy_(stage[i], non_blocking=True)
+                stage_ev[i].record(stream)
+                stage_used[i] = True
+                n_upload += 1
             last_bt = bt_np.copy()
+        host_t["alloc"] += t1 - t0
+        host_t["upload"] += time.perf_counter() - t1
 
     # ---- parity check: step 0, layer 0, sampled sequences, against the oracle
     host_step(0)
@@ -300,34 +333,79 @@ def main():
         log("copy calibration: 3 copies of %d MiB (read %d B + write %d B each)" % (args.copy_calibration_mib, n, n))
         del src, dst
 
+    # ---- launch mode. Graph: the R layer calls of a step are captured once as
+    # a HIP graph over fixed step buffers; each step copies its lengths and new
+    # tokens into them, then replays the graph (no Python per layer).
+    graph = None
+    if args.graph:
+        lens_cur = lens_all[0].clone()
+        pos_cur = pos_all[0].clone()
+        kn_cur = knew[0].clone()
+        vn_cur = vnew[0].clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            for layer in range(R):
+                layer_call(layer, lens_cur, pos_cur, kn_cur, vn_cur, cap)
+        torch.cuda.synchronize()
+
+    def run_step(step, per_call_events=None):
+        if graph is not None:
+            lens_cur.copy_(lens_all[step], non_blocking=True)
+            pos_cur.copy_(pos_all[step], non_blocking=True)
+            kn_cur.copy_(knew[step], non_blocking=True)
+            vn_cur.copy_(vnew[step], non_blocking=True)
+            if per_call_events is not None:
+                per_call_events[0].record(stream)
+            graph.replay()
+            if per_call_events is not None:
+                per_call_events[1].record(stream)
+        else:
+            # one call per step is bracketed by events (the layer rotates with the
+            # step): an event record costs a few microseconds of GPU time itself
+            timed = step % R
+            for layer in range(R):
+                if per_call_events is not None and layer == timed:
+                    per_call_events[0].record(stream)
+                layer_step(step, layer)
+                if per_call_events is not None and layer == timed:
+                    per_call_events[1].record(stream)
+
     # ---- warmup
     for step in range(args.warmup):
         host_step(step)
-        for layer in range(R):
-            layer_step(step, layer)
+        run_step(step)
     torch.cuda.synchronize()
 
-    # ---- timed: HIP events on the launch stream around every decode call
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(args.steps * R)]
+    # ---- timed: HIP events on the launch stream around the decode calls (the
+    # graph replay of a step's R calls, or one eager call per step)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
+    host_s = launch_s = 0.0
+    host_t["alloc"] = host_t["upload"] = 0.0
     for i in range(args.steps):
         step = args.warmup + i
+        h0 = time.perf_counter()
         host_step(step)
-        for layer in range(R):
-            e0, e1 = ev[i * R + layer]
-            e0.record(stream)
-            layer_step(step, layer)
-            e1.record(stream)
+        h1 = time.perf_counter()
+        run_step(step, ev[i])
+        host_s += h1 - h0
+        launch_s += time.perf_counter() - h1
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
-    call_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    log("host per step: allocator %.1f us, table upload %.1f us, launching the layer calls %.1f us; GPU %.1f us "
+        "per step" % (host_t["alloc"] / args.steps * 1e6, host_t["upload"] / args.steps * 1e6,
+                      launch_s / args.steps * 1e6, total_ms / args.steps * 1e3))
+    if graph is not None:
+        call_ms = np.array([e[0].elapsed_time(e[1]) / R for e in ev])
+    else:
+        call_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
     ms_per_step = total_ms / args.steps
     ms_per_layer = ms_per_step / R
 
@@ -369,6 +447,7 @@ def main():
             "partition_tokens": part,
             "layers_per_step": R,
             "append": "fused" if fused else "separate",
+            "launch": "eager" if graph is None else "hip graph per step (%d layer calls)" % R,
             "shared_prefix_path": bool(prefix_tokens),
             "tokens_per_s_definition": "batch / (time of one attention layer-step: append + decode), "
                                        "i.e. sequences advanced per second through one layer",

@@ -80,6 +80,30 @@ int pkv_abi_version(void);
 /* ------------------------------------------------------------------------ */
 
 /*
+ * pkv_block_table_patch -- set entries of a device block table from a short
+ * host list, without a host-to-device copy.
+ *
+ * Decode grows the page table one page at a time as sequences cross page
+ * boundaries (pages are taken on demand, dpshk §4.2; pgsm §4.3), so after a
+ * step only a few entries differ from the device copy. The entries travel in
+ * the kernel arguments of a one-workgroup launch (up to 128 per launch; longer
+ * lists take several), so the update is ordered on `stream` like any kernel
+ * and needs no staging buffer or DMA.
+ *
+ *   block_table : int32 [B][max_pages] device, written at the listed entries.
+ *   rows, cols, pages: int32 [n] HOST arrays (read during the call; the
+ *                 caller may reuse them on return): entry (rows[i], cols[i])
+ *                 becomes pages[i]. List each entry at most once: two
+ *                 writes of one entry in the same launch land in no set
+ *                 order.
+ * Errors: PKV_ERR_INVALID_ARG (n < 0, a row outside [0, B), a column outside
+ * [0, max_pages), a page below -1, null pointers, misaligned table; nothing is
+ * launched), PKV_ERR_HIP.
+ */
+int pkv_block_table_patch(int32_t* block_table, int32_t B, int32_t max_pages, const int32_t* rows,
+                          const int32_t* cols, const int32_t* pages, int32_t n, void* stream);
+
+/*
  * pkv_kv_append -- write each sequence's new-token K and V into its page slot.
  *
  * Decode appends the new token's K and V (one D-vector per KV head each) to

@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     PkvError,
     PageAllocator,
     append_paged_decode_attention,
+    block_table_patch,
     decode_workspace_bytes,
     kv_append,
     lib,

@@ -33,6 +33,7 @@ _SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_abi_version": (ctypes.c_int, []),
     "pkv_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_block_table_patch": (ctypes.c_int, [_vp, _i32, _i32, _ip, _ip, _ip, _i32, _vp]),
     "pkv_decode_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     "pkv_paged_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                                   _i32, _i32, ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]),
@@ -112,6 +113,21 @@ def _stream(stream):
 # ---------------------------------------------------------------------------
 # device entry points
 # ---------------------------------------------------------------------------
+
+def block_table_patch(block_table, rows, cols, pages, stream=None):
+    """pkv_block_table_patch: block_table[rows[i], cols[i]] = pages[i] on the device (host lists)."""
+    if block_table.dim() != 2:
+        raise ValueError("block_table must be [B][max_pages]")
+    B, max_pages = block_table.shape
+    r, rp = _host_i32(rows, "rows")
+    c, cp = _host_i32(cols, "cols")
+    g, gp = _host_i32(pages, "pages")
+    if not (r.shape == c.shape == g.shape) or r.ndim != 1:
+        raise ValueError("rows, cols and pages must be 1-D and of one length")
+    _check(lib().pkv_block_table_patch(_dev_ptr(block_table, torch.int32, "block_table"), B, max_pages, rp, cp, gp,
+                                       len(r), _stream(stream)), "pkv_block_table_patch")
+    return block_table
+
 
 def kv_append(k_new, v_new, k_pool, v_pool, block_table, pos, stream=None):
     """pkv_kv_append: write k_new/v_new [B][Hkv][D] at slot pos[b] of each sequence."""

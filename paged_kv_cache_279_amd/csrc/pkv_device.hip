@@ -44,6 +44,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t v4u32_t __attribute__((ext_vector_type(4)));
 
 // Tuning knobs (compile-time; the defaults are the measured best on MI355X).
 #ifndef PKV_PREFETCH_DEPTH
@@ -64,13 +65,19 @@ constexpr bool kPrioBalance = PKV_PRIO_BALANCE != 0;   // level workgroups shari
 #endif
 
 constexpr int kWave = 64;
-constexpr int kWaves = 4;
+#ifndef PKV_WAVES
+#define PKV_WAVES 4
+#endif
+constexpr int kWaves = PKV_WAVES;          // waves per workgroup
 constexpr int kThreads = kWave * kWaves;
 constexpr int kBlk = 16;                   // tokens per block (= one sub-block)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr size_t kWsAlign = 256;
-constexpr int32_t kMaxPartitions = 4096;   // partial slots per (sequence, head) (reduce kernel LDS)
-constexpr int32_t kMaxFlatBatch = 4096;    // sequences per split call (LDS prefix sums)
+constexpr int32_t kMaxPartitions = 1024;   // partial slots per (sequence, head) (reduce kernel LDS)
+#ifndef PKV_MAX_FLAT_BATCH
+#define PKV_MAX_FLAT_BATCH 4096
+#endif
+constexpr int32_t kMaxFlatBatch = PKV_MAX_FLAT_BATCH;    // sequences per split call (LDS prefix sums)
 // Online-softmax rescaling is deferred until a head's block maximum exceeds
 // the running reference by this much (base-2 exponent units): probabilities
 // then stay below 2^8 and fp16/fp32 ranges are never approached.
@@ -177,6 +184,26 @@ __global__ __launch_bounds__(D) void kv_append_kernel(const half_t* __restrict__
 }
 
 // -------------------------------------------------------------------------
+// block-table patch
+// -------------------------------------------------------------------------
+
+// Entries of one patch launch, passed by value in the kernel arguments so the
+// update needs no host-to-device copy.
+constexpr int kPatchMax = 128;
+struct TablePatch {
+  int32_t n;
+  int32_t row[kPatchMax];
+  int32_t col[kPatchMax];
+  int32_t page[kPatchMax];
+};
+
+__global__ __launch_bounds__(kPatchMax) void table_patch_kernel(int32_t* __restrict__ bt, int32_t max_pages,
+                                                                TablePatch patch) {
+  const int i = threadIdx.x;
+  if (i < patch.n) bt[(int64_t)patch.row[i] * max_pages + patch.col[i]] = patch.page[i];
+}
+
+// -------------------------------------------------------------------------
 // decode: partition kernel
 // -------------------------------------------------------------------------
 
@@ -188,6 +215,16 @@ struct WaveState {
   float m_ref;     // running reference max of this lane's column (base-2 units)
   float l_part;    // this lane's share of the column's softmax denominator
   bool bad_page;   // a page id outside [0, N) was met
+};
+
+// The token appended by this call, when it falls in the streamed range:
+// block blk of the range (< 0: none), row u of that block, and its K and V
+// ([D] fp16 each).
+struct NewToken {
+  int32_t blk;
+  int32_t u;
+  const half_t* k;
+  const half_t* v;
 };
 
 // Issue priority from the share of the workgroup's work still ahead of it.
@@ -209,14 +246,21 @@ __device__ __forceinline__ void set_priority(int32_t remaining, int32_t quota) {
 // col, dims 32 j + 8 quad .. + 8). Shared by the prefix and the private roles.
 // quota > 0: the range is part of a workgroup share of quota blocks with
 // `after` blocks following it; the wave's priority follows what is left.
-template <int D, int32_t kPolicy>
+//
+// kAppend: the new token nt is taken from k_new / v_new instead of the pool:
+// the wave that streams its block loads the token's operand slices with its
+// other loads, patches them into the block's registers before use, and writes
+// them to the pool from there. No other wave reads that row, so the write
+// needs no ordering against the loads.
+template <int D, int32_t kPolicy, bool kAppend>
 __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32_t* bt_row, int32_t kvh,
                                               int32_t start, int32_t end, int32_t first, int32_t stride,
-                                              int32_t quota, int32_t after,
+                                              int32_t quota, int32_t after, const NewToken& nt,
                                               const half8_t (&qb)[D / 32], WaveState<D>& st, int lane) {
   constexpr int KL = D / 32;           // 16-byte loads per lane per block, for K and for V
   constexpr int NT = D / 16;           // 16-dim output tiles
   const int quad = lane >> 4;          // MFMA k-group: tokens 4 quad .. 4 quad + 3
+  const int col = lane & 15;
   const int32_t pmask = (1 << p.p_shift) - 1;
   const int64_t tile_elems = (int64_t)D << p.p_shift;       // one (page, kvh) tile
   const int32_t nblocks = (end - start + kBlk - 1) / kBlk;
@@ -237,9 +281,26 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
       bad = page < 0 || page >= p.N;
     }
     if (__builtin_amdgcn_ballot_w64(bad) != 0) st.bad_page = true;   // the row becomes NaN later
-    pg = bad ? 0 : page;                                                // stay in bounds
+    pg = bad ? -1 : page;
     kb = k0;
   };
+
+  // appended token: K slice of lane (col, quad) for row u = col, and the two V
+  // values of lane (col, quad = u / 4) per 32 dims (dims 32 j + col, + 16)
+  uint4 kn[KL];
+  uint32_t vn[KL];
+  int64_t new_off = -1;                // element offset of the token's block (valid page), else -1
+  if constexpr (kAppend) {
+    if (nt.blk >= 0) {
+#pragma unroll
+      for (int j = 0; j < KL; ++j) {
+        kn[j] = *reinterpret_cast<const uint4*>(nt.k + 32 * j + 8 * quad);
+        const uint32_t lo = reinterpret_cast<const uint16_t*>(nt.v)[32 * j + col];
+        const uint32_t hi = reinterpret_cast<const uint16_t*>(nt.v)[32 * j + 16 + col];
+        vn[j] = lo | (hi << 16);
+      }
+    }
+  }
 
   // Loads go through buffer descriptors built per 16-token block (base = the
   // block's sub-block, size 16 * D halves). Past the last block the size is 0:
@@ -251,8 +312,12 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     const int32_t blk = first + k * stride;
     const bool live = blk < nblocks;
     const int32_t t0 = start + (live ? blk : 0) * kBlk;
-    const int32_t page = __builtin_amdgcn_readlane(pg, k - kb);
+    const int32_t pid = __builtin_amdgcn_readlane(pg, k - kb);
+    const int32_t page = pid < 0 ? 0 : pid;                        // stay in bounds
     const int64_t off = ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)(t0 & pmask) * D;
+    if constexpr (kAppend) {
+      if (live && blk == nt.blk && pid >= 0) new_off = off;
+    }
     const int32_t bytes = live ? kBlk * D * 2 : 0;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_pool + off), (short)0, bytes, kBufferFlags);
@@ -268,6 +333,48 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
 
   auto consume = [&](int32_t blk, uint4 kr[KL], uint4 vr[KL]) {
     const int32_t t0 = start + blk * kBlk;
+    if constexpr (kAppend) {
+      if (blk == nt.blk) {
+        // K: row u sits in lanes col == u; V: row u is half u % 4 of each
+        // 4-half group in lanes quad == u / 4
+        const bool kl = col == nt.u;
+        const bool vl = quad == (nt.u >> 2);
+        const uint32_t sh = (nt.u & 1) * 16;
+        const uint32_t keep = ~(0xFFFFu << sh);
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+          if (kl) kr[j] = kn[j];
+          const uint32_t lo = (vn[j] & 0xFFFFu) << sh;
+          const uint32_t hi = (vn[j] >> 16) << sh;
+          if (vl) {
+            if (nt.u & 2) {
+              vr[j].y = (vr[j].y & keep) | lo;
+              vr[j].w = (vr[j].w & keep) | hi;
+            } else {
+              vr[j].x = (vr[j].x & keep) | lo;
+              vr[j].z = (vr[j].z & keep) | hi;
+            }
+          }
+        }
+        if (new_off >= 0) {
+          const int32_t bytes = kBlk * D * 2;
+          const __amdgpu_buffer_rsrc_t kws =
+              __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_pool_w + new_off), (short)0, bytes, kBufferFlags);
+          const __amdgpu_buffer_rsrc_t vws =
+              __builtin_amdgcn_make_buffer_rsrc((void*)(p.v_pool_w + new_off), (short)0, bytes, kBufferFlags);
+          const int32_t hoff = (nt.u & 3) * 2;
+#pragma unroll
+          for (int j = 0; j < KL; ++j) {
+            if (kl) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, kn[j]), kws,
+                                                           lane * 16 + j * 1024, 0, 0);
+            if (vl) {
+              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(vn[j] & 0xFFFFu), vws, lane * 16 + j * 1024 + hoff, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(vn[j] >> 16), vws, lane * 16 + j * 1024 + 8 + hoff, 0, 0);
+            }
+          }
+        }
+      }
+    }
     // scores of tokens 4 quad + i for query row col
     float4_t s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -365,6 +472,7 @@ struct KernelShared {
     WgShared<D, G> priv;
   } tile;
   int32_t cum[kMaxFlatBatch];    // inclusive prefix sums of private blocks per sequence
+  int32_t len[kMaxFlatBatch];    // lens
   int32_t wsum[kWaves];
 };
 
@@ -374,10 +482,10 @@ struct KernelShared {
 // waves merge through LDS and every (column c, dim d) goes to
 // emit(c, d, M, Ls, O): the column's base-2 score max, softmax denominator
 // and unnormalised output. Callers must be workgroup-uniform.
-template <int D, int NC, int32_t kPolicy, class RowFn, class EmitFn>
+template <int D, int NC, int32_t kPolicy, bool kAppend, class RowFn, class EmitFn>
 __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>& sh, const int32_t* bt_row,
                                           int32_t kvh, int32_t start, int32_t end, int32_t quota, int32_t after,
-                                          RowFn qrow, EmitFn emit, int lane, int wave) {
+                                          const NewToken& nt, RowFn qrow, EmitFn emit, int lane, int wave) {
   constexpr int KL = D / 32;
   constexpr int NT = D / 16;
   const int col = lane & 15;
@@ -393,7 +501,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
   }
   WaveState<D> st;
   init_state<D>(st);
-  stream_blocks<D, kPolicy>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, qb, st, lane);
+  stream_blocks<D, kPolicy, kAppend>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, nt, qb, st, lane);
   // per-column denominators of this wave: sum the 4 quads of column col
   st.l_part += __shfl_xor(st.l_part, 16);
   st.l_part += __shfl_xor(st.l_part, 32);
@@ -430,21 +538,6 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
   }
   // the LDS is reused by the caller's next range
   __syncthreads();
-}
-
-// Writes the new token of sequence b, KV head kvh (position t) into its slot;
-// threads 0 .. D - 1 take part.
-template <int D>
-__device__ __forceinline__ void append_token(const DecodeParams& p, const int32_t* bt_row, int32_t b, int32_t kvh,
-                                             int32_t t) {
-  const int32_t page = bt_row[t >> p.p_shift];
-  if (page >= 0 && page < p.N) {
-    const int64_t tile_elems = (int64_t)D << p.p_shift;
-    const int32_t pmask = (1 << p.p_shift) - 1;
-    const int64_t sub = ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)((t & pmask) >> 4) * (kBlk * D);
-    const int64_t src = ((int64_t)b * p.Hkv + kvh) * D;
-    store_token<D>(p.k_pool_w + sub, p.v_pool_w + sub, t & 15, p.k_new + src, p.v_new + src, threadIdx.x);
-  }
 }
 
 // Unsplit (partition_tokens == 0): workgroup (KV head, sequence) over the
@@ -489,11 +582,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
       return;
     }
     const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
+    NewToken nt{-1, 0, nullptr, nullptr};
     if constexpr (FUSED) {
-      append_token<D>(p, bt_row, b, kvh, Lc - 1);
-      __syncthreads();   // the stores are visible to this workgroup's loads below
+      const int64_t src = ((int64_t)b * p.Hkv + kvh) * D;
+      nt = NewToken{(Lc - 1) >> 4, (Lc - 1) & 15, p.k_new + src, p.v_new + src};
     }
-    run_range<D, G, kKvLoadPolicy>(p, sh, bt_row, kvh, 0, Lc, 0, 0, [&](int c) -> int64_t { return head_row0 + c; },
+    run_range<D, G, kKvLoadPolicy, FUSED>(p, sh, bt_row, kvh, 0, Lc, 0, 0, nt, [&](int c) -> int64_t { return head_row0 + c; },
                     [&](int c, int d, float, float Ls, float O) {
                       const float r = Ls > 0.f ? O / Ls : (Ls == 0.f ? 0.f : __builtin_nanf(""));
                       p.out[(head_row0 + c) * D + d] = (half_t)(Ls != Ls ? __builtin_nanf("") : r);
@@ -501,12 +595,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
                     lane, wave);
   } else {
     int32_t* sm_cum = smem.cum;
+    int32_t* sm_len = smem.len;
     int32_t* sm_wsum = smem.wsum;
     const int32_t wg = blockIdx.x;
     const int32_t per = (p.B + kThreads - 1) / kThreads;
     const int32_t b0 = threadIdx.x * per;
     auto priv_blocks = [&](int32_t bb) -> int32_t {
       const int32_t L = p.lens[bb];
+      sm_len[bb] = L;
       const bool bad = L < p.min_len || L > p.max_context || L > (p.max_pages << p.p_shift);
       return bad ? 0 : (L - p.prefix_tokens + kBlk - 1) / kBlk;
     };
@@ -572,8 +668,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
         };
         const int64_t slot = slot_base + rt;
         // the prefix pages are the same in every row of the table: read row 0
-        run_range<D, 16, kPrefixLoadPolicy>(p, smem.tile.prefix, p.bt, kvh, blk0 * kBlk, (blk0 + piece_n) * kBlk, quota,
-                                            after + g1 - g - piece_n, qrow,
+        run_range<D, 16, kPrefixLoadPolicy, false>(p, smem.tile.prefix, p.bt, kvh, blk0 * kBlk, (blk0 + piece_n) * kBlk,
+                                                   quota, after + g1 - g - piece_n, NewToken{-1, 0, nullptr, nullptr}, qrow,
                                             [&](int c, int d, float M, float Ls, float O) {
                                               const int64_t ps = slot * 16 + c;
                                               p.flat_o[ps * D + d] = O;
@@ -601,18 +697,22 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
         const int32_t seg_n = sm_cum[b] - seg_first;
         const int32_t blk0 = g - seg_first;
         const int32_t piece_n = min(g1 - g, seg_n - blk0);
-        const int32_t L = p.lens[b];
+        const int32_t L = sm_len[b];
         const int32_t start = p.prefix_tokens + blk0 * kBlk;
         const int32_t end = min(L, p.prefix_tokens + (blk0 + piece_n) * kBlk);
         const int64_t head_row0 = (int64_t)b * p.Hq + (int64_t)kvh * G;
         const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
+        NewToken nt{-1, 0, nullptr, nullptr};
         if constexpr (FUSED) {
           // the piece holding the sequence's last block owns its new token
-          if (blk0 + piece_n == seg_n) append_token<D>(p, bt_row, b, kvh, end - 1);
-          __syncthreads();   // the stores are visible to this workgroup's loads below
+          if (blk0 + piece_n == seg_n) {
+            const int64_t src = ((int64_t)b * p.Hkv + kvh) * D;
+            nt = NewToken{(end - 1 - start) >> 4, (end - 1) & 15, p.k_new + src, p.v_new + src};
+          }
         }
         const int64_t slot = slot_base + p.n_tiles + Wk + b;
-        run_range<D, G, kKvLoadPolicy>(p, smem.tile.priv, bt_row, kvh, start, end, quota, after + g1 - g - piece_n,
+        run_range<D, G, kKvLoadPolicy, FUSED>(p, smem.tile.priv, bt_row, kvh, start, end, quota,
+                                              after + g1 - g - piece_n, nt,
                                        [&](int c) -> int64_t { return c < G ? head_row0 + c : -1; },
                                        [&](int c, int d, float M, float Ls, float O) {
                                          const int64_t ps = slot * 16 + c;
@@ -645,13 +745,15 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
 // One workgroup of D threads per (sequence, query head). Its partials are the
 // pieces of the head's prefix tile segment (column = its row within the tile)
 // and of its private segment, made by KV head kvh's workgroups j0 .. j1 of the
-// balanced schedule (slot segment + j of each list). Maxima are loaded in
-// parallel into LDS, the merge weights exp2(m_j - M) computed once, and thread
-// d sums output dim d over the partials with independent loads.
+// balanced schedule (slot segment + j of each list). Every load is issued
+// before any arithmetic: the maxima and denominators go to LDS, and thread d
+// holds output dim d of the first partials in registers; then each thread
+// merges over all partials with weights exp2(m_j - M).
 template <int D>
 __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
-  __shared__ float sm_w[kMaxPartitions];
-  __shared__ float sm_red[D / kWave];
+  constexpr int kR = 8;               // partials whose outputs are loaded up front
+  __shared__ float sm_m[kMaxPartitions];
+  __shared__ float sm_l[kMaxPartitions];
   const int64_t bh = blockIdx.x;
   const int32_t b = (int32_t)(bh / p.Hq);
   const int32_t h = (int32_t)(bh % p.Hq);
@@ -690,46 +792,33 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
                    : (slot_base + p.n_tiles + Wk + b + jb + (j - np1)) * 16 + hg;
   };
 
-  // M = max_j m_j
-  float M = kNegInf();
-  for (int32_t j = d; j < np; j += D) {
-    const float mj = p.flat_m[idx(j)];
-    sm_w[j] = mj;
-    M = fmaxf(M, mj);
-  }
-  for (int off = 32; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
-  if ((d & (kWave - 1)) == 0) sm_red[d / kWave] = M;
-  __syncthreads();
-  M = sm_red[0];
-#pragma unroll
-  for (int w = 1; w < D / kWave; ++w) M = fmaxf(M, sm_red[w]);
-  const float Ms = M == kNegInf() ? 0.f : M;
-  __syncthreads();
-  // weights and the denominator
-  float Lp = 0.f;
-  for (int32_t j = d; j < np; j += D) {
-    const float wj = fast_exp2(sm_w[j] - Ms);
-    sm_w[j] = wj;
-    Lp = fmaf(wj, p.flat_l[idx(j)], Lp);
-  }
-  for (int off = 32; off > 0; off >>= 1) Lp += __shfl_xor(Lp, off);
-  if ((d & (kWave - 1)) == 0) sm_red[d / kWave] = Lp;
-  __syncthreads();
-  float Ls = 0.f;
-#pragma unroll
-  for (int w = 0; w < D / kWave; ++w) Ls += sm_red[w];
-  // numerator of dim d, four independent partial sums
   const float* po = p.flat_o + d;
-  float O0 = 0.f, O1 = 0.f, O2 = 0.f, O3 = 0.f;
-  int32_t j = 0;
-  for (; j + 4 <= np; j += 4) {
-    O0 = fmaf(sm_w[j + 0], po[idx(j + 0) * D], O0);
-    O1 = fmaf(sm_w[j + 1], po[idx(j + 1) * D], O1);
-    O2 = fmaf(sm_w[j + 2], po[idx(j + 2) * D], O2);
-    O3 = fmaf(sm_w[j + 3], po[idx(j + 3) * D], O3);
+  float ov[kR];
+#pragma unroll
+  for (int j = 0; j < kR; ++j) ov[j] = j < np ? po[idx(j) * D] : 0.f;
+  for (int32_t j = d; j < np; j += D) {
+    const int64_t q = idx(j);
+    sm_m[j] = p.flat_m[q];
+    sm_l[j] = p.flat_l[q];
   }
-  for (; j < np; ++j) O0 = fmaf(sm_w[j], po[idx(j) * D], O0);
-  const float O = (O0 + O1) + (O2 + O3);
+  __syncthreads();
+  float M = kNegInf();
+  for (int32_t j = 0; j < np; ++j) M = fmaxf(M, sm_m[j]);
+  const float Ms = M == kNegInf() ? 0.f : M;
+  float Ls = 0.f, O = 0.f;
+#pragma unroll
+  for (int j = 0; j < kR; ++j) {
+    if (j < np) {
+      const float wj = fast_exp2(sm_m[j] - Ms);
+      Ls = fmaf(wj, sm_l[j], Ls);
+      O = fmaf(wj, ov[j], O);
+    }
+  }
+  for (int32_t j = kR; j < np; ++j) {
+    const float wj = fast_exp2(sm_m[j] - Ms);
+    Ls = fmaf(wj, sm_l[j], Ls);
+    O = fmaf(wj, po[idx(j) * D], O);
+  }
   float res = Ls > 0.f ? O / Ls : 0.f;
   if (bad_len || Ls != Ls) res = __builtin_nanf("");
   p.out[bh * D + d] = (half_t)res;
@@ -941,6 +1030,30 @@ int workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context, int32
 }  // namespace
 
 extern "C" {
+
+int pkv_block_table_patch(int32_t* block_table, int32_t B, int32_t max_pages, const int32_t* rows,
+                          const int32_t* cols, const int32_t* pages, int32_t n, void* stream) {
+  if (B < 0 || max_pages <= 0 || n < 0) return PKV_ERR_INVALID_ARG;
+  if (n == 0) return PKV_OK;
+  if (!block_table || !rows || !cols || !pages || !aligned(block_table, 4)) return PKV_ERR_INVALID_ARG;
+  for (int32_t i = 0; i < n; ++i) {
+    if (rows[i] < 0 || rows[i] >= B || cols[i] < 0 || cols[i] >= max_pages || pages[i] < -1)
+      return PKV_ERR_INVALID_ARG;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t at = 0; at < n; at += kPatchMax) {
+    TablePatch patch;
+    patch.n = min(n - at, kPatchMax);
+    for (int32_t i = 0; i < patch.n; ++i) {
+      patch.row[i] = rows[at + i];
+      patch.col[i] = cols[at + i];
+      patch.page[i] = pages[at + i];
+    }
+    hipLaunchKernelGGL(table_patch_kernel, dim3(1), dim3(kPatchMax), 0, s, block_table, max_pages, patch);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  }
+  return PKV_OK;
+}
 
 int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool, const int32_t* block_table,
                   int32_t max_pages, const int32_t* pos, int32_t B, int32_t Hkv, int32_t D, int32_t P, int32_t N,

@@ -197,3 +197,24 @@ def test_validate_tables_matches_model(B, width, P, N, seed, excl):
         kind, prow, pentry = problems[0]
         assert rc == pkv.PKV_ERR_INVALID_TABLE
         assert (row, entry, rule) == (prow, pentry, rules[kind])
+
+
+def test_block_table_patch_argument_checks(pkv):
+    f = pkv.lib().pkv_block_table_patch
+    vp, ip = ctypes.c_void_p, ctypes.POINTER(ctypes.c_int32)
+
+    def call(rows, cols, pages, B=4, max_pages=8, table=16, n=None):
+        r = np.asarray(rows, np.int32)
+        c = np.asarray(cols, np.int32)
+        g = np.asarray(pages, np.int32)
+        return f(vp(table), B, max_pages, r.ctypes.data_as(ip), c.ctypes.data_as(ip), g.ctypes.data_as(ip),
+                 len(r) if n is None else n, None)
+
+    # fake device pointer: every case fails (or is a no-op) before any launch
+    assert call([], [], []) == 0
+    assert call([0], [0], [0], n=-1) == 1
+    assert call([4], [0], [1]) == 1            # row outside [0, B)
+    assert call([0], [8], [1]) == 1            # column outside [0, max_pages)
+    assert call([0], [0], [-2]) == 1           # page below -1
+    assert call([0], [0], [1], table=2) == 1   # misaligned table
+    assert call([0], [0], [1], table=0) == 1

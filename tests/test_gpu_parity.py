@@ -433,3 +433,68 @@ def test_shared_prefix_argument_checks():
         with pytest.raises(m.PkvError) as e:
             m.paged_decode_attention_shared_prefix(*args, part, prefix)
         assert e.value.status == m.PKV_ERR_INVALID_ARG
+
+
+# ---------------------------------------------------------------------------
+# HIP graph capture: a captured decode call replays to the eager result
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_graph_replay_matches_eager(fused):
+    w = wl(3, None, 6)
+    step = 0
+    lens = w.lens(step)
+    prefix = w.shared_prefix_pages * w.P
+    part = 512
+    say("graph replay fused=%s" % fused)
+    m = pkv()
+    k0, v0 = poison_unused(w, lens - 1 if fused else lens)
+    kp, vp = dev(k0), dev(v0)
+    q, bt, dl = dev(w.q), dev(w.block_table), dev(lens)
+    kn, vn = dev(w.k_new[step]), dev(w.v_new[step])
+    ws = torch.empty(m.decode_workspace_bytes(w.B, w.Hq, w.D, int(lens.max()), part, prefix), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((w.B, w.Hq, w.D), dtype=torch.float16, device="cuda")
+
+    def call(stream=None):
+        m.paged_decode_attention_shared_prefix(q, kp, vp, bt, dl, int(lens.max()), w.scale, part, prefix,
+                                               k_new=kn if fused else None, v_new=vn if fused else None, out=out,
+                                               workspace=ws, stream=stream)
+
+    call()
+    torch.cuda.synchronize()
+    eager = host(out).copy()
+    eager_k, eager_v = host(kp).copy(), host(vp).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(torch.cuda.current_stream())
+    for rep in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(out).view(np.uint16), eager.view(np.uint16)), "replay %d" % rep
+        # the fused append writes the same token again: the pools stay as after the eager call
+        assert np.array_equal(host(kp).view(np.uint16), eager_k.view(np.uint16))
+        assert np.array_equal(host(vp).view(np.uint16), eager_v.view(np.uint16))
+        _ = torch.ones(1024, device="cuda").sum().item()      # eager work between replays
+
+
+def test_block_table_patch_matches_host_table():
+    m = pkv()
+    rng = np.random.default_rng(5)
+    B, W = 37, 300
+    base = rng.integers(-1, 5000, size=(B, W)).astype(np.int32)
+    d = dev(base)
+    # 300 distinct entries: three launches of up to 128
+    flat = rng.choice(B * W, size=300, replace=False)
+    rows, cols = flat // W, flat % W
+    pages = rng.integers(-1, 5000, size=300).astype(np.int32)
+    say("table patch n=300")
+    m.block_table_patch(d, rows, cols, pages)
+    torch.cuda.synchronize()
+    expect = base.copy()
+    expect[rows, cols] = pages
+    assert np.array_equal(host(d), expect)
+    m.block_table_patch(d, [], [], [])        # nothing to do
+    assert np.array_equal(host(d), expect)

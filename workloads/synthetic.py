@@ -20,7 +20,9 @@ few thousand tokens as on dpshk §2.1):
 1. tiny: B=1, Hq=Hkv=4, D=64, 256 tokens, P=16, the 16 pages at the first 16
    entries of a permutation of a 64-page pool, scale 1/8, no append.
 2. llama2-7b-mha: B=8, Hq=Hkv=32, D=128, cached context ~ U{200..4096}, P=16,
-   pool sized to the demand, append one token then attend over context+1.
+   pool sized to the demand, append one token then attend over context+1;
+   1024-token partitions (the split path: 8 sequences alone fill too few
+   workgroups).
 3. llama3-8b-gqa-prefix: B=64, Hq=32, Hkv=8, D=128, P=16; every sequence starts
    with the same 128 pages (a 2048-token system prefix); private context
    ~ round(LogNormal(ln 1024, ln 2)) clipped to [128, 8192]; append one token;
@@ -161,7 +163,8 @@ def workload(number, page_size=None, seed=None, batch=None):
     if number == 2:
         B = batch or 8
         ctx = rng.integers(200, 4096, size=B, endpoint=True)
-        return _build("llama2-7b-mha", rng, seed, B, 32, 32, 128, 16, ctx, ctx + 1, 1, 1.0 / math.sqrt(128))
+        return _build("llama2-7b-mha", rng, seed, B, 32, 32, 128, 16, ctx, ctx + 1, 1, 1.0 / math.sqrt(128),
+                      partition_tokens=1024)
     if number == 3:
         B = batch or 64
         private = np.clip(np.rint(rng.lognormal(math.log(1024.0), math.log(2.0), size=B)), 128, 8192).astype(np.int64)
