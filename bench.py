@@ -105,10 +105,17 @@ def algorithmic_bytes(lens, B, Hq, Hkv, D, P, shared_tokens):
 
 
 def kernel_source_digest():
+    """sha256 of the device source with comments and whitespace removed, so a
+    comment edit does not orphan the committed counter summary."""
     import hashlib
+    import re
     path = os.path.join(ROOT, "paged_kv_cache_279_amd", "csrc", "pkv_device.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()
 
 
 def measured_traffic(workload_name, config_key):
@@ -124,7 +131,7 @@ def measured_traffic(workload_name, config_key):
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256") != kernel_source_digest():
+    if rec.get("kernel_code_sha256") != kernel_source_digest():
         return None
     entry = rec.get("configs", {}).get(config_key)
     if not entry or entry.get("workload") != workload_name:

@@ -188,8 +188,9 @@ int pkv_paged_decode_attention(void* out, const void* q, const void* k_pool, con
  * Same result as pkv_kv_append(k_new, v_new, ..., pos = lens - 1) followed by
  * pkv_paged_decode_attention(...): the new token is part of the context it
  * attends to (hotelren §3.1: write the new K/V at the end, then attend). The
- * workgroup that owns the last partition of (b, KV head) writes the new K/V
- * into the pool and uses them from registers, saving a launch per step.
+ * wave that streams the block holding the new token takes its K/V from k_new /
+ * v_new into registers, uses them there and writes them to the pool, saving
+ * a launch per step.
  * lens[b] >= 1 is the context after the append; lens[b] == 0 writes a zero
  * row and appends nothing. Arguments as in the two calls above.
  */

@@ -25,12 +25,14 @@
 // The group of G = Hq / Hkv query heads shares every K/V byte (G <= 16 fills
 // the 16 MFMA columns); each K/V byte is read from memory once per step.
 //
-// Decode kernel organisation: one workgroup of 4 waves per (sequence, KV head,
-// partition). A wave owns 16-token blocks blk = wave, wave + 4, ... of the
-// partition and keeps its own online-softmax state (running max per head,
-// partial sums, fp32 output tile); the next block's loads are in flight while
-// the current one is consumed. At the end the 4 waves merge through LDS into
-// either the final fp16 row or a (max, sum, unnormalised output) partial.
+// Decode kernel organisation: a workgroup of 4 waves streams a range of
+// 16-token blocks of one KV head (a whole context when unsplit; a piece of the
+// balanced split schedule otherwise). A wave owns blocks blk = wave, wave + 4,
+// ... of the range and keeps its own online-softmax state (running max per
+// column, partial sums, fp32 output tile); the next blocks' loads are in flight
+// while the current one is consumed. At the end of the range the 4 waves merge
+// through LDS into either the final fp16 rows or a (max, sum, unnormalised
+// output) partial per column.
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -243,7 +245,7 @@ __device__ __forceinline__ void set_priority(int32_t remaining, int32_t quota) {
 // Streams blocks first, first + stride, ... (< nblocks) of the token range
 // [start, end) of the tiles reached through bt_row / kvh, for the query rows
 // held in qb (B operand of the score MFMA: lane (col, quad) holds query row
-// col, dims 32 j + 8 quad .. + 8). Shared by the prefix and the private roles.
+// col, dims 32 j + 8 quad .. + 8). Shared by prefix tiles and private ranges.
 // quota > 0: the range is part of a workgroup share of quota blocks with
 // `after` blocks following it; the wave's priority follows what is left.
 //
