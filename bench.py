@@ -59,6 +59,8 @@ def parse_args():
                          "Python (slower on this stack: graph launch costs more than it saves)")
     ap.add_argument("--patch-max", type=int, default=1024,
                     help="table changes per step applied in place by pkv_block_table_patch; more -> full upload")
+    ap.add_argument("--no-stream-peak", action="store_true",
+                    help="skip the streaming-read ceiling measurement (pkv_probe_stream_read)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="minimum oracle time for the CPU baseline")
     ap.add_argument("--check-sequences", type=int, default=8)
@@ -139,6 +141,32 @@ def measured_traffic(workload_name, config_key):
     return (entry["fetch_kib_per_call"] * rec["fetch_scale"] + entry["write_kib_per_call"] * rec["write_scale"]) * 1024
 
 
+def streaming_peak(torch, pkv, nbytes, stream, n_buf=8, reps=4):
+    """Streaming-read rate over the decode call's byte count: pkv_probe_stream_read
+    over random 4 KiB tiles of n_buf rotating buffers (so the 256 MB
+    Infinity Cache holds none of them), timed back to back with HIP events."""
+    n_tiles = max(1, int(nbytes) // 4096)
+    bufs = [torch.ones(n_tiles * 4096, dtype=torch.uint8, device="cuda") for _ in range(n_buf)]
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(7)
+    order = torch.randperm(n_tiles, device="cuda", generator=gen).to(torch.int32)
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
+    for b in bufs:
+        pkv.probe_stream_read(b, order, sink, stream=stream)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for r in range(n_buf * reps):
+        pkv.probe_stream_read(bufs[r % n_buf], order, sink, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / (n_buf * reps)
+    del bufs
+    torch.cuda.empty_cache()
+    return n_tiles * 4096 / us / 1e3, us, n_tiles * 4096
+
+
 def cpu_baseline(w, seconds):
     """Time the oracle (as it stands) on layer 0 of the workload: append then
     decode for every sequence, repeated until ``seconds`` have passed."""
@@ -147,7 +175,8 @@ def cpu_baseline(w, seconds):
     step = 0
     lens = w.lens(step)
     passes = 0
-    with threadpool_limits(limits=1):
+    cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         while True:
             kp, vp = oracle.kv_append(w.k_pool, w.v_pool, w.k_new[step], w.v_new[step], w.block_table,
@@ -160,10 +189,11 @@ def cpu_baseline(w, seconds):
     return {
         "value": passes * w.B / dt,
         "unit": "tokens/s",
-        "cores": 1,
+        "cores": cores,
         "kind": "oracle",
         "sample": "%d pass(es) of append + decode over layer 0 of workload '%s' (%d sequences, %d cached tokens), "
-                  "numpy fp64, one thread; %.1f s" % (passes, w.name, w.B, int(lens.sum()), dt),
+                  "numpy fp64 with %d BLAS threads (the oracle's Python loops run on one); %.1f s"
+                  % (passes, w.name, w.B, int(lens.sum()), cores, dt),
         "cpu_model": cpu_model(),
         "host_cores_available": len(os.sched_getaffinity(0)),
         "numpy": np.__version__,
@@ -481,6 +511,14 @@ def main():
             "avg_launch_us": round(call_avg_s * 1e6, 3),
         },
     }
+    if not args.no_stream_peak:
+        peak_gbps, peak_us, peak_bytes = streaming_peak(torch, pkv, bytes_per_call, stream)
+        log("streaming-read ceiling: %.1f MB in %.2f us = %.0f GB/s" % (peak_bytes / 1e6, peak_us, peak_gbps))
+        result["roofline"]["streaming_read_peak"] = {
+            "value": round(peak_gbps, 1), "unit": "GB/s", "bytes": peak_bytes, "us": round(peak_us, 3),
+            "how": "pkv_probe_stream_read: the call's byte count as random 4 KiB tiles, non-temporal 16-byte "
+                   "loads, 8 rotating buffers, back-to-back launches"}
+        result["roofline"]["frac_of_streaming_peak"] = round(achieved / peak_gbps, 4)
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (>= %.0f s)" % args.cpu_seconds)
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)

@@ -248,6 +248,27 @@ int pkv_paged_decode_attention_shared_prefix(void* out, const void* q, const voi
                                              float scale, int32_t partition_tokens, int32_t prefix_tokens,
                                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pkv_probe_stream_read -- measurement aid (not part of decode): read
+ * n_tiles 4 KiB tiles of `base` in the order tile_order gives, with the decode
+ * kernel's access pattern (16-byte non-temporal loads per lane, two tiles in
+ * flight per wave), to measure the streaming-read rate the decode kernels are
+ * compared against (pgsm §4.2 makes decode a KV-read-bound step, so this
+ * rate, not the spec sheet, is what the kernels can reach).
+ *
+ *   base       : device buffer of `bytes` bytes, read only.
+ *   tile_order : int32 [n_tiles] device, normally a permutation of
+ *                [0, bytes / 4096); entries outside that range are clamped
+ *                into it.
+ *   waves      : waves to spread the tiles over (consecutive runs per wave).
+ *   sink       : int32 [1] device; written only on a 1-in-2^32 fold value,
+ *                so the loads cannot be dropped.
+ * Errors: PKV_ERR_INVALID_ARG (n_tiles < 0, waves <= 0, bytes below
+ * n_tiles * 4096, null or misaligned pointers), PKV_ERR_HIP.
+ */
+int pkv_probe_stream_read(const void* base, size_t bytes, const int32_t* tile_order, int32_t n_tiles,
+                          int32_t waves, int32_t* sink, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host page allocator (CPU only; no device calls)                           */
 /* ------------------------------------------------------------------------ */

@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     lib,
     paged_decode_attention,
     paged_decode_attention_shared_prefix,
+    probe_stream_read,
     status_string,
     validate_tables,
 )

@@ -34,6 +34,7 @@ _SIGNATURES = {
     "pkv_abi_version": (ctypes.c_int, []),
     "pkv_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_block_table_patch": (ctypes.c_int, [_vp, _i32, _i32, _ip, _ip, _ip, _i32, _vp]),
+    "pkv_probe_stream_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _i32, _i32, _vp, _vp]),
     "pkv_decode_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     "pkv_paged_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                                   _i32, _i32, ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]),
@@ -127,6 +128,17 @@ def block_table_patch(block_table, rows, cols, pages, stream=None):
     _check(lib().pkv_block_table_patch(_dev_ptr(block_table, torch.int32, "block_table"), B, max_pages, rp, cp, gp,
                                        len(r), _stream(stream)), "pkv_block_table_patch")
     return block_table
+
+
+def probe_stream_read(buf, tile_order, sink, waves=8192, stream=None):
+    """pkv_probe_stream_read: read the 4 KiB tiles of ``buf`` (a uint8 device
+    tensor) in ``tile_order`` (int32 device) -- the streaming-read ceiling."""
+    if buf.dtype != torch.uint8 or tile_order.dtype != torch.int32 or tile_order.dim() != 1:
+        raise ValueError("buf must be uint8, tile_order 1-D int32")
+    _check(lib().pkv_probe_stream_read(_dev_ptr(buf, torch.uint8, "buf"), buf.numel(),
+                                       _dev_ptr(tile_order, torch.int32, "tile_order"), tile_order.numel(),
+                                       int(waves), _dev_ptr(sink, torch.int32, "sink"), _stream(stream)),
+           "pkv_probe_stream_read")
 
 
 def kv_append(k_new, v_new, k_pool, v_pool, block_table, pos, stream=None):

@@ -186,6 +186,54 @@ __global__ __launch_bounds__(D) void kv_append_kernel(const half_t* __restrict__
 }
 
 // -------------------------------------------------------------------------
+// measurement aid: streaming-read ceiling
+// -------------------------------------------------------------------------
+
+// Each wave reads tiles [w * per_wave, (w + 1) * per_wave) of tile_order (4 KiB
+// tiles of base) with the decode kernel's access pattern: per lane 16-byte
+// non-temporal buffer loads, a rolling prefetch of two tiles, descriptors
+// of size 0 past the end. The data is folded into one word so the loads stay.
+__global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* __restrict__ base,
+                                                               const int32_t* __restrict__ tile_order,
+                                                               int32_t n_tiles, int64_t max_tile,
+                                                               int32_t per_wave, int32_t* __restrict__ sink) {
+  constexpr int kRing = 3;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wave = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+  const int64_t t0 = wave * per_wave;
+  if (t0 >= n_tiles) return;
+  const int32_t n = (int32_t)min((int64_t)per_wave, (int64_t)n_tiles - t0);
+  uint4 r[kRing][4];
+  uint32_t acc = 0;
+  auto load = [&](int32_t i, uint4* dst) {
+    const bool live = i < n;
+    const int64_t tile = min(max((int64_t)tile_order[t0 + (live ? i : 0)], (int64_t)0), max_tile);
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(base + tile * 4096), (short)0, live ? 4096 : 0, kBufferFlags);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dst[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rs, lane * 16 + j * 1024, 0, 2));
+  };
+  load(0, r[0]);
+  load(1, r[1]);
+  int32_t i = 0;
+  while (true) {
+#pragma unroll
+    for (int q = 0; q < kRing; ++q) {
+      if (i >= n) {
+        if (acc == 0x9E3779B9u) sink[0] = (int32_t)acc;
+        return;
+      }
+      load(i + 2, r[(q + 2) % kRing]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc ^= r[q][j].x ^ r[q][j].y ^ r[q][j].z ^ r[q][j].w;
+      ++i;
+    }
+  }
+}
+
+// -------------------------------------------------------------------------
 // block-table patch
 // -------------------------------------------------------------------------
 
@@ -1032,6 +1080,22 @@ int workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context, int32
 }  // namespace
 
 extern "C" {
+
+int pkv_probe_stream_read(const void* base, size_t bytes, const int32_t* tile_order, int32_t n_tiles,
+                          int32_t waves, int32_t* sink, void* stream) {
+  if (n_tiles < 0 || waves <= 0) return PKV_ERR_INVALID_ARG;
+  if (n_tiles == 0) return PKV_OK;
+  if (!base || !tile_order || !sink || !aligned(base, 16) || !aligned(tile_order, 4) || !aligned(sink, 4))
+    return PKV_ERR_INVALID_ARG;
+  if (bytes / 4096 < static_cast<size_t>(n_tiles)) return PKV_ERR_INVALID_ARG;
+  const int64_t per_wave = (static_cast<int64_t>(n_tiles) + waves - 1) / waves;
+  const int64_t grid = (static_cast<int64_t>(waves) + kWaves - 1) / kWaves;
+  if (grid > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
+  hipLaunchKernelGGL(stream_read_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const char*>(base), tile_order, n_tiles,
+                     static_cast<int64_t>(bytes / 4096) - 1, static_cast<int32_t>(per_wave), sink);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
 
 int pkv_block_table_patch(int32_t* block_table, int32_t B, int32_t max_pages, const int32_t* rows,
                           const int32_t* cols, const int32_t* pages, int32_t n, void* stream) {

@@ -218,3 +218,14 @@ def test_block_table_patch_argument_checks(pkv):
     assert call([0], [0], [-2]) == 1           # page below -1
     assert call([0], [0], [1], table=2) == 1   # misaligned table
     assert call([0], [0], [1], table=0) == 1
+
+
+def test_probe_stream_read_argument_checks(pkv):
+    f = pkv.lib().pkv_probe_stream_read
+    vp = ctypes.c_void_p
+    assert f(vp(256), 1 << 20, vp(256), 0, 64, vp(256), None) == 0          # nothing to read
+    assert f(vp(256), 1 << 20, vp(256), -1, 64, vp(256), None) == 1
+    assert f(vp(256), 1 << 20, vp(256), 16, 0, vp(256), None) == 1          # no waves
+    assert f(vp(256), 4096 * 15, vp(256), 16, 64, vp(256), None) == 1       # buffer smaller than the tiles
+    assert f(vp(0), 1 << 20, vp(256), 16, 64, vp(256), None) == 1
+    assert f(vp(8), 1 << 20, vp(256), 16, 64, vp(256), None) == 1           # misaligned

@@ -498,3 +498,63 @@ def test_block_table_patch_matches_host_table():
     assert np.array_equal(host(d), expect)
     m.block_table_patch(d, [], [], [])        # nothing to do
     assert np.array_equal(host(d), expect)
+
+
+# ---------------------------------------------------------------------------
+# page sweep: 64 steps with pages taken on demand vs reserved up front
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("P", [16, 64])
+def test_page_sweep_lazy_allocation_is_bit_identical(P):
+    """The 64 append + decode steps of the page-sweep workload, run (a) on the
+    workload's table with pages for every step reserved up front and (b) with
+    the host allocator taking pages only when a sequence crosses a page
+    boundary (a different physical page order, the device table patched with
+    pkv_block_table_patch). Outputs and logical K/V agree bit for bit at every
+    step; steps 0, the first page-crossing step and 63 match the oracle."""
+    m = pkv()
+    w = wl(5, P, 4)
+    B, N, part = w.B, w.N, w.partition_tokens
+    say("page sweep lazy vs reserved P=%d" % P)
+    # (b): the same logical context in other physical pages
+    order = np.random.default_rng(99).permutation(N).astype(np.int32)
+    alloc = m.PageAllocator(N, P, free_order=order)
+    bt_b = np.full(w.block_table.shape, -1, np.int32)
+    alloc.reserve_batch(np.arange(B), w.context, bt_b)
+    k_b = np.full_like(w.k_pool, np.nan)
+    v_b = np.full_like(w.v_pool, np.nan)
+    for b in range(B):
+        for j in range(-(-int(w.context[b]) // P)):
+            k_b[bt_b[b, j]] = w.k_pool[w.block_table[b, j]]
+            v_b[bt_b[b, j]] = w.v_pool[w.block_table[b, j]]
+    ka, va, kb, vb = dev(w.k_pool), dev(w.v_pool), dev(k_b), dev(v_b)
+    bt_a_dev, bt_b_dev = dev(w.block_table), dev(bt_b)
+    q = dev(w.q)
+    crossing = next(s for s in range(w.steps) if np.any(w.pos(s) % P == 0))
+    check_steps = {0, crossing, w.steps - 1}
+    ref_k, ref_v = w.k_pool.copy(), w.v_pool.copy()
+    for s in range(w.steps):
+        lens = w.lens(s)
+        prev = bt_b.copy()
+        alloc.reserve_batch(np.arange(B), lens, bt_b)
+        rows, cols = np.nonzero(bt_b != prev)
+        m.block_table_patch(bt_b_dev, rows, cols, bt_b[rows, cols])
+        kn, vn, dl = dev(w.k_new[s]), dev(w.v_new[s]), dev(lens)
+        out_a = m.append_paged_decode_attention(q, kn, vn, ka, va, bt_a_dev, dl, int(lens.max()), w.scale, part)
+        out_b = m.append_paged_decode_attention(q, kn, vn, kb, vb, bt_b_dev, dl, int(lens.max()), w.scale, part)
+        torch.cuda.synchronize()
+        ga, gb = host(out_a), host(out_b)
+        assert np.array_equal(ga.view(np.uint16), gb.view(np.uint16)), "step %d" % s
+        ref_k, ref_v = oracle.kv_append(ref_k, ref_v, w.k_new[s], w.v_new[s], w.block_table, w.pos(s), P)
+        if s in check_steps:
+            assert np.array_equal(host(ka).view(np.uint16), ref_k.view(np.uint16)), "pool after step %d" % s
+            ref = oracle.decode_attention(w.q, ref_k, ref_v, w.block_table, lens, w.scale, P)
+            check_close(out_a, ref, "page sweep P=%d step %d" % (P, s))
+    # every logical token of (b) equals (a); slots past the end differ by design
+    final = w.lens(w.steps - 1)
+    for pa, pb, kind in ((host(ka), host(kb), "k"), (host(va), host(vb), "v")):
+        for b in range(B):
+            for h in range(w.Hkv):
+                xa = oracle.gather_sequence(pa, w.block_table[b], int(final[b]), h, P, kind)
+                xb = oracle.gather_sequence(pb, bt_b[b], int(final[b]), h, P, kind)
+                assert np.array_equal(xa, xb)
