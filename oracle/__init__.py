@@ -34,4 +34,17 @@ from .paged_decode import (  # noqa: F401
     decode_partials,
     lse_merge,
 )
+from .quant_k8 import (  # noqa: F401
+    k8_subblock_bytes,
+    k8_pool_bytes,
+    k8_code_offset,
+    k8_scale_offset,
+    quantize_k,
+    k8_write_token,
+    k8_read_token,
+    quantize_k_pool,
+    k8_gather_sequence,
+    decode_attention_k8,
+    kv_append_k8,
+)
 from .allocator import PageAllocatorModel, OutOfPages, validate_tables  # noqa: F401

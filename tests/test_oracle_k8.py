@@ -1,0 +1,215 @@
+"""Pins for the int8-key oracle (oracle/quant_k8.py).
+
+* exact quantiser cases: zero vectors, a grid the scale divides exactly, ties
+  rounded half to even;
+* the quantiser's error bound (|k - code * scale| <= scale / 2, the extreme
+  value reaching +-127) on random vectors;
+* the storage format is a bijection (every code and scale byte has one home)
+  and writing then gathering returns each token's dequantised key;
+* brute force: textbook attention over the contiguous dequantised keys equals
+  the oracle reading them scattered through permuted int8 pages;
+* the append changes exactly one token's codes, scale and value per head;
+* planted mistakes in the module's source trip at least one of these pins.
+"""
+
+import math
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import quant_k8
+
+
+def _fp16(x):
+    return np.asarray(x, np.float16)
+
+
+# ---------------------------------------------------------------------------
+# quantiser
+# ---------------------------------------------------------------------------
+
+def _check_quantiser(mod):
+    # zero vector: scale 0, zero codes
+    codes, scale = mod.quantize_k(np.zeros(64, np.float16))
+    assert scale == 0 and not codes.any()
+    # a grid the scale divides exactly: amax = 127 / 16 gives scale 1 / 16
+    vals = np.zeros(64)
+    vals[:6] = [127, -64, 1, 0, -127, 3]
+    codes, scale = mod.quantize_k(_fp16(vals / 16))
+    assert scale == np.float32(1 / 16)
+    assert codes[:6].tolist() == [127, -64, 1, 0, -127, 3] and not codes[6:].any()
+    # ties: with amax = 127 the scale is exactly 1 and halves round to even
+    vals = np.zeros(64)
+    vals[:7] = [127, 2.5, 3.5, -2.5, 0.5, 1.5, -0.5]
+    codes, scale = mod.quantize_k(_fp16(vals))
+    assert scale == 1.0
+    assert codes[:7].tolist() == [127, 2, 4, -2, 0, 2, 0]
+    # error bound on random vectors
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        k = _fp16(rng.standard_normal(128) * rng.choice([1e-3, 1.0, 30.0]))
+        codes, scale = mod.quantize_k(k)
+        kf = k.astype(np.float64)
+        amax = np.abs(kf).max()
+        assert scale == np.float32(np.float32(amax) / np.float32(127))
+        assert codes.dtype == np.int8 and np.abs(codes.astype(int)).max() == 127
+        assert np.abs(codes.astype(int)).max() <= 127
+        # half a step, plus the fp32 rounding of k / scale (|k / scale| <= 127, so <= 127 * 2^-24 steps)
+        err = np.abs(kf - codes.astype(np.float64) * float(scale))
+        assert err.max() <= float(scale) * (0.5 + 127 * 2.0 ** -24)
+
+
+def test_quantiser_pins():
+    _check_quantiser(quant_k8)
+
+
+# ---------------------------------------------------------------------------
+# storage format
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_format_is_a_bijection(D):
+    u, d = np.meshgrid(np.arange(16), np.arange(D), indexing="ij")
+    offs = oracle.k8_code_offset(u, d, D).ravel()
+    assert sorted(offs.tolist()) == list(range(16 * D))
+    so = oracle.k8_scale_offset(np.arange(16), D)
+    assert so.tolist() == list(range(16 * D, 16 * D + 64, 4))
+    assert oracle.k8_subblock_bytes(D) == 16 * D + 64
+    assert oracle.k8_pool_bytes(10, 8, 32, D) == 10 * 8 * 2 * (16 * D + 64)
+
+
+def _paged_fp16_pool(rng, N, Hkv, P, D):
+    return _fp16(rng.standard_normal((N, Hkv, P, D)))
+
+
+@pytest.mark.parametrize("P,D", [(16, 64), (32, 128)])
+def test_write_then_gather_returns_dequantised_tokens(P, D):
+    rng = np.random.default_rng(P + D)
+    N, Hkv = 5, 2
+    kp = _paged_fp16_pool(rng, N, Hkv, P, D)
+    pool8 = oracle.quantize_k_pool(kp)
+    assert pool8.shape == (N, Hkv, P // 16, 16 * D + 64)
+    # one sequence over pages in a permuted order
+    bt = rng.permutation(N).astype(np.int32)
+    L = N * P - 3
+    for h in range(Hkv):
+        got = oracle.k8_gather_sequence(pool8, bt, L, h, P, D)
+        for t in range(L):
+            page, off = int(bt[t // P]), t % P
+            codes, scale = oracle.quantize_k(oracle.read_token(kp, page, h, off, "k"))
+            assert np.array_equal(got[t], codes.astype(np.float64) * float(scale))
+            c2, s2 = oracle.k8_read_token(pool8, page, h, off, D)
+            assert np.array_equal(c2, codes) and s2 == scale
+
+
+# ---------------------------------------------------------------------------
+# decode over int8 keys
+# ---------------------------------------------------------------------------
+
+def _textbook(q, K, V, scale):
+    s = [scale * sum(a * b for a, b in zip(q, k)) for k in K]
+    m = max(s)
+    p = [math.exp(x - m) for x in s]
+    z = sum(p)
+    return [sum(p[t] * V[t][d] for t in range(len(K))) / z for d in range(len(q))]
+
+
+def _check_decode(mod, seed=7):
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, D, P = 2, 4, 2, 64, 16
+    N = 7
+    lens = np.array([1, 57], np.int32)
+    kp = _paged_fp16_pool(rng, N, Hkv, P, D)
+    vp = _paged_fp16_pool(rng, N, Hkv, P, D)
+    q = _fp16(rng.standard_normal((B, Hq, D)))
+    perm = rng.permutation(N).astype(np.int32)
+    bt = np.stack([perm[:4], perm[3:7]]).astype(np.int32)
+    pool8 = oracle.quantize_k_pool(kp)
+    got = mod.decode_attention_k8(q, pool8, vp, bt, lens, 0.125, P)
+    g = Hq // Hkv
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // g
+            K, V = [], []
+            for t in range(int(lens[b])):
+                page, off = int(bt[b, t // P]), t % P
+                codes, scale = oracle.quantize_k(oracle.read_token(kp, page, kvh, off, "k"))
+                K.append((codes.astype(np.float64) * float(scale)).tolist())
+                V.append(oracle.read_token(vp, page, kvh, off, "v").astype(np.float64).tolist())
+            ref = _textbook(q[b, h].astype(np.float64).tolist(), K, V, float(np.float32(0.125)))
+            np.testing.assert_allclose(got[b, h], ref, rtol=0, atol=1e-12)
+    # with keys that quantise exactly (a grid of the scale) the int8 decode equals fp16 decode
+    grid = np.zeros_like(kp)
+    for page in range(N):
+        for h in range(Hkv):
+            for t in range(P):
+                vec = rng.integers(-127, 128, size=D) / 64
+                vec[0] = 127 / 64                            # every token's amax is 127/64: scale 1/64
+                oracle.write_token(grid, page, h, t, _fp16(vec), "k")
+    exact = mod.decode_attention_k8(q, oracle.quantize_k_pool(grid), vp, bt, lens, 0.125, P)
+    np.testing.assert_allclose(exact, oracle.decode_attention(q, grid, vp, bt, lens, 0.125, P), rtol=0, atol=1e-12)
+
+
+def test_decode_k8_brute_force_and_exact_grid():
+    _check_decode(quant_k8)
+
+
+def test_append_k8_touches_one_token_per_head():
+    rng = np.random.default_rng(11)
+    N, Hkv, P, D, B = 6, 2, 16, 128, 3
+    kp = _paged_fp16_pool(rng, N, Hkv, P, D)
+    vp = _paged_fp16_pool(rng, N, Hkv, P, D)
+    pool8 = oracle.quantize_k_pool(kp)
+    bt = np.array([[0, 1], [2, 3], [4, 5]], np.int32)
+    pos = np.array([0, 17, 31], np.int32)
+    kn = _fp16(rng.standard_normal((B, Hkv, D)))
+    vn = _fp16(rng.standard_normal((B, Hkv, D)))
+    k2, v2 = oracle.kv_append_k8(pool8, vp, kn, vn, bt, pos, P)
+    assert np.count_nonzero(k2 != pool8) <= B * Hkv * (D + 4)
+    assert np.count_nonzero(v2.view(np.uint16) != vp.view(np.uint16)) <= B * Hkv * D
+    for b in range(B):
+        page, off = int(bt[b, pos[b] // P]), int(pos[b] % P)
+        for h in range(Hkv):
+            codes, scale = oracle.k8_read_token(k2, page, h, off, D)
+            c0, s0 = oracle.quantize_k(kn[b, h])
+            assert np.array_equal(codes, c0) and scale == s0
+            assert np.array_equal(oracle.read_token(v2, page, h, off, "v"), vn[b, h])
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes
+# ---------------------------------------------------------------------------
+
+K8_MUTANTS = [
+    ("codes = np.rint(k / scale)", "codes = np.trunc(k / scale)"),                    # truncation
+    ("scale = np.float32(amax / np.float32(127.0))", "scale = np.float32(amax / np.float32(128.0))"),
+    ("return codes.view(np.int8).astype(np.float64)", "return codes.astype(np.float64)"),   # unsigned codes
+    ("* scales.astype(np.float64)[:, None]", "* scales.astype(np.float64)[::-1, None]"),   # scales of other tokens
+    ("within = t % page_size", "within = (t + 1) % page_size"),                       # slot off by one
+    ("p = np.exp(s - s.max())", "p = np.exp(s.max() - s)"),                          # sign
+    ("s = s64 * (keys @ q[b, h].astype(np.float64))", "s = keys @ q[b, h].astype(np.float64)"),  # dropped scale
+]
+
+
+def _k8_pins_pass(mod):
+    try:
+        with np.errstate(all="ignore"):
+            _check_quantiser(mod)
+            _check_decode(mod)
+        return True
+    except Exception:
+        return False
+
+
+@pytest.mark.parametrize("old,new", K8_MUTANTS)
+def test_planted_mistake_is_caught(old, new):
+    src = open(quant_k8.__file__).read()
+    assert src.count(old) == 1, old
+    mutant = types.ModuleType("oracle.quant_k8_mutant")
+    mutant.__dict__["__file__"] = "<mutant>"
+    mutant.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), mutant.__dict__)
+    assert _k8_pins_pass(quant_k8)
+    assert not _k8_pins_pass(mutant), "planted mistake not detected: %r -> %r" % (old, new)
