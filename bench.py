@@ -59,6 +59,9 @@ def parse_args():
                          "Python (slower on this stack: graph launch costs more than it saves)")
     ap.add_argument("--patch-max", type=int, default=1024,
                     help="table changes per step applied in place by pkv_block_table_patch; more -> full upload")
+    ap.add_argument("--int8-keys", action="store_true",
+                    help="keys as int8 codes with a per-token fp32 scale, values fp16 (pkv_kv_append_k8 + "
+                         "pkv_paged_decode_attention_k8)")
     ap.add_argument("--no-stream-peak", action="store_true",
                     help="skip the streaming-read ceiling measurement (pkv_probe_stream_read)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -93,15 +96,17 @@ def cpu_model():
     return platform.processor() or None
 
 
-def algorithmic_bytes(lens, B, Hq, Hkv, D, P, shared_tokens):
+def algorithmic_bytes(lens, B, Hq, Hkv, D, P, shared_tokens, k_bytes=None):
     """Unique bytes one layer-step must move: every attended K/V byte once
     (shared-prefix tokens once for the whole batch), q in, out, new K/V in and
-    written, the block-table entries and lengths."""
+    written, the block-table entries and lengths. ``k_bytes``: stored bytes of
+    one token's key per KV head (2 D for fp16, D + 4 for int8 codes + scale)."""
+    kb = 2 * D if k_bytes is None else k_bytes
     lens = np.asarray(lens, dtype=np.int64)
     kv_tokens = int(lens.sum()) - shared_tokens * (len(lens) - 1)
-    kv = kv_tokens * Hkv * D * 2 * 2
+    kv = kv_tokens * Hkv * (kb + 2 * D)
     q_out = 2 * B * Hq * D * 2
-    new_kv = 2 * 2 * B * Hkv * D * 2          # read k_new/v_new, write them to the pool
+    new_kv = B * Hkv * (2 * 2 * D + kb + 2 * D)   # read k_new/v_new (fp16), write them to the pools
     table = int(sum(-(-int(n) // P) for n in lens)) * 4 + B * 4
     return kv + q_out + new_kv + table, kv
 
@@ -223,7 +228,8 @@ def main():
     part = w.partition_tokens if args.partition is None else args.partition
     R = args.layers
     total_steps = args.warmup + args.steps
-    fused = not args.separate_append
+    k8 = args.int8_keys
+    fused = not args.separate_append and not k8       # the int8-key path appends with its own kernel
     prefix_tokens = 0 if args.no_shared_prefix else w.shared_prefix_pages * w.P
     if w.steps == 0:
         raise SystemExit("workload %d has no append; pick 2-5" % args.workload)
@@ -256,20 +262,34 @@ def main():
     gen = torch.Generator(device=dev)
     gen.manual_seed(1000 + args.workload)
     k_pools, v_pools = [], []
+
+    def random_k8_pool():
+        # codes uniform in [-127, 127], positive fp32 scales: timing does not depend on the values
+        codes = torch.randint(-127, 128, (N, Hkv, P // 16, 16 * D), dtype=torch.int8, device=dev, generator=gen)
+        scales = torch.randn((N, Hkv, P // 16, 16), device=dev, generator=gen).abs_().mul_(0.05).add_(0.005)
+        return torch.cat([codes.view(torch.uint8), scales.view(torch.uint8)], dim=-1).contiguous()
+
     for layer in range(R):
-        kp = torch.empty((N, Hkv, P, D), dtype=torch.float16, device=dev)
         vp = torch.empty((N, Hkv, P, D), dtype=torch.float16, device=dev)
+        if k8:
+            kp = random_k8_pool()
+        else:
+            kp = torch.empty((N, Hkv, P, D), dtype=torch.float16, device=dev)
         if layer == 0:
-            kp[:w.N].copy_(put(w.k_pool))
+            if not k8:
+                kp[:w.N].copy_(put(w.k_pool))
             vp[:w.N].copy_(put(w.v_pool))
             if N > w.N:
-                kp[w.N:].normal_(generator=gen)
+                if not k8:
+                    kp[w.N:].normal_(generator=gen)
                 vp[w.N:].normal_(generator=gen)
         else:
-            kp.normal_(generator=gen)
+            if not k8:
+                kp.normal_(generator=gen)
             vp.normal_(generator=gen)
         k_pools.append(kp)
         v_pools.append(vp)
+    k8_layer0 = k_pools[0].cpu().numpy() if k8 else None
     q = put(w.q)
     knew = torch.empty((total_steps, B, Hkv, D), dtype=torch.float16, device=dev)
     vnew = torch.empty_like(knew)
@@ -291,7 +311,11 @@ def main():
     scale = w.scale
 
     def layer_call(layer, lens, pos, kn, vn, s):
-        if prefix_tokens:
+        if k8:
+            pkv.kv_append_k8(kn, vn, k_pools[layer], v_pools[layer], bt_dev, pos, stream=s)
+            pkv.paged_decode_attention_k8(q, k_pools[layer], v_pools[layer], bt_dev, lens, max_context, scale, part,
+                                          prefix_tokens, out=out, workspace=workspace, stream=s)
+        elif prefix_tokens:
             if not fused:
                 raise SystemExit("the shared-prefix bench path runs with the fused append")
             pkv.paged_decode_attention_shared_prefix(
@@ -349,14 +373,21 @@ def main():
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     sample = np.linspace(0, B - 1, min(B, args.check_sequences)).astype(int)
-    kp0, vp0 = oracle.kv_append(w.k_pool, w.v_pool, w.k_new[0], w.v_new[0], w.block_table, w.pos(0), P)
-    ref = oracle.decode_attention(w.q[sample], kp0, vp0, w.block_table[sample], w.lens(0)[sample], scale, P)
+    if k8:
+        kp0, vp0 = oracle.kv_append_k8(k8_layer0[:w.N], w.v_pool, w.k_new[0], w.v_new[0], w.block_table, w.pos(0), P)
+        ref = oracle.decode_attention_k8(w.q[sample], kp0, vp0, w.block_table[sample], w.lens(0)[sample], scale, P)
+    else:
+        kp0, vp0 = oracle.kv_append(w.k_pool, w.v_pool, w.k_new[0], w.v_new[0], w.block_table, w.pos(0), P)
+        ref = oracle.decode_attention(w.q[sample], kp0, vp0, w.block_table[sample], w.lens(0)[sample], scale, P)
     max_err = float(np.abs(got[sample] - ref).max())
     log("parity (layer 0, step 0, %d sequences): max_abs_err=%.3e" % (len(sample), max_err))
     if not max_err <= 4e-3:
         raise SystemExit("parity check failed: %.3e" % max_err)
     # the check ran step 0 on layer 0 already; restore its pools so every layer starts alike
-    k_pools[0][:w.N].copy_(put(w.k_pool))
+    if k8:
+        k_pools[0].copy_(put(k8_layer0))
+    else:
+        k_pools[0][:w.N].copy_(put(w.k_pool))
     v_pools[0][:w.N].copy_(put(w.v_pool))
 
     if args.copy_calibration_mib:
@@ -446,14 +477,15 @@ def main():
     ms_per_step = total_ms / args.steps
     ms_per_layer = ms_per_step / R
 
-    config_key = "%s:P%d:part%d:%s:%s" % (w.name, P, part, "fused" if fused else "separate",
-                                         "prefix" if prefix_tokens else "noprefix")
+    config_key = "%s:P%d:part%d:%s:%s%s" % (w.name, P, part, "fused" if fused else "separate",
+                                           "prefix" if prefix_tokens else "noprefix", ":k8" if k8 else "")
     # algorithmic bytes of the timed steps (lengths grow by one per step)
     bytes_steps = []
     kv_steps = []
     for i in range(args.steps):
         step = args.warmup + i
-        tot, kv = algorithmic_bytes(w.context + step + 1, B, Hq, Hkv, D, P, prefix_pages * P)
+        tot, kv = algorithmic_bytes(w.context + step + 1, B, Hq, Hkv, D, P, prefix_pages * P,
+                                    k_bytes=(D + 4) if k8 else None)
         bytes_steps.append(tot)
         kv_steps.append(kv)
     bytes_per_call = float(np.mean(bytes_steps))
@@ -478,7 +510,7 @@ def main():
         "config": {
             "workload": w.name,
             "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": P,
-            "kv_dtype": "f16", "accumulate": "f32",
+            "kv_dtype": "k int8 + fp32 scale per token and head, v f16" if k8 else "f16", "accumulate": "f32",
             "mean_context": float(np.mean(w.context + args.warmup + 1 + (args.steps - 1) / 2)),
             "shared_prefix_tokens": prefix_pages * P,
             "partition_tokens": part,
@@ -499,8 +531,9 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged decode call (%spartition kernel%s + log-sum-exp reduce)" % (
-                "shared-prefix + " if prefix_tokens else "", " with fused append" if fused else ""),
+            "kernel": "paged decode call (%s%spartition kernel%s + log-sum-exp reduce)" % (
+                "int8-key append + int8-key " if k8 else "", "shared-prefix + " if prefix_tokens else "",
+                " with fused append" if fused else ""),
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

@@ -248,6 +248,57 @@ int pkv_paged_decode_attention_shared_prefix(void* out, const void* q, const voi
                                              float scale, int32_t partition_tokens, int32_t prefix_tokens,
                                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Key-only int8 pages                                                       */
+/* ------------------------------------------------------------------------ */
+/*
+ * Keys quantised to int8, values kept fp16: quantising the KV cache halves
+ * its memory but costs attention precision on long sequences, so the pages
+ * advise quantising the keys only (dpshk §4.4), block-wise (pgsm §4.2). Here a
+ * block is one token's D keys of one KV head, with its own fp32 scale: appends
+ * never rewrite older tokens (pgsm §4.3), so a page-wide scale would have to
+ * clip later tokens. Per token and KV head: scale = amax / 127 and
+ * code = rint(k / scale) (IEEE fp32, half to even; amax == 0 gives scale 0,
+ * codes 0); the dequantised key is code * scale.
+ *
+ * int8-key pool: bytes [N][Hkv][P / 16][16 * D + 64]. A 16-token sub-block holds
+ * the 16 x D codes, then the 16 fp32 scales (token u at byte 16 * D + 4 u).
+ * The code of token u, dim d is at byte
+ *   ((d / 64) * 64 + ((d / 8) % 4) * 16 + u) * 16 + ((d / 32) % 2) * 8 + d % 8,
+ * so each 16-byte run holds one lane's matrix-core operand bytes for 64 dims.
+ * The V pool is the fp16 pool described above. K bytes per token and head:
+ * D + 4 instead of 2 D.
+ * Supported: D in {64, 128}, P in {16, 32, 64, 128}, Hq / Hkv in {1..16}.
+ */
+
+/* pkv_k8_pool_bytes -- size of an int8-key pool. Errors: PKV_ERR_INVALID_ARG
+ * (null bytes, N < 0, Hkv <= 0), PKV_ERR_UNSUPPORTED (D or P). */
+int pkv_k8_pool_bytes(int32_t N, int32_t Hkv, int32_t P, int32_t D, size_t* bytes);
+
+/*
+ * pkv_kv_append_k8 -- as pkv_kv_append, with the key quantised into the
+ * int8-key pool (codes and scale of the one token written) and the value into
+ * the fp16 V pool. A position outside [0, max_pages * P) or a page id outside
+ * [0, N) skips that sequence. Errors as pkv_kv_append.
+ */
+int pkv_kv_append_k8(const void* k_new, const void* v_new, void* k_pool8, void* v_pool, const int32_t* block_table,
+                     int32_t max_pages, const int32_t* pos, int32_t B, int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                     void* stream);
+
+/*
+ * pkv_paged_decode_attention_k8 -- pkv_paged_decode_attention (prefix_tokens
+ * == 0) or pkv_paged_decode_attention_shared_prefix without append
+ * (prefix_tokens > 0) over int8 keys: s_t = scale * scale_t * <q, code_t>,
+ * the rest as for fp16 keys (fp32 accumulation, fp16 output). Workspace:
+ * pkv_decode_workspace_bytes / pkv_decode_workspace_bytes_shared_prefix.
+ * Errors as those calls.
+ */
+int pkv_paged_decode_attention_k8(void* out, const void* q, const void* k_pool8, const void* v_pool,
+                                  const int32_t* block_table, int32_t max_pages, const int32_t* lens, int32_t B,
+                                  int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N, int32_t max_context,
+                                  float scale, int32_t partition_tokens, int32_t prefix_tokens, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /*
  * pkv_probe_stream_read -- measurement aid (not part of decode): read
  * n_tiles 4 KiB tiles of `base` in the order tile_order gives, with the decode

@@ -18,9 +18,12 @@ from .binding import (  # noqa: F401
     append_paged_decode_attention,
     block_table_patch,
     decode_workspace_bytes,
+    k8_pool_bytes,
     kv_append,
+    kv_append_k8,
     lib,
     paged_decode_attention,
+    paged_decode_attention_k8,
     paged_decode_attention_shared_prefix,
     probe_stream_read,
     status_string,

@@ -35,6 +35,11 @@ _SIGNATURES = {
     "pkv_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_block_table_patch": (ctypes.c_int, [_vp, _i32, _i32, _ip, _ip, _ip, _i32, _vp]),
     "pkv_probe_stream_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _i32, _i32, _vp, _vp]),
+    "pkv_k8_pool_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
+    "pkv_kv_append_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_paged_decode_attention_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
+                                                     _i32, _i32, ctypes.c_float, _i32, _i32, _vp, ctypes.c_size_t,
+                                                     _vp]),
     "pkv_decode_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     "pkv_paged_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                                   _i32, _i32, ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]),
@@ -154,6 +159,48 @@ def kv_append(k_new, v_new, k_pool, v_pool, block_table, pos, stream=None):
                              _dev_ptr(block_table, torch.int32, "block_table"), max_pages,
                              _dev_ptr(pos, torch.int32, "pos"), B, Hkv, D, P, N, _stream(stream))
     _check(rc, "pkv_kv_append")
+
+
+def k8_pool_bytes(N, Hkv, P, D):
+    """pkv_k8_pool_bytes: bytes of an int8-key pool [N][Hkv][P/16][16 D + 64]."""
+    out = ctypes.c_size_t(0)
+    _check(lib().pkv_k8_pool_bytes(N, Hkv, P, D, ctypes.byref(out)), "pkv_k8_pool_bytes")
+    return out.value
+
+
+def _k8_shape(k_pool8, v_pool):
+    N, Hkv, P, D = v_pool.shape
+    if k_pool8.dtype != torch.uint8 or tuple(k_pool8.shape) != (N, Hkv, P // 16, 16 * D + 64):
+        raise ValueError("k_pool8 must be uint8 [N][Hkv][P/16][16 D + 64] matching v_pool [N][Hkv][P][D]")
+    return N, Hkv, P, D
+
+
+def kv_append_k8(k_new, v_new, k_pool8, v_pool, block_table, pos, stream=None):
+    """pkv_kv_append_k8: quantise k_new into the int8-key pool, write v_new into the fp16 V pool."""
+    N, Hkv, P, D = _k8_shape(k_pool8, v_pool)
+    B, max_pages = block_table.shape
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D) or tuple(pos.shape) != (B,):
+        raise ValueError("shape mismatch")
+    _check(lib().pkv_kv_append_k8(_dev_ptr(k_new, torch.float16, "k_new"), _dev_ptr(v_new, torch.float16, "v_new"),
+                                  _dev_ptr(k_pool8, torch.uint8, "k_pool8"), _dev_ptr(v_pool, torch.float16, "v_pool"),
+                                  _dev_ptr(block_table, torch.int32, "block_table"), max_pages,
+                                  _dev_ptr(pos, torch.int32, "pos"), B, Hkv, D, P, N, _stream(stream)),
+           "pkv_kv_append_k8")
+
+
+def paged_decode_attention_k8(q, k_pool8, v_pool, block_table, lens, max_context, scale, partition_tokens=0,
+                              prefix_tokens=0, out=None, workspace=None, stream=None):
+    """pkv_paged_decode_attention_k8: decode over int8 keys and fp16 values; returns ``out``."""
+    N, Hkv, P, D = _k8_shape(k_pool8, v_pool)
+    out, (_, _, _, _, B, Hq, max_pages), ws_ptr, ws_len = _decode_args(
+        out, q, v_pool, v_pool, block_table, lens, max_context, partition_tokens, workspace, prefix_tokens)
+    rc = lib().pkv_paged_decode_attention_k8(
+        _dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"), _dev_ptr(k_pool8, torch.uint8, "k_pool8"),
+        _dev_ptr(v_pool, torch.float16, "v_pool"), _dev_ptr(block_table, torch.int32, "block_table"), max_pages,
+        _dev_ptr(lens, torch.int32, "lens"), B, Hq, Hkv, D, P, N, int(max_context), float(scale),
+        int(partition_tokens), int(prefix_tokens), ws_ptr, ws_len, _stream(stream))
+    _check(rc, "pkv_paged_decode_attention_k8")
+    return out
 
 
 def decode_workspace_bytes(B, Hq, D, max_context, partition_tokens, prefix_tokens=0):

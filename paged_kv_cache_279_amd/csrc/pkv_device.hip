@@ -100,6 +100,7 @@ struct DecodeParams {
   half_t* out;               // [B][Hq][D]
   const half_t* q;           // [B][Hq][D]
   const half_t* k_pool;      // [N][Hkv][P*D] tiles
+  const uint8_t* k8;         // int8-key pool: [N][Hkv][P/16][16 D + 64] bytes (codes, then fp32 scales)
   const half_t* v_pool;
   half_t* k_pool_w;          // same pools, written by the fused append
   half_t* v_pool_w;
@@ -136,6 +137,24 @@ __device__ __forceinline__ half4_t lo4(const uint4& v) {
 
 __device__ __forceinline__ half4_t hi4(const uint4& v) {
   return __builtin_bit_cast(half4_t, make_uint2(v.z, v.w));
+}
+
+// Eight signed int8 codes (bytes of a, then b) as fp16, exactly: byte c
+// becomes the half 0x6400 | (c + 128) = 1024 + c + 128, then 1152 is
+// subtracted (every integer below 2048 is exact in fp16).
+__device__ __forceinline__ half2_t bytes_to_h2(uint32_t x, uint32_t sel) {
+  const half2_t biased = __builtin_bit_cast(half2_t, __builtin_amdgcn_perm(0x64646464u, x, sel));
+  return biased - half2_t{(half_t)1152.0f, (half_t)1152.0f};
+}
+
+__device__ __forceinline__ half8_t codes_to_h8(uint32_t a, uint32_t b) {
+  a ^= 0x80808080u;
+  b ^= 0x80808080u;
+  const half2_t h0 = bytes_to_h2(a, 0x04010400u);   // bytes 0, 1
+  const half2_t h1 = bytes_to_h2(a, 0x04030402u);   // bytes 2, 3
+  const half2_t h2 = bytes_to_h2(b, 0x04010400u);
+  const half2_t h3 = bytes_to_h2(b, 0x04030402u);
+  return half8_t{h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
 }
 
 // Offsets (halves) inside a 16-token sub-block of D dims; see the layout note.
@@ -253,6 +272,46 @@ __global__ __launch_bounds__(kPatchMax) void table_patch_kernel(int32_t* __restr
   if (i < patch.n) bt[(int64_t)patch.row[i] * max_pages + patch.col[i]] = patch.page[i];
 }
 
+// One workgroup of D threads per (b, kvh): quantises the new token's key to
+// int8 with its own fp32 scale (scale = amax / 127, code = rint(k / scale),
+// IEEE fp32, half to even; amax = 0 gives scale 0 and zero codes) and writes
+// codes and scale into the int8-key sub-block, the value into the fp16 V tile.
+template <int D>
+__global__ __launch_bounds__(D) void kv_append_k8_kernel(const half_t* __restrict__ k_new,
+                                                         const half_t* __restrict__ v_new, uint8_t* __restrict__ k8,
+                                                         half_t* __restrict__ v_pool, const int32_t* __restrict__ bt,
+                                                         int32_t max_pages, const int32_t* __restrict__ pos,
+                                                         int32_t Hkv, int32_t p_shift, int32_t N) {
+  __shared__ float sm_max[D / kWave];
+  const int32_t kvh = blockIdx.x % Hkv;
+  const int32_t b = blockIdx.x / Hkv;
+  const int d = threadIdx.x;
+  const int32_t t = pos[b];
+  if (t < 0 || (t >> p_shift) >= max_pages) return;
+  const int32_t page = bt[(int64_t)b * max_pages + (t >> p_shift)];
+  if (page < 0 || page >= N) return;
+  const int64_t src = ((int64_t)b * Hkv + kvh) * D;
+  const float kv = (float)k_new[src + d];
+  float m = fabsf(kv);
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((d & (kWave - 1)) == 0) sm_max[d / kWave] = m;
+  __syncthreads();
+  float amax = sm_max[0];
+#pragma unroll
+  for (int w = 1; w < D / kWave; ++w) amax = fmaxf(amax, sm_max[w]);
+  const float qs = amax / 127.0f;
+  int32_t code = 0;
+  if (amax > 0.f) code = max(-127, min(127, (int32_t)rintf(kv / qs)));
+  const int32_t u = t & 15;
+  const int64_t sub = ((((int64_t)page * Hkv + kvh) << (p_shift - 4)) + ((t & ((1 << p_shift) - 1)) >> 4)) *
+                      (kBlk * D + 64);
+  const int32_t cofs = ((d / 64) * 64 + ((d / 8) % 4) * 16 + u) * 16 + ((d / 32) % 2) * 8 + d % 8;
+  k8[sub + cofs] = (uint8_t)(int8_t)code;
+  if (d == 0) *reinterpret_cast<float*>(k8 + sub + kBlk * D + 4 * u) = amax > 0.f ? qs : 0.f;
+  const int64_t vsub = ((((int64_t)page * Hkv + kvh) * D) << p_shift) + (int64_t)((t & ((1 << p_shift) - 1)) >> 4) * (kBlk * D);
+  v_pool[vsub + v_sub_off<D>(u, d)] = v_new[src + d];
+}
+
 // -------------------------------------------------------------------------
 // decode: partition kernel
 // -------------------------------------------------------------------------
@@ -297,12 +356,17 @@ __device__ __forceinline__ void set_priority(int32_t remaining, int32_t quota) {
 // quota > 0: the range is part of a workgroup share of quota blocks with
 // `after` blocks following it; the wave's priority follows what is left.
 //
+// kK8: keys come from the int8 pool: per block the lane loads its 8 codes per
+// 32 dims (16 bytes per 64 dims) and the fp32 scales of tokens 4 quad .. + 3;
+// the codes widen exactly to fp16 for the score MFMA and each score is then
+// multiplied by its token's scale (s_t = scale_t * <codes_t, q>).
+//
 // kAppend: the new token nt is taken from k_new / v_new instead of the pool:
 // the wave that streams its block loads the token's operand slices with its
 // other loads, patches them into the block's registers before use, and writes
 // them to the pool from there. No other wave reads that row, so the write
 // needs no ordering against the loads.
-template <int D, int32_t kPolicy, bool kAppend>
+template <int D, int32_t kPolicy, bool kAppend, bool kK8>
 __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32_t* bt_row, int32_t kvh,
                                               int32_t start, int32_t end, int32_t first, int32_t stride,
                                               int32_t quota, int32_t after, const NewToken& nt,
@@ -313,6 +377,8 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
   const int col = lane & 15;
   const int32_t pmask = (1 << p.p_shift) - 1;
   const int64_t tile_elems = (int64_t)D << p.p_shift;       // one (page, kvh) tile
+  constexpr int32_t kSub8 = kBlk * D + 64;                   // int8-key sub-block bytes
+  static_assert(!kK8 || (D % 64 == 0 && !kAppend), "int8 keys: D % 64 == 0, no fused append");
   const int32_t nblocks = (end - start + kBlk - 1) / kBlk;
   const float c = p.scale_log2;
 
@@ -369,13 +435,25 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
       if (live && blk == nt.blk && pid >= 0) new_off = off;
     }
     const int32_t bytes = live ? kBlk * D * 2 : 0;
-    const __amdgpu_buffer_rsrc_t krs =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_pool + off), (short)0, bytes, kBufferFlags);
+    if constexpr (kK8) {
+      // codes: 16 bytes per lane per 64 dims; then the 16 bytes of scales of tokens 4 quad .. + 3
+      const int64_t sub = (((int64_t)page * p.Hkv + kvh) << (p.p_shift - 4)) + ((t0 & pmask) >> 4);
+      const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+          (void*)(p.k8 + sub * kSub8), (short)0, live ? kSub8 : 0, kBufferFlags);
+#pragma unroll
+      for (int j = 0; j < D / 64; ++j)
+        kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, lane * 16 + j * 1024, 0, kPolicy));
+      kr[D / 64] =
+          __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, kBlk * D + quad * 16, 0, kPolicy));
+    } else {
+      const __amdgpu_buffer_rsrc_t krs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_pool + off), (short)0, bytes, kBufferFlags);
+#pragma unroll
+      for (int j = 0; j < KL; ++j)
+        kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, lane * 16 + j * 1024, 0, kPolicy));
+    }
     const __amdgpu_buffer_rsrc_t vrs =
         __builtin_amdgcn_make_buffer_rsrc((void*)(p.v_pool + off), (short)0, bytes, kBufferFlags);
-#pragma unroll
-    for (int j = 0; j < KL; ++j)
-      kr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, lane * 16 + j * 1024, 0, kPolicy));
 #pragma unroll
     for (int j = 0; j < KL; ++j)
       vr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, lane * 16 + j * 1024, 0, kPolicy));
@@ -427,8 +505,22 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     }
     // scores of tokens 4 quad + i for query row col
     float4_t s = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (kK8) {
 #pragma unroll
-    for (int j = 0; j < KL; ++j) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kr[j]), qb[j], s, 0, 0, 0);
+      for (int j = 0; j < KL; ++j) {
+        const uint4 w = kr[j / 2];
+        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(codes_to_h8((j & 1) ? w.z : w.x, (j & 1) ? w.w : w.y), qb[j], s,
+                                                   0, 0, 0);
+      }
+      const uint4 sc = kr[D / 64];
+      s[0] *= __builtin_bit_cast(float, sc.x);
+      s[1] *= __builtin_bit_cast(float, sc.y);
+      s[2] *= __builtin_bit_cast(float, sc.z);
+      s[3] *= __builtin_bit_cast(float, sc.w);
+    } else {
+#pragma unroll
+      for (int j = 0; j < KL; ++j) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kr[j]), qb[j], s, 0, 0, 0);
+    }
     const int32_t rem = end - t0;      // valid tokens in this block (>= 1)
     if (rem < kBlk) {
       // tail: mask scores of absent tokens and zero their values (never 0 * NaN)
@@ -532,7 +624,7 @@ struct KernelShared {
 // waves merge through LDS and every (column c, dim d) goes to
 // emit(c, d, M, Ls, O): the column's base-2 score max, softmax denominator
 // and unnormalised output. Callers must be workgroup-uniform.
-template <int D, int NC, int32_t kPolicy, bool kAppend, class RowFn, class EmitFn>
+template <int D, int NC, int32_t kPolicy, bool kAppend, bool kK8, class RowFn, class EmitFn>
 __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>& sh, const int32_t* bt_row,
                                           int32_t kvh, int32_t start, int32_t end, int32_t quota, int32_t after,
                                           const NewToken& nt, RowFn qrow, EmitFn emit, int lane, int wave) {
@@ -551,7 +643,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
   }
   WaveState<D> st;
   init_state<D>(st);
-  stream_blocks<D, kPolicy, kAppend>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, nt, qb, st, lane);
+  stream_blocks<D, kPolicy, kAppend, kK8>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, nt, qb, st, lane);
   // per-column denominators of this wave: sum the 4 quads of column col
   st.l_part += __shfl_xor(st.l_part, 16);
   st.l_part += __shfl_xor(st.l_part, 32);
@@ -611,7 +703,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
 // writes slot kvh * (NT + B + 2 Wk) + s + j, private segments numbered after
 // NT + Wk: walking a list in order increases s or j (or both) by one each
 // step, so the slots are distinct; each slot holds 16 columns.
-template <int D, int G, bool SPLIT, bool FUSED>
+template <int D, int G, bool SPLIT, bool FUSED, bool K8>
 __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodeParams p) {
   static_assert(D % 32 == 0 && G >= 1 && G <= 16, "shape");
   const int lane = threadIdx.x & (kWave - 1);
@@ -637,7 +729,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
       const int64_t src = ((int64_t)b * p.Hkv + kvh) * D;
       nt = NewToken{(Lc - 1) >> 4, (Lc - 1) & 15, p.k_new + src, p.v_new + src};
     }
-    run_range<D, G, kKvLoadPolicy, FUSED>(p, sh, bt_row, kvh, 0, Lc, 0, 0, nt, [&](int c) -> int64_t { return head_row0 + c; },
+    run_range<D, G, kKvLoadPolicy, FUSED, K8>(p, sh, bt_row, kvh, 0, Lc, 0, 0, nt, [&](int c) -> int64_t { return head_row0 + c; },
                     [&](int c, int d, float, float Ls, float O) {
                       const float r = Ls > 0.f ? O / Ls : (Ls == 0.f ? 0.f : __builtin_nanf(""));
                       p.out[(head_row0 + c) * D + d] = (half_t)(Ls != Ls ? __builtin_nanf("") : r);
@@ -718,7 +810,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
         };
         const int64_t slot = slot_base + rt;
         // the prefix pages are the same in every row of the table: read row 0
-        run_range<D, 16, kPrefixLoadPolicy, false>(p, smem.tile.prefix, p.bt, kvh, blk0 * kBlk, (blk0 + piece_n) * kBlk,
+        run_range<D, 16, kPrefixLoadPolicy, false, K8>(p, smem.tile.prefix, p.bt, kvh, blk0 * kBlk, (blk0 + piece_n) * kBlk,
                                                    quota, after + g1 - g - piece_n, NewToken{-1, 0, nullptr, nullptr}, qrow,
                                             [&](int c, int d, float M, float Ls, float O) {
                                               const int64_t ps = slot * 16 + c;
@@ -761,7 +853,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
           }
         }
         const int64_t slot = slot_base + p.n_tiles + Wk + b;
-        run_range<D, G, kKvLoadPolicy, FUSED>(p, smem.tile.priv, bt_row, kvh, start, end, quota,
+        run_range<D, G, kKvLoadPolicy, FUSED, K8>(p, smem.tile.priv, bt_row, kvh, start, end, quota,
                                               after + g1 - g - piece_n, nt,
                                        [&](int c) -> int64_t { return c < G ? head_row0 + c : -1; },
                                        [&](int c, int d, float M, float Ls, float O) {
@@ -955,34 +1047,34 @@ int64_t max_slots(int32_t B, int32_t Hq, bool prefix) {
          2 * (static_cast<int64_t>(PKV_FLAT_WORKGROUPS) + Hq);
 }
 
-template <int D, int G, bool SPLIT, bool FUSED>
+template <int D, int G, bool SPLIT, bool FUSED, bool K8>
 hipError_t launch_partition(const DecodeParams& p, hipStream_t stream, int64_t grid) {
-  hipLaunchKernelGGL((decode_partition_kernel<D, G, SPLIT, FUSED>), dim3(static_cast<uint32_t>(grid)),
+  hipLaunchKernelGGL((decode_partition_kernel<D, G, SPLIT, FUSED, K8>), dim3(static_cast<uint32_t>(grid)),
                      dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool SPLIT, bool FUSED>
+template <int D, bool SPLIT, bool FUSED, bool K8>
 hipError_t dispatch_g(int G, const DecodeParams& p, hipStream_t s, int64_t grid) {
   switch (G) {
-    case 1: return launch_partition<D, 1, SPLIT, FUSED>(p, s, grid);
-    case 2: return launch_partition<D, 2, SPLIT, FUSED>(p, s, grid);
-    case 4: return launch_partition<D, 4, SPLIT, FUSED>(p, s, grid);
-    case 8: return launch_partition<D, 8, SPLIT, FUSED>(p, s, grid);
-    default: return launch_partition<D, 16, SPLIT, FUSED>(p, s, grid);
+    case 1: return launch_partition<D, 1, SPLIT, FUSED, K8>(p, s, grid);
+    case 2: return launch_partition<D, 2, SPLIT, FUSED, K8>(p, s, grid);
+    case 4: return launch_partition<D, 4, SPLIT, FUSED, K8>(p, s, grid);
+    case 8: return launch_partition<D, 8, SPLIT, FUSED, K8>(p, s, grid);
+    default: return launch_partition<D, 16, SPLIT, FUSED, K8>(p, s, grid);
   }
 }
 
-template <bool SPLIT, bool FUSED>
+template <bool SPLIT, bool FUSED, bool K8>
 hipError_t dispatch_d(int D, int G, const DecodeParams& p, hipStream_t s, int64_t grid) {
-  return D == 64 ? dispatch_g<64, SPLIT, FUSED>(G, p, s, grid) : dispatch_g<128, SPLIT, FUSED>(G, p, s, grid);
+  return D == 64 ? dispatch_g<64, SPLIT, FUSED, K8>(G, p, s, grid) : dispatch_g<128, SPLIT, FUSED, K8>(G, p, s, grid);
 }
 
 int decode_common(void* out, const void* q, const void* k_new, const void* v_new, const void* k_pool,
                   const void* v_pool, void* k_pool_w, void* v_pool_w, const int32_t* bt, int32_t max_pages,
                   const int32_t* lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
                   int32_t max_context, float scale, int32_t partition_tokens, int32_t prefix_tokens,
-                  void* workspace, size_t workspace_bytes, void* stream, bool fused) {
+                  void* workspace, size_t workspace_bytes, void* stream, bool fused, bool k8 = false) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || N <= 0 || max_pages <= 0 || max_context < 0 ||
       partition_tokens < 0 || prefix_tokens < 0)
     return PKV_ERR_INVALID_ARG;
@@ -1013,7 +1105,8 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   DecodeParams prm{};
   prm.out = static_cast<half_t*>(out);
   prm.q = static_cast<const half_t*>(q);
-  prm.k_pool = static_cast<const half_t*>(k_pool);
+  if (k8) prm.k8 = static_cast<const uint8_t*>(k_pool);
+  else prm.k_pool = static_cast<const half_t*>(k_pool);
   prm.v_pool = static_cast<const half_t*>(v_pool);
   prm.k_pool_w = static_cast<half_t*>(k_pool_w);
   prm.v_pool_w = static_cast<half_t*>(v_pool_w);
@@ -1053,8 +1146,12 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   const int64_t grid = plan.grid;
   hipError_t e = hipSuccess;
   if (grid > 0) {
-    if (plan.split) e = fused ? dispatch_d<true, true>(D, G, prm, s, grid) : dispatch_d<true, false>(D, G, prm, s, grid);
-    else e = fused ? dispatch_d<false, true>(D, G, prm, s, grid) : dispatch_d<false, false>(D, G, prm, s, grid);
+    if (k8) e = plan.split ? dispatch_d<true, false, true>(D, G, prm, s, grid)
+                           : dispatch_d<false, false, true>(D, G, prm, s, grid);
+    else if (plan.split)
+      e = fused ? dispatch_d<true, true, false>(D, G, prm, s, grid) : dispatch_d<true, false, false>(D, G, prm, s, grid);
+    else
+      e = fused ? dispatch_d<false, true, false>(D, G, prm, s, grid) : dispatch_d<false, false, false>(D, G, prm, s, grid);
     if (e != hipSuccess) return PKV_ERR_HIP;
   }
   if (plan.split) {
@@ -1178,6 +1275,55 @@ int pkv_append_paged_decode_attention(void* out, const void* q, const void* k_ne
                                       void* workspace, size_t workspace_bytes, void* stream) {
   return decode_common(out, q, k_new, v_new, k_pool, v_pool, k_pool, v_pool, block_table, max_pages, lens, B, Hq,
                        Hkv, D, P, N, max_context, scale, partition_tokens, 0, workspace, workspace_bytes, stream, true);
+}
+
+int pkv_k8_pool_bytes(int32_t N, int32_t Hkv, int32_t P, int32_t D, size_t* bytes) {
+  if (!bytes || N < 0 || Hkv <= 0) return PKV_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
+  if (log2_page(P) < 0) return PKV_ERR_UNSUPPORTED;
+  *bytes = static_cast<size_t>(N) * Hkv * (P / kBlk) * (kBlk * D + 64);
+  return PKV_OK;
+}
+
+int pkv_kv_append_k8(const void* k_new, const void* v_new, void* k_pool8, void* v_pool, const int32_t* block_table,
+                     int32_t max_pages, const int32_t* pos, int32_t B, int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                     void* stream) {
+  if (B < 0 || Hkv <= 0 || D <= 0 || P <= 0 || N <= 0 || max_pages <= 0) return PKV_ERR_INVALID_ARG;
+  if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
+  const int p_shift = log2_page(P);
+  if (p_shift < 0) return PKV_ERR_UNSUPPORTED;
+  if (B == 0) return PKV_OK;
+  if (!k_new || !v_new || !k_pool8 || !v_pool || !block_table || !pos) return PKV_ERR_INVALID_ARG;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pool8, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_table, 4) || !aligned(pos, 4))
+    return PKV_ERR_INVALID_ARG;
+  const int64_t rows = static_cast<int64_t>(B) * Hkv;
+  if (rows > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
+  const int64_t pool_elems = static_cast<int64_t>(N) * Hkv * P * D;
+  if (pool_elems / N / Hkv / P != D) return PKV_ERR_INVALID_ARG;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const half_t* kn = static_cast<const half_t*>(k_new);
+  const half_t* vn = static_cast<const half_t*>(v_new);
+  uint8_t* k8 = static_cast<uint8_t*>(k_pool8);
+  half_t* vp = static_cast<half_t*>(v_pool);
+  if (D == 64)
+    hipLaunchKernelGGL(kv_append_k8_kernel<64>, dim3(static_cast<uint32_t>(rows)), dim3(64), 0, s, kn, vn, k8, vp,
+                       block_table, max_pages, pos, Hkv, p_shift, N);
+  else
+    hipLaunchKernelGGL(kv_append_k8_kernel<128>, dim3(static_cast<uint32_t>(rows)), dim3(128), 0, s, kn, vn, k8, vp,
+                       block_table, max_pages, pos, Hkv, p_shift, N);
+  return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_paged_decode_attention_k8(void* out, const void* q, const void* k_pool8, const void* v_pool,
+                                  const int32_t* block_table, int32_t max_pages, const int32_t* lens, int32_t B,
+                                  int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N, int32_t max_context,
+                                  float scale, int32_t partition_tokens, int32_t prefix_tokens, void* workspace,
+                                  size_t workspace_bytes, void* stream) {
+  if (prefix_tokens > 0 && (P <= 0 || prefix_tokens % P != 0)) return PKV_ERR_INVALID_ARG;
+  return decode_common(out, q, nullptr, nullptr, k_pool8, v_pool, nullptr, nullptr, block_table, max_pages, lens, B,
+                       Hq, Hkv, D, P, N, max_context, scale, partition_tokens, prefix_tokens, workspace,
+                       workspace_bytes, stream, false, true);
 }
 
 int pkv_paged_decode_attention_shared_prefix(void* out, const void* q, const void* k_new, const void* v_new,
