@@ -229,7 +229,7 @@ def main():
     R = args.layers
     total_steps = args.warmup + args.steps
     k8 = args.int8_keys
-    fused = not args.separate_append and not k8       # the int8-key path appends with its own kernel
+    fused = not args.separate_append
     prefix_tokens = 0 if args.no_shared_prefix else w.shared_prefix_pages * w.P
     if w.steps == 0:
         raise SystemExit("workload %d has no append; pick 2-5" % args.workload)
@@ -312,9 +312,11 @@ def main():
 
     def layer_call(layer, lens, pos, kn, vn, s):
         if k8:
-            pkv.kv_append_k8(kn, vn, k_pools[layer], v_pools[layer], bt_dev, pos, stream=s)
+            if not fused:
+                pkv.kv_append_k8(kn, vn, k_pools[layer], v_pools[layer], bt_dev, pos, stream=s)
             pkv.paged_decode_attention_k8(q, k_pools[layer], v_pools[layer], bt_dev, lens, max_context, scale, part,
-                                          prefix_tokens, out=out, workspace=workspace, stream=s)
+                                          prefix_tokens, k_new=kn if fused else None, v_new=vn if fused else None,
+                                          out=out, workspace=workspace, stream=s)
         elif prefix_tokens:
             if not fused:
                 raise SystemExit("the shared-prefix bench path runs with the fused append")
@@ -532,8 +534,8 @@ def main():
         "roofline": {
             "bound": "hbm",
             "kernel": "paged decode call (%s%spartition kernel%s + log-sum-exp reduce)" % (
-                "int8-key append + int8-key " if k8 else "", "shared-prefix + " if prefix_tokens else "",
-                " with fused append" if fused else ""),
+                ("int8-key " if fused else "int8-key append + int8-key ") if k8 else "",
+                "shared-prefix + " if prefix_tokens else "", " with fused append" if fused else ""),
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

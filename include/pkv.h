@@ -286,18 +286,23 @@ int pkv_kv_append_k8(const void* k_new, const void* v_new, void* k_pool8, void* 
                      void* stream);
 
 /*
- * pkv_paged_decode_attention_k8 -- pkv_paged_decode_attention (prefix_tokens
- * == 0) or pkv_paged_decode_attention_shared_prefix without append
- * (prefix_tokens > 0) over int8 keys: s_t = scale * scale_t * <q, code_t>,
- * the rest as for fp16 keys (fp32 accumulation, fp16 output). Workspace:
- * pkv_decode_workspace_bytes / pkv_decode_workspace_bytes_shared_prefix.
- * Errors as those calls.
+ * pkv_paged_decode_attention_k8 -- pkv_paged_decode_attention_shared_prefix
+ * (prefix_tokens == 0: no shared prefix, and then partition_tokens may be 0)
+ * over int8 keys: s_t = scale * scale_t * <q, code_t>, the rest as for fp16
+ * keys (fp32 accumulation, fp16 output).
+ *   k_new, v_new : both NULL (no append) or both fp16 [B][Hkv][D]: append each
+ *                  sequence's new token at lens[b] - 1 first, in the same
+ *                  launch. The key is quantised exactly as pkv_kv_append_k8
+ *                  does (same codes, same scale, bit for bit), written to the
+ *                  pool and used from registers.
+ * Workspace: pkv_decode_workspace_bytes / pkv_decode_workspace_bytes_shared_prefix.
+ * Errors as pkv_paged_decode_attention_shared_prefix.
  */
-int pkv_paged_decode_attention_k8(void* out, const void* q, const void* k_pool8, const void* v_pool,
-                                  const int32_t* block_table, int32_t max_pages, const int32_t* lens, int32_t B,
-                                  int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N, int32_t max_context,
-                                  float scale, int32_t partition_tokens, int32_t prefix_tokens, void* workspace,
-                                  size_t workspace_bytes, void* stream);
+int pkv_paged_decode_attention_k8(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool8,
+                                  void* v_pool, const int32_t* block_table, int32_t max_pages, const int32_t* lens,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                                  int32_t max_context, float scale, int32_t partition_tokens, int32_t prefix_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pkv_probe_stream_read -- measurement aid (not part of decode): read

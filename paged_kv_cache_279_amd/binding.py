@@ -37,9 +37,9 @@ _SIGNATURES = {
     "pkv_probe_stream_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _i32, _i32, _vp, _vp]),
     "pkv_k8_pool_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     "pkv_kv_append_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
-    "pkv_paged_decode_attention_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
-                                                     _i32, _i32, ctypes.c_float, _i32, _i32, _vp, ctypes.c_size_t,
-                                                     _vp]),
+    "pkv_paged_decode_attention_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
+                                                     _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _i32, _vp,
+                                                     ctypes.c_size_t, _vp]),
     "pkv_decode_workspace_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     "pkv_paged_decode_attention": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32,
                                                   _i32, _i32, ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]),
@@ -189,13 +189,23 @@ def kv_append_k8(k_new, v_new, k_pool8, v_pool, block_table, pos, stream=None):
 
 
 def paged_decode_attention_k8(q, k_pool8, v_pool, block_table, lens, max_context, scale, partition_tokens=0,
-                              prefix_tokens=0, out=None, workspace=None, stream=None):
-    """pkv_paged_decode_attention_k8: decode over int8 keys and fp16 values; returns ``out``."""
+                              prefix_tokens=0, k_new=None, v_new=None, out=None, workspace=None, stream=None):
+    """pkv_paged_decode_attention_k8: decode over int8 keys and fp16 values, with the
+    new token appended (and its key quantised) first when k_new/v_new are given; returns ``out``."""
     N, Hkv, P, D = _k8_shape(k_pool8, v_pool)
     out, (_, _, _, _, B, Hq, max_pages), ws_ptr, ws_len = _decode_args(
         out, q, v_pool, v_pool, block_table, lens, max_context, partition_tokens, workspace, prefix_tokens)
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+            raise ValueError("k_new/v_new must be [B][Hkv][D]")
+        kn, vn = _dev_ptr(k_new, torch.float16, "k_new"), _dev_ptr(v_new, torch.float16, "v_new")
+    else:
+        kn, vn = ctypes.c_void_p(0), ctypes.c_void_p(0)
     rc = lib().pkv_paged_decode_attention_k8(
-        _dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"), _dev_ptr(k_pool8, torch.uint8, "k_pool8"),
+        _dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"), kn, vn,
+        _dev_ptr(k_pool8, torch.uint8, "k_pool8"),
         _dev_ptr(v_pool, torch.float16, "v_pool"), _dev_ptr(block_table, torch.int32, "block_table"), max_pages,
         _dev_ptr(lens, torch.int32, "lens"), B, Hq, Hkv, D, P, N, int(max_context), float(scale),
         int(partition_tokens), int(prefix_tokens), ws_ptr, ws_len, _stream(stream))

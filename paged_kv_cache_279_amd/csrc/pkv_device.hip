@@ -101,6 +101,7 @@ struct DecodeParams {
   const half_t* q;           // [B][Hq][D]
   const half_t* k_pool;      // [N][Hkv][P*D] tiles
   const uint8_t* k8;         // int8-key pool: [N][Hkv][P/16][16 D + 64] bytes (codes, then fp32 scales)
+  uint8_t* k8_w;             // same pool, written by the fused append
   const half_t* v_pool;
   half_t* k_pool_w;          // same pools, written by the fused append
   half_t* v_pool_w;
@@ -378,7 +379,7 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
   const int32_t pmask = (1 << p.p_shift) - 1;
   const int64_t tile_elems = (int64_t)D << p.p_shift;       // one (page, kvh) tile
   constexpr int32_t kSub8 = kBlk * D + 64;                   // int8-key sub-block bytes
-  static_assert(!kK8 || (D % 64 == 0 && !kAppend), "int8 keys: D % 64 == 0, no fused append");
+  static_assert(!kK8 || D % 64 == 0, "int8 keys: D % 64 == 0");
   const int32_t nblocks = (end - start + kBlk - 1) / kBlk;
   const float c = p.scale_log2;
 
@@ -405,7 +406,10 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
   // values of lane (col, quad = u / 4) per 32 dims (dims 32 j + col, + 16)
   uint4 kn[KL];
   uint32_t vn[KL];
+  uint2 kc[KL];                        // int8 keys: the lane's 8 codes per 32 dims of the new token
+  float kq = 0.f;                      // int8 keys: the new token's scale
   int64_t new_off = -1;                // element offset of the token's block (valid page), else -1
+  int64_t new_sub8 = -1;               // int8 keys: byte offset of the token's sub-block
   if constexpr (kAppend) {
     if (nt.blk >= 0) {
 #pragma unroll
@@ -414,6 +418,34 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
         const uint32_t lo = reinterpret_cast<const uint16_t*>(nt.v)[32 * j + col];
         const uint32_t hi = reinterpret_cast<const uint16_t*>(nt.v)[32 * j + 16 + col];
         vn[j] = lo | (hi << 16);
+      }
+      if constexpr (kK8) {
+        // quantise as the append kernel does: the 4 quads of a column hold all
+        // D dims between them, so two shuffles give amax; then
+        // scale = amax / 127 and code = rint(k / scale) in IEEE fp32
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+          const half8_t h = as_h8(kn[j]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)h[e]));
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const float qs = amax / 127.0f;
+        kq = amax > 0.f ? qs : 0.f;
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+          const half8_t h = as_h8(kn[j]);
+          uint32_t w[2] = {0u, 0u};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            int32_t c = 0;
+            if (amax > 0.f) c = max(-127, min(127, (int32_t)rintf((float)h[e] / qs)));
+            w[e / 4] |= ((uint32_t)c & 0xFFu) << (8 * (e % 4));
+          }
+          kc[j] = make_uint2(w[0], w[1]);
+        }
       }
     }
   }
@@ -432,7 +464,11 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     const int32_t page = pid < 0 ? 0 : pid;                        // stay in bounds
     const int64_t off = ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)(t0 & pmask) * D;
     if constexpr (kAppend) {
-      if (live && blk == nt.blk && pid >= 0) new_off = off;
+      if (live && blk == nt.blk && pid >= 0) {
+        new_off = off;
+        if constexpr (kK8)
+          new_sub8 = ((((int64_t)page * p.Hkv + kvh) << (p.p_shift - 4)) + ((t0 & pmask) >> 4)) * kSub8;
+      }
     }
     const int32_t bytes = live ? kBlk * D * 2 : 0;
     if constexpr (kK8) {
@@ -469,9 +505,35 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
         const bool vl = quad == (nt.u >> 2);
         const uint32_t sh = (nt.u & 1) * 16;
         const uint32_t keep = ~(0xFFFFu << sh);
+        if constexpr (kK8) {
+          // codes into the lane's 16-byte run of each 64 dims, scale into slot u % 4 of the scale run
+#pragma unroll
+          for (int j = 0; j < KL; ++j) {
+            if (kl) {
+              if (j & 1) {
+                kr[j / 2].z = kc[j].x;
+                kr[j / 2].w = kc[j].y;
+              } else {
+                kr[j / 2].x = kc[j].x;
+                kr[j / 2].y = kc[j].y;
+              }
+            }
+          }
+          if (vl) {
+            const uint32_t qb32 = __builtin_bit_cast(uint32_t, kq);
+            switch (nt.u & 3) {
+              case 0: kr[D / 64].x = qb32; break;
+              case 1: kr[D / 64].y = qb32; break;
+              case 2: kr[D / 64].z = qb32; break;
+              default: kr[D / 64].w = qb32; break;
+            }
+          }
+        }
 #pragma unroll
         for (int j = 0; j < KL; ++j) {
-          if (kl) kr[j] = kn[j];
+          if constexpr (!kK8) {
+            if (kl) kr[j] = kn[j];
+          }
           const uint32_t lo = (vn[j] & 0xFFFFu) << sh;
           const uint32_t hi = (vn[j] >> 16) << sh;
           if (vl) {
@@ -486,15 +548,33 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
         }
         if (new_off >= 0) {
           const int32_t bytes = kBlk * D * 2;
-          const __amdgpu_buffer_rsrc_t kws =
-              __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_pool_w + new_off), (short)0, bytes, kBufferFlags);
           const __amdgpu_buffer_rsrc_t vws =
               __builtin_amdgcn_make_buffer_rsrc((void*)(p.v_pool_w + new_off), (short)0, bytes, kBufferFlags);
           const int32_t hoff = (nt.u & 3) * 2;
+          if constexpr (kK8) {
+            const __amdgpu_buffer_rsrc_t kws =
+                __builtin_amdgcn_make_buffer_rsrc((void*)(p.k8_w + new_sub8), (short)0, kSub8, kBufferFlags);
+#pragma unroll
+            for (int j = 0; j < KL; ++j) {
+              if (kl) {
+                const int32_t o = (j / 2) * 1024 + lane * 16 + (j & 1) * 8;
+                __builtin_amdgcn_raw_buffer_store_b32(kc[j].x, kws, o, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(kc[j].y, kws, o + 4, 0, 0);
+              }
+            }
+            if (kl && quad == 0)
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, kq), kws, kBlk * D + 4 * nt.u, 0, 0);
+          }
 #pragma unroll
           for (int j = 0; j < KL; ++j) {
-            if (kl) __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, kn[j]), kws,
-                                                           lane * 16 + j * 1024, 0, 0);
+            if constexpr (!kK8) {
+              if (kl) {
+                const __amdgpu_buffer_rsrc_t kws =
+                    __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_pool_w + new_off), (short)0, bytes, kBufferFlags);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, kn[j]), kws, lane * 16 + j * 1024,
+                                                       0, 0);
+              }
+            }
             if (vl) {
               __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(vn[j] & 0xFFFFu), vws, lane * 16 + j * 1024 + hoff, 0, 0);
               __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(vn[j] >> 16), vws, lane * 16 + j * 1024 + 8 + hoff, 0, 0);
@@ -1105,8 +1185,12 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   DecodeParams prm{};
   prm.out = static_cast<half_t*>(out);
   prm.q = static_cast<const half_t*>(q);
-  if (k8) prm.k8 = static_cast<const uint8_t*>(k_pool);
-  else prm.k_pool = static_cast<const half_t*>(k_pool);
+  if (k8) {
+    prm.k8 = static_cast<const uint8_t*>(k_pool);
+    prm.k8_w = static_cast<uint8_t*>(k_pool_w);
+  } else {
+    prm.k_pool = static_cast<const half_t*>(k_pool);
+  }
   prm.v_pool = static_cast<const half_t*>(v_pool);
   prm.k_pool_w = static_cast<half_t*>(k_pool_w);
   prm.v_pool_w = static_cast<half_t*>(v_pool_w);
@@ -1146,8 +1230,10 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   const int64_t grid = plan.grid;
   hipError_t e = hipSuccess;
   if (grid > 0) {
-    if (k8) e = plan.split ? dispatch_d<true, false, true>(D, G, prm, s, grid)
-                           : dispatch_d<false, false, true>(D, G, prm, s, grid);
+    if (k8 && fused)
+      e = plan.split ? dispatch_d<true, true, true>(D, G, prm, s, grid) : dispatch_d<false, true, true>(D, G, prm, s, grid);
+    else if (k8)
+      e = plan.split ? dispatch_d<true, false, true>(D, G, prm, s, grid) : dispatch_d<false, false, true>(D, G, prm, s, grid);
     else if (plan.split)
       e = fused ? dispatch_d<true, true, false>(D, G, prm, s, grid) : dispatch_d<true, false, false>(D, G, prm, s, grid);
     else
@@ -1315,15 +1401,16 @@ int pkv_kv_append_k8(const void* k_new, const void* v_new, void* k_pool8, void* 
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
 }
 
-int pkv_paged_decode_attention_k8(void* out, const void* q, const void* k_pool8, const void* v_pool,
-                                  const int32_t* block_table, int32_t max_pages, const int32_t* lens, int32_t B,
-                                  int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N, int32_t max_context,
-                                  float scale, int32_t partition_tokens, int32_t prefix_tokens, void* workspace,
-                                  size_t workspace_bytes, void* stream) {
-  if (prefix_tokens > 0 && (P <= 0 || prefix_tokens % P != 0)) return PKV_ERR_INVALID_ARG;
-  return decode_common(out, q, nullptr, nullptr, k_pool8, v_pool, nullptr, nullptr, block_table, max_pages, lens, B,
-                       Hq, Hkv, D, P, N, max_context, scale, partition_tokens, prefix_tokens, workspace,
-                       workspace_bytes, stream, false, true);
+int pkv_paged_decode_attention_k8(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool8,
+                                  void* v_pool, const int32_t* block_table, int32_t max_pages, const int32_t* lens,
+                                  int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                                  int32_t max_context, float scale, int32_t partition_tokens, int32_t prefix_tokens,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  if ((k_new == nullptr) != (v_new == nullptr)) return PKV_ERR_INVALID_ARG;
+  const bool fused = k_new != nullptr;
+  return decode_common(out, q, k_new, v_new, k_pool8, v_pool, k_pool8, v_pool, block_table, max_pages, lens, B, Hq,
+                       Hkv, D, P, N, max_context, scale, partition_tokens, prefix_tokens, workspace, workspace_bytes,
+                       stream, fused, true);
 }
 
 int pkv_paged_decode_attention_shared_prefix(void* out, const void* q, const void* k_new, const void* v_new,

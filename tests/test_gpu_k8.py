@@ -186,3 +186,30 @@ def test_append_then_decode_k8_equals_quantised_fp16_within_bound():
     qerr = np.abs(host(got).astype(np.float64) - ref16).max()
     say("int8 keys vs fp16 keys: max abs difference %.3e" % qerr)
     assert qerr < 2e-2
+
+
+@pytest.mark.parametrize("number,batch,part,use_prefix", [(2, 3, 0, False), (2, 3, 1024, False), (3, 6, 512, True),
+                                                          (3, 6, 512, False), (5, 5, 512, False)])
+def test_fused_append_decode_k8_matches_oracle(number, batch, part, use_prefix):
+    """Append in the decode launch: the key is quantised in registers exactly as
+    the append kernel does (pools byte-identical to the oracle's append), and the
+    output matches the oracle's decode over the appended pools."""
+    w = workload(number, page_size=64 if number == 5 else None, batch=batch)
+    step = w.steps - 1
+    lens = w.lens(step)
+    rng = np.random.default_rng(500 + number)
+    live = _live_tokens(w.N, w.P, w.block_table, lens - 1)      # the new slots are poisoned too
+    pool8 = random_k8_pool(rng, w.N, w.Hkv, w.P, w.D, live)
+    vp = poison_v(w.v_pool, live)
+    prefix = w.shared_prefix_pages * w.P if use_prefix else 0
+    say("fused k8", w.name, "B=%d part=%d prefix=%d" % (w.B, part, prefix))
+    k8d, vd = dev(pool8), dev(vp)
+    got = pkv().paged_decode_attention_k8(dev(w.q), k8d, vd, dev(w.block_table), dev(lens), int(lens.max()), w.scale,
+                                          part, prefix_tokens=prefix, k_new=dev(w.k_new[step]),
+                                          v_new=dev(w.v_new[step]))
+    torch.cuda.synchronize()
+    rk, rv = oracle.kv_append_k8(pool8, vp, w.k_new[step], w.v_new[step], w.block_table, w.pos(step), w.P)
+    assert np.array_equal(host(k8d), rk)
+    assert np.array_equal(host(vd).view(np.uint16), rv.view(np.uint16))
+    ref = oracle.decode_attention_k8(w.q, rk, rv, w.block_table, lens, w.scale, w.P)
+    check_close(got, ref, "fused k8 %s" % w.name)
