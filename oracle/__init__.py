@@ -30,6 +30,7 @@ from .paged_decode import (  # noqa: F401
     write_token,
     gather_sequence,
     decode_attention,
+    decode_attention_multi,
     kv_append,
     decode_partials,
     lse_merge,

@@ -197,6 +197,32 @@ def decode_attention(q, k_pool, v_pool, block_table, lens, scale, page_size):
     return out
 
 
+def decode_attention_multi(q, k_pool, v_pool, block_table, lens, scale, page_size):
+    """Attention for the last ``k`` tokens of every sequence at once.
+
+    ``q`` is ``[B][k][Hq][D]``: the queries of a sequence's last ``k`` positions
+    ``lens[b] - k .. lens[b] - 1``, whose keys and values are already in the
+    cache. Each query attends causally: query ``i`` sees tokens
+    ``0 .. lens[b] - k + i``. This is the attention of verifying ``k`` drafted
+    tokens in one pass or of one chunk of a chunked prefill (pgsm §3.2 names
+    both: speculative decoding checks several candidate tokens in parallel,
+    chunked prefill processes a prompt in pieces over the paged cache); each
+    query is exactly a single-token decode step over its own prefix, so it is
+    computed as one (``decode_attention`` with length ``lens[b] - k + i + 1``).
+    Returns float64 ``[B][k][Hq][D]``; a row whose query would start before
+    token 0 (``lens[b] < k``) is all NaN.
+    """
+    b_count, k, hq, d = q.shape
+    out = np.zeros((b_count, k, hq, d), dtype=np.float64)
+    for i in range(k):
+        li = np.asarray(lens, dtype=np.int64) - k + i + 1
+        valid = li >= 1
+        li_safe = np.where(valid, li, 0)
+        out[:, i] = decode_attention(q[:, i], k_pool, v_pool, block_table, li_safe, scale, page_size)
+        out[~valid, i] = np.nan
+    return out
+
+
 def kv_append(k_pool, v_pool, k_new, v_new, block_table, pos, page_size):
     """Return copies of the pools with each sequence's new token written.
 
