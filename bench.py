@@ -59,6 +59,9 @@ def parse_args():
                          "Python (slower on this stack: graph launch costs more than it saves)")
     ap.add_argument("--patch-max", type=int, default=1024,
                     help="table changes per step applied in place by pkv_block_table_patch; more -> full upload")
+    ap.add_argument("--n-query", type=int, default=1,
+                    help="chunk of K new tokens per sequence and step (K appends, then one causal multi-query "
+                         "attention call, pkv_paged_decode_attention_multi); tokens/s counts B * K per layer-step")
     ap.add_argument("--int8-keys", action="store_true",
                     help="keys as int8 codes with a per-token fp32 scale, values fp16 (pkv_kv_append_k8 + "
                          "pkv_paged_decode_attention_k8)")
@@ -96,7 +99,7 @@ def cpu_model():
     return platform.processor() or None
 
 
-def algorithmic_bytes(lens, B, Hq, Hkv, D, P, shared_tokens, k_bytes=None):
+def algorithmic_bytes(lens, B, Hq, Hkv, D, P, shared_tokens, k_bytes=None, n_query=1):
     """Unique bytes one layer-step must move: every attended K/V byte once
     (shared-prefix tokens once for the whole batch), q in, out, new K/V in and
     written, the block-table entries and lengths. ``k_bytes``: stored bytes of
@@ -105,8 +108,8 @@ def algorithmic_bytes(lens, B, Hq, Hkv, D, P, shared_tokens, k_bytes=None):
     lens = np.asarray(lens, dtype=np.int64)
     kv_tokens = int(lens.sum()) - shared_tokens * (len(lens) - 1)
     kv = kv_tokens * Hkv * (kb + 2 * D)
-    q_out = 2 * B * Hq * D * 2
-    new_kv = B * Hkv * (2 * 2 * D + kb + 2 * D)   # read k_new/v_new (fp16), write them to the pools
+    q_out = 2 * n_query * B * Hq * D * 2
+    new_kv = n_query * B * Hkv * (2 * 2 * D + kb + 2 * D)   # read k_new/v_new (fp16), write them to the pools
     table = int(sum(-(-int(n) // P) for n in lens)) * 4 + B * 4
     return kv + q_out + new_kv + table, kv
 
@@ -229,16 +232,19 @@ def main():
     R = args.layers
     total_steps = args.warmup + args.steps
     k8 = args.int8_keys
-    fused = not args.separate_append
+    KQ = args.n_query
+    fused = not args.separate_append and KQ == 1
     prefix_tokens = 0 if args.no_shared_prefix else w.shared_prefix_pages * w.P
     if w.steps == 0:
         raise SystemExit("workload %d has no append; pick 2-5" % args.workload)
+    if KQ > 1 and (prefix_tokens or k8 or args.graph):
+        raise SystemExit("--n-query runs without a shared prefix (--no-shared-prefix), int8 keys or graphs")
     log("workload %s: B=%d Hq=%d Hkv=%d D=%d P=%d part=%d layers=%d fused=%s" % (w.name, B, Hq, Hkv, D, P, part, R,
                                                                                   fused))
 
     # ---- a1: page allocator (host). Pages for every step are drawn on demand.
     prefix_pages = w.shared_prefix_pages
-    final_ctx = w.context.astype(np.int64) + max(total_steps, w.steps)   # tokens after the last step
+    final_ctx = w.context.astype(np.int64) + KQ * max(total_steps, w.steps)   # tokens after the last step
     need = prefix_pages + sum(-(-int(n) // P) - prefix_pages for n in final_ctx)
     N = max(need, w.N)
     free_order = np.concatenate([w.perm, np.arange(w.N, N, dtype=np.int32)]).astype(np.int32)
@@ -298,8 +304,20 @@ def main():
     knew[0].copy_(put(w.k_new[0]))
     vnew[0].copy_(put(w.v_new[0]))
     bt_dev = torch.from_numpy(bt_np).to(dev)
-    lens_all = torch.from_numpy((w.context[None, :] + 1 + np.arange(total_steps)[:, None]).astype(np.int32)).to(dev)
+    lens_all = torch.from_numpy((w.context[None, :] + KQ * (1 + np.arange(total_steps)[:, None])).astype(np.int32)).to(dev)
     pos_all = lens_all - 1
+    if KQ > 1:
+        # the chunk's K positions per step, and K tokens (step 0: the workload's token first) per step
+        pos_chunk = torch.stack([lens_all - KQ + i for i in range(KQ)], dim=1)      # [steps][K][B]
+        knew_mq = torch.empty((total_steps, KQ, B, Hkv, D), dtype=torch.float16, device=dev)
+        vnew_mq = torch.empty_like(knew_mq)
+        knew_mq.normal_(generator=gen)
+        vnew_mq.normal_(generator=gen)
+        knew_mq[0, 0].copy_(put(w.k_new[0]))
+        vnew_mq[0, 0].copy_(put(w.v_new[0]))
+        q_mq = torch.empty((B, KQ, Hq, D), dtype=torch.float16, device=dev)
+        q_mq.normal_(generator=gen)
+        out_mq = torch.empty((B, KQ, Hq, D), dtype=torch.float16, device=dev)
     max_context = int(final_ctx.max())
     ws_bytes = pkv.decode_workspace_bytes(B, Hq, D, max_context, part, prefix_tokens)
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
@@ -311,7 +329,13 @@ def main():
     scale = w.scale
 
     def layer_call(layer, lens, pos, kn, vn, s):
-        if k8:
+        if KQ > 1:
+            # pos [K][B], kn / vn [K][B][Hkv][D]: K appends, then the chunk's attention
+            for i in range(KQ):
+                pkv.kv_append(kn[i], vn[i], k_pools[layer], v_pools[layer], bt_dev, pos[i], stream=s)
+            pkv.paged_decode_attention_multi(q_mq, k_pools[layer], v_pools[layer], bt_dev, lens, max_context, scale,
+                                             part, out=out_mq, workspace=workspace, stream=s)
+        elif k8:
             if not fused:
                 pkv.kv_append_k8(kn, vn, k_pools[layer], v_pools[layer], bt_dev, pos, stream=s)
             pkv.paged_decode_attention_k8(q, k_pools[layer], v_pools[layer], bt_dev, lens, max_context, scale, part,
@@ -332,7 +356,10 @@ def main():
                                        out=out, workspace=workspace, stream=s)
 
     def layer_step(step, layer):
-        layer_call(layer, lens_all[step], pos_all[step], knew[step], vnew[step], stream)
+        if KQ > 1:
+            layer_call(layer, lens_all[step], pos_chunk[step], knew_mq[step], vnew_mq[step], stream)
+        else:
+            layer_call(layer, lens_all[step], pos_all[step], knew[step], vnew[step], stream)
 
     last_bt = bt_np.copy()
     host_t = {"alloc": 0.0, "upload": 0.0}
@@ -348,7 +375,7 @@ def main():
         # a1: grow every sequence to hold this step's token; upload the table if it changed
         nonlocal last_bt, n_upload
         t0 = time.perf_counter()
-        alloc.reserve_batch(seqs, w.context + step + 1, bt_np)
+        alloc.reserve_batch(seqs, w.context + KQ * (step + 1), bt_np)
         changed = not np.array_equal(bt_np, last_bt)
         t1 = time.perf_counter()
         if changed:
@@ -375,7 +402,19 @@ def main():
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
     sample = np.linspace(0, B - 1, min(B, args.check_sequences)).astype(int)
-    if k8:
+    if KQ > 1:
+        got = out_mq.cpu().numpy().astype(np.float64)
+        kp0, vp0 = w.k_pool, w.v_pool
+        bt0 = bt_np[:, :]
+        kn0, vn0 = knew_mq[0].cpu().numpy(), vnew_mq[0].cpu().numpy()
+        kpool_full = k_pools[0].cpu().numpy()            # pages beyond the workload's pool were drawn on device
+        vpool_full = v_pools[0].cpu().numpy()
+        for i in range(KQ):
+            kpool_full, vpool_full = oracle.kv_append(kpool_full, vpool_full, kn0[i], vn0[i], bt0,
+                                                      (w.context + i).astype(np.int32), P)
+        ref = oracle.decode_attention_multi(q_mq.cpu().numpy()[sample], kpool_full, vpool_full, bt0[sample],
+                                            (w.context + KQ).astype(np.int32)[sample], scale, P)
+    elif k8:
         kp0, vp0 = oracle.kv_append_k8(k8_layer0[:w.N], w.v_pool, w.k_new[0], w.v_new[0], w.block_table, w.pos(0), P)
         ref = oracle.decode_attention_k8(w.q[sample], kp0, vp0, w.block_table[sample], w.lens(0)[sample], scale, P)
     else:
@@ -486,15 +525,15 @@ def main():
     kv_steps = []
     for i in range(args.steps):
         step = args.warmup + i
-        tot, kv = algorithmic_bytes(w.context + step + 1, B, Hq, Hkv, D, P, prefix_pages * P,
-                                    k_bytes=(D + 4) if k8 else None)
+        tot, kv = algorithmic_bytes(w.context + KQ * (step + 1), B, Hq, Hkv, D, P, prefix_pages * P,
+                                    k_bytes=(D + 4) if k8 else None, n_query=KQ)
         bytes_steps.append(tot)
         kv_steps.append(kv)
     bytes_per_call = float(np.mean(bytes_steps))
     kv_per_call = float(np.mean(kv_steps))
     call_avg_s = float(call_ms.mean()) / 1e3
     achieved = bytes_per_call / call_avg_s / 1e9
-    tokens_per_s = B / (ms_per_layer / 1e3)
+    tokens_per_s = B * KQ / (ms_per_layer / 1e3)
 
     result = {
         "metric": "decode tokens/s and effective KV-read HBM GB/s (% of peak), GQA 32/8, d=128",
@@ -513,14 +552,18 @@ def main():
             "workload": w.name,
             "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": P,
             "kv_dtype": "k int8 + fp32 scale per token and head, v f16" if k8 else "f16", "accumulate": "f32",
-            "mean_context": float(np.mean(w.context + args.warmup + 1 + (args.steps - 1) / 2)),
+            "mean_context": float(np.mean(w.context + KQ * (args.warmup + 1 + (args.steps - 1) / 2))),
+            "queries_per_sequence": KQ,
             "shared_prefix_tokens": prefix_pages * P,
             "partition_tokens": part,
             "layers_per_step": R,
             "append": "fused" if fused else "separate",
             "launch": "eager" if graph is None else "hip graph per step (%d layer calls)" % R,
             "shared_prefix_path": bool(prefix_tokens),
-            "tokens_per_s_definition": "batch / (time of one attention layer-step: append + decode), "
+            "tokens_per_s_definition": ("batch * queries per sequence / (time of one attention layer-step: "
+                                        "appends + chunk attention), i.e. tokens verified per second through one "
+                                        "layer") if KQ > 1 else
+                                       "batch / (time of one attention layer-step: append + decode), "
                                        "i.e. sequences advanced per second through one layer",
             "tokens_per_s_32_layers": round(tokens_per_s / 32, 1),
             "ms_per_layer_step": round(ms_per_layer, 5),
@@ -533,9 +576,10 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "paged decode call (%s%spartition kernel%s + log-sum-exp reduce)" % (
-                ("int8-key " if fused else "int8-key append + int8-key ") if k8 else "",
-                "shared-prefix + " if prefix_tokens else "", " with fused append" if fused else ""),
+            "kernel": ("%d appends + multi-query partition kernel + log-sum-exp reduce" % KQ) if KQ > 1 else
+                      "paged decode call (%s%spartition kernel%s + log-sum-exp reduce)" % (
+                          ("int8-key " if fused else "int8-key append + int8-key ") if k8 else "",
+                          "shared-prefix + " if prefix_tokens else "", " with fused append" if fused else ""),
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",

@@ -248,6 +248,33 @@ int pkv_paged_decode_attention_shared_prefix(void* out, const void* q, const voi
                                              float scale, int32_t partition_tokens, int32_t prefix_tokens,
                                              void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * pkv_paged_decode_attention_multi -- attention for a chunk of the last
+ * n_query tokens of every sequence at once, causal within the chunk: the
+ * verification of drafted tokens in speculative decoding, or one chunk of a
+ * chunked prefill, over the same paged cache (pgsm §3.2 names both).
+ *
+ * Query i (0 <= i < n_query) of sequence b sits at position
+ * lens[b] - n_query + i and attends tokens 0 .. lens[b] - n_query + i: each
+ * query gets exactly the single-token decode of its own prefix. The chunk's
+ * keys and values must already be in the cache (pkv_kv_append per token).
+ *
+ *   out          : fp16 [B][n_query][Hq][D] device, written.
+ *   q            : fp16 [B][n_query][Hq][D] device, read.
+ *   n_query      : >= 1, with n_query * (Hq / Hkv) <= 16 (the query rows of a
+ *                  KV head fill one 16-column matrix-core tile; otherwise
+ *                  PKV_ERR_UNSUPPORTED).
+ *   lens[b]      : tokens in the cache including the whole chunk; a row with
+ *                  lens[b] < n_query (or beyond max_context / the table) is NaN.
+ * Other arguments, the workspace (pkv_decode_workspace_bytes) and errors as
+ * pkv_paged_decode_attention.
+ */
+int pkv_paged_decode_attention_multi(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, int32_t max_pages, const int32_t* lens, int32_t B,
+                                     int32_t n_query, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                                     int32_t max_context, float scale, int32_t partition_tokens, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Key-only int8 pages                                                       */
 /* ------------------------------------------------------------------------ */

@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     lib,
     paged_decode_attention,
     paged_decode_attention_k8,
+    paged_decode_attention_multi,
     paged_decode_attention_shared_prefix,
     probe_stream_read,
     status_string,

@@ -36,6 +36,9 @@ _SIGNATURES = {
     "pkv_block_table_patch": (ctypes.c_int, [_vp, _i32, _i32, _ip, _ip, _ip, _i32, _vp]),
     "pkv_probe_stream_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _i32, _i32, _vp, _vp]),
     "pkv_k8_pool_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
+    "pkv_paged_decode_attention_multi": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                                        _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _vp,
+                                                        ctypes.c_size_t, _vp]),
     "pkv_kv_append_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_paged_decode_attention_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                                      _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _i32, _vp,
@@ -159,6 +162,34 @@ def kv_append(k_new, v_new, k_pool, v_pool, block_table, pos, stream=None):
                              _dev_ptr(block_table, torch.int32, "block_table"), max_pages,
                              _dev_ptr(pos, torch.int32, "pos"), B, Hkv, D, P, N, _stream(stream))
     _check(rc, "pkv_kv_append")
+
+
+def paged_decode_attention_multi(q, k_pool, v_pool, block_table, lens, max_context, scale, partition_tokens=0,
+                                 out=None, workspace=None, stream=None):
+    """pkv_paged_decode_attention_multi: q [B][n_query][Hq][D], the last n_query tokens of
+    each sequence, causal within the chunk; returns ``out`` [B][n_query][Hq][D]."""
+    B, nq, Hq, D = q.shape
+    N, Hkv, P, Dk = k_pool.shape
+    _, max_pages = block_table.shape
+    if Dk != D or tuple(v_pool.shape) != tuple(k_pool.shape) or block_table.shape[0] != B or tuple(lens.shape) != (B,):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((B, nq, Hq, D), dtype=torch.float16, device=q.device)
+    if tuple(out.shape) != (B, nq, Hq, D):
+        raise ValueError("out must be [B][n_query][Hq][D]")
+    ws_bytes = decode_workspace_bytes(B, Hq, D, max_context, partition_tokens)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    rc = lib().pkv_paged_decode_attention_multi(
+        _dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"),
+        _dev_ptr(k_pool, torch.float16, "k_pool"), _dev_ptr(v_pool, torch.float16, "v_pool"),
+        _dev_ptr(block_table, torch.int32, "block_table"), max_pages, _dev_ptr(lens, torch.int32, "lens"),
+        B, nq, Hq, Hkv, D, P, N, int(max_context), float(scale), int(partition_tokens), ws_ptr, ws_len,
+        _stream(stream))
+    _check(rc, "pkv_paged_decode_attention_multi")
+    return out
 
 
 def k8_pool_bytes(N, Hkv, P, D):

@@ -115,6 +115,7 @@ struct DecodeParams {
   int32_t max_context;
   int32_t prefix_tokens;     // shared leading tokens (0 = none), multiple of P
   int32_t min_len;           // split mode: shorter sequences are invalid (NaN rows)
+  int32_t nq;                // queries per sequence (1 = decode; > 1: the chunk of the last nq tokens)
   int32_t n_tiles;           // 16-row query tiles per KV head that read the prefix (0 = none)
   int32_t n_flat_wgs;        // workgroups of the balanced split schedule
   int32_t min_piece;         // minimum blocks per piece
@@ -362,15 +363,20 @@ __device__ __forceinline__ void set_priority(int32_t remaining, int32_t quota) {
 // the codes widen exactly to fp16 for the score MFMA and each score is then
 // multiplied by its token's scale (s_t = scale_t * <codes_t, q>).
 //
+// kMQ: the column of lane (col, quad) may see tokens up to clim only (the
+// causal bound of its query within a chunk); clim_min is the smallest bound of
+// the wave, so blocks wholly below it skip the mask.
+//
 // kAppend: the new token nt is taken from k_new / v_new instead of the pool:
 // the wave that streams its block loads the token's operand slices with its
 // other loads, patches them into the block's registers before use, and writes
 // them to the pool from there. No other wave reads that row, so the write
 // needs no ordering against the loads.
-template <int D, int32_t kPolicy, bool kAppend, bool kK8>
+template <int D, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ>
 __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32_t* bt_row, int32_t kvh,
                                               int32_t start, int32_t end, int32_t first, int32_t stride,
                                               int32_t quota, int32_t after, const NewToken& nt,
+                                              int32_t clim, int32_t clim_min,
                                               const half8_t (&qb)[D / 32], WaveState<D>& st, int lane) {
   constexpr int KL = D / 32;           // 16-byte loads per lane per block, for K and for V
   constexpr int NT = D / 16;           // 16-dim output tiles
@@ -601,6 +607,12 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
 #pragma unroll
       for (int j = 0; j < KL; ++j) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kr[j]), qb[j], s, 0, 0, 0);
     }
+    if constexpr (kMQ) {
+      if (t0 + kBlk - 1 > clim_min) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = t0 + 4 * quad + i <= clim ? s[i] : kNegInf();
+      }
+    }
     const int32_t rem = end - t0;      // valid tokens in this block (>= 1)
     if (rem < kBlk) {
       // tail: mask scores of absent tokens and zero their values (never 0 * NaN)
@@ -622,7 +634,11 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     bm *= c;                            // block max of column col, base-2 units (c > 0)
     if (__builtin_amdgcn_ballot_w64(bm > st.m_ref + kRescaleSlack) != 0) {
       const float m_new = fmaxf(st.m_ref, bm);
-      const float alpha = fast_exp2(st.m_ref - m_new);         // 0 on the first block
+      float alpha = fast_exp2(st.m_ref - m_new);               // 0 on the first block
+      if constexpr (kMQ) {
+        // a causally masked column may have seen no token yet: -inf - -inf
+        if (m_new == kNegInf()) alpha = 1.f;
+      }
       st.l_part *= alpha;
       // output row 4 quad + i belongs to column 4 quad + i, whose alpha sits in lane 4 quad + i
 #pragma unroll
@@ -634,8 +650,10 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
       st.m_ref = m_new;
     }
     float pr[4];
+    float mref = st.m_ref;
+    if constexpr (kMQ) mref = mref == kNegInf() ? 0.f : mref;   // all its scores are -inf then: p = 0
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(s[i], c, -st.m_ref));
+    for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(s[i], c, -mref));
     st.l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
     const half4_t pa = {(half_t)pr[0], (half_t)pr[1], (half_t)pr[2], (half_t)pr[3]};
 #pragma unroll
@@ -704,10 +722,13 @@ struct KernelShared {
 // waves merge through LDS and every (column c, dim d) goes to
 // emit(c, d, M, Ls, O): the column's base-2 score max, softmax denominator
 // and unnormalised output. Callers must be workgroup-uniform.
-template <int D, int NC, int32_t kPolicy, bool kAppend, bool kK8, class RowFn, class EmitFn>
+// kMQ: column c is query c / g of the chunk (g = mq_g heads per query); query
+// i may see tokens up to mq_last0 + i.
+template <int D, int NC, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ = false, class RowFn, class EmitFn>
 __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>& sh, const int32_t* bt_row,
                                           int32_t kvh, int32_t start, int32_t end, int32_t quota, int32_t after,
-                                          const NewToken& nt, RowFn qrow, EmitFn emit, int lane, int wave) {
+                                          const NewToken& nt, RowFn qrow, EmitFn emit, int lane, int wave,
+                                          int32_t mq_last0 = 0, int32_t mq_g = 1) {
   constexpr int KL = D / 32;
   constexpr int NT = D / 16;
   const int col = lane & 15;
@@ -723,7 +744,13 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
   }
   WaveState<D> st;
   init_state<D>(st);
-  stream_blocks<D, kPolicy, kAppend, kK8>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, nt, qb, st, lane);
+  int32_t clim = 0x7fffffff;
+  if constexpr (kMQ) {
+    const int32_t qi = col / mq_g;
+    clim = qi < p.nq ? mq_last0 + qi : 0x7fffffff;
+  }
+  stream_blocks<D, kPolicy, kAppend, kK8, kMQ>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, nt, clim,
+                                               mq_last0, qb, st, lane);
   // per-column denominators of this wave: sum the 4 quads of column col
   st.l_part += __shfl_xor(st.l_part, 16);
   st.l_part += __shfl_xor(st.l_part, 32);
@@ -783,14 +810,38 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
 // writes slot kvh * (NT + B + 2 Wk) + s + j, private segments numbered after
 // NT + Wk: walking a list in order increases s or j (or both) by one each
 // step, so the slots are distinct; each slot holds 16 columns.
-template <int D, int G, bool SPLIT, bool FUSED, bool K8>
+template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ>
 __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodeParams p) {
+  static_assert(!MQ || (!FUSED && !K8), "chunks of queries: fp16 keys, no fused append");
   static_assert(D % 32 == 0 && G >= 1 && G <= 16, "shape");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   __shared__ KernelShared<D, G> smem;
 
-  if constexpr (!SPLIT) {
+  if constexpr (!SPLIT && MQ) {
+    // a chunk of nq queries per sequence: columns (query i, head g) = i * G + g
+    const int32_t kvh = blockIdx.x % p.Hkv;
+    const int32_t b = blockIdx.x / p.Hkv;
+    const int32_t L = p.lens[b];
+    const bool bad_len = L < p.nq || L > p.max_context || L > (p.max_pages << p.p_shift);
+    const int32_t ncol = p.nq * G;
+    auto row = [&](int c) -> int64_t { return ((int64_t)b * p.nq + c / G) * p.Hq + (int64_t)kvh * G + c % G; };
+    if (bad_len) {
+      for (int i = threadIdx.x; i < ncol * D; i += kThreads) p.out[row(i / D) * D + i % D] = (half_t)__builtin_nanf("");
+      return;
+    }
+    const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
+    run_range<D, 16, kKvLoadPolicy, false, false, true>(
+        p, smem.tile.prefix, bt_row, kvh, 0, L, 0, 0, NewToken{-1, 0, nullptr, nullptr},
+        [&](int c) -> int64_t { return c < ncol ? row(c) : -1; },
+        [&](int c, int d, float, float Ls, float O) {
+          if (c < ncol) {
+            const float r = Ls > 0.f ? O / Ls : (Ls == 0.f ? 0.f : __builtin_nanf(""));
+            p.out[row(c) * D + d] = (half_t)(Ls != Ls ? __builtin_nanf("") : r);
+          }
+        },
+        lane, wave, L - p.nq, G);
+  } else if constexpr (!SPLIT) {
     WgShared<D, G>& sh = smem.tile.priv;
     const int32_t kvh = blockIdx.x % p.Hkv;
     const int32_t b = blockIdx.x / p.Hkv;
@@ -933,18 +984,29 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
           }
         }
         const int64_t slot = slot_base + p.n_tiles + Wk + b;
-        run_range<D, G, kKvLoadPolicy, FUSED, K8>(p, smem.tile.priv, bt_row, kvh, start, end, quota,
-                                              after + g1 - g - piece_n, nt,
-                                       [&](int c) -> int64_t { return c < G ? head_row0 + c : -1; },
-                                       [&](int c, int d, float M, float Ls, float O) {
-                                         const int64_t ps = slot * 16 + c;
-                                         p.flat_o[ps * D + d] = O;
-                                         if (d == 0) {
-                                           p.flat_m[ps] = M;
-                                           p.flat_l[ps] = Ls;
-                                         }
-                                       },
-                                       lane, wave);
+        auto emit = [&](int c, int d, float M, float Ls, float O) {
+          const int64_t ps = slot * 16 + c;
+          p.flat_o[ps * D + d] = O;
+          if (d == 0) {
+            p.flat_m[ps] = M;
+            p.flat_l[ps] = Ls;
+          }
+        };
+        if constexpr (MQ) {
+          // columns (query i, head g) = i * G + g of the chunk of the last nq tokens
+          const int32_t ncol = p.nq * G;
+          run_range<D, 16, kKvLoadPolicy, false, false, true>(
+              p, smem.tile.prefix, bt_row, kvh, start, end, quota, after + g1 - g - piece_n, nt,
+              [&](int c) -> int64_t {
+                return c < ncol ? ((int64_t)b * p.nq + c / G) * p.Hq + (int64_t)kvh * G + c % G : -1;
+              },
+              emit, lane, wave, L - p.nq, G);
+        } else {
+          run_range<D, G, kKvLoadPolicy, FUSED, K8>(p, smem.tile.priv, bt_row, kvh, start, end, quota,
+                                                    after + g1 - g - piece_n, nt,
+                                                    [&](int c) -> int64_t { return c < G ? head_row0 + c : -1; },
+                                                    emit, lane, wave);
+        }
         g += piece_n;
       }
     };
@@ -976,8 +1038,9 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
   constexpr int kR = 8;               // partials whose outputs are loaded up front
   __shared__ float sm_m[kMaxPartitions];
   __shared__ float sm_l[kMaxPartitions];
-  const int64_t bh = blockIdx.x;
-  const int32_t b = (int32_t)(bh / p.Hq);
+  const int64_t bh = blockIdx.x;                    // row (b * nq + query) * Hq + h of out
+  const int32_t b = (int32_t)(bh / ((int64_t)p.nq * p.Hq));
+  const int32_t qi = (int32_t)((bh / p.Hq) % p.nq);
   const int32_t h = (int32_t)(bh % p.Hq);
   const int32_t G = p.Hq / p.Hkv;
   const int32_t kvh = h / G;
@@ -1011,7 +1074,7 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
   const int32_t np = bad_len ? 0 : np1 + np2;
   auto idx = [&](int32_t j) -> int64_t {
     return j < np1 ? (slot_base + rt + ja + j) * 16 + ct
-                   : (slot_base + p.n_tiles + Wk + b + jb + (j - np1)) * 16 + hg;
+                   : (slot_base + p.n_tiles + Wk + b + jb + (j - np1)) * 16 + qi * G + hg;
   };
 
   const float* po = p.flat_o + d;
@@ -1127,34 +1190,36 @@ int64_t max_slots(int32_t B, int32_t Hq, bool prefix) {
          2 * (static_cast<int64_t>(PKV_FLAT_WORKGROUPS) + Hq);
 }
 
-template <int D, int G, bool SPLIT, bool FUSED, bool K8>
+template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ>
 hipError_t launch_partition(const DecodeParams& p, hipStream_t stream, int64_t grid) {
-  hipLaunchKernelGGL((decode_partition_kernel<D, G, SPLIT, FUSED, K8>), dim3(static_cast<uint32_t>(grid)),
+  hipLaunchKernelGGL((decode_partition_kernel<D, G, SPLIT, FUSED, K8, MQ>), dim3(static_cast<uint32_t>(grid)),
                      dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool SPLIT, bool FUSED, bool K8>
+template <int D, bool SPLIT, bool FUSED, bool K8, bool MQ = false>
 hipError_t dispatch_g(int G, const DecodeParams& p, hipStream_t s, int64_t grid) {
   switch (G) {
-    case 1: return launch_partition<D, 1, SPLIT, FUSED, K8>(p, s, grid);
-    case 2: return launch_partition<D, 2, SPLIT, FUSED, K8>(p, s, grid);
-    case 4: return launch_partition<D, 4, SPLIT, FUSED, K8>(p, s, grid);
-    case 8: return launch_partition<D, 8, SPLIT, FUSED, K8>(p, s, grid);
-    default: return launch_partition<D, 16, SPLIT, FUSED, K8>(p, s, grid);
+    case 1: return launch_partition<D, 1, SPLIT, FUSED, K8, MQ>(p, s, grid);
+    case 2: return launch_partition<D, 2, SPLIT, FUSED, K8, MQ>(p, s, grid);
+    case 4: return launch_partition<D, 4, SPLIT, FUSED, K8, MQ>(p, s, grid);
+    case 8: return launch_partition<D, 8, SPLIT, FUSED, K8, MQ>(p, s, grid);
+    default: return launch_partition<D, 16, SPLIT, FUSED, K8, MQ>(p, s, grid);
   }
 }
 
-template <bool SPLIT, bool FUSED, bool K8>
+template <bool SPLIT, bool FUSED, bool K8, bool MQ = false>
 hipError_t dispatch_d(int D, int G, const DecodeParams& p, hipStream_t s, int64_t grid) {
-  return D == 64 ? dispatch_g<64, SPLIT, FUSED, K8>(G, p, s, grid) : dispatch_g<128, SPLIT, FUSED, K8>(G, p, s, grid);
+  return D == 64 ? dispatch_g<64, SPLIT, FUSED, K8, MQ>(G, p, s, grid)
+                 : dispatch_g<128, SPLIT, FUSED, K8, MQ>(G, p, s, grid);
 }
 
 int decode_common(void* out, const void* q, const void* k_new, const void* v_new, const void* k_pool,
                   const void* v_pool, void* k_pool_w, void* v_pool_w, const int32_t* bt, int32_t max_pages,
                   const int32_t* lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
                   int32_t max_context, float scale, int32_t partition_tokens, int32_t prefix_tokens,
-                  void* workspace, size_t workspace_bytes, void* stream, bool fused, bool k8 = false) {
+                  void* workspace, size_t workspace_bytes, void* stream, bool fused, bool k8 = false,
+                  int32_t nq = 1) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || N <= 0 || max_pages <= 0 || max_context < 0 ||
       partition_tokens < 0 || prefix_tokens < 0)
     return PKV_ERR_INVALID_ARG;
@@ -1162,7 +1227,11 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
     return PKV_ERR_INVALID_ARG;
   const int G = Hq / Hkv;
+  if (nq < 1) return PKV_ERR_INVALID_ARG;
+  if (nq > 1 && (fused || k8 || prefix_tokens > 0)) return PKV_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(nq) * G > 16) return PKV_ERR_UNSUPPORTED;     // one 16-column matrix-core tile
+  if (static_cast<int64_t>(B) * nq * Hq > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
   const int p_shift = log2_page(P);
   if (p_shift < 0) return PKV_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PKV_ERR_UNSUPPORTED;
@@ -1206,8 +1275,9 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   prm.p_shift = p_shift;
   prm.max_context = max_context;
   prm.prefix_tokens = prefix_tokens;
-  // an appended token must land in a private page
-  prm.min_len = prefix_tokens + (fused && prefix_tokens > 0 ? 1 : 0);
+  // an appended token must land in a private page; each query of a chunk needs a token
+  prm.min_len = max(prefix_tokens + (fused && prefix_tokens > 0 ? 1 : 0), nq > 1 ? nq : 0);
+  prm.nq = nq;
   prm.n_tiles = plan.n_tiles;
   prm.n_flat_wgs = plan.n_flat_wgs;
   prm.min_piece = plan.min_piece;
@@ -1230,7 +1300,10 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   const int64_t grid = plan.grid;
   hipError_t e = hipSuccess;
   if (grid > 0) {
-    if (k8 && fused)
+    if (nq > 1)
+      e = plan.split ? dispatch_d<true, false, false, true>(D, G, prm, s, grid)
+                     : dispatch_d<false, false, false, true>(D, G, prm, s, grid);
+    else if (k8 && fused)
       e = plan.split ? dispatch_d<true, true, true>(D, G, prm, s, grid) : dispatch_d<false, true, true>(D, G, prm, s, grid);
     else if (k8)
       e = plan.split ? dispatch_d<true, false, true>(D, G, prm, s, grid) : dispatch_d<false, false, true>(D, G, prm, s, grid);
@@ -1241,7 +1314,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
     if (e != hipSuccess) return PKV_ERR_HIP;
   }
   if (plan.split) {
-    const uint32_t rows = static_cast<uint32_t>(static_cast<int64_t>(B) * Hq);
+    const uint32_t rows = static_cast<uint32_t>(static_cast<int64_t>(B) * nq * Hq);
     if (D == 64) hipLaunchKernelGGL(lse_reduce_kernel<64>, dim3(rows), dim3(64), 0, s, prm);
     else hipLaunchKernelGGL(lse_reduce_kernel<128>, dim3(rows), dim3(128), 0, s, prm);
     if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
@@ -1411,6 +1484,18 @@ int pkv_paged_decode_attention_k8(void* out, const void* q, const void* k_new, c
   return decode_common(out, q, k_new, v_new, k_pool8, v_pool, k_pool8, v_pool, block_table, max_pages, lens, B, Hq,
                        Hkv, D, P, N, max_context, scale, partition_tokens, prefix_tokens, workspace, workspace_bytes,
                        stream, fused, true);
+}
+
+int pkv_paged_decode_attention_multi(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                     const int32_t* block_table, int32_t max_pages, const int32_t* lens, int32_t B,
+                                     int32_t n_query, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                                     int32_t max_context, float scale, int32_t partition_tokens, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  if (n_query < 1) return PKV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * n_query > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
+  return decode_common(out, q, nullptr, nullptr, k_pool, v_pool, nullptr, nullptr, block_table, max_pages, lens, B,
+                       Hq, Hkv, D, P, N, max_context, scale, partition_tokens, 0, workspace, workspace_bytes, stream,
+                       false, false, n_query);
 }
 
 int pkv_paged_decode_attention_shared_prefix(void* out, const void* q, const void* k_new, const void* v_new,
