@@ -66,7 +66,8 @@ typedef enum pkv_status {
   PKV_ERR_OUT_OF_PAGES = 3,         /* allocator cannot cover a reservation */
   PKV_ERR_WORKSPACE_TOO_SMALL = 4,  /* split decode given too little workspace */
   PKV_ERR_HIP = 5,                  /* a kernel launch failed */
-  PKV_ERR_INVALID_TABLE = 6         /* pkv_validate_tables found a bad entry */
+  PKV_ERR_INVALID_TABLE = 6,        /* pkv_validate_tables found a bad entry */
+  PKV_ERR_NOT_FOUND = 7             /* pkv_alloc_cache_lookup: no entry under the key */
 } pkv_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -416,6 +417,71 @@ int pkv_alloc_table(const pkv_allocator* alloc, int32_t seq, int32_t* bt_row, in
 
 /* Reference count of `page` into *count. */
 int pkv_alloc_refcount(const pkv_allocator* alloc, int32_t page, int32_t* count);
+
+/*
+ * Prefix cache. A request's prompt KV can be kept after the request ends and
+ * shared by later requests with the same prefix (shared prefixes: dpshk §4.2,
+ * pgsm §3.2; reuse across requests: pgsm §4.3).
+ *
+ * pkv_alloc_cache_insert -- keep the pages of the first n_tokens tokens of
+ * `seq` under `key` (a caller-chosen identifier of the prompt, e.g. a hash of
+ * its tokens). The cache holds one reference on each page, so the pages outlive
+ * the sequence. An existing key is only marked as used. Errors:
+ * PKV_ERR_INVALID_ARG (n_tokens <= 0, seq holds fewer tokens' pages).
+ *
+ * pkv_alloc_cache_lookup -- pages (into `pages`, capacity max_pages; NULL to
+ * ask the count only) and token count under `key`; marks it as used. A new
+ * sequence starts from them with pkv_alloc_share_prefix. Errors:
+ * PKV_ERR_NOT_FOUND, PKV_ERR_INVALID_ARG (capacity too small).
+ *
+ * pkv_alloc_cache_evict -- drop the entry (its references); unknown keys are
+ * a no-op. pkv_alloc_cache_entries -- number of entries (-1 for NULL).
+ *
+ * Eviction: when a reservation (pkv_alloc_reserve*, pkv_alloc_prepare_append)
+ * needs more pages than are free, the least recently used entries (by insert
+ * or lookup) are dropped one at a time until it fits -- only if dropping all
+ * of them would make it fit; otherwise nothing changes (PKV_ERR_OUT_OF_PAGES).
+ */
+int pkv_alloc_cache_insert(pkv_allocator* alloc, uint64_t key, int32_t seq, int32_t n_tokens);
+int pkv_alloc_cache_lookup(pkv_allocator* alloc, uint64_t key, int32_t* pages, int32_t max_pages,
+                           int32_t* n_pages, int32_t* n_tokens);
+int pkv_alloc_cache_evict(pkv_allocator* alloc, uint64_t key);
+int32_t pkv_alloc_cache_entries(const pkv_allocator* alloc);
+
+/*
+ * pkv_alloc_prepare_append -- ready a batch for writing token pos[i] of
+ * sequence seqs[i] (copy on write of shared pages). Each table grows to hold
+ * the token (as pkv_alloc_reserve); if the page the token lands in is shared
+ * (count > 1: a shared prefix, or a cached prompt), the sequence gets a
+ * private page in its place, the old page's count drops by one, and the pair
+ * (copy_src[k], copy_dst[k]) is reported: the caller copies the old page's
+ * contents into the new one on the device (pkv_copy_pages) before the write.
+ * Batch order decides who copies: once the others have their own copies, the
+ * last sharer keeps the page. All or nothing: planned first, committed only if
+ * the free list (after evictions) covers it.
+ *   seqs, pos : int32 [B] host (distinct sequences, pos >= 0).
+ *   copy_src, copy_dst: int32 [B] host, written; *n_copies pairs are used.
+ *   block_table: optional int32 [B][max_pages] host: rows of the batch
+ *               rewritten (-1 past each table), as pkv_alloc_reserve_batch.
+ * Errors: PKV_ERR_INVALID_ARG (duplicates, negatives, a table wider than
+ * max_pages), PKV_ERR_OUT_OF_PAGES (nothing changed).
+ */
+int pkv_alloc_prepare_append(pkv_allocator* alloc, int32_t B, const int32_t* seqs, const int32_t* pos,
+                             int32_t* copy_src, int32_t* copy_dst, int32_t* n_copies, int32_t* block_table,
+                             int32_t max_pages);
+
+/*
+ * pkv_copy_pages -- copy whole pages of one pool on the device: page dst[i]
+ * becomes a copy of page src[i] (page_bytes bytes each: Hkv * P * D * 2 for a
+ * fp16 pool, pkv_k8_pool_bytes(1, ...) for an int8-key pool). Call it for the
+ * K and the V pool with the pairs pkv_alloc_prepare_append reports. The pairs
+ * travel in the kernel arguments (64 per launch). src and dst are HOST arrays.
+ * Errors: PKV_ERR_INVALID_ARG (a page outside [0, N), a page both copied to
+ * and from in one call, page_bytes not a positive multiple of 16, misaligned
+ * pool), PKV_ERR_HIP.
+ */
+int pkv_copy_pages(void* pool, size_t page_bytes, int32_t N, const int32_t* src, const int32_t* dst, int32_t n,
+                   void* stream);
 
 /*
  * pkv_validate_tables -- check host copies of a block table and lengths.

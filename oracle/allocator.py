@@ -19,6 +19,29 @@ allocator must reproduce exactly:
   nothing changes and ``OutOfPages`` is raised;
 * shared pages carry a reference count; a page returns to the free list when
   its count reaches zero; ``free`` releases a sequence's pages in table order.
+
+The prefix-cache lifecycle (the pages ask for shared prefixes, dpshk §4.2 and
+pgsm §3.2, and for reuse of a prompt's KV across requests, pgsm §4.3; the
+mechanics below are this library's reading):
+* ``cache_insert(key, seq, n_tokens)`` keeps the pages holding the first
+  ``n_tokens`` tokens of ``seq`` under ``key`` (a caller-chosen identifier of
+  the prompt, e.g. a hash of its tokens); the cache holds one reference on each
+  page, so the pages outlive the sequence; inserting an existing key only
+  refreshes it;
+* ``cache_lookup(key)`` returns ``(pages, n_tokens)`` (or None) and refreshes
+  the entry; a new sequence starts from them with ``share_prefix``;
+* entries are ordered by last use (insert or lookup, a counter per event);
+  when a reservation needs more pages than are free, the least recently used
+  entries are dropped (their references released) one at a time until the
+  request fits -- but only if dropping all of them would make it fit;
+  otherwise nothing changes and ``OutOfPages`` is raised;
+* ``prepare_append(seqs, pos)`` readies a batch for writing token ``pos[i]`` of
+  sequence ``seqs[i]``: the table grows to hold it (as ``reserve``), and if the
+  page it lands in is shared (count > 1) the sequence gets a private copy:
+  a new page replaces it in the table, the old page's count drops by one, and
+  the pair (old, new) is returned so the caller copies the page's contents on
+  the device before writing (copy on write). The whole batch is planned first
+  and committed only if the free list (after evictions) covers it.
 """
 
 from collections import deque
@@ -44,12 +67,75 @@ class PageAllocatorModel:
         self.free_list = deque(order)
         self.refcount = [0] * num_pages
         self.tables = {}
+        self.cache = {}          # key -> [pages, n_tokens, last_use]
+        self.clock = 0
 
     def free_count(self):
         return len(self.free_list)
 
     def table(self, seq):
         return list(self.tables.get(seq, []))
+
+    # -- prefix cache ---------------------------------------------------------
+
+    def _tick(self):
+        self.clock += 1
+        return self.clock
+
+    def cache_insert(self, key, seq, n_tokens):
+        """Keep the pages of ``seq``'s first ``n_tokens`` tokens under ``key``."""
+        have = self.tables.get(seq, [])
+        n_pages = pages_for_tokens(n_tokens, self.page_size)
+        if n_tokens <= 0 or n_pages > len(have):
+            raise ValueError("the sequence does not hold that many tokens")
+        if key in self.cache:
+            self.cache[key][2] = self._tick()
+            return list(self.cache[key][0])
+        pages = list(have[:n_pages])
+        for p in pages:
+            self.refcount[p] += 1
+        self.cache[key] = [pages, int(n_tokens), self._tick()]
+        return list(pages)
+
+    def cache_lookup(self, key):
+        """``(pages, n_tokens)`` kept under ``key`` (refreshed), or None."""
+        entry = self.cache.get(key)
+        if entry is None:
+            return None
+        entry[2] = self._tick()
+        return list(entry[0]), entry[1]
+
+    def _release(self, pages):
+        for p in pages:
+            self.refcount[p] -= 1
+            if self.refcount[p] == 0:
+                self.free_list.append(p)
+
+    def cache_evict(self, key):
+        """Drop ``key``'s entry (its references); unknown keys are a no-op."""
+        entry = self.cache.pop(key, None)
+        if entry is not None:
+            self._release(entry[0])
+
+    def _make_room(self, need):
+        """Evict least recently used entries until ``need`` pages are free, if
+        evicting all of them would do; else change nothing and raise."""
+        if need <= len(self.free_list):
+            return
+        # pages that evicting every entry would free: counts held only by the cache
+        held = {}
+        for pages, _, _ in self.cache.values():
+            for p in pages:
+                held[p] = held.get(p, 0) + 1
+        freeable = sum(1 for p, c in held.items() if self.refcount[p] == c)
+        if need > len(self.free_list) + freeable:
+            raise OutOfPages()
+        for key in sorted(self.cache, key=lambda k: self.cache[k][2]):
+            if need <= len(self.free_list):
+                break
+            self.cache_evict(key)
+
+    # -- pages of sequences ---------------------------------------------------
 
     def reserve(self, seq, n_tokens):
         """Make sequence ``seq`` hold at least ``n_tokens`` tokens of pages."""
@@ -60,8 +146,7 @@ class PageAllocatorModel:
         if need <= 0:
             self.tables.setdefault(seq, have)
             return self.table(seq)
-        if need > len(self.free_list):
-            raise OutOfPages()
+        self._make_room(need)
         new = [self.free_list.popleft() for _ in range(need)]
         for p in new:
             self.refcount[p] = 1
@@ -85,10 +170,36 @@ class PageAllocatorModel:
 
     def free(self, seq):
         """Release every page of ``seq``; unknown sequences are a no-op."""
-        for p in self.tables.pop(seq, []):
-            self.refcount[p] -= 1
-            if self.refcount[p] == 0:
-                self.free_list.append(p)
+        self._release(self.tables.pop(seq, []))
+
+    def prepare_append(self, seqs, pos):
+        """Ready every ``seqs[i]`` to have token ``pos[i]`` written (see the
+        module notes); returns the list of ``(src, dst)`` page copies."""
+        seqs = [int(x) for x in seqs]
+        pos = [int(x) for x in pos]
+        if len(set(seqs)) != len(seqs) or any(s < 0 for s in seqs) or any(t < 0 for t in pos):
+            raise ValueError("bad batch")
+        need = 0
+        for s, t in zip(seqs, pos):
+            have = self.tables.get(s, [])
+            j = t // self.page_size
+            grow = max(0, j + 1 - len(have))
+            shared = j < len(have) and self.refcount[have[j]] > 1
+            need += grow + (1 if shared else 0)
+        self._make_room(need)
+        copies = []
+        for s, t in zip(seqs, pos):
+            self.reserve(s, t + 1)
+            tab = self.tables[s]
+            j = t // self.page_size
+            old = tab[j]
+            if self.refcount[old] > 1:
+                new = self.free_list.popleft()
+                self.refcount[new] = 1
+                self.refcount[old] -= 1
+                tab[j] = new
+                copies.append((old, new))
+        return copies
 
 
 def validate_tables(block_table, lens, page_size, num_pages, exclusive_tail=False):

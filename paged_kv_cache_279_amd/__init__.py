@@ -13,10 +13,12 @@ from .binding import (  # noqa: F401
     PKV_ERR_WORKSPACE_TOO_SMALL,
     PKV_ERR_HIP,
     PKV_ERR_INVALID_TABLE,
+    PKV_ERR_NOT_FOUND,
     PkvError,
     PageAllocator,
     append_paged_decode_attention,
     block_table_patch,
+    copy_pages,
     decode_workspace_bytes,
     k8_pool_bytes,
     kv_append,

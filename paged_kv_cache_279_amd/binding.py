@@ -24,6 +24,7 @@ PKV_ERR_OUT_OF_PAGES = 3
 PKV_ERR_WORKSPACE_TOO_SMALL = 4
 PKV_ERR_HIP = 5
 PKV_ERR_INVALID_TABLE = 6
+PKV_ERR_NOT_FOUND = 7
 
 _i32 = ctypes.c_int32
 _vp = ctypes.c_void_p
@@ -63,6 +64,12 @@ _SIGNATURES = {
     "pkv_alloc_free_count": (ctypes.c_int32, [_vp]),
     "pkv_alloc_table": (ctypes.c_int, [_vp, _i32, _ip, _i32, _ip]),
     "pkv_alloc_refcount": (ctypes.c_int, [_vp, _i32, _ip]),
+    "pkv_alloc_cache_insert": (ctypes.c_int, [_vp, ctypes.c_uint64, _i32, _i32]),
+    "pkv_alloc_cache_lookup": (ctypes.c_int, [_vp, ctypes.c_uint64, _ip, _i32, _ip, _ip]),
+    "pkv_alloc_cache_evict": (ctypes.c_int, [_vp, ctypes.c_uint64]),
+    "pkv_alloc_cache_entries": (ctypes.c_int32, [_vp]),
+    "pkv_alloc_prepare_append": (ctypes.c_int, [_vp, _i32, _ip, _ip, _ip, _ip, _ip, _ip, _i32]),
+    "pkv_copy_pages": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _ip, _ip, _i32, _vp]),
     "pkv_validate_tables": (ctypes.c_int, [_ip, _ip, _i32, _i32, _i32, _i32, _i32, _ip, _ip, _ip]),
 }
 
@@ -147,6 +154,20 @@ def probe_stream_read(buf, tile_order, sink, waves=8192, stream=None):
                                        _dev_ptr(tile_order, torch.int32, "tile_order"), tile_order.numel(),
                                        int(waves), _dev_ptr(sink, torch.int32, "sink"), _stream(stream)),
            "pkv_probe_stream_read")
+
+
+def copy_pages(pool, src, dst, stream=None):
+    """pkv_copy_pages: page dst[i] of ``pool`` (a device tensor whose first axis is the
+    page) becomes a copy of page src[i]."""
+    s, sp = _host_i32(src, "src")
+    d, dp = _host_i32(dst, "dst")
+    if s.shape != d.shape:
+        raise ValueError("src and dst must have one length")
+    if not pool.is_cuda or not pool.is_contiguous():
+        raise ValueError("pool must be a contiguous device tensor")
+    page_bytes = pool[0].numel() * pool.element_size()
+    _check(lib().pkv_copy_pages(ctypes.c_void_p(pool.data_ptr()), page_bytes, pool.shape[0], sp, dp, len(s),
+                                _stream(stream)), "pkv_copy_pages")
 
 
 def kv_append(k_new, v_new, k_pool, v_pool, block_table, pos, stream=None):
@@ -406,6 +427,49 @@ class PageAllocator:
         _check(lib().pkv_alloc_table(self._h, seq, row.ctypes.data_as(_ip), len(row), ctypes.byref(n)),
                "pkv_alloc_table")
         return row[:n.value].tolist()
+
+    def cache_insert(self, key, seq, n_tokens):
+        _check(lib().pkv_alloc_cache_insert(self._h, int(key), seq, n_tokens), "pkv_alloc_cache_insert")
+
+    def cache_lookup(self, key):
+        """(pages, n_tokens) kept under ``key``, or None."""
+        n = ctypes.c_int32(0)
+        t = ctypes.c_int32(0)
+        rc = lib().pkv_alloc_cache_lookup(self._h, int(key), None, 0, ctypes.byref(n), ctypes.byref(t))
+        if rc == PKV_ERR_NOT_FOUND:
+            return None
+        _check(rc, "pkv_alloc_cache_lookup")
+        pages = np.zeros(max(1, n.value), np.int32)
+        _check(lib().pkv_alloc_cache_lookup(self._h, int(key), pages.ctypes.data_as(_ip), len(pages),
+                                            ctypes.byref(n), ctypes.byref(t)), "pkv_alloc_cache_lookup")
+        return pages[:n.value].tolist(), t.value
+
+    def cache_evict(self, key):
+        _check(lib().pkv_alloc_cache_evict(self._h, int(key)), "pkv_alloc_cache_evict")
+
+    def cache_entries(self):
+        return int(lib().pkv_alloc_cache_entries(self._h))
+
+    def prepare_append(self, seqs, pos, block_table=None):
+        """Copy on write for a batch about to write token pos[i] of seqs[i]; returns the
+        (src, dst) page copies to perform, and rewrites the batch rows of ``block_table``."""
+        s, sp = _host_i32(seqs, "seqs")
+        t, tp = _host_i32(pos, "pos")
+        if s.shape != t.shape:
+            raise ValueError("seqs and pos must have one length")
+        src = np.zeros(max(1, len(s)), np.int32)
+        dst = np.zeros(max(1, len(s)), np.int32)
+        n = ctypes.c_int32(0)
+        if block_table is not None:
+            if block_table.dtype != np.int32 or not block_table.flags.c_contiguous:
+                raise ValueError("block_table must be a C-contiguous int32 array")
+            bp, width = block_table.ctypes.data_as(_ip), block_table.shape[1]
+        else:
+            bp, width = None, 0
+        _check(lib().pkv_alloc_prepare_append(self._h, len(s), sp, tp, src.ctypes.data_as(_ip),
+                                              dst.ctypes.data_as(_ip), ctypes.byref(n), bp, width),
+               "pkv_alloc_prepare_append")
+        return list(zip(src[:n.value].tolist(), dst[:n.value].tolist()))
 
     def refcount(self, page):
         c = ctypes.c_int32(0)

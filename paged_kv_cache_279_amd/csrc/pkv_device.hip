@@ -37,6 +37,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <vector>
+
 #include "pkv.h"
 
 namespace {
@@ -252,6 +255,28 @@ __global__ __launch_bounds__(kThreads) void stream_read_kernel(const char* __res
       ++i;
     }
   }
+}
+
+// -------------------------------------------------------------------------
+// page copies (copy on write of shared pages)
+// -------------------------------------------------------------------------
+
+constexpr int kCopyMax = 64;
+struct PageCopies {
+  int32_t n;
+  int32_t src[kCopyMax];
+  int32_t dst[kCopyMax];
+};
+
+// Workgroup (i, chunk) copies 16-byte words chunk, chunk + grid.y, ... of pair i.
+__global__ __launch_bounds__(kThreads) void copy_pages_kernel(uint4* __restrict__ pool, int64_t page_words,
+                                                              PageCopies pairs) {
+  const int i = blockIdx.x;
+  if (i >= pairs.n) return;
+  const uint4* from = pool + (int64_t)pairs.src[i] * page_words;
+  uint4* to = pool + (int64_t)pairs.dst[i] * page_words;
+  for (int64_t w = (int64_t)blockIdx.y * kThreads + threadIdx.x; w < page_words; w += (int64_t)gridDim.y * kThreads)
+    to[w] = from[w];
 }
 
 // -------------------------------------------------------------------------
@@ -1351,6 +1376,37 @@ int pkv_probe_stream_read(const void* base, size_t bytes, const int32_t* tile_or
                      static_cast<hipStream_t>(stream), static_cast<const char*>(base), tile_order, n_tiles,
                      static_cast<int64_t>(bytes / 4096) - 1, static_cast<int32_t>(per_wave), sink);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_copy_pages(void* pool, size_t page_bytes, int32_t N, const int32_t* src, const int32_t* dst, int32_t n,
+                   void* stream) {
+  if (n < 0 || N <= 0 || page_bytes == 0 || page_bytes % 16 != 0) return PKV_ERR_INVALID_ARG;
+  if (n == 0) return PKV_OK;
+  if (!pool || !src || !dst || !aligned(pool, 16)) return PKV_ERR_INVALID_ARG;
+  std::vector<char> is_src(static_cast<size_t>(N), 0), is_dst(static_cast<size_t>(N), 0);
+  for (int32_t i = 0; i < n; ++i) {
+    if (src[i] < 0 || src[i] >= N || dst[i] < 0 || dst[i] >= N || src[i] == dst[i]) return PKV_ERR_INVALID_ARG;
+    if (is_dst[dst[i]]) return PKV_ERR_INVALID_ARG;        // two copies into one page
+    is_src[src[i]] = 1;
+    is_dst[dst[i]] = 1;
+  }
+  for (int32_t i = 0; i < n; ++i)
+    if (is_src[dst[i]]) return PKV_ERR_INVALID_ARG;        // a page both read and written
+  const int64_t words = static_cast<int64_t>(page_bytes / 16);
+  const uint32_t chunks = static_cast<uint32_t>(std::min<int64_t>(64, (words + kThreads - 1) / kThreads));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t at = 0; at < n; at += kCopyMax) {
+    PageCopies pc;
+    pc.n = std::min(n - at, kCopyMax);
+    for (int32_t i = 0; i < pc.n; ++i) {
+      pc.src[i] = src[at + i];
+      pc.dst[i] = dst[at + i];
+    }
+    hipLaunchKernelGGL(copy_pages_kernel, dim3(static_cast<uint32_t>(pc.n), chunks), dim3(kThreads), 0, s,
+                       static_cast<uint4*>(pool), words, pc);
+    if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
+  }
+  return PKV_OK;
 }
 
 int pkv_block_table_patch(int32_t* block_table, int32_t B, int32_t max_pages, const int32_t* rows,

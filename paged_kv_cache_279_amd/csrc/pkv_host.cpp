@@ -20,12 +20,20 @@
 
 #include "pkv.h"
 
+struct pkv_cache_entry {
+  std::vector<int32_t> pages;
+  int32_t n_tokens = 0;
+  uint64_t last_use = 0;                         // allocator clock at the last insert / lookup
+};
+
 struct pkv_allocator {
   int32_t num_pages = 0;
   int32_t page_size = 0;
   std::deque<int32_t> free_list;                 // FIFO: pop front, push back
-  std::vector<int32_t> refcount;                 // per page
+  std::vector<int32_t> refcount;                 // per page: tables + cache entries holding it
   std::unordered_map<int32_t, std::vector<int32_t>> tables;
+  std::unordered_map<uint64_t, pkv_cache_entry> cache;   // prefix cache
+  uint64_t clock = 0;
   mutable std::mutex mu;
 };
 
@@ -37,6 +45,49 @@ void write_row(const std::vector<int32_t>& pages, int32_t* row, int32_t max_page
   if (!row) return;
   const int32_t n = static_cast<int32_t>(pages.size());
   for (int32_t j = 0; j < max_pages; ++j) row[j] = j < n ? pages[j] : -1;
+}
+
+void release(pkv_allocator* a, const std::vector<int32_t>& pages) {
+  for (int32_t p : pages) {
+    if (--a->refcount[p] == 0) a->free_list.push_back(p);
+  }
+}
+
+// Prefix-cache eviction: drop least recently used entries until `need` pages
+// are free, if dropping every entry would free enough (pages held only by the
+// cache); otherwise change nothing. Callers hold the lock.
+bool make_room(pkv_allocator* a, int64_t need) {
+  if (need <= static_cast<int64_t>(a->free_list.size())) return true;
+  std::unordered_map<int32_t, int32_t> held;
+  for (const auto& kv : a->cache)
+    for (int32_t p : kv.second.pages) held[p] += 1;
+  int64_t freeable = 0;
+  for (const auto& kv : held)
+    if (a->refcount[kv.first] == kv.second) freeable += 1;
+  if (need > static_cast<int64_t>(a->free_list.size()) + freeable) return false;
+  std::vector<std::pair<uint64_t, uint64_t>> order;   // (last use, key)
+  order.reserve(a->cache.size());
+  for (const auto& kv : a->cache) order.emplace_back(kv.second.last_use, kv.first);
+  std::sort(order.begin(), order.end());
+  for (const auto& o : order) {
+    if (need <= static_cast<int64_t>(a->free_list.size())) break;
+    auto it = a->cache.find(o.second);
+    release(a, it->second.pages);
+    a->cache.erase(it);
+  }
+  return true;
+}
+
+// Grow `seq`'s table to `want` pages from the front of the free list (room
+// already made). Callers hold the lock.
+void grow(pkv_allocator* a, int32_t seq, int64_t want) {
+  std::vector<int32_t>& tab = a->tables[seq];
+  while (static_cast<int64_t>(tab.size()) < want) {
+    const int32_t p = a->free_list.front();
+    a->free_list.pop_front();
+    a->refcount[p] = 1;
+    tab.push_back(p);
+  }
 }
 
 }  // namespace
@@ -52,6 +103,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_WORKSPACE_TOO_SMALL: return "PKV_ERR_WORKSPACE_TOO_SMALL";
     case PKV_ERR_HIP: return "PKV_ERR_HIP";
     case PKV_ERR_INVALID_TABLE: return "PKV_ERR_INVALID_TABLE";
+    case PKV_ERR_NOT_FOUND: return "PKV_ERR_NOT_FOUND";
     default: return "PKV_ERR_UNKNOWN";
   }
 }
@@ -102,18 +154,9 @@ int pkv_alloc_reserve_batch(pkv_allocator* a, int32_t B, const int32_t* seqs, co
     if (block_table && std::max(want, have) > max_pages) return PKV_ERR_INVALID_ARG;
     need_total += std::max<int64_t>(0, want - have);
   }
-  if (need_total > static_cast<int64_t>(a->free_list.size())) return PKV_ERR_OUT_OF_PAGES;
+  if (!make_room(a, need_total)) return PKV_ERR_OUT_OF_PAGES;
   // commit: pages leave the free list in batch order
-  for (int32_t i = 0; i < B; ++i) {
-    const int64_t want = pages_for(n_tokens[i], a->page_size);
-    std::vector<int32_t>& tab = a->tables[seqs[i]];
-    while (static_cast<int64_t>(tab.size()) < want) {
-      const int32_t p = a->free_list.front();
-      a->free_list.pop_front();
-      a->refcount[p] = 1;
-      tab.push_back(p);
-    }
-  }
+  for (int32_t i = 0; i < B; ++i) grow(a, seqs[i], pages_for(n_tokens[i], a->page_size));
   if (block_table) {
     for (int32_t i = 0; i < B; ++i)
       write_row(a->tables[seqs[i]], block_table + static_cast<int64_t>(i) * max_pages, max_pages);
@@ -154,10 +197,103 @@ int pkv_alloc_free(pkv_allocator* a, int32_t seq) {
   std::lock_guard<std::mutex> lock(a->mu);
   auto tab = a->tables.find(seq);
   if (tab == a->tables.end()) return PKV_OK;
-  for (int32_t p : tab->second) {
-    if (--a->refcount[p] == 0) a->free_list.push_back(p);
-  }
+  release(a, tab->second);
   a->tables.erase(tab);
+  return PKV_OK;
+}
+
+int pkv_alloc_cache_insert(pkv_allocator* a, uint64_t key, int32_t seq, int32_t n_tokens) {
+  if (!a || n_tokens <= 0) return PKV_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(a->mu);
+  auto tab = a->tables.find(seq);
+  const int64_t n_pages = pages_for(n_tokens, a->page_size);
+  if (tab == a->tables.end() || n_pages > static_cast<int64_t>(tab->second.size())) return PKV_ERR_INVALID_ARG;
+  auto it = a->cache.find(key);
+  if (it != a->cache.end()) {
+    it->second.last_use = ++a->clock;
+    return PKV_OK;
+  }
+  pkv_cache_entry e;
+  e.pages.assign(tab->second.begin(), tab->second.begin() + n_pages);
+  for (int32_t p : e.pages) a->refcount[p] += 1;
+  e.n_tokens = n_tokens;
+  e.last_use = ++a->clock;
+  a->cache.emplace(key, std::move(e));
+  return PKV_OK;
+}
+
+int pkv_alloc_cache_lookup(pkv_allocator* a, uint64_t key, int32_t* pages, int32_t max_pages, int32_t* n_pages,
+                           int32_t* n_tokens) {
+  if (!a || max_pages < 0 || (max_pages > 0 && !pages)) return PKV_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(a->mu);
+  auto it = a->cache.find(key);
+  if (it == a->cache.end()) return PKV_ERR_NOT_FOUND;
+  const pkv_cache_entry& e = it->second;
+  if (pages && static_cast<int64_t>(e.pages.size()) > max_pages) return PKV_ERR_INVALID_ARG;
+  it->second.last_use = ++a->clock;
+  if (pages) std::copy(e.pages.begin(), e.pages.end(), pages);
+  if (n_pages) *n_pages = static_cast<int32_t>(e.pages.size());
+  if (n_tokens) *n_tokens = e.n_tokens;
+  return PKV_OK;
+}
+
+int pkv_alloc_cache_evict(pkv_allocator* a, uint64_t key) {
+  if (!a) return PKV_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(a->mu);
+  auto it = a->cache.find(key);
+  if (it == a->cache.end()) return PKV_OK;
+  release(a, it->second.pages);
+  a->cache.erase(it);
+  return PKV_OK;
+}
+
+int32_t pkv_alloc_cache_entries(const pkv_allocator* a) {
+  if (!a) return -1;
+  std::lock_guard<std::mutex> lock(a->mu);
+  return static_cast<int32_t>(a->cache.size());
+}
+
+int pkv_alloc_prepare_append(pkv_allocator* a, int32_t B, const int32_t* seqs, const int32_t* pos,
+                             int32_t* copy_src, int32_t* copy_dst, int32_t* n_copies, int32_t* block_table,
+                             int32_t max_pages) {
+  if (!a || B < 0 || (B > 0 && (!seqs || !pos || !copy_src || !copy_dst)) || !n_copies) return PKV_ERR_INVALID_ARG;
+  if (block_table && max_pages < 0) return PKV_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lock(a->mu);
+  // plan with the counts as they stand: new pages to grow into, plus one per shared page written
+  int64_t need = 0;
+  std::unordered_set<int32_t> in_batch;
+  for (int32_t i = 0; i < B; ++i) {
+    if (seqs[i] < 0 || pos[i] < 0 || !in_batch.insert(seqs[i]).second) return PKV_ERR_INVALID_ARG;
+    auto tab = a->tables.find(seqs[i]);
+    const int64_t have = tab == a->tables.end() ? 0 : static_cast<int64_t>(tab->second.size());
+    const int64_t j = pos[i] / a->page_size;
+    if (block_table && std::max(j + 1, have) > max_pages) return PKV_ERR_INVALID_ARG;
+    need += std::max<int64_t>(0, j + 1 - have);
+    if (j < have && a->refcount[tab->second[j]] > 1) need += 1;
+  }
+  if (!make_room(a, need)) return PKV_ERR_OUT_OF_PAGES;
+  int32_t n = 0;
+  for (int32_t i = 0; i < B; ++i) {
+    const int64_t j = pos[i] / a->page_size;
+    grow(a, seqs[i], j + 1);
+    std::vector<int32_t>& tab = a->tables[seqs[i]];
+    const int32_t old = tab[j];
+    if (a->refcount[old] > 1) {
+      const int32_t fresh = a->free_list.front();
+      a->free_list.pop_front();
+      a->refcount[fresh] = 1;
+      a->refcount[old] -= 1;
+      tab[j] = fresh;
+      copy_src[n] = old;
+      copy_dst[n] = fresh;
+      ++n;
+    }
+  }
+  *n_copies = n;
+  if (block_table) {
+    for (int32_t i = 0; i < B; ++i)
+      write_row(a->tables[seqs[i]], block_table + static_cast<int64_t>(i) * max_pages, max_pages);
+  }
   return PKV_OK;
 }
 
