@@ -31,6 +31,7 @@ from .paged_decode import (  # noqa: F401
     gather_sequence,
     decode_attention,
     decode_attention_multi,
+    decode_attention_window,
     kv_append,
     decode_partials,
     lse_merge,

@@ -197,6 +197,48 @@ def decode_attention(q, k_pool, v_pool, block_table, lens, scale, page_size):
     return out
 
 
+def decode_attention_window(q, k_pool, v_pool, ring_table, lens, window, scale, page_size):
+    """Decode attention over the last ``window`` tokens, pages kept in a ring.
+
+    The static, fixed-capacity variant of the KV cache (hotelren §3.1: a ring
+    buffer of preallocated storage that overwrites its oldest entries) expressed
+    through the page table: sequence ``b`` owns ``R = ring_table.shape[1]``
+    pages, and logical page ``j`` lives in page ``ring_table[b][j % R]``, so a
+    new page overwrites the one ``R`` pages older. Query ``b`` attends tokens
+    ``max(0, lens[b] - window) .. lens[b] - 1`` (the window must fit in the
+    ring: ``window <= (R - 1) * P + 1``); token ``t`` is slot ``t % P`` of page
+    ``ring_table[b][(t // P) % R]``. Otherwise exactly ``decode_attention``.
+    Returns float64 ``[B][Hq][D]``; ``lens[b] == 0`` gives zeros.
+    """
+    b_count, hq, d = q.shape
+    n, hkv, p, dim = k_pool.shape
+    ring = np.asarray(ring_table, dtype=np.int64)
+    r = ring.shape[1]
+    if window <= 0 or window > (r - 1) * page_size + 1:
+        raise ValueError("the window must fit in the ring")
+    g = _check_heads(hq, hkv)
+    s64 = _scale64(scale)
+    out = np.zeros((b_count, hq, d), dtype=np.float64)
+    for b in range(b_count):
+        length = int(lens[b])
+        if length == 0:
+            continue
+        t = np.arange(max(0, length - window), length)
+        pages = ring[b][(t // page_size) % r]
+        slots = (t % page_size)[:, None]
+        for kvh in range(hkv):
+            keys = _tiles(k_pool)[pages[:, None], kvh, k_tile_offset(slots, np.arange(dim)[None, :], p, dim)]
+            vals = _tiles(v_pool)[pages[:, None], kvh, v_tile_offset(slots, np.arange(dim)[None, :], p, dim)]
+            keys = keys.astype(np.float64)
+            vals = vals.astype(np.float64)
+            for i in range(g):
+                h = kvh * g + i
+                sc = s64 * (keys @ q[b, h].astype(np.float64))
+                w = np.exp(sc - sc.max())
+                out[b, h] = (w @ vals) / w.sum()
+    return out
+
+
 def decode_attention_multi(q, k_pool, v_pool, block_table, lens, scale, page_size):
     """Attention for the last ``k`` tokens of every sequence at once.
 
