@@ -276,6 +276,48 @@ int pkv_paged_decode_attention_multi(void* out, const void* q, const void* k_poo
                                      int32_t max_context, float scale, int32_t partition_tokens, void* workspace,
                                      size_t workspace_bytes, void* stream);
 
+/*
+ * pkv_paged_decode_attention_window -- decode over the last `window` tokens
+ * of every sequence, its pages kept in a ring: the fixed-capacity cache that
+ * overwrites its oldest entries (hotelren §3.1), through the page table.
+ *
+ * Sequence b owns ring_pages pages, row b of ring_table; its logical page j
+ * (tokens j * P .. j * P + P - 1) lives in page ring_table[b][j % ring_pages],
+ * so a new page overwrites the one ring_pages pages older. Query b attends
+ * tokens max(0, lens[b] - window) .. lens[b] - 1 only, with softmax, scaling
+ * and layout as in pkv_paged_decode_attention; token t is slot t % P of page
+ * ring_table[b][(t / P) % ring_pages]. Pages of the ring that the window does
+ * not reach are never read; slots of a reached page that lie before the window
+ * are read and masked (their values never reach the output, NaN included).
+ *
+ *   ring_table   : int32 [B][ring_pages] device, read; every entry the window
+ *                  reaches must be in [0, N) (else the row is NaN).
+ *   ring_pages   : >= 1; window <= (ring_pages - 1) * P + 1, so that the pages
+ *                  a window touches are distinct ring entries.
+ *   lens[b]      : tokens of the sequence so far (any length up to
+ *                  2^31 - 65; negative or longer makes the row NaN); 0 gives a
+ *                  zero row.
+ *   window       : >= 1 tokens attended.
+ *   k_new, v_new : both NULL, or both fp16 [B][Hkv][D]: append each
+ *                  sequence's new token at position lens[b] - 1 (into its
+ *                  ring page) in the same launch, as
+ *                  pkv_append_paged_decode_attention does.
+ *   partition_tokens: 0 = one workgroup per (sequence, KV head); > 0 = the
+ *                  split path over the window's blocks, workspace from
+ *                  pkv_decode_workspace_bytes(B, Hq, D, window,
+ *                  partition_tokens, ...).
+ * Other arguments as pkv_paged_decode_attention.
+ * Errors: PKV_ERR_INVALID_ARG (window <= 0, ring_pages <= 0, a window that
+ * does not fit the ring, k_new without v_new, and the checks of
+ * pkv_paged_decode_attention); PKV_ERR_UNSUPPORTED, PKV_ERR_WORKSPACE_TOO_SMALL
+ * and PKV_ERR_HIP as there.
+ */
+int pkv_paged_decode_attention_window(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                                      void* v_pool, const int32_t* ring_table, int32_t ring_pages, const int32_t* lens,
+                                      int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                                      int32_t window, float scale, int32_t partition_tokens, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Key-only int8 pages                                                       */
 /* ------------------------------------------------------------------------ */

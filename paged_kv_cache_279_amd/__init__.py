@@ -28,6 +28,7 @@ from .binding import (  # noqa: F401
     paged_decode_attention_k8,
     paged_decode_attention_multi,
     paged_decode_attention_shared_prefix,
+    paged_decode_attention_window,
     probe_stream_read,
     status_string,
     validate_tables,

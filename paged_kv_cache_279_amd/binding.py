@@ -40,6 +40,9 @@ _SIGNATURES = {
     "pkv_paged_decode_attention_multi": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                                         _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _vp,
                                                         ctypes.c_size_t, _vp]),
+    "pkv_paged_decode_attention_window": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                                         _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _vp,
+                                                         ctypes.c_size_t, _vp]),
     "pkv_kv_append_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_paged_decode_attention_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                                      _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _i32, _vp,
@@ -210,6 +213,38 @@ def paged_decode_attention_multi(q, k_pool, v_pool, block_table, lens, max_conte
         B, nq, Hq, Hkv, D, P, N, int(max_context), float(scale), int(partition_tokens), ws_ptr, ws_len,
         _stream(stream))
     _check(rc, "pkv_paged_decode_attention_multi")
+    return out
+
+
+def paged_decode_attention_window(q, k_pool, v_pool, ring_table, lens, window, scale, partition_tokens=0,
+                                  k_new=None, v_new=None, out=None, workspace=None, stream=None):
+    """pkv_paged_decode_attention_window: attend the last ``window`` tokens of each sequence,
+    logical page j in ``ring_table[b][j % ring_pages]``; with k_new / v_new the new token is
+    appended at lens[b] - 1 in the same launch. Returns ``out`` [B][Hq][D]."""
+    B, Hq, D = q.shape
+    N, Hkv, P, Dk = k_pool.shape
+    _, ring_pages = ring_table.shape
+    if Dk != D or tuple(v_pool.shape) != tuple(k_pool.shape) or ring_table.shape[0] != B or tuple(lens.shape) != (B,):
+        raise ValueError("shape mismatch")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None and (tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D)):
+        raise ValueError("k_new / v_new must be [B][Hkv][D]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
+    ws_bytes = decode_workspace_bytes(B, Hq, D, int(window), partition_tokens)
+    if workspace is None and ws_bytes > 0:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    kn = _dev_ptr(k_new, torch.float16, "k_new") if k_new is not None else ctypes.c_void_p(0)
+    vn = _dev_ptr(v_new, torch.float16, "v_new") if v_new is not None else ctypes.c_void_p(0)
+    rc = lib().pkv_paged_decode_attention_window(
+        _dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"), kn, vn,
+        _dev_ptr(k_pool, torch.float16, "k_pool"), _dev_ptr(v_pool, torch.float16, "v_pool"),
+        _dev_ptr(ring_table, torch.int32, "ring_table"), ring_pages, _dev_ptr(lens, torch.int32, "lens"),
+        B, Hq, Hkv, D, P, N, int(window), float(scale), int(partition_tokens), ws_ptr, ws_len, _stream(stream))
+    _check(rc, "pkv_paged_decode_attention_window")
     return out
 
 

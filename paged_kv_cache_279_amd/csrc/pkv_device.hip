@@ -83,6 +83,8 @@ constexpr int32_t kMaxPartitions = 1024;   // partial slots per (sequence, head)
 #define PKV_MAX_FLAT_BATCH 4096
 #endif
 constexpr int32_t kMaxFlatBatch = PKV_MAX_FLAT_BATCH;    // sequences per split call (LDS prefix sums)
+// sliding window: longest sequence (its token positions plus a block stay in int32)
+constexpr int32_t kWindowMaxLen = 0x7fffffff - 64;
 // Online-softmax rescaling is deferred until a head's block maximum exceeds
 // the running reference by this much (base-2 exponent units): probabilities
 // then stay below 2^8 and fp16/fp32 ranges are never approached.
@@ -119,6 +121,8 @@ struct DecodeParams {
   int32_t prefix_tokens;     // shared leading tokens (0 = none), multiple of P
   int32_t min_len;           // split mode: shorter sequences are invalid (NaN rows)
   int32_t nq;                // queries per sequence (1 = decode; > 1: the chunk of the last nq tokens)
+  int32_t ring;              // sliding window: pages per sequence in its ring (logical page j -> entry j % ring)
+  int32_t window;            // sliding window: tokens attended (the last `window`)
   int32_t n_tiles;           // 16-row query tiles per KV head that read the prefix (0 = none)
   int32_t n_flat_wgs;        // workgroups of the balanced split schedule
   int32_t min_piece;         // minimum blocks per piece
@@ -388,6 +392,10 @@ __device__ __forceinline__ void set_priority(int32_t remaining, int32_t quota) {
 // the codes widen exactly to fp16 for the score MFMA and each score is then
 // multiplied by its token's scale (s_t = scale_t * <codes_t, q>).
 //
+// kWin: the pages of a sequence form a ring (logical page j is table entry
+// j % ring) and tokens below win_lo, the window start, are masked, scores and
+// values (start <= win_lo < start + 16).
+//
 // kMQ: the column of lane (col, quad) may see tokens up to clim only (the
 // causal bound of its query within a chunk); clim_min is the smallest bound of
 // the wave, so blocks wholly below it skip the mask.
@@ -397,11 +405,11 @@ __device__ __forceinline__ void set_priority(int32_t remaining, int32_t quota) {
 // other loads, patches them into the block's registers before use, and writes
 // them to the pool from there. No other wave reads that row, so the write
 // needs no ordering against the loads.
-template <int D, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ>
+template <int D, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ, bool kWin>
 __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32_t* bt_row, int32_t kvh,
                                               int32_t start, int32_t end, int32_t first, int32_t stride,
                                               int32_t quota, int32_t after, const NewToken& nt,
-                                              int32_t clim, int32_t clim_min,
+                                              int32_t clim, int32_t clim_min, int32_t win_lo,
                                               const half8_t (&qb)[D / 32], WaveState<D>& st, int lane) {
   constexpr int KL = D / 32;           // 16-byte loads per lane per block, for K and for V
   constexpr int NT = D / 16;           // 16-dim output tiles
@@ -425,7 +433,9 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     int32_t page = 0;
     bool bad = false;
     if (blk < nblocks) {
-      page = bt_row[(start + blk * kBlk) >> p.p_shift];
+      int32_t entry = (start + blk * kBlk) >> p.p_shift;
+      if constexpr (kWin) entry %= p.ring;
+      page = bt_row[entry];
       bad = page < 0 || page >= p.N;
     }
     if (__builtin_amdgcn_ballot_w64(bad) != 0) st.bad_page = true;   // the row becomes NaN later
@@ -632,6 +642,23 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
 #pragma unroll
       for (int j = 0; j < KL; ++j) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kr[j]), qb[j], s, 0, 0, 0);
     }
+    if constexpr (kWin) {
+      if (t0 < win_lo) {
+        // tokens before the window: masked scores, zeroed values (never 0 * NaN)
+        const int32_t tq = t0 + 4 * quad;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) s[i] = tq + i >= win_lo ? s[i] : kNegInf();
+        const uint32_t m0 = (tq + 0 >= win_lo ? 0x0000FFFFu : 0u) | (tq + 1 >= win_lo ? 0xFFFF0000u : 0u);
+        const uint32_t m1 = (tq + 2 >= win_lo ? 0x0000FFFFu : 0u) | (tq + 3 >= win_lo ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+          vr[j].x &= m0;
+          vr[j].y &= m1;
+          vr[j].z &= m0;
+          vr[j].w &= m1;
+        }
+      }
+    }
     if constexpr (kMQ) {
       if (t0 + kBlk - 1 > clim_min) {
 #pragma unroll
@@ -749,11 +776,12 @@ struct KernelShared {
 // and unnormalised output. Callers must be workgroup-uniform.
 // kMQ: column c is query c / g of the chunk (g = mq_g heads per query); query
 // i may see tokens up to mq_last0 + i.
-template <int D, int NC, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ = false, class RowFn, class EmitFn>
+template <int D, int NC, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ = false, bool kWin = false, class RowFn,
+          class EmitFn>
 __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>& sh, const int32_t* bt_row,
                                           int32_t kvh, int32_t start, int32_t end, int32_t quota, int32_t after,
                                           const NewToken& nt, RowFn qrow, EmitFn emit, int lane, int wave,
-                                          int32_t mq_last0 = 0, int32_t mq_g = 1) {
+                                          int32_t mq_last0 = 0, int32_t mq_g = 1, int32_t lo = 0) {
   constexpr int KL = D / 32;
   constexpr int NT = D / 16;
   const int col = lane & 15;
@@ -774,8 +802,8 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
     const int32_t qi = col / mq_g;
     clim = qi < p.nq ? mq_last0 + qi : 0x7fffffff;
   }
-  stream_blocks<D, kPolicy, kAppend, kK8, kMQ>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, nt, clim,
-                                               mq_last0, qb, st, lane);
+  stream_blocks<D, kPolicy, kAppend, kK8, kMQ, kWin>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, nt,
+                                                     clim, mq_last0, lo, qb, st, lane);
   // per-column denominators of this wave: sum the 4 quads of column col
   st.l_part += __shfl_xor(st.l_part, 16);
   st.l_part += __shfl_xor(st.l_part, 32);
@@ -835,9 +863,10 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
 // writes slot kvh * (NT + B + 2 Wk) + s + j, private segments numbered after
 // NT + Wk: walking a list in order increases s or j (or both) by one each
 // step, so the slots are distinct; each slot holds 16 columns.
-template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ>
+template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ, bool WIN = false>
 __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodeParams p) {
   static_assert(!MQ || (!FUSED && !K8), "chunks of queries: fp16 keys, no fused append");
+  static_assert(!WIN || (!MQ && !K8), "sliding window: fp16 keys, single queries");
   static_assert(D % 32 == 0 && G >= 1 && G <= 16, "shape");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -871,7 +900,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
     const int32_t kvh = blockIdx.x % p.Hkv;
     const int32_t b = blockIdx.x / p.Hkv;
     const int32_t L = p.lens[b];
-    const bool bad_len = L < 0 || L > p.max_context || L > (p.max_pages << p.p_shift);
+    const bool bad_len = L < 0 || L > p.max_context || (!WIN && L > (p.max_pages << p.p_shift));
     const int32_t Lc = bad_len ? 0 : L;
     const int64_t head_row0 = (int64_t)b * p.Hq + (int64_t)kvh * G;
     if (Lc == 0) {
@@ -880,17 +909,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
       return;
     }
     const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
+    // sliding window: attend [lo, L), streamed from the 16-aligned block below lo
+    const int32_t lo = WIN ? max(0, Lc - p.window) : 0;
+    const int32_t s0 = lo & ~(kBlk - 1);
     NewToken nt{-1, 0, nullptr, nullptr};
     if constexpr (FUSED) {
       const int64_t src = ((int64_t)b * p.Hkv + kvh) * D;
-      nt = NewToken{(Lc - 1) >> 4, (Lc - 1) & 15, p.k_new + src, p.v_new + src};
+      nt = NewToken{(Lc - 1 - s0) >> 4, (Lc - 1) & 15, p.k_new + src, p.v_new + src};
     }
-    run_range<D, G, kKvLoadPolicy, FUSED, K8>(p, sh, bt_row, kvh, 0, Lc, 0, 0, nt, [&](int c) -> int64_t { return head_row0 + c; },
-                    [&](int c, int d, float, float Ls, float O) {
-                      const float r = Ls > 0.f ? O / Ls : (Ls == 0.f ? 0.f : __builtin_nanf(""));
-                      p.out[(head_row0 + c) * D + d] = (half_t)(Ls != Ls ? __builtin_nanf("") : r);
-                    },
-                    lane, wave);
+    run_range<D, G, kKvLoadPolicy, FUSED, K8, false, WIN>(
+        p, sh, bt_row, kvh, s0, Lc, 0, 0, nt, [&](int c) -> int64_t { return head_row0 + c; },
+        [&](int c, int d, float, float Ls, float O) {
+          const float r = Ls > 0.f ? O / Ls : (Ls == 0.f ? 0.f : __builtin_nanf(""));
+          p.out[(head_row0 + c) * D + d] = (half_t)(Ls != Ls ? __builtin_nanf("") : r);
+        },
+        lane, wave, 0, 1, lo);
   } else {
     int32_t* sm_cum = smem.cum;
     int32_t* sm_len = smem.len;
@@ -898,11 +931,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
     const int32_t wg = blockIdx.x;
     const int32_t per = (p.B + kThreads - 1) / kThreads;
     const int32_t b0 = threadIdx.x * per;
+    // first streamed token of a sequence: after the shared prefix, or the
+    // 16-aligned block below the window start
+    auto first_token = [&](int32_t L) -> int32_t {
+      return WIN ? max(0, L - p.window) & ~(kBlk - 1) : p.prefix_tokens;
+    };
     auto priv_blocks = [&](int32_t bb) -> int32_t {
       const int32_t L = p.lens[bb];
       sm_len[bb] = L;
-      const bool bad = L < p.min_len || L > p.max_context || L > (p.max_pages << p.p_shift);
-      return bad ? 0 : (L - p.prefix_tokens + kBlk - 1) / kBlk;
+      const bool bad = L < p.min_len || L > p.max_context || (!WIN && L > (p.max_pages << p.p_shift));
+      return bad ? 0 : (L - first_token(L) + kBlk - 1) / kBlk;
     };
     int32_t local = 0;
     for (int32_t i = 0; i < per; ++i) {
@@ -996,8 +1034,9 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
         const int32_t blk0 = g - seg_first;
         const int32_t piece_n = min(g1 - g, seg_n - blk0);
         const int32_t L = sm_len[b];
-        const int32_t start = p.prefix_tokens + blk0 * kBlk;
-        const int32_t end = min(L, p.prefix_tokens + (blk0 + piece_n) * kBlk);
+        const int32_t s0 = first_token(L);
+        const int32_t start = s0 + blk0 * kBlk;
+        const int32_t end = min(L, s0 + (blk0 + piece_n) * kBlk);
         const int64_t head_row0 = (int64_t)b * p.Hq + (int64_t)kvh * G;
         const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
         NewToken nt{-1, 0, nullptr, nullptr};
@@ -1027,10 +1066,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
               },
               emit, lane, wave, L - p.nq, G);
         } else {
-          run_range<D, G, kKvLoadPolicy, FUSED, K8>(p, smem.tile.priv, bt_row, kvh, start, end, quota,
-                                                    after + g1 - g - piece_n, nt,
-                                                    [&](int c) -> int64_t { return c < G ? head_row0 + c : -1; },
-                                                    emit, lane, wave);
+          run_range<D, G, kKvLoadPolicy, FUSED, K8, false, WIN>(
+              p, smem.tile.priv, bt_row, kvh, start, end, quota, after + g1 - g - piece_n, nt,
+              [&](int c) -> int64_t { return c < G ? head_row0 + c : -1; }, emit, lane, wave, 0, 1,
+              WIN ? max(0, L - p.window) : 0);
         }
         g += piece_n;
       }
@@ -1072,7 +1111,7 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
   const int32_t hg = h % G;
   const int d = threadIdx.x;
   const int32_t L = p.lens[b];
-  const bool bad_len = L < p.min_len || L > p.max_context || L > (p.max_pages << p.p_shift);
+  const bool bad_len = L < p.min_len || L > p.max_context || (p.ring == 0 && L > (p.max_pages << p.p_shift));
   const int32_t Qv = p.flat_hdr[1];
   const int32_t Qp = p.flat_hdr[2];
   const int32_t Wk = p.n_flat_wgs / p.Hkv;
@@ -1215,28 +1254,28 @@ int64_t max_slots(int32_t B, int32_t Hq, bool prefix) {
          2 * (static_cast<int64_t>(PKV_FLAT_WORKGROUPS) + Hq);
 }
 
-template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ>
+template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ, bool WIN>
 hipError_t launch_partition(const DecodeParams& p, hipStream_t stream, int64_t grid) {
-  hipLaunchKernelGGL((decode_partition_kernel<D, G, SPLIT, FUSED, K8, MQ>), dim3(static_cast<uint32_t>(grid)),
+  hipLaunchKernelGGL((decode_partition_kernel<D, G, SPLIT, FUSED, K8, MQ, WIN>), dim3(static_cast<uint32_t>(grid)),
                      dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool SPLIT, bool FUSED, bool K8, bool MQ = false>
+template <int D, bool SPLIT, bool FUSED, bool K8, bool MQ = false, bool WIN = false>
 hipError_t dispatch_g(int G, const DecodeParams& p, hipStream_t s, int64_t grid) {
   switch (G) {
-    case 1: return launch_partition<D, 1, SPLIT, FUSED, K8, MQ>(p, s, grid);
-    case 2: return launch_partition<D, 2, SPLIT, FUSED, K8, MQ>(p, s, grid);
-    case 4: return launch_partition<D, 4, SPLIT, FUSED, K8, MQ>(p, s, grid);
-    case 8: return launch_partition<D, 8, SPLIT, FUSED, K8, MQ>(p, s, grid);
-    default: return launch_partition<D, 16, SPLIT, FUSED, K8, MQ>(p, s, grid);
+    case 1: return launch_partition<D, 1, SPLIT, FUSED, K8, MQ, WIN>(p, s, grid);
+    case 2: return launch_partition<D, 2, SPLIT, FUSED, K8, MQ, WIN>(p, s, grid);
+    case 4: return launch_partition<D, 4, SPLIT, FUSED, K8, MQ, WIN>(p, s, grid);
+    case 8: return launch_partition<D, 8, SPLIT, FUSED, K8, MQ, WIN>(p, s, grid);
+    default: return launch_partition<D, 16, SPLIT, FUSED, K8, MQ, WIN>(p, s, grid);
   }
 }
 
-template <bool SPLIT, bool FUSED, bool K8, bool MQ = false>
+template <bool SPLIT, bool FUSED, bool K8, bool MQ = false, bool WIN = false>
 hipError_t dispatch_d(int D, int G, const DecodeParams& p, hipStream_t s, int64_t grid) {
-  return D == 64 ? dispatch_g<64, SPLIT, FUSED, K8, MQ>(G, p, s, grid)
-                 : dispatch_g<128, SPLIT, FUSED, K8, MQ>(G, p, s, grid);
+  return D == 64 ? dispatch_g<64, SPLIT, FUSED, K8, MQ, WIN>(G, p, s, grid)
+                 : dispatch_g<128, SPLIT, FUSED, K8, MQ, WIN>(G, p, s, grid);
 }
 
 int decode_common(void* out, const void* q, const void* k_new, const void* v_new, const void* k_pool,
@@ -1244,7 +1283,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
                   const int32_t* lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
                   int32_t max_context, float scale, int32_t partition_tokens, int32_t prefix_tokens,
                   void* workspace, size_t workspace_bytes, void* stream, bool fused, bool k8 = false,
-                  int32_t nq = 1) {
+                  int32_t nq = 1, int32_t window = 0) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || N <= 0 || max_pages <= 0 || max_context < 0 ||
       partition_tokens < 0 || prefix_tokens < 0)
     return PKV_ERR_INVALID_ARG;
@@ -1254,6 +1293,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   const int G = Hq / Hkv;
   if (nq < 1) return PKV_ERR_INVALID_ARG;
   if (nq > 1 && (fused || k8 || prefix_tokens > 0)) return PKV_ERR_INVALID_ARG;
+  if (window < 0 || (window > 0 && (nq > 1 || k8 || prefix_tokens > 0))) return PKV_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(nq) * G > 16) return PKV_ERR_UNSUPPORTED;     // one 16-column matrix-core tile
   if (static_cast<int64_t>(B) * nq * Hq > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
@@ -1261,7 +1301,11 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   if (p_shift < 0) return PKV_ERR_UNSUPPORTED;
   if (G != 1 && G != 2 && G != 4 && G != 8 && G != 16) return PKV_ERR_UNSUPPORTED;
   if (prefix_tokens % P != 0) return PKV_ERR_INVALID_ARG;       // shared pages hold prefix tokens only
-  if (static_cast<int64_t>(max_context) > (static_cast<int64_t>(max_pages) << p_shift)) return PKV_ERR_INVALID_ARG;
+  if (window == 0 && static_cast<int64_t>(max_context) > (static_cast<int64_t>(max_pages) << p_shift))
+    return PKV_ERR_INVALID_ARG;
+  // a ring of max_pages pages holds every page a window of this many tokens touches
+  if (window > 0 && static_cast<int64_t>(window) > (static_cast<int64_t>(max_pages) - 1) * P + 1)
+    return PKV_ERR_INVALID_ARG;
   Plan plan;
   const int rc = make_plan(B, Hq, Hkv, max_context, partition_tokens, prefix_tokens, &plan);
   if (rc != PKV_OK) return rc;
@@ -1303,6 +1347,8 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   // an appended token must land in a private page; each query of a chunk needs a token
   prm.min_len = max(prefix_tokens + (fused && prefix_tokens > 0 ? 1 : 0), nq > 1 ? nq : 0);
   prm.nq = nq;
+  prm.ring = window > 0 ? max_pages : 0;
+  prm.window = window;
   prm.n_tiles = plan.n_tiles;
   prm.n_flat_wgs = plan.n_flat_wgs;
   prm.min_piece = plan.min_piece;
@@ -1325,7 +1371,13 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   const int64_t grid = plan.grid;
   hipError_t e = hipSuccess;
   if (grid > 0) {
-    if (nq > 1)
+    if (window > 0 && fused)
+      e = plan.split ? dispatch_d<true, true, false, false, true>(D, G, prm, s, grid)
+                     : dispatch_d<false, true, false, false, true>(D, G, prm, s, grid);
+    else if (window > 0)
+      e = plan.split ? dispatch_d<true, false, false, false, true>(D, G, prm, s, grid)
+                     : dispatch_d<false, false, false, false, true>(D, G, prm, s, grid);
+    else if (nq > 1)
       e = plan.split ? dispatch_d<true, false, false, true>(D, G, prm, s, grid)
                      : dispatch_d<false, false, false, true>(D, G, prm, s, grid);
     else if (k8 && fused)
@@ -1552,6 +1604,19 @@ int pkv_paged_decode_attention_multi(void* out, const void* q, const void* k_poo
   return decode_common(out, q, nullptr, nullptr, k_pool, v_pool, nullptr, nullptr, block_table, max_pages, lens, B,
                        Hq, Hkv, D, P, N, max_context, scale, partition_tokens, 0, workspace, workspace_bytes, stream,
                        false, false, n_query);
+}
+
+int pkv_paged_decode_attention_window(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool,
+                                      void* v_pool, const int32_t* ring_table, int32_t ring_pages, const int32_t* lens,
+                                      int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                                      int32_t window, float scale, int32_t partition_tokens, void* workspace,
+                                      size_t workspace_bytes, void* stream) {
+  if ((k_new == nullptr) != (v_new == nullptr)) return PKV_ERR_INVALID_ARG;
+  if (window <= 0 || ring_pages <= 0) return PKV_ERR_INVALID_ARG;
+  const bool fused = k_new != nullptr;
+  return decode_common(out, q, k_new, v_new, k_pool, v_pool, k_pool, v_pool, ring_table, ring_pages, lens, B, Hq, Hkv,
+                       D, P, N, kWindowMaxLen, scale, partition_tokens, 0, workspace, workspace_bytes, stream, fused,
+                       false, 1, window);
 }
 
 int pkv_paged_decode_attention_shared_prefix(void* out, const void* q, const void* k_new, const void* v_new,

@@ -67,6 +67,29 @@ def test_decode_argument_checks_precede_any_launch(pkv, over, code):
     assert _decode(pkv, **over) == code
 
 
+def _window(pkv, **over):
+    a = dict(out=16, q=16, kn=0, vn=0, k_pool=16, v_pool=16, bt=16, ring=4, lens=16, B=1, Hq=4, Hkv=4, D=64, P=16,
+             N=8, window=49, scale=0.125, part=0, ws=0, ws_bytes=0)
+    a.update(over)
+    vp = ctypes.c_void_p
+    return pkv.lib().pkv_paged_decode_attention_window(
+        vp(a["out"]), vp(a["q"]), vp(a["kn"]), vp(a["vn"]), vp(a["k_pool"]), vp(a["v_pool"]), vp(a["bt"]), a["ring"],
+        vp(a["lens"]), a["B"], a["Hq"], a["Hkv"], a["D"], a["P"], a["N"], a["window"], a["scale"], a["part"],
+        vp(a["ws"]), a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(window=0), 1), (dict(window=-3), 1), (dict(ring=0), 1),
+    (dict(window=50), 1),                     # (ring - 1) * P + 1 = 49 is the largest window of 4 pages
+    (dict(ring=1, window=2), 1), (dict(kn=16), 1), (dict(vn=16), 1), (dict(kn=16, vn=8), 1),
+    (dict(D=96), 2), (dict(P=8), 2), (dict(Hq=12, Hkv=4), 2), (dict(part=24), 1), (dict(part=16, ws=0), 1),
+    (dict(part=16, ws=256, ws_bytes=8), 4), (dict(bt=2), 1), (dict(scale=float("nan")), 1),
+    (dict(B=0, out=0, q=0), 0), (dict(B=0, out=0, q=0, ring=1, window=1), 0),
+])
+def test_window_argument_checks_precede_any_launch(pkv, over, code):
+    assert _window(pkv, **over) == code
+
+
 def test_append_argument_checks(pkv):
     f = pkv.lib().pkv_kv_append
     vp = ctypes.c_void_p
