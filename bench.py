@@ -47,7 +47,8 @@ def parse_args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=3, help="workload number (3 = Llama-3-8B GQA, shared prefix)")
+    ap.add_argument("--workload", type=int, default=3,
+                    help="workload number (3 = Llama-3-8B GQA, shared prefix; 6 = 4096-token sliding window)")
     ap.add_argument("--page-size", type=int, default=None, help="page size (workload 5 only)")
     ap.add_argument("--layers", type=int, default=8, help="distinct layer pools per step (working set >> 256 MB MALL)")
     ap.add_argument("--partition", type=int, default=None, help="partition tokens (0 = unsplit)")
@@ -114,6 +115,20 @@ def algorithmic_bytes(lens, B, Hq, Hkv, D, P, shared_tokens, k_bytes=None, n_que
     return kv + q_out + new_kv + table, kv
 
 
+def algorithmic_bytes_window(lens, B, Hq, Hkv, D, P, window):
+    """Unique bytes of one sliding-window layer-step: the K/V of the last
+    ``window`` tokens of each sequence, q in, out, the new K/V read and
+    written, the ring entries the window touches and the lengths."""
+    lens = np.asarray(lens, dtype=np.int64)
+    lo = np.maximum(lens - window, 0)
+    kv_tokens = int((lens - lo).sum())
+    kv = kv_tokens * Hkv * 4 * D
+    q_out = 2 * B * Hq * D * 2
+    new_kv = B * Hkv * 2 * 2 * D * 2
+    table = int(((lens - 1) // P - lo // P + 1).clip(min=0).sum()) * 4 + B * 4
+    return kv + q_out + new_kv + table, kv
+
+
 def kernel_source_digest():
     """sha256 of the device source with comments and whitespace removed, so a
     comment edit does not orphan the committed counter summary."""
@@ -175,6 +190,14 @@ def streaming_peak(torch, pkv, nbytes, stream, n_buf=8, reps=4):
     return n_tiles * 4096 / us / 1e3, us, n_tiles * 4096
 
 
+def logical_table(ring, n_tokens, P):
+    """Block table of logical pages 0 .. ceil(n / P) - 1 of ring-paged
+    sequences (logical page j in ring entry j % R), for the oracle's append."""
+    R = ring.shape[1]
+    width = max(1, -(-int(n_tokens) // P))
+    return np.ascontiguousarray(ring[:, np.arange(width) % R])
+
+
 def cpu_baseline(w, seconds):
     """Time the oracle (as it stands) on layer 0 of the workload: append then
     decode for every sequence, repeated until ``seconds`` have passed."""
@@ -184,12 +207,16 @@ def cpu_baseline(w, seconds):
     lens = w.lens(step)
     passes = 0
     cores = max(1, min(16, len(os.sched_getaffinity(0))))
+    logical = logical_table(w.block_table, int(lens.max()), w.P) if w.window else w.block_table
     with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         while True:
-            kp, vp = oracle.kv_append(w.k_pool, w.v_pool, w.k_new[step], w.v_new[step], w.block_table,
+            kp, vp = oracle.kv_append(w.k_pool, w.v_pool, w.k_new[step], w.v_new[step], logical,
                                       w.pos(step), w.P)
-            oracle.decode_attention(w.q, kp, vp, w.block_table, lens, w.scale, w.P)
+            if w.window:
+                oracle.decode_attention_window(w.q, kp, vp, w.block_table, lens, w.window, w.scale, w.P)
+            else:
+                oracle.decode_attention(w.q, kp, vp, w.block_table, lens, w.scale, w.P)
             passes += 1
             if time.perf_counter() - t0 >= seconds:
                 break
@@ -235,6 +262,9 @@ def main():
     KQ = args.n_query
     fused = not args.separate_append and KQ == 1
     prefix_tokens = 0 if args.no_shared_prefix else w.shared_prefix_pages * w.P
+    W = w.window
+    if W and (k8 or KQ > 1 or not fused or args.graph):
+        raise SystemExit("the sliding-window workload runs fp16 keys, one query, the fused append, eagerly")
     if w.steps == 0:
         raise SystemExit("workload %d has no append; pick 2-5" % args.workload)
     if KQ > 1 and (prefix_tokens or k8 or args.graph):
@@ -242,13 +272,18 @@ def main():
     log("workload %s: B=%d Hq=%d Hkv=%d D=%d P=%d part=%d layers=%d fused=%s" % (w.name, B, Hq, Hkv, D, P, part, R,
                                                                                   fused))
 
-    # ---- a1: page allocator (host). Pages for every step are drawn on demand.
+    # ---- a1: page allocator (host). Pages for every step are drawn on demand;
+    # a sliding window holds a fixed ring of pages per sequence, reserved once.
     prefix_pages = w.shared_prefix_pages
     final_ctx = w.context.astype(np.int64) + KQ * max(total_steps, w.steps)   # tokens after the last step
-    need = prefix_pages + sum(-(-int(n) // P) - prefix_pages for n in final_ctx)
+    if W:
+        need = w.N
+        max_pages = w.max_pages
+    else:
+        need = prefix_pages + sum(-(-int(n) // P) - prefix_pages for n in final_ctx)
+        max_pages = max(-(-int(n) // P) for n in final_ctx)
     N = max(need, w.N)
     free_order = np.concatenate([w.perm, np.arange(w.N, N, dtype=np.int32)]).astype(np.int32)
-    max_pages = max(-(-int(n) // P) for n in final_ctx)
     alloc = pkv.PageAllocator(N, P, free_order=free_order)
     seqs = np.arange(B, dtype=np.int32)
     if prefix_pages:
@@ -258,7 +293,7 @@ def main():
             alloc.share_prefix(b, alloc.table(owner))
     bt_np = np.full((B, max_pages), -1, dtype=np.int32)          # the allocator's table (host)
     # the workload reserves pages for all of its own steps up front (page-sweep: 64 steps)
-    alloc.reserve_batch(seqs, w.context + w.steps, bt_np)
+    alloc.reserve_batch(seqs, np.full(B, max_pages * P) if W else w.context + w.steps, bt_np)
     assert np.array_equal(bt_np[:, :w.max_pages], w.block_table), "allocator layout differs from the workload"
 
     # ---- device buffers
@@ -319,7 +354,7 @@ def main():
         q_mq.normal_(generator=gen)
         out_mq = torch.empty((B, KQ, Hq, D), dtype=torch.float16, device=dev)
     max_context = int(final_ctx.max())
-    ws_bytes = pkv.decode_workspace_bytes(B, Hq, D, max_context, part, prefix_tokens)
+    ws_bytes = pkv.decode_workspace_bytes(B, Hq, D, W or max_context, part, prefix_tokens)
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
     torch.cuda.synchronize()
@@ -329,7 +364,10 @@ def main():
     scale = w.scale
 
     def layer_call(layer, lens, pos, kn, vn, s):
-        if KQ > 1:
+        if W:
+            pkv.paged_decode_attention_window(q, k_pools[layer], v_pools[layer], bt_dev, lens, W, scale, part,
+                                              k_new=kn, v_new=vn, out=out, workspace=workspace, stream=s)
+        elif KQ > 1:
             # pos [K][B], kn / vn [K][B][Hkv][D]: K appends, then the chunk's attention
             for i in range(KQ):
                 pkv.kv_append(kn[i], vn[i], k_pools[layer], v_pools[layer], bt_dev, pos[i], stream=s)
@@ -374,6 +412,8 @@ def main():
     def host_step(step):
         # a1: grow every sequence to hold this step's token; upload the table if it changed
         nonlocal last_bt, n_upload
+        if W:
+            return                       # the ring is fixed: nothing to allocate or upload
         t0 = time.perf_counter()
         alloc.reserve_batch(seqs, w.context + KQ * (step + 1), bt_np)
         changed = not np.array_equal(bt_np, last_bt)
@@ -414,6 +454,11 @@ def main():
                                                       (w.context + i).astype(np.int32), P)
         ref = oracle.decode_attention_multi(q_mq.cpu().numpy()[sample], kpool_full, vpool_full, bt0[sample],
                                             (w.context + KQ).astype(np.int32)[sample], scale, P)
+    elif W:
+        kp0, vp0 = oracle.kv_append(w.k_pool, w.v_pool, w.k_new[0], w.v_new[0],
+                                    logical_table(w.block_table, int(w.lens(0).max()), P), w.pos(0), P)
+        ref = oracle.decode_attention_window(w.q[sample], kp0, vp0, w.block_table[sample], w.lens(0)[sample], W,
+                                             scale, P)
     elif k8:
         kp0, vp0 = oracle.kv_append_k8(k8_layer0[:w.N], w.v_pool, w.k_new[0], w.v_new[0], w.block_table, w.pos(0), P)
         ref = oracle.decode_attention_k8(w.q[sample], kp0, vp0, w.block_table[sample], w.lens(0)[sample], scale, P)
@@ -525,8 +570,11 @@ def main():
     kv_steps = []
     for i in range(args.steps):
         step = args.warmup + i
-        tot, kv = algorithmic_bytes(w.context + KQ * (step + 1), B, Hq, Hkv, D, P, prefix_pages * P,
-                                    k_bytes=(D + 4) if k8 else None, n_query=KQ)
+        if W:
+            tot, kv = algorithmic_bytes_window(w.context + step + 1, B, Hq, Hkv, D, P, W)
+        else:
+            tot, kv = algorithmic_bytes(w.context + KQ * (step + 1), B, Hq, Hkv, D, P, prefix_pages * P,
+                                        k_bytes=(D + 4) if k8 else None, n_query=KQ)
         bytes_steps.append(tot)
         kv_steps.append(kv)
     bytes_per_call = float(np.mean(bytes_steps))
@@ -554,6 +602,8 @@ def main():
             "kv_dtype": "k int8 + fp32 scale per token and head, v f16" if k8 else "f16", "accumulate": "f32",
             "mean_context": float(np.mean(w.context + KQ * (args.warmup + 1 + (args.steps - 1) / 2))),
             "queries_per_sequence": KQ,
+            "window_tokens": W or None,
+            "ring_pages": max_pages if W else None,
             "shared_prefix_tokens": prefix_pages * P,
             "partition_tokens": part,
             "layers_per_step": R,
@@ -576,7 +626,8 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": ("%d appends + multi-query partition kernel + log-sum-exp reduce" % KQ) if KQ > 1 else
+            "kernel": "sliding-window partition kernel with fused append + log-sum-exp reduce" if W else
+                      ("%d appends + multi-query partition kernel + log-sum-exp reduce" % KQ) if KQ > 1 else
                       "paged decode call (%s%spartition kernel%s + log-sum-exp reduce)" % (
                           ("int8-key " if fused else "int8-key append + int8-key ") if k8 else "",
                           "shared-prefix + " if prefix_tokens else "", " with fused append" if fused else ""),

@@ -279,7 +279,7 @@ int pkv_paged_decode_attention_multi(void* out, const void* q, const void* k_poo
 /*
  * pkv_paged_decode_attention_window -- decode over the last `window` tokens
  * of every sequence, its pages kept in a ring: the fixed-capacity cache that
- * overwrites its oldest entries (hotelren §3.1), through the page table.
+ * overwrites its oldest entries (hotelren §3.2), through the page table.
  *
  * Sequence b owns ring_pages pages, row b of ring_table; its logical page j
  * (tokens j * P .. j * P + P - 1) lives in page ring_table[b][j % ring_pages],

@@ -200,7 +200,7 @@ def decode_attention(q, k_pool, v_pool, block_table, lens, scale, page_size):
 def decode_attention_window(q, k_pool, v_pool, ring_table, lens, window, scale, page_size):
     """Decode attention over the last ``window`` tokens, pages kept in a ring.
 
-    The static, fixed-capacity variant of the KV cache (hotelren §3.1: a ring
+    The static, fixed-capacity variant of the KV cache (hotelren §3.2: a ring
     buffer of preallocated storage that overwrites its oldest entries) expressed
     through the page table: sequence ``b`` owns ``R = ring_table.shape[1]``
     pages, and logical page ``j`` lives in page ``ring_table[b][j % R]``, so a

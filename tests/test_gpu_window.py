@@ -145,10 +145,11 @@ def test_window_invalid_rows_are_nan_and_others_unaffected(part):
     check_close(got[good], ref, "window valid rows")
 
 
-def test_window_full_size_sampled():
+@pytest.mark.parametrize("part", [0, 512])
+def test_window_full_size_sampled(part):
     """Llama-3-8B heads (32 query, 8 KV, D = 128), 16-token pages, a 4096-token
-    window in a ring of 257 pages, 32 sequences of 4 k .. 32 k tokens: the split
-    path as the decode benchmark runs it, checked on sampled sequences."""
+    window in a ring of 257 pages, 32 sequences of 4 k .. 32 k tokens: unsplit
+    as the decode benchmark runs it, and split; checked on sampled sequences."""
     D, Hq, Hkv, P, W = 128, 32, 8, 16, 4096
     R = (W - 1) // P + 1 + 1
     B = 32
@@ -157,9 +158,9 @@ def test_window_full_size_sampled():
     lens[:3] = [W - 1, W, 1]
     ring, kp, vp, q, _ = ring_case(2025, B, Hq, Hkv, D, P, R, lens, W)
     scale = 1.0 / math.sqrt(D)
-    say("window full size B=%d W=%d R=%d" % (B, W, R))
+    say("window full size B=%d W=%d R=%d part=%d" % (B, W, R, part))
     got = host(pkv().paged_decode_attention_window(dev(q), dev(kp), dev(vp), dev(ring), dev(lens), W, scale,
-                                                   512)).astype(np.float64)
+                                                   part)).astype(np.float64)
     sample = np.array([0, 1, 2, 7, 18, 31])
     ref = oracle.decode_attention_window(q[sample], kp, vp, ring[sample], lens[sample], W, scale, P)
     check_close(got[sample], ref, "window full size")

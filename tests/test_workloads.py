@@ -64,3 +64,14 @@ def test_poison_marks_only_unused_slots():
         assert np.all(np.isfinite(vals))
         assert np.all(np.isfinite(keys))
     assert np.isnan(k.astype(np.float32)).sum() == w.N * w.P * w.Hkv * w.D - sum(int(n) for n in lens) * w.Hkv * w.D
+
+
+def test_sliding_window_workload_ring():
+    w = workload(6, batch=4)
+    assert (w.Hq, w.Hkv, w.D, w.P, w.window) == (32, 8, 128, 16, 4096)
+    R = w.block_table.shape[1]
+    # a 4096-token window that starts inside a page touches 257 pages
+    assert R == 257 and (R - 1) * w.P + 1 >= w.window
+    assert w.N == w.B * R and sorted(w.block_table.ravel().tolist()) == list(range(w.N))
+    assert w.context.min() >= w.window and w.context.max() <= 8 * w.window and w.steps == 1
+    assert w.k_pool.shape == (w.N, 8, 16, 128)

@@ -32,6 +32,13 @@ few thousand tokens as on dpshk §2.1):
 5. page-sweep: B=32, Hq=32, Hkv=8, D=128, cached context ~ U{200..4000},
    P in {16, 32, 64, 128}, 64 consecutive append+decode steps; pages for all 64
    steps reserved up front; 512-token partitions.
+6. sliding-window-4096: B=32, Hq=32, Hkv=8, D=128, P=16, a 4096-token window
+   over a ring of 257 pages per sequence (the most pages a 4096-token window
+   touches), cached context ~ U{4096..32768} (the ring has wrapped up to eight
+   times), append one token; ``block_table`` is the ring table [B][257] drawn
+   as consecutive entries of the permutation of the B * 257 pages; unsplit
+   (once every window is full, each (sequence, KV head) carries the same 4096
+   tokens: 256 equal workgroups, one per compute unit).
 """
 
 import math
@@ -63,6 +70,7 @@ class DecodeWorkload:
     partition_tokens: int = 0
     shared_prefix_pages: int = 0
     perm: np.ndarray = field(default=None, repr=False)
+    window: int = 0          # > 0: attend the last `window` tokens; block_table is a ring of pages
 
     @property
     def steps(self):
@@ -142,7 +150,7 @@ def _build(name, rng, seed, B, Hq, Hkv, D, P, context, tokens_needed, steps, sca
 
 
 def workload(number, page_size=None, seed=None, batch=None):
-    """Build workload ``number`` (1..5). ``page_size`` applies to workload 5
+    """Build workload ``number`` (1..6). ``page_size`` applies to workload 5
     (default 16); ``batch`` shrinks B for quick tests (same recipe)."""
     seed = number if seed is None else seed
     rng = np.random.default_rng(seed)
@@ -183,4 +191,20 @@ def workload(number, page_size=None, seed=None, batch=None):
         ctx = rng.integers(200, 4000, size=B, endpoint=True)
         return _build("page-sweep-p%d" % P, rng, seed, B, 32, 8, 128, P, ctx, ctx + steps, steps,
                       1.0 / math.sqrt(128), partition_tokens=512)
-    raise ValueError("workload number must be 1..5")
+    if number == 6:
+        B = batch or 32
+        P, W = 16, 4096
+        R = (W - 1) // P + 2
+        ctx = rng.integers(W, 8 * W, size=B, endpoint=True)
+        n_pages = B * R
+        perm = rng.permutation(n_pages).astype(np.int32)
+        ring = perm.reshape(B, R).copy()
+        q = _normal_fp16(seed, 1, (B, 32, 128))
+        k_pool = _normal_fp16(seed, 2, (n_pages, 8, P, 128))
+        v_pool = _normal_fp16(seed, 3, (n_pages, 8, P, 128))
+        k_new = _normal_fp16(seed, 4, (1, B, 8, 128))
+        v_new = _normal_fp16(seed, 5, (1, B, 8, 128))
+        return DecodeWorkload("sliding-window-4096", B, 32, 8, 128, P, n_pages, 1.0 / math.sqrt(128), q, k_pool,
+                              v_pool, ring, ctx.astype(np.int32), k_new, v_new, partition_tokens=0, perm=perm,
+                              window=W)
+    raise ValueError("workload number must be 1..6")
