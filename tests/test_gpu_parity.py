@@ -558,3 +558,39 @@ def test_page_sweep_lazy_allocation_is_bit_identical(P):
                 xa = oracle.gather_sequence(pa, w.block_table[b], int(final[b]), h, P, kind)
                 xb = oracle.gather_sequence(pb, bt_b[b], int(final[b]), h, P, kind)
                 assert np.array_equal(xa, xb)
+
+
+def test_one_workspace_serves_calls_of_every_shape():
+    """One workspace reused across split calls of different batch, head and
+    prefix shapes (and the same call twice, bit-identical) gives the oracle's
+    result every time: no call depends on what an earlier call left in it."""
+    m = pkv()
+    cases = [(3, 6, 512, True), (2, 3, 1024, False), (5, 7, 64, False), (3, 9, 512, False), (4, 1, 512, False),
+             (3, 6, 512, True)]
+    sizes = []
+    for number, batch, part, use_prefix in cases:
+        w = wl(number, batch=batch)
+        lens = w.lens(w.steps - 1)
+        prefix = w.shared_prefix_pages * w.P if use_prefix else 0
+        sizes.append(m.decode_workspace_bytes(w.B, w.Hq, w.D, int(lens.max()), part, prefix))
+    ws = torch.full((max(sizes),), 0xA5, dtype=torch.uint8, device="cuda")     # arbitrary prior contents
+    first = None
+    for i, (number, batch, part, use_prefix) in enumerate(cases):
+        w = wl(number, batch=batch)
+        lens = w.lens(w.steps - 1)
+        prefix = w.shared_prefix_pages * w.P if use_prefix else 0
+        kp, vp = poison_unused(w, lens)
+        say("shared workspace call %d: %s B=%d part=%d prefix=%d" % (i, w.name, w.B, part, prefix))
+        if prefix:
+            got = m.paged_decode_attention_shared_prefix(dev(w.q), dev(kp), dev(vp), dev(w.block_table), dev(lens),
+                                                         int(lens.max()), w.scale, part, prefix, workspace=ws)
+        else:
+            got = m.paged_decode_attention(dev(w.q), dev(kp), dev(vp), dev(w.block_table), dev(lens),
+                                           int(lens.max()), w.scale, part, workspace=ws)
+        torch.cuda.synchronize()
+        ref = oracle.decode_attention(w.q, kp, vp, w.block_table, lens, w.scale, w.P)
+        check_close(got, ref, "shared workspace call %d" % i)
+        if i == 0:
+            first = host(got).copy()
+        elif i == len(cases) - 1:
+            assert np.array_equal(host(got).view(np.uint16), first.view(np.uint16))
