@@ -123,6 +123,19 @@ def _dev_ptr(t, dtype, name, ndim=None):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _workspace_arg(workspace, ws_bytes, device):
+    """Pointer and byte size of the split-mode workspace: the caller's (a
+    contiguous device tensor of any dtype; the library checks the size), or a
+    new one of ``ws_bytes`` bytes; NULL and 0 when none is needed or given."""
+    if workspace is None:
+        if ws_bytes == 0:
+            return ctypes.c_void_p(0), 0
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous device tensor")
+    return ctypes.c_void_p(workspace.data_ptr()), workspace.numel() * workspace.element_size()
+
+
 def _stream(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -202,10 +215,7 @@ def paged_decode_attention_multi(q, k_pool, v_pool, block_table, lens, max_conte
     if tuple(out.shape) != (B, nq, Hq, D):
         raise ValueError("out must be [B][n_query][Hq][D]")
     ws_bytes = decode_workspace_bytes(B, Hq, D, max_context, partition_tokens)
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_len = _workspace_arg(workspace, ws_bytes, q.device)
     rc = lib().pkv_paged_decode_attention_multi(
         _dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"),
         _dev_ptr(k_pool, torch.float16, "k_pool"), _dev_ptr(v_pool, torch.float16, "v_pool"),
@@ -232,11 +242,10 @@ def paged_decode_attention_window(q, k_pool, v_pool, ring_table, lens, window, s
         raise ValueError("k_new / v_new must be [B][Hkv][D]")
     if out is None:
         out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B][Hq][D]")
     ws_bytes = decode_workspace_bytes(B, Hq, D, int(window), partition_tokens)
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_len = _workspace_arg(workspace, ws_bytes, q.device)
     kn = _dev_ptr(k_new, torch.float16, "k_new") if k_new is not None else ctypes.c_void_p(0)
     vn = _dev_ptr(v_new, torch.float16, "v_new") if v_new is not None else ctypes.c_void_p(0)
     rc = lib().pkv_paged_decode_attention_window(
@@ -324,10 +333,7 @@ def _decode_args(out, q, k_pool, v_pool, block_table, lens, max_context, partiti
     if tuple(out.shape) != (B, Hq, D):
         raise ValueError("out must be [B][Hq][D]")
     ws_bytes = decode_workspace_bytes(B, Hq, D, max_context, partition_tokens, prefix_tokens)
-    if workspace is None and ws_bytes > 0:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    ws_ptr = ctypes.c_void_p(workspace.data_ptr()) if workspace is not None else ctypes.c_void_p(0)
-    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_len = _workspace_arg(workspace, ws_bytes, q.device)
     return out, (N, Hkv, P, D, B, Hq, max_pages), ws_ptr, ws_len
 
 

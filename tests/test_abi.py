@@ -361,3 +361,24 @@ def test_copy_pages_argument_checks(pkv):
     assert call([0, 2], [2, 3]) == 1             # page 2 both written and read
     assert call([0], [1], page_bytes=100) == 1   # not a multiple of 16
     assert call([0], [1], pool=8) == 1           # misaligned
+
+
+def test_binding_rejects_mismatched_buffers_before_any_call(pkv):
+    """The binding checks what the C ABI cannot see (buffer shapes, devices,
+    contiguity) before it passes a pointer on."""
+    import torch
+    from paged_kv_cache_279_amd import binding
+    with pytest.raises(ValueError):
+        binding._workspace_arg(torch.zeros(64, dtype=torch.uint8), 0, "cpu")        # host memory
+    assert binding._workspace_arg(None, 0, "cpu")[1] == 0
+    B, Hq, Hkv, D, P, R = 2, 8, 2, 64, 16, 4
+    q = torch.zeros((B, Hq, D), dtype=torch.float16)
+    pool = torch.zeros((8, Hkv, P, D), dtype=torch.float16)
+    ring = torch.zeros((B, R), dtype=torch.int32)
+    lens = torch.zeros((B,), dtype=torch.int32)
+    with pytest.raises(ValueError, match="out must be"):
+        pkv.paged_decode_attention_window(q, pool, pool, ring, lens, 40, 0.125, out=torch.zeros((B, Hq, D - 1)))
+    with pytest.raises(ValueError, match="out must be"):
+        pkv.paged_decode_attention(q, pool, pool, ring, lens, 64, 0.125, out=torch.zeros((B, Hq + 1, D)))
+    with pytest.raises(ValueError, match="shape mismatch"):
+        pkv.paged_decode_attention(q, pool, pool, ring, lens[:1], 64, 0.125)
