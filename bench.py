@@ -144,8 +144,9 @@ def kernel_source_digest():
 
 
 def measured_traffic(workload_name, config_key):
-    """HBM bytes per decode call from the committed rocprofv3 counter summary,
-    if it was taken on this exact kernel source and configuration; else None.
+    """HBM bytes per partition-kernel launch from the committed rocprofv3
+    counter summary, if it was taken on this exact kernel source and
+    configuration; else None.
 
     FETCH_SIZE / WRITE_SIZE are KiB per dispatch; each is scaled by what the
     same counter reads for a plain device copy of known size (the summary
@@ -161,7 +162,8 @@ def measured_traffic(workload_name, config_key):
     entry = rec.get("configs", {}).get(config_key)
     if not entry or entry.get("workload") != workload_name:
         return None
-    return (entry["fetch_kib_per_call"] * rec["fetch_scale"] + entry["write_kib_per_call"] * rec["write_scale"]) * 1024
+    k = entry["partition_kernel"]
+    return (k["fetch_kib"] * rec["fetch_scale"] + k["write_kib"] * rec["write_scale"]) * 1024
 
 
 def streaming_peak(torch, pkv, nbytes, stream, n_buf=8, reps=4):
@@ -503,7 +505,7 @@ def main():
                 layer_call(layer, lens_cur, pos_cur, kn_cur, vn_cur, cap)
         torch.cuda.synchronize()
 
-    def run_step(step, per_call_events=None):
+    def run_step(step, per_call_events=None, kernel_events=None):
         if graph is not None:
             lens_cur.copy_(lens_all[step], non_blocking=True)
             pos_cur.copy_(pos_all[step], non_blocking=True)
@@ -521,6 +523,9 @@ def main():
             for layer in range(R):
                 if per_call_events is not None and layer == timed:
                     per_call_events[0].record(stream)
+                if kernel_events is not None and layer == timed:
+                    # the partition kernel of this call records its own start and stop
+                    pkv.profile_next_partition_kernel(*kernel_events)
                 layer_step(step, layer)
                 if per_call_events is not None and layer == timed:
                     per_call_events[1].record(stream)
@@ -534,6 +539,12 @@ def main():
     # ---- timed: HIP events on the launch stream around the decode calls (the
     # graph replay of a step's R calls, or one eager call per step)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    kev = None
+    if graph is None:
+        kev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for pair in kev:                       # torch creates an event on its first record
+            for e in pair:
+                e.record(stream)
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -546,7 +557,14 @@ def main():
         h0 = time.perf_counter()
         host_step(step)
         h1 = time.perf_counter()
-        run_step(step, ev[i])
+        # eager: even timed steps time the partition kernel (its own launch events),
+        # odd ones the whole call, so that no step carries both
+        if kev is not None and i % 2 == 0:
+            run_step(step, None, kev[i])
+        elif kev is not None:
+            run_step(step, ev[i], None)
+        else:
+            run_step(step, ev[i])
         host_s += h1 - h0
         launch_s += time.perf_counter() - h1
     t_end.record(stream)
@@ -558,8 +576,10 @@ def main():
                       launch_s / args.steps * 1e6, total_ms / args.steps * 1e3))
     if graph is not None:
         call_ms = np.array([e[0].elapsed_time(e[1]) / R for e in ev])
+        kernel_ms = None
     else:
-        call_ms = np.array([e[0].elapsed_time(e[1]) for e in ev])
+        call_ms = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(1, args.steps, 2)])
+        kernel_ms = np.array([kev[i][0].elapsed_time(kev[i][1]) for i in range(0, args.steps, 2)])
     ms_per_step = total_ms / args.steps
     ms_per_layer = ms_per_step / R
 
@@ -579,8 +599,14 @@ def main():
         kv_steps.append(kv)
     bytes_per_call = float(np.mean(bytes_steps))
     kv_per_call = float(np.mean(kv_steps))
-    call_avg_s = float(call_ms.mean()) / 1e3
-    achieved = bytes_per_call / call_avg_s / 1e9
+    call_avg_s = float(call_ms.mean()) / 1e3 if len(call_ms) else float("nan")
+    call_gbps = bytes_per_call / call_avg_s / 1e9
+    # the dominant kernel: the partition kernel, timed by its own start/stop events;
+    # in split mode the merge kernel writes the output rows, so they are not its bytes
+    split = part > 0
+    kernel_bytes = bytes_per_call - (2 * B * KQ * Hq * D if split else 0)
+    kernel_avg_s = float(kernel_ms.mean()) / 1e3 if kernel_ms is not None else call_avg_s
+    achieved = kernel_bytes / kernel_avg_s / 1e9
     tokens_per_s = B * KQ / (ms_per_layer / 1e3)
 
     result = {
@@ -626,23 +652,35 @@ def main():
         },
         "roofline": {
             "bound": "hbm",
-            "kernel": "sliding-window partition kernel with fused append + log-sum-exp reduce" if W else
-                      ("%d appends + multi-query partition kernel + log-sum-exp reduce" % KQ) if KQ > 1 else
-                      "paged decode call (%s%spartition kernel%s + log-sum-exp reduce)" % (
-                          ("int8-key " if fused else "int8-key append + int8-key ") if k8 else "",
-                          "shared-prefix + " if prefix_tokens else "", " with fused append" if fused else ""),
+            "kernel": "decode_partition_kernel (%s%s%s%s%s)" % (
+                "split" if split else "unsplit",
+                ", shared prefix" if prefix_tokens else "", ", int8 keys" if k8 else "",
+                ", %d-query chunks" % KQ if KQ > 1 else ", sliding window" if W else "",
+                ", fused append" if fused else ""),
             "achieved": round(achieved, 1),
             "peak": PEAK_HBM_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_HBM_GBPS, 4),
             "traffic": measured_traffic(w.name, config_key),
-            "traffic_unit": "bytes per decode call (FETCH_SIZE x fetch scale + WRITE_SIZE x write scale)",
-            "bytes_per_launch": round(bytes_per_call),
-            "avg_launch_us": round(call_avg_s * 1e6, 3),
+            "traffic_unit": "HBM bytes per partition-kernel launch (FETCH_SIZE x fetch scale + WRITE_SIZE x write "
+                            "scale)",
+            "bytes_per_launch": round(kernel_bytes),
+            "avg_launch_us": round(kernel_avg_s * 1e6, 3),
+            "timing": ("hipExtLaunchKernel start/stop events of the partition kernel: one layer call on every even "
+                       "timed step (odd steps time the whole call)"
+                       if kernel_ms is not None else "graph replay events / layers (whole call)"),
+            "call": {
+                "what": "whole decode call: partition kernel%s, launch gap and two event records" % (
+                    " + log-sum-exp merge kernel" if split else ""),
+                "avg_us": round(call_avg_s * 1e6, 3) if len(call_ms) else None,
+                "bytes": round(bytes_per_call),
+                "achieved_gbps": round(call_gbps, 1) if len(call_ms) else None,
+                "frac": round(call_gbps / PEAK_HBM_GBPS, 4) if len(call_ms) else None,
+            },
         },
     }
     if not args.no_stream_peak:
-        peak_gbps, peak_us, peak_bytes = streaming_peak(torch, pkv, bytes_per_call, stream)
+        peak_gbps, peak_us, peak_bytes = streaming_peak(torch, pkv, kernel_bytes, stream)
         log("streaming-read ceiling: %.1f MB in %.2f us = %.0f GB/s" % (peak_bytes / 1e6, peak_us, peak_gbps))
         result["roofline"]["streaming_read_peak"] = {
             "value": round(peak_gbps, 1), "unit": "GB/s", "bytes": peak_bytes, "us": round(peak_us, 3),

@@ -395,6 +395,23 @@ int pkv_paged_decode_attention_k8(void* out, const void* q, const void* k_new, c
 int pkv_probe_stream_read(const void* base, size_t bytes, const int32_t* tile_order, int32_t n_tiles,
                           int32_t waves, int32_t* sink, void* stream);
 
+/*
+ * pkv_profile_next_partition_kernel -- measurement aid (not part of decode):
+ * the next decode call made on this host thread (any pkv_*decode_attention*
+ * entry point) launches its partition kernel -- the kernel that reads the
+ * cache -- with hipExtLaunchKernel and these two events, which then record
+ * that kernel's start and stop on the call's stream; hipEventElapsedTime
+ * gives the kernel's own duration, without the merge kernel or the launch
+ * gap between them. The hook is consumed by that next call whether or not it
+ * launches (a call that returns an error records nothing). Either event may
+ * be NULL.
+ *
+ *   start_event, stop_event: hipEvent_t, created by the caller (with timing),
+ *                  owned by the caller; not for use under stream capture.
+ * Returns PKV_OK.
+ */
+int pkv_profile_next_partition_kernel(void* start_event, void* stop_event);
+
 /* ------------------------------------------------------------------------ */
 /* Host page allocator (CPU only; no device calls)                           */
 /* ------------------------------------------------------------------------ */

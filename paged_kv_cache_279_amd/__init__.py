@@ -30,6 +30,7 @@ from .binding import (  # noqa: F401
     paged_decode_attention_shared_prefix,
     paged_decode_attention_window,
     probe_stream_read,
+    profile_next_partition_kernel,
     status_string,
     validate_tables,
 )

@@ -36,6 +36,7 @@ _SIGNATURES = {
     "pkv_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_block_table_patch": (ctypes.c_int, [_vp, _i32, _i32, _ip, _ip, _ip, _i32, _vp]),
     "pkv_probe_stream_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _i32, _i32, _vp, _vp]),
+    "pkv_profile_next_partition_kernel": (ctypes.c_int, [_vp, _vp]),
     "pkv_k8_pool_bytes": (ctypes.c_int, [_i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     "pkv_paged_decode_attention_multi": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                                         _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _vp,
@@ -170,6 +171,19 @@ def probe_stream_read(buf, tile_order, sink, waves=8192, stream=None):
                                        _dev_ptr(tile_order, torch.int32, "tile_order"), tile_order.numel(),
                                        int(waves), _dev_ptr(sink, torch.int32, "sink"), _stream(stream)),
            "pkv_probe_stream_read")
+
+
+def profile_next_partition_kernel(start, stop):
+    """pkv_profile_next_partition_kernel: the next decode call on this thread records
+    its partition kernel's start and stop into ``start`` / ``stop``
+    (torch.cuda.Event(enable_timing=True), each recorded once before so that it exists)."""
+    handles = []
+    for ev in (start, stop):
+        h = int(getattr(ev, "cuda_event", 0) or 0)
+        if h == 0:
+            raise ValueError("record the event once first: torch creates it on its first record")
+        handles.append(ctypes.c_void_p(h))
+    _check(lib().pkv_profile_next_partition_kernel(*handles), "pkv_profile_next_partition_kernel")
 
 
 def copy_pages(pool, src, dst, stream=None):

@@ -34,6 +34,7 @@
 // through LDS into either the final fp16 rows or a (max, sum, unnormalised
 // output) partial per column.
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -1254,8 +1255,23 @@ int64_t max_slots(int32_t B, int32_t Hq, bool prefix) {
          2 * (static_cast<int64_t>(PKV_FLAT_WORKGROUPS) + Hq);
 }
 
+// Measurement hook: events that the next decode call made on this host thread
+// hands to the launch of its partition kernel (see
+// pkv_profile_next_partition_kernel), and the pair that call took.
+thread_local hipEvent_t t_prof_armed[2] = {nullptr, nullptr};
+thread_local hipEvent_t t_prof_call[2] = {nullptr, nullptr};
+
 template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ, bool WIN>
 hipError_t launch_partition(const DecodeParams& p, hipStream_t stream, int64_t grid) {
+  const void* fn = reinterpret_cast<const void*>(&decode_partition_kernel<D, G, SPLIT, FUSED, K8, MQ, WIN>);
+  if (t_prof_call[0] || t_prof_call[1]) {
+    // the start and stop of this kernel alone go into the caller's events
+    DecodeParams arg = p;
+    void* args[] = {&arg};
+    const hipError_t e = hipExtLaunchKernel(fn, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), args, 0, stream,
+                                            t_prof_call[0], t_prof_call[1], 0);
+    return e != hipSuccess ? e : hipGetLastError();
+  }
   hipLaunchKernelGGL((decode_partition_kernel<D, G, SPLIT, FUSED, K8, MQ, WIN>), dim3(static_cast<uint32_t>(grid)),
                      dim3(kThreads), 0, stream, p);
   return hipGetLastError();
@@ -1284,6 +1300,10 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
                   int32_t max_context, float scale, int32_t partition_tokens, int32_t prefix_tokens,
                   void* workspace, size_t workspace_bytes, void* stream, bool fused, bool k8 = false,
                   int32_t nq = 1, int32_t window = 0) {
+  // an armed measurement hook belongs to this call, whatever it returns
+  t_prof_call[0] = t_prof_armed[0];
+  t_prof_call[1] = t_prof_armed[1];
+  t_prof_armed[0] = t_prof_armed[1] = nullptr;
   if (B < 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || N <= 0 || max_pages <= 0 || max_context < 0 ||
       partition_tokens < 0 || prefix_tokens < 0)
     return PKV_ERR_INVALID_ARG;
@@ -1413,6 +1433,12 @@ int workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context, int32
 }  // namespace
 
 extern "C" {
+
+int pkv_profile_next_partition_kernel(void* start_event, void* stop_event) {
+  t_prof_armed[0] = static_cast<hipEvent_t>(start_event);
+  t_prof_armed[1] = static_cast<hipEvent_t>(stop_event);
+  return PKV_OK;
+}
 
 int pkv_probe_stream_read(const void* base, size_t bytes, const int32_t* tile_order, int32_t n_tiles,
                           int32_t waves, int32_t* sink, void* stream) {

@@ -382,3 +382,14 @@ def test_binding_rejects_mismatched_buffers_before_any_call(pkv):
         pkv.paged_decode_attention(q, pool, pool, ring, lens, 64, 0.125, out=torch.zeros((B, Hq + 1, D)))
     with pytest.raises(ValueError, match="shape mismatch"):
         pkv.paged_decode_attention(q, pool, pool, ring, lens[:1], 64, 0.125)
+
+
+def test_profile_hook_is_consumed_by_the_next_call(pkv):
+    """The measurement hook takes any two handles and the next decode call,
+    even one that fails its argument checks before any launch, consumes it."""
+    import ctypes
+    lib = pkv.lib()
+    assert lib.pkv_profile_next_partition_kernel(None, None) == 0
+    assert lib.pkv_profile_next_partition_kernel(ctypes.c_void_p(0x1000), ctypes.c_void_p(0x2000)) == 0
+    assert _decode(pkv, D=96) == 2           # consumes the hook, launches nothing
+    assert _decode(pkv, B=0, out=0, q=0) == 0

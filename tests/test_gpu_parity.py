@@ -594,3 +594,30 @@ def test_one_workspace_serves_calls_of_every_shape():
             first = host(got).copy()
         elif i == len(cases) - 1:
             assert np.array_equal(host(got).view(np.uint16), first.view(np.uint16))
+
+
+@pytest.mark.parametrize("part", [0, 512])
+def test_profile_hook_times_the_partition_kernel(part):
+    """pkv_profile_next_partition_kernel: the partition kernel launched with the
+    caller's events gives the same output bit for bit, and its own duration is
+    positive and no longer than the whole call's."""
+    m = pkv()
+    w = wl(2, batch=3)
+    lens = w.lens(0)
+    q, kp, vp, bt, dl = dev(w.q), dev(w.k_pool), dev(w.v_pool), dev(w.block_table), dev(lens)
+    ref = host(m.paged_decode_attention(q, kp, vp, bt, dl, int(lens.max()), w.scale, part)).copy()
+    k0, k1, c0, c1 = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    s = torch.cuda.current_stream()
+    for e in (k0, k1):
+        e.record(s)
+    torch.cuda.synchronize()
+    say("profile hook part=%d" % part)
+    c0.record(s)
+    m.profile_next_partition_kernel(k0, k1)
+    got = m.paged_decode_attention(q, kp, vp, bt, dl, int(lens.max()), w.scale, part)
+    c1.record(s)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(got).view(np.uint16), ref.view(np.uint16))
+    kernel_ms, call_ms = k0.elapsed_time(k1), c0.elapsed_time(c1)
+    say("kernel %.2f us, call %.2f us" % (kernel_ms * 1e3, call_ms * 1e3))
+    assert 0 < kernel_ms <= call_ms
