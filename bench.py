@@ -61,8 +61,9 @@ def parse_args():
     ap.add_argument("--patch-max", type=int, default=1024,
                     help="table changes per step applied in place by pkv_block_table_patch; more -> full upload")
     ap.add_argument("--n-query", type=int, default=1,
-                    help="chunk of K new tokens per sequence and step (K appends, then one causal multi-query "
-                         "attention call, pkv_paged_decode_attention_multi); tokens/s counts B * K per layer-step")
+                    help="chunk of K new tokens per sequence and step (one chunk append, then one causal "
+                         "multi-query attention call, pkv_paged_decode_attention_multi); tokens/s counts B * K per "
+                         "layer-step")
     ap.add_argument("--int8-keys", action="store_true",
                     help="keys as int8 codes with a per-token fp32 scale, values fp16 (pkv_kv_append_k8 + "
                          "pkv_paged_decode_attention_k8)")
@@ -269,8 +270,8 @@ def main():
         raise SystemExit("the sliding-window workload runs fp16 keys, one query, the fused append, eagerly")
     if w.steps == 0:
         raise SystemExit("workload %d has no append; pick 2-5" % args.workload)
-    if KQ > 1 and (prefix_tokens or k8 or args.graph):
-        raise SystemExit("--n-query runs without a shared prefix (--no-shared-prefix), int8 keys or graphs")
+    if KQ > 1 and (k8 or args.graph):
+        raise SystemExit("--n-query runs without int8 keys or graphs")
     log("workload %s: B=%d Hq=%d Hkv=%d D=%d P=%d part=%d layers=%d fused=%s" % (w.name, B, Hq, Hkv, D, P, part, R,
                                                                                   fused))
 
@@ -345,18 +346,20 @@ def main():
     pos_all = lens_all - 1
     if KQ > 1:
         # the chunk's K positions per step, and K tokens (step 0: the workload's token first) per step
-        pos_chunk = torch.stack([lens_all - KQ + i for i in range(KQ)], dim=1)      # [steps][K][B]
-        knew_mq = torch.empty((total_steps, KQ, B, Hkv, D), dtype=torch.float16, device=dev)
+        pos_chunk = (lens_all - KQ).contiguous()                    # [steps][B]: first position of each chunk
+        knew_mq = torch.empty((total_steps, B, KQ, Hkv, D), dtype=torch.float16, device=dev)
         vnew_mq = torch.empty_like(knew_mq)
         knew_mq.normal_(generator=gen)
         vnew_mq.normal_(generator=gen)
-        knew_mq[0, 0].copy_(put(w.k_new[0]))
-        vnew_mq[0, 0].copy_(put(w.v_new[0]))
+        knew_mq[0, :, 0].copy_(put(w.k_new[0]))
+        vnew_mq[0, :, 0].copy_(put(w.v_new[0]))
         q_mq = torch.empty((B, KQ, Hq, D), dtype=torch.float16, device=dev)
         q_mq.normal_(generator=gen)
         out_mq = torch.empty((B, KQ, Hq, D), dtype=torch.float16, device=dev)
     max_context = int(final_ctx.max())
-    ws_bytes = pkv.decode_workspace_bytes(B, Hq, D, W or max_context, part, prefix_tokens)
+    # chunks of queries with a shared prefix: the chunk rows count as sequences in the workspace query
+    ws_rows = B * KQ if KQ > 1 and prefix_tokens else B
+    ws_bytes = pkv.decode_workspace_bytes(ws_rows, Hq, D, W or max_context, part, prefix_tokens)
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
     torch.cuda.synchronize()
@@ -370,11 +373,11 @@ def main():
             pkv.paged_decode_attention_window(q, k_pools[layer], v_pools[layer], bt_dev, lens, W, scale, part,
                                               k_new=kn, v_new=vn, out=out, workspace=workspace, stream=s)
         elif KQ > 1:
-            # pos [K][B], kn / vn [K][B][Hkv][D]: K appends, then the chunk's attention
-            for i in range(KQ):
-                pkv.kv_append(kn[i], vn[i], k_pools[layer], v_pools[layer], bt_dev, pos[i], stream=s)
+            # pos [B], kn / vn [B][K][Hkv][D]: the chunk's K tokens in one append launch, then its attention
+            pkv.kv_append_chunk(kn, vn, k_pools[layer], v_pools[layer], bt_dev, pos, stream=s)
             pkv.paged_decode_attention_multi(q_mq, k_pools[layer], v_pools[layer], bt_dev, lens, max_context, scale,
-                                             part, out=out_mq, workspace=workspace, stream=s)
+                                             part, out=out_mq, workspace=workspace, stream=s,
+                                             prefix_tokens=prefix_tokens)
         elif k8:
             if not fused:
                 pkv.kv_append_k8(kn, vn, k_pools[layer], v_pools[layer], bt_dev, pos, stream=s)
@@ -452,7 +455,7 @@ def main():
         kpool_full = k_pools[0].cpu().numpy()            # pages beyond the workload's pool were drawn on device
         vpool_full = v_pools[0].cpu().numpy()
         for i in range(KQ):
-            kpool_full, vpool_full = oracle.kv_append(kpool_full, vpool_full, kn0[i], vn0[i], bt0,
+            kpool_full, vpool_full = oracle.kv_append(kpool_full, vpool_full, kn0[:, i], vn0[:, i], bt0,
                                                       (w.context + i).astype(np.int32), P)
         ref = oracle.decode_attention_multi(q_mq.cpu().numpy()[sample], kpool_full, vpool_full, bt0[sample],
                                             (w.context + KQ).astype(np.int32)[sample], scale, P)
@@ -637,7 +640,7 @@ def main():
             "launch": "eager" if graph is None else "hip graph per step (%d layer calls)" % R,
             "shared_prefix_path": bool(prefix_tokens),
             "tokens_per_s_definition": ("batch * queries per sequence / (time of one attention layer-step: "
-                                        "appends + chunk attention), i.e. tokens verified per second through one "
+                                        "chunk append + chunk attention), i.e. tokens verified per second through one "
                                         "layer") if KQ > 1 else
                                        "batch / (time of one attention layer-step: append + decode), "
                                        "i.e. sequences advanced per second through one layer",

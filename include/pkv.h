@@ -128,6 +128,24 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_po
                   int32_t B, int32_t Hkv, int32_t D, int32_t P, int32_t N, void* stream);
 
 /*
+ * pkv_kv_append_chunk -- pkv_kv_append for n_tokens consecutive tokens per
+ * sequence in one launch: the keys and values of a chunk (the drafted tokens
+ * a verification step scores, or a prefill chunk; pgsm §3.2), written in
+ * place like single tokens (pgsm §4.3).
+ *
+ *   k_new, v_new : fp16 [B][n_tokens][Hkv][D] device, read.
+ *   pos          : int32 [B] device: token i of sequence b goes to position
+ *                  pos[b] + i (every position must have its page in the
+ *                  table; a position outside it, or a page id outside [0, N),
+ *                  skips that token).
+ *   n_tokens     : >= 1; n_tokens == 1 is pkv_kv_append.
+ * Other arguments and errors as pkv_kv_append.
+ */
+int pkv_kv_append_chunk(const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                        const int32_t* block_table, int32_t max_pages, const int32_t* pos, int32_t B,
+                        int32_t n_tokens, int32_t Hkv, int32_t D, int32_t P, int32_t N, void* stream);
+
+/*
  * pkv_decode_workspace_bytes -- workspace size split-context decode needs.
  *
  * In split mode the private tokens of every sequence are divided among a
@@ -317,6 +335,36 @@ int pkv_paged_decode_attention_window(void* out, const void* q, const void* k_ne
                                       int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
                                       int32_t window, float scale, int32_t partition_tokens, void* workspace,
                                       size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_paged_decode_attention_multi_shared_prefix -- the chunked attention of
+ * pkv_paged_decode_attention_multi for a batch whose sequences all begin with
+ * the same prefix_tokens tokens in the same pages (drafted tokens verified
+ * against a shared system prompt; pgsm §3.2 names both the chunks and prefix
+ * reuse).
+ *
+ * Same result as pkv_paged_decode_attention_multi. The shared pages are read
+ * as in pkv_paged_decode_attention_shared_prefix: once per KV head and 16
+ * query rows, the rows now being the n_query * (Hq / Hkv) chunk rows of every
+ * sequence. Every prefix token precedes every query of a chunk, so the prefix
+ * needs no causal mask.
+ *
+ *   prefix_tokens: as in pkv_paged_decode_attention_shared_prefix; a row with
+ *                  lens[b] < prefix_tokens + n_query (a chunk reaching into
+ *                  the prefix) is NaN.
+ *   partition_tokens: > 0 (this path always splits).
+ *   workspace    : at least pkv_decode_workspace_bytes_shared_prefix(
+ *                  B * n_query, Hq, D, max_context, partition_tokens,
+ *                  prefix_tokens) bytes (the chunk rows count as sequences
+ *                  there; B * n_query <= 4096).
+ * Other arguments and errors as pkv_paged_decode_attention_multi.
+ */
+int pkv_paged_decode_attention_multi_shared_prefix(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                                   const int32_t* block_table, int32_t max_pages, const int32_t* lens,
+                                                   int32_t B, int32_t n_query, int32_t Hq, int32_t Hkv, int32_t D,
+                                                   int32_t P, int32_t N, int32_t max_context, float scale,
+                                                   int32_t partition_tokens, int32_t prefix_tokens, void* workspace,
+                                                   size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* Key-only int8 pages                                                       */

@@ -22,6 +22,7 @@ from .binding import (  # noqa: F401
     decode_workspace_bytes,
     k8_pool_bytes,
     kv_append,
+    kv_append_chunk,
     kv_append_k8,
     lib,
     paged_decode_attention,

@@ -34,6 +34,8 @@ _SIGNATURES = {
     "pkv_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pkv_abi_version": (ctypes.c_int, []),
     "pkv_kv_append": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
+    "pkv_kv_append_chunk": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                            _vp]),
     "pkv_block_table_patch": (ctypes.c_int, [_vp, _i32, _i32, _ip, _ip, _ip, _i32, _vp]),
     "pkv_probe_stream_read": (ctypes.c_int, [_vp, ctypes.c_size_t, _vp, _i32, _i32, _vp, _vp]),
     "pkv_profile_next_partition_kernel": (ctypes.c_int, [_vp, _vp]),
@@ -44,6 +46,10 @@ _SIGNATURES = {
     "pkv_paged_decode_attention_window": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                                          _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _vp,
                                                          ctypes.c_size_t, _vp]),
+    "pkv_paged_decode_attention_multi_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                                                      _i32, _i32, _i32, _i32, _i32, _i32,
+                                                                      ctypes.c_float, _i32, _i32, _vp,
+                                                                      ctypes.c_size_t, _vp]),
     "pkv_kv_append_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_paged_decode_attention_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                                      _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _i32, _vp,
@@ -215,10 +221,30 @@ def kv_append(k_new, v_new, k_pool, v_pool, block_table, pos, stream=None):
     _check(rc, "pkv_kv_append")
 
 
+def kv_append_chunk(k_new, v_new, k_pool, v_pool, block_table, pos, stream=None):
+    """pkv_kv_append_chunk: write k_new/v_new [B][n_tokens][Hkv][D]; token i of sequence b
+    goes to position pos[b] + i."""
+    N, Hkv, P, D = k_pool.shape
+    B, max_pages = block_table.shape
+    if k_new.dim() != 4 or tuple(k_new.shape) != tuple(v_new.shape) or k_new.shape[0] != B or \
+            tuple(k_new.shape[2:]) != (Hkv, D) or tuple(v_pool.shape) != tuple(k_pool.shape):
+        raise ValueError("k_new/v_new must be [B][n_tokens][Hkv][D] matching the pools and the table")
+    if tuple(pos.shape) != (B,):
+        raise ValueError("pos must be [B]")
+    rc = lib().pkv_kv_append_chunk(_dev_ptr(k_new, torch.float16, "k_new"), _dev_ptr(v_new, torch.float16, "v_new"),
+                                   _dev_ptr(k_pool, torch.float16, "k_pool"), _dev_ptr(v_pool, torch.float16, "v_pool"),
+                                   _dev_ptr(block_table, torch.int32, "block_table"), max_pages,
+                                   _dev_ptr(pos, torch.int32, "pos"), B, int(k_new.shape[1]), Hkv, D, P, N,
+                                   _stream(stream))
+    _check(rc, "pkv_kv_append_chunk")
+
+
 def paged_decode_attention_multi(q, k_pool, v_pool, block_table, lens, max_context, scale, partition_tokens=0,
-                                 out=None, workspace=None, stream=None):
+                                 out=None, workspace=None, stream=None, prefix_tokens=0):
     """pkv_paged_decode_attention_multi: q [B][n_query][Hq][D], the last n_query tokens of
-    each sequence, causal within the chunk; returns ``out`` [B][n_query][Hq][D]."""
+    each sequence, causal within the chunk; returns ``out`` [B][n_query][Hq][D]. With
+    prefix_tokens > 0 the batch shares its first prefix_tokens tokens
+    (pkv_paged_decode_attention_multi_shared_prefix)."""
     B, nq, Hq, D = q.shape
     N, Hkv, P, Dk = k_pool.shape
     _, max_pages = block_table.shape
@@ -228,15 +254,23 @@ def paged_decode_attention_multi(q, k_pool, v_pool, block_table, lens, max_conte
         out = torch.empty((B, nq, Hq, D), dtype=torch.float16, device=q.device)
     if tuple(out.shape) != (B, nq, Hq, D):
         raise ValueError("out must be [B][n_query][Hq][D]")
-    ws_bytes = decode_workspace_bytes(B, Hq, D, max_context, partition_tokens)
+    if prefix_tokens:
+        # the chunk rows count as sequences in the workspace query
+        ws_bytes = decode_workspace_bytes(B * nq, Hq, D, max_context, partition_tokens, prefix_tokens)
+    else:
+        ws_bytes = decode_workspace_bytes(B, Hq, D, max_context, partition_tokens)
     ws_ptr, ws_len = _workspace_arg(workspace, ws_bytes, q.device)
-    rc = lib().pkv_paged_decode_attention_multi(
-        _dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"),
-        _dev_ptr(k_pool, torch.float16, "k_pool"), _dev_ptr(v_pool, torch.float16, "v_pool"),
-        _dev_ptr(block_table, torch.int32, "block_table"), max_pages, _dev_ptr(lens, torch.int32, "lens"),
-        B, nq, Hq, Hkv, D, P, N, int(max_context), float(scale), int(partition_tokens), ws_ptr, ws_len,
-        _stream(stream))
-    _check(rc, "pkv_paged_decode_attention_multi")
+    ptrs = (_dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"),
+            _dev_ptr(k_pool, torch.float16, "k_pool"), _dev_ptr(v_pool, torch.float16, "v_pool"),
+            _dev_ptr(block_table, torch.int32, "block_table"), max_pages, _dev_ptr(lens, torch.int32, "lens"),
+            B, nq, Hq, Hkv, D, P, N, int(max_context), float(scale), int(partition_tokens))
+    if prefix_tokens:
+        rc = lib().pkv_paged_decode_attention_multi_shared_prefix(*ptrs, int(prefix_tokens), ws_ptr, ws_len,
+                                                                  _stream(stream))
+        _check(rc, "pkv_paged_decode_attention_multi_shared_prefix")
+    else:
+        rc = lib().pkv_paged_decode_attention_multi(*ptrs, ws_ptr, ws_len, _stream(stream))
+        _check(rc, "pkv_paged_decode_attention_multi")
     return out
 
 

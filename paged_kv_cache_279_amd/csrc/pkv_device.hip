@@ -201,16 +201,20 @@ __global__ __launch_bounds__(D) void kv_append_kernel(const half_t* __restrict__
                                                       const half_t* __restrict__ v_new, half_t* __restrict__ k_pool,
                                                       half_t* __restrict__ v_pool, const int32_t* __restrict__ bt,
                                                       int32_t max_pages, const int32_t* __restrict__ pos, int32_t Hkv,
-                                                      int32_t p_shift, int32_t N) {
+                                                      int32_t p_shift, int32_t N, int32_t n_tokens) {
+  // workgroup (sequence b, token i of its chunk, KV head): token i goes to position pos[b] + i
   const int32_t kvh = blockIdx.x % Hkv;
-  const int32_t b = blockIdx.x / Hkv;
-  const int32_t t = pos[b];
-  if (t < 0 || (t >> p_shift) >= max_pages) return;
+  const int32_t bi = blockIdx.x / Hkv;
+  const int32_t b = bi / n_tokens;
+  const int32_t p0 = pos[b];
+  if (p0 < 0 || p0 > 0x7fffffff - n_tokens) return;
+  const int32_t t = p0 + bi % n_tokens;
+  if ((t >> p_shift) >= max_pages) return;
   const int32_t page = bt[(int64_t)b * max_pages + (t >> p_shift)];
   if (page < 0 || page >= N) return;
   const int64_t tile = (((int64_t)page * Hkv + kvh) * D) << p_shift;
   const int64_t sub = tile + (int64_t)((t & ((1 << p_shift) - 1)) >> 4) * (kBlk * D);
-  const int64_t src = ((int64_t)b * Hkv + kvh) * D;
+  const int64_t src = ((int64_t)bi * Hkv + kvh) * D;
   store_token<D>(k_pool + sub, v_pool + sub, t & 15, k_new + src, v_new + src, threadIdx.x);
 }
 
@@ -998,7 +1002,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
         const int32_t rt = g / PB;
         const int32_t blk0 = g - rt * PB;
         const int32_t piece_n = min(g1 - g, PB - blk0);
-        const int32_t rows = p.B * G;
+        // row r = (sequence * nq + query) * G + head in group: q row (r / G) * Hq + kvh * G + r % G
+        const int32_t rows = p.B * p.nq * G;
         auto qrow = [&](int c) -> int64_t {
           const int32_t r = rt * 16 + c;
           return r < rows ? (int64_t)(r / G) * p.Hq + (int64_t)kvh * G + r % G : -1;
@@ -1118,8 +1123,8 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
   const int32_t Wk = p.n_flat_wgs / p.Hkv;
   const int32_t PB = p.prefix_tokens / kBlk;
   const int64_t slot_base = (int64_t)kvh * (p.n_tiles + p.B + 2 * Wk);
-  // prefix tile segment of row r = b * G + hg
-  const int32_t r = b * G + hg;
+  // prefix tile segment of row r = (b * nq + qi) * G + hg
+  const int32_t r = (b * p.nq + qi) * G + hg;
   const int32_t rt = r / 16;
   const int32_t ct = r % 16;
   int32_t np1 = 0, ja = 0;
@@ -1226,7 +1231,7 @@ struct Plan {
 };
 
 int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_context, int32_t partition_tokens,
-              int32_t prefix_tokens, Plan* pl) {
+              int32_t prefix_tokens, Plan* pl, int32_t nq = 1) {
   if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_context < 0 || partition_tokens < 0 ||
       partition_tokens % kBlk != 0 || prefix_tokens < 0 || prefix_tokens % kBlk != 0 || prefix_tokens > max_context)
     return PKV_ERR_INVALID_ARG;
@@ -1234,7 +1239,7 @@ int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_context, int32_t p
   Plan p{};
   p.split = partition_tokens > 0;
   if (p.split && B > kMaxFlatBatch) return PKV_ERR_INVALID_ARG;
-  const int64_t rows = static_cast<int64_t>(B) * (Hq / Hkv);
+  const int64_t rows = static_cast<int64_t>(B) * nq * (Hq / Hkv);    // query rows per KV head
   p.n_tiles = prefix_tokens > 0 ? static_cast<int32_t>((rows + 15) / 16) : 0;
   // a whole number of workgroups per KV head, at least one
   p.n_flat_wgs = p.split ? max(PKV_FLAT_WORKGROUPS / Hkv, 1) * Hkv : 0;
@@ -1312,7 +1317,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
     return PKV_ERR_INVALID_ARG;
   const int G = Hq / Hkv;
   if (nq < 1) return PKV_ERR_INVALID_ARG;
-  if (nq > 1 && (fused || k8 || prefix_tokens > 0)) return PKV_ERR_INVALID_ARG;
+  if (nq > 1 && (fused || k8)) return PKV_ERR_INVALID_ARG;
   if (window < 0 || (window > 0 && (nq > 1 || k8 || prefix_tokens > 0))) return PKV_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(nq) * G > 16) return PKV_ERR_UNSUPPORTED;     // one 16-column matrix-core tile
@@ -1327,7 +1332,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   if (window > 0 && static_cast<int64_t>(window) > (static_cast<int64_t>(max_pages) - 1) * P + 1)
     return PKV_ERR_INVALID_ARG;
   Plan plan;
-  const int rc = make_plan(B, Hq, Hkv, max_context, partition_tokens, prefix_tokens, &plan);
+  const int rc = make_plan(B, Hq, Hkv, max_context, partition_tokens, prefix_tokens, &plan, nq);
   if (rc != PKV_OK) return rc;
   if (B == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !bt || !lens) return PKV_ERR_INVALID_ARG;
@@ -1364,8 +1369,8 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   prm.p_shift = p_shift;
   prm.max_context = max_context;
   prm.prefix_tokens = prefix_tokens;
-  // an appended token must land in a private page; each query of a chunk needs a token
-  prm.min_len = max(prefix_tokens + (fused && prefix_tokens > 0 ? 1 : 0), nq > 1 ? nq : 0);
+  // an appended token must land in a private page; a chunk of queries lies after the prefix
+  prm.min_len = nq > 1 ? prefix_tokens + nq : prefix_tokens + (fused && prefix_tokens > 0 ? 1 : 0);
   prm.nq = nq;
   prm.ring = window > 0 ? max_pages : 0;
   prm.window = window;
@@ -1511,10 +1516,10 @@ int pkv_block_table_patch(int32_t* block_table, int32_t B, int32_t max_pages, co
   return PKV_OK;
 }
 
-int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool, const int32_t* block_table,
-                  int32_t max_pages, const int32_t* pos, int32_t B, int32_t Hkv, int32_t D, int32_t P, int32_t N,
-                  void* stream) {
-  if (B < 0 || Hkv <= 0 || D <= 0 || P <= 0 || N <= 0 || max_pages <= 0) return PKV_ERR_INVALID_ARG;
+int pkv_kv_append_chunk(const void* k_new, const void* v_new, void* k_pool, void* v_pool, const int32_t* block_table,
+                        int32_t max_pages, const int32_t* pos, int32_t B, int32_t n_tokens, int32_t Hkv, int32_t D,
+                        int32_t P, int32_t N, void* stream) {
+  if (B < 0 || n_tokens <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || N <= 0 || max_pages <= 0) return PKV_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
   const int p_shift = log2_page(P);
   if (p_shift < 0) return PKV_ERR_UNSUPPORTED;
@@ -1523,7 +1528,7 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_po
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
       !aligned(block_table, 4) || !aligned(pos, 4))
     return PKV_ERR_INVALID_ARG;
-  const int64_t rows = static_cast<int64_t>(B) * Hkv;
+  const int64_t rows = static_cast<int64_t>(B) * n_tokens * Hkv;
   if (rows > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
   const int64_t pool_elems = static_cast<int64_t>(N) * Hkv * P * D;
   if (pool_elems / N / Hkv / P != D) return PKV_ERR_INVALID_ARG;
@@ -1534,11 +1539,17 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_po
   half_t* vp = static_cast<half_t*>(v_pool);
   if (D == 64)
     hipLaunchKernelGGL(kv_append_kernel<64>, dim3(static_cast<uint32_t>(rows)), dim3(64), 0, s, kn, vn, kp, vp,
-                       block_table, max_pages, pos, Hkv, p_shift, N);
+                       block_table, max_pages, pos, Hkv, p_shift, N, n_tokens);
   else
     hipLaunchKernelGGL(kv_append_kernel<128>, dim3(static_cast<uint32_t>(rows)), dim3(128), 0, s, kn, vn, kp, vp,
-                       block_table, max_pages, pos, Hkv, p_shift, N);
+                       block_table, max_pages, pos, Hkv, p_shift, N, n_tokens);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_pool, const int32_t* block_table,
+                  int32_t max_pages, const int32_t* pos, int32_t B, int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                  void* stream) {
+  return pkv_kv_append_chunk(k_new, v_new, k_pool, v_pool, block_table, max_pages, pos, B, 1, Hkv, D, P, N, stream);
 }
 
 int pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context, int32_t partition_tokens,
@@ -1643,6 +1654,19 @@ int pkv_paged_decode_attention_window(void* out, const void* q, const void* k_ne
   return decode_common(out, q, k_new, v_new, k_pool, v_pool, k_pool, v_pool, ring_table, ring_pages, lens, B, Hq, Hkv,
                        D, P, N, kWindowMaxLen, scale, partition_tokens, 0, workspace, workspace_bytes, stream, fused,
                        false, 1, window);
+}
+
+int pkv_paged_decode_attention_multi_shared_prefix(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                                   const int32_t* block_table, int32_t max_pages, const int32_t* lens,
+                                                   int32_t B, int32_t n_query, int32_t Hq, int32_t Hkv, int32_t D,
+                                                   int32_t P, int32_t N, int32_t max_context, float scale,
+                                                   int32_t partition_tokens, int32_t prefix_tokens, void* workspace,
+                                                   size_t workspace_bytes, void* stream) {
+  if (n_query < 1) return PKV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * n_query > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
+  return decode_common(out, q, nullptr, nullptr, k_pool, v_pool, nullptr, nullptr, block_table, max_pages, lens, B,
+                       Hq, Hkv, D, P, N, max_context, scale, partition_tokens, prefix_tokens, workspace,
+                       workspace_bytes, stream, false, false, n_query);
 }
 
 int pkv_paged_decode_attention_shared_prefix(void* out, const void* q, const void* k_new, const void* v_new,

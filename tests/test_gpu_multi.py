@@ -105,3 +105,79 @@ def test_multi_query_argument_checks():
         m.paged_decode_attention_multi(q, dev(w.k_pool), dev(w.v_pool), dev(w.block_table), dev(lens),
                                        int(lens.max()), w.scale, 512)
     assert e.value.status == m.PKV_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("batch,nq,part", [(6, 4, 512), (6, 2, 1024), (3, 3, 256), (None, 4, 1024), (5, 1, 512)])
+def test_multi_query_shared_prefix_matches_oracle(batch, nq, part):
+    """Chunks of queries over a batch sharing its first 2048 tokens: the prefix
+    read once per KV head and 16 chunk rows, the private blocks causal within
+    the chunk; against the oracle's chunked attention over the same table."""
+    m = pkv()
+    w = workload(3, batch=batch)
+    prefix = w.shared_prefix_pages * w.P
+    lens = w.lens(0)
+    kp, vp = poison_unused(w, lens)
+    rng = np.random.default_rng(70 + nq)
+    q = rng.standard_normal((w.B, nq, w.Hq, w.D)).astype(np.float16)
+    say("multi shared prefix B=%d nq=%d part=%d" % (w.B, nq, part))
+    got = m.paged_decode_attention_multi(dev(q), dev(kp), dev(vp), dev(w.block_table), dev(lens), int(lens.max()),
+                                         w.scale, part, prefix_tokens=prefix)
+    torch.cuda.synchronize()
+    sample = np.arange(w.B) if w.B <= 8 else np.linspace(0, w.B - 1, 8).astype(int)
+    ref = oracle.decode_attention_multi(q[sample], kp, vp, w.block_table[sample], lens[sample], w.scale, w.P)
+    check_close(torch.from_numpy(host(got)[sample]), ref, "multi shared prefix B=%d nq=%d" % (w.B, nq))
+    plain = m.paged_decode_attention_multi(dev(q), dev(kp), dev(vp), dev(w.block_table), dev(lens), int(lens.max()),
+                                           w.scale, part)
+    # the prefix path and the per-sequence path agree within the tolerance everywhere
+    err = np.abs(host(got).astype(np.float64) - host(plain).astype(np.float64)).max()
+    assert err <= TOL, err
+
+
+def test_multi_query_shared_prefix_rows_reaching_into_the_prefix_are_nan():
+    m = pkv()
+    w = workload(3, batch=4)
+    prefix = w.shared_prefix_pages * w.P
+    lens = w.lens(0).copy()
+    nq = 4
+    lens[1] = prefix + nq - 1          # the chunk's first query would sit in the prefix
+    lens[2] = prefix + nq              # the smallest valid length: the chunk right after the prefix
+    kp, vp = poison_unused(w, np.maximum(lens, prefix))
+    q = np.random.default_rng(5).standard_normal((w.B, nq, w.Hq, w.D)).astype(np.float16)
+    say("multi shared prefix short rows")
+    got = host(m.paged_decode_attention_multi(dev(q), dev(kp), dev(vp), dev(w.block_table), dev(lens),
+                                              int(lens.max()), w.scale, 512, prefix_tokens=prefix))
+    assert np.all(np.isnan(got[1].astype(np.float64)))
+    good = [0, 2, 3]
+    ref = oracle.decode_attention_multi(q[good], kp, vp, w.block_table[good], lens[good], w.scale, w.P)
+    check_close(torch.from_numpy(got[good]), ref, "multi shared prefix valid rows")
+
+
+@pytest.mark.parametrize("number,page_size,batch,nq", [(2, None, 3, 4), (5, 32, 5, 3), (3, None, 4, 16), (1, None, None, 2),
+                                                       (5, 128, 6, 7)])
+def test_kv_append_chunk_bit_exact(number, page_size, batch, nq):
+    """pkv_kv_append_chunk writes token i of every sequence at pos[b] + i: the
+    pools equal, byte for byte, the oracle's single-token append applied for
+    each i; tokens past the table or at negative positions are skipped."""
+    m = pkv()
+    w = workload(number, page_size=page_size, batch=batch)
+    width = w.block_table.shape[1] * w.P
+    pos0 = (w.context + w.steps - nq).astype(np.int32)         # the chunk ends at the last slot the table holds
+    if w.B >= 3:
+        pos0[1] = width - 1                                     # only its first token has a page
+        pos0[2] = -1                                            # skipped
+    rng = np.random.default_rng(nq)
+    kn = rng.standard_normal((w.B, nq, w.Hkv, w.D)).astype(np.float16)
+    vn = rng.standard_normal((w.B, nq, w.Hkv, w.D)).astype(np.float16)
+    kd, vd = dev(w.k_pool), dev(w.v_pool)
+    say("append chunk", w.name, "B=%d nq=%d P=%d" % (w.B, nq, w.P))
+    m.kv_append_chunk(dev(kn), dev(vn), kd, vd, dev(w.block_table), dev(pos0))
+    torch.cuda.synchronize()
+    rk, rv = w.k_pool, w.v_pool
+    for i in range(nq):
+        t = pos0.astype(np.int64) + i
+        sel = np.nonzero((pos0 >= 0) & (t < width))[0]
+        sel = np.array([b for b in sel if w.block_table[b, t[b] // w.P] >= 0], dtype=np.int64)
+        if len(sel):
+            rk, rv = oracle.kv_append(rk, rv, kn[sel, i], vn[sel, i], w.block_table[sel], t[sel].astype(np.int32), w.P)
+    assert np.array_equal(host(kd).view(np.uint16), rk.view(np.uint16))
+    assert np.array_equal(host(vd).view(np.uint16), rv.view(np.uint16))
