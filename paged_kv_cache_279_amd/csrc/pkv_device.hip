@@ -80,6 +80,7 @@ constexpr int kBlk = 16;                   // tokens per block (= one sub-block)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr size_t kWsAlign = 256;
 constexpr int32_t kMaxPartitions = 1024;   // partial slots per (sequence, head) (reduce kernel LDS)
+constexpr uint32_t kWaveMergeRows = 4096;  // output rows from which the one-wave-per-row merge runs
 #ifndef PKV_MAX_FLAT_BATCH
 #define PKV_MAX_FLAT_BATCH 4096
 #endif
@@ -1179,6 +1180,99 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
   p.out[bh * D + d] = (half_t)res;
 }
 
+// The same merge with one wave per row (four rows per workgroup, lane l
+// holding output dims l and l + 64): no LDS and no barriers; lane j loads
+// partial j's max (64 at a time) and a shuffle tree gives the row max; the
+// partials' outputs are accumulated in order, kR at a time, exactly as
+// above. Calls with many rows (chunks of queries) take this one: half the
+// waves of the kernel above, and it keeps up when thousands of rows queue.
+template <int D>
+__global__ __launch_bounds__(kThreads) void lse_reduce_wave_kernel(DecodeParams p) {
+  constexpr int kR = 8;               // partials loaded per batch
+  constexpr int DPL = D / kWave;      // output dims per lane
+  static_assert(D % kWave == 0, "D is a multiple of the wave size");
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t bh = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);   // row (b * nq + query) * Hq + h of out
+  if (bh >= (int64_t)p.B * p.nq * p.Hq) return;                            // the whole wave
+  const int32_t b = (int32_t)(bh / ((int64_t)p.nq * p.Hq));
+  const int32_t qi = (int32_t)((bh / p.Hq) % p.nq);
+  const int32_t h = (int32_t)(bh % p.Hq);
+  const int32_t G = p.Hq / p.Hkv;
+  const int32_t kvh = h / G;
+  const int32_t hg = h % G;
+  const int32_t L = p.lens[b];
+  const bool bad_len = L < p.min_len || L > p.max_context || (p.ring == 0 && L > (p.max_pages << p.p_shift));
+  const int32_t Qv = p.flat_hdr[1];
+  const int32_t Qp = p.flat_hdr[2];
+  const int32_t Wk = p.n_flat_wgs / p.Hkv;
+  const int32_t PB = p.prefix_tokens / kBlk;
+  const int64_t slot_base = (int64_t)kvh * (p.n_tiles + p.B + 2 * Wk);
+  const int32_t r = (b * p.nq + qi) * G + hg;
+  const int32_t rt = r / 16;
+  const int32_t ct = r % 16;
+  int32_t np1 = 0, ja = 0;
+  if (PB > 0) {
+    const int32_t u0 = rt * PB;
+    ja = u0 / Qp;
+    np1 = (u0 + PB - 1) / Qp - ja + 1;
+  }
+  const int32_t prev = b > 0 ? p.flat_cum[b - 1] : 0;
+  const int32_t nblk = p.flat_cum[b] - prev;
+  int32_t np2 = 0, jb = 0;
+  if (nblk > 0) {
+    jb = prev / Qv;
+    np2 = (prev + nblk - 1) / Qv - jb + 1;
+  }
+  const int32_t np = bad_len ? 0 : np1 + np2;
+  auto idx = [&](int32_t j) -> int64_t {
+    return j < np1 ? (slot_base + rt + ja + j) * 16 + ct
+                   : (slot_base + p.n_tiles + Wk + b + jb + (j - np1)) * 16 + qi * G + hg;
+  };
+  const float* po = p.flat_o + lane;
+  float mv[kR], lv[kR], ov[kR][DPL];
+  auto load_batch = [&](int32_t j0) {
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      const bool live = j0 + k < np;
+      const int64_t q = live ? idx(j0 + k) : 0;
+      mv[k] = live ? p.flat_m[q] : 0.f;
+      lv[k] = live ? p.flat_l[q] : 0.f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) ov[k][e] = live ? po[q * D + e * kWave] : 0.f;
+    }
+  };
+  load_batch(0);
+  float M = kNegInf();
+  for (int32_t j0 = 0; j0 < np; j0 += kWave) {
+    const int32_t j = j0 + lane;
+    M = fmaxf(M, j < np ? p.flat_m[idx(j)] : kNegInf());
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
+  const float Ms = M == kNegInf() ? 0.f : M;
+  float Ls = 0.f, O[DPL];
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) O[e] = 0.f;
+  for (int32_t j0 = 0; j0 < np; j0 += kR) {
+    if (j0 > 0) load_batch(j0);
+#pragma unroll
+    for (int k = 0; k < kR; ++k) {
+      if (j0 + k < np) {
+        const float wj = fast_exp2(mv[k] - Ms);
+        Ls = fmaf(wj, lv[k], Ls);
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) O[e] = fmaf(wj, ov[k][e], O[e]);
+      }
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < DPL; ++e) {
+    float res = Ls > 0.f ? O[e] / Ls : 0.f;
+    if (bad_len || Ls != Ls) res = __builtin_nanf("");
+    p.out[bh * D + lane + e * kWave] = (half_t)res;
+  }
+}
+
 // -------------------------------------------------------------------------
 // host side
 // -------------------------------------------------------------------------
@@ -1417,8 +1511,15 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   }
   if (plan.split) {
     const uint32_t rows = static_cast<uint32_t>(static_cast<int64_t>(B) * nq * Hq);
-    if (D == 64) hipLaunchKernelGGL(lse_reduce_kernel<64>, dim3(rows), dim3(64), 0, s, prm);
-    else hipLaunchKernelGGL(lse_reduce_kernel<128>, dim3(rows), dim3(128), 0, s, prm);
+    if (rows >= kWaveMergeRows) {
+      const uint32_t wgs = (rows + kWaves - 1) / kWaves;        // one wave per row
+      if (D == 64) hipLaunchKernelGGL(lse_reduce_wave_kernel<64>, dim3(wgs), dim3(kThreads), 0, s, prm);
+      else hipLaunchKernelGGL(lse_reduce_wave_kernel<128>, dim3(wgs), dim3(kThreads), 0, s, prm);
+    } else if (D == 64) {
+      hipLaunchKernelGGL(lse_reduce_kernel<64>, dim3(rows), dim3(64), 0, s, prm);
+    } else {
+      hipLaunchKernelGGL(lse_reduce_kernel<128>, dim3(rows), dim3(128), 0, s, prm);
+    }
     if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   }
   return PKV_OK;
