@@ -67,7 +67,8 @@ typedef enum pkv_status {
   PKV_ERR_WORKSPACE_TOO_SMALL = 4,  /* split decode given too little workspace */
   PKV_ERR_HIP = 5,                  /* a kernel launch failed */
   PKV_ERR_INVALID_TABLE = 6,        /* pkv_validate_tables found a bad entry */
-  PKV_ERR_NOT_FOUND = 7             /* pkv_alloc_cache_lookup: no entry under the key */
+  PKV_ERR_NOT_FOUND = 7,            /* pkv_alloc_cache_lookup: no entry under the key */
+  PKV_ERR_HOST_MEMORY = 8           /* the host allocator's own bookkeeping could not grow */
 } pkv_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -475,6 +476,9 @@ int pkv_profile_next_partition_kernel(void* start_event, void* stop_event);
  *     when its count reaches zero.
  * Sequence ids are caller-chosen non-negative int32. One allocator may be used
  * from several threads (calls are serialised internally).
+ * Every allocator call may also return PKV_ERR_HOST_MEMORY when host memory
+ * for its own tables runs out; the allocator's state is then unspecified and
+ * it should be destroyed. No C++ exception leaves the library.
  */
 typedef struct pkv_allocator pkv_allocator;
 

@@ -14,6 +14,7 @@ from .binding import (  # noqa: F401
     PKV_ERR_HIP,
     PKV_ERR_INVALID_TABLE,
     PKV_ERR_NOT_FOUND,
+    PKV_ERR_HOST_MEMORY,
     PkvError,
     PageAllocator,
     append_paged_decode_attention,

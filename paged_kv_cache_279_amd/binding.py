@@ -25,6 +25,7 @@ PKV_ERR_WORKSPACE_TOO_SMALL = 4
 PKV_ERR_HIP = 5
 PKV_ERR_INVALID_TABLE = 6
 PKV_ERR_NOT_FOUND = 7
+PKV_ERR_HOST_MEMORY = 8
 
 _i32 = ctypes.c_int32
 _vp = ctypes.c_void_p

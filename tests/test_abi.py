@@ -40,7 +40,8 @@ def test_status_strings_and_version(pkv):
     assert pkv.lib().pkv_abi_version() == 1
     for code, name in [(0, "PKV_OK"), (1, "PKV_ERR_INVALID_ARG"), (2, "PKV_ERR_UNSUPPORTED"),
                        (3, "PKV_ERR_OUT_OF_PAGES"), (4, "PKV_ERR_WORKSPACE_TOO_SMALL"), (5, "PKV_ERR_HIP"),
-                       (6, "PKV_ERR_INVALID_TABLE"), (7, "PKV_ERR_NOT_FOUND"), (99, "PKV_ERR_UNKNOWN")]:
+                       (6, "PKV_ERR_INVALID_TABLE"), (7, "PKV_ERR_NOT_FOUND"), (8, "PKV_ERR_HOST_MEMORY"),
+                       (99, "PKV_ERR_UNKNOWN")]:
         assert pkv.status_string(code) == name
 
 
