@@ -256,12 +256,12 @@ def decode_attention_multi(q, k_pool, v_pool, block_table, lens, scale, page_siz
     """
     b_count, k, hq, d = q.shape
     out = np.zeros((b_count, k, hq, d), dtype=np.float64)
+    lens64 = np.asarray(lens, dtype=np.int64)
+    short = lens64 < k                  # the chunk would reach before token 0: the whole row is invalid
     for i in range(k):
-        li = np.asarray(lens, dtype=np.int64) - k + i + 1
-        valid = li >= 1
-        li_safe = np.where(valid, li, 0)
-        out[:, i] = decode_attention(q[:, i], k_pool, v_pool, block_table, li_safe, scale, page_size)
-        out[~valid, i] = np.nan
+        li = np.where(short, 0, lens64 - k + i + 1)
+        out[:, i] = decode_attention(q[:, i], k_pool, v_pool, block_table, li, scale, page_size)
+    out[short] = np.nan
     return out
 
 

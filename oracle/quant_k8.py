@@ -161,6 +161,25 @@ def decode_attention_k8(q, pool8, v_pool, block_table, lens, scale, page_size):
     return out
 
 
+def decode_attention_multi_k8(q, pool8, v_pool, block_table, lens, scale, page_size):
+    """Chunks of queries over int8 keys: ``q`` is ``[B][k][Hq][D]``, query ``i``
+    of sequence ``b`` sits at position ``lens[b] - k + i`` and sees tokens
+    ``0 .. lens[b] - k + i`` (the reading of chunked attention taken for fp16
+    keys in ``decode_attention_multi``), each query computed as the int8-key
+    decode step over its own prefix (``decode_attention_k8`` with length
+    ``lens[b] - k + i + 1``). Returns float64 ``[B][k][Hq][D]``; a row with
+    ``lens[b] < k`` is all NaN."""
+    b_count, k, hq, d = q.shape
+    out = np.zeros((b_count, k, hq, d), dtype=np.float64)
+    lens64 = np.asarray(lens, dtype=np.int64)
+    short = lens64 < k                  # the chunk would reach before token 0: the whole row is invalid
+    for i in range(k):
+        li = np.where(short, 0, lens64 - k + i + 1)
+        out[:, i] = decode_attention_k8(q[:, i], pool8, v_pool, block_table, li, scale, page_size)
+    out[short] = np.nan
+    return out
+
+
 def kv_append_k8(pool8, v_pool, k_new, v_new, block_table, pos, page_size):
     """Copies of the pools with each sequence's new token written: its key
     quantised (``quantize_k``) into the int8 pool, its value as fp16 (the

@@ -213,3 +213,63 @@ def test_planted_mistake_is_caught(old, new):
     exec(compile(src.replace(old, new), "<mutant>", "exec"), mutant.__dict__)
     assert _k8_pins_pass(quant_k8)
     assert not _k8_pins_pass(mutant), "planted mistake not detected: %r -> %r" % (old, new)
+
+
+# ---------------------------------------------------------------------------
+# chunks of queries over int8 keys
+# ---------------------------------------------------------------------------
+
+def _check_multi_k8(fn, seed=21):
+    """Brute force: the causal textbook over the contiguous dequantised keys
+    (each token's codes and scale from the quantiser) against the oracle
+    reading int8 pages in permuted order; k = 1 is single-query int8 decode."""
+    from test_oracle_multi import causal_textbook
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, D, P, k = 2, 4, 2, 64, 16, 3
+    G = Hq // Hkv
+    N = 8
+    lens = np.array([k + 2, 41], np.int32)
+    kp = _paged_fp16_pool(rng, N, Hkv, P, D)
+    vp = _paged_fp16_pool(rng, N, Hkv, P, D)
+    pool8 = oracle.quantize_k_pool(kp)
+    perm = rng.permutation(N).astype(np.int32)
+    bt = np.stack([perm[:3], perm[3:6]]).astype(np.int32)
+    q = _fp16(rng.standard_normal((B, k, Hq, D)))
+    got = fn(q, pool8, vp, bt, lens, 0.125, P)
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // G
+            K, V = [], []
+            for t in range(int(lens[b])):
+                page, off = int(bt[b, t // P]), t % P
+                codes, sc = oracle.quantize_k(oracle.read_token(kp, page, kvh, off, "k"))
+                K.append((codes.astype(np.float64) * float(sc)).tolist())
+                V.append(oracle.read_token(vp, page, kvh, off, "v").astype(np.float64).tolist())
+            ref = causal_textbook(q[b, :, h].astype(np.float64).tolist(), K, V, float(np.float32(0.125)))
+            np.testing.assert_allclose(got[b, :, h], ref, rtol=0, atol=1e-12)
+    one = fn(q[:, -1:], pool8, vp, bt, lens, 0.125, P)
+    np.testing.assert_array_equal(one[:, 0], oracle.decode_attention_k8(q[:, -1], pool8, vp, bt, lens, 0.125, P))
+    short = fn(q, pool8, vp, bt, np.array([k - 1, 41], np.int32), 0.125, P)
+    assert np.all(np.isnan(short[0])) and np.all(np.isfinite(short[1]))
+
+
+def test_multi_k8_brute_force():
+    _check_multi_k8(oracle.decode_attention_multi_k8)
+
+
+@pytest.mark.parametrize("old,new", [
+    ("li = np.where(short, 0, lens64 - k + i + 1)\n        out[:, i] = decode_attention_k8",
+     "li = np.where(short, 0, lens64 - k + i)\n        out[:, i] = decode_attention_k8"),
+    ("out[:, i] = decode_attention_k8(q[:, i],", "out[:, i] = decode_attention_k8(q[:, k - 1 - i],"),
+    ("short = lens64 < k                  # the chunk would reach before token 0: the whole row is invalid\n    for i in range(k):\n        li = np.where(short, 0, lens64 - k + i + 1)\n        out[:, i] = decode_attention_k8",
+     "short = lens64 < 1                  # the chunk would reach before token 0: the whole row is invalid\n    for i in range(k):\n        li = np.where(short, 0, lens64 - k + i + 1)\n        out[:, i] = decode_attention_k8"),
+])
+def test_multi_k8_planted_mistake_is_caught(old, new):
+    src = open(quant_k8.__file__).read()
+    assert src.count(old) == 1, old
+    mutant = types.ModuleType("oracle.quant_k8_mutant")
+    mutant.__dict__["__file__"] = "<mutant>"
+    mutant.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), mutant.__dict__)
+    with pytest.raises(AssertionError):
+        _check_multi_k8(mutant.decode_attention_multi_k8)

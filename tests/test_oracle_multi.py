@@ -82,8 +82,8 @@ def test_causality_within_the_chunk():
     moved = oracle.decode_attention_multi(qm, kp2, vp, bt, lens, 0.3, P)
     assert np.array_equal(moved[:, :-1], base[:, :-1])
     assert not np.allclose(moved[:, -1], base[:, -1])
-    # a sequence shorter than the chunk has NaN rows for the queries before its start
+    # a sequence shorter than the chunk is an invalid row: all of it NaN, the others untouched
     short = lens.copy()
     short[0] = 2
     nanrows = oracle.decode_attention_multi(qm, kp, vp, bt, short, 0.3, P)
-    assert np.all(np.isnan(nanrows[0, :2])) and np.all(np.isfinite(nanrows[0, 2:]))
+    assert np.all(np.isnan(nanrows[0])) and np.array_equal(nanrows[1], base[1])
