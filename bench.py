@@ -270,8 +270,8 @@ def main():
         raise SystemExit("the sliding-window workload runs fp16 keys, one query, the fused append, eagerly")
     if w.steps == 0:
         raise SystemExit("workload %d has no append; pick 2-5" % args.workload)
-    if KQ > 1 and (k8 or args.graph):
-        raise SystemExit("--n-query runs without int8 keys or graphs")
+    if KQ > 1 and args.graph:
+        raise SystemExit("--n-query runs without graphs")
     log("workload %s: B=%d Hq=%d Hkv=%d D=%d P=%d part=%d layers=%d fused=%s" % (w.name, B, Hq, Hkv, D, P, part, R,
                                                                                   fused))
 
@@ -374,10 +374,16 @@ def main():
                                               k_new=kn, v_new=vn, out=out, workspace=workspace, stream=s)
         elif KQ > 1:
             # pos [B], kn / vn [B][K][Hkv][D]: the chunk's K tokens in one append launch, then its attention
-            pkv.kv_append_chunk(kn, vn, k_pools[layer], v_pools[layer], bt_dev, pos, stream=s)
-            pkv.paged_decode_attention_multi(q_mq, k_pools[layer], v_pools[layer], bt_dev, lens, max_context, scale,
-                                             part, out=out_mq, workspace=workspace, stream=s,
-                                             prefix_tokens=prefix_tokens)
+            if k8:
+                pkv.kv_append_k8_chunk(kn, vn, k_pools[layer], v_pools[layer], bt_dev, pos, stream=s)
+                pkv.paged_decode_attention_multi_k8(q_mq, k_pools[layer], v_pools[layer], bt_dev, lens, max_context,
+                                                    scale, part, prefix_tokens=prefix_tokens, out=out_mq,
+                                                    workspace=workspace, stream=s)
+            else:
+                pkv.kv_append_chunk(kn, vn, k_pools[layer], v_pools[layer], bt_dev, pos, stream=s)
+                pkv.paged_decode_attention_multi(q_mq, k_pools[layer], v_pools[layer], bt_dev, lens, max_context,
+                                                 scale, part, out=out_mq, workspace=workspace, stream=s,
+                                                 prefix_tokens=prefix_tokens)
         elif k8:
             if not fused:
                 pkv.kv_append_k8(kn, vn, k_pools[layer], v_pools[layer], bt_dev, pos, stream=s)
@@ -454,11 +460,13 @@ def main():
         kn0, vn0 = knew_mq[0].cpu().numpy(), vnew_mq[0].cpu().numpy()
         kpool_full = k_pools[0].cpu().numpy()            # pages beyond the workload's pool were drawn on device
         vpool_full = v_pools[0].cpu().numpy()
+        append = oracle.kv_append_k8 if k8 else oracle.kv_append
         for i in range(KQ):
-            kpool_full, vpool_full = oracle.kv_append(kpool_full, vpool_full, kn0[:, i], vn0[:, i], bt0,
-                                                      (w.context + i).astype(np.int32), P)
-        ref = oracle.decode_attention_multi(q_mq.cpu().numpy()[sample], kpool_full, vpool_full, bt0[sample],
-                                            (w.context + KQ).astype(np.int32)[sample], scale, P)
+            kpool_full, vpool_full = append(kpool_full, vpool_full, kn0[:, i], vn0[:, i], bt0,
+                                            (w.context + i).astype(np.int32), P)
+        chunk = oracle.decode_attention_multi_k8 if k8 else oracle.decode_attention_multi
+        ref = chunk(q_mq.cpu().numpy()[sample], kpool_full, vpool_full, bt0[sample],
+                    (w.context + KQ).astype(np.int32)[sample], scale, P)
     elif W:
         kp0, vp0 = oracle.kv_append(w.k_pool, w.v_pool, w.k_new[0], w.v_new[0],
                                     logical_table(w.block_table, int(w.lens(0).max()), P), w.pos(0), P)

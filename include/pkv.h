@@ -405,6 +405,18 @@ int pkv_kv_append_k8(const void* k_new, const void* v_new, void* k_pool8, void* 
                      void* stream);
 
 /*
+ * pkv_kv_append_k8_chunk -- pkv_kv_append_k8 for n_tokens consecutive tokens
+ * per sequence in one launch (k_new, v_new fp16 [B][n_tokens][Hkv][D]; token
+ * i of sequence b goes to position pos[b] + i), each key quantised on its
+ * own as in pkv_kv_append_k8. Positions outside the table and page ids
+ * outside [0, N) skip that token. Other arguments and errors as
+ * pkv_kv_append_k8; n_tokens >= 1.
+ */
+int pkv_kv_append_k8_chunk(const void* k_new, const void* v_new, void* k_pool8, void* v_pool,
+                           const int32_t* block_table, int32_t max_pages, const int32_t* pos, int32_t B,
+                           int32_t n_tokens, int32_t Hkv, int32_t D, int32_t P, int32_t N, void* stream);
+
+/*
  * pkv_paged_decode_attention_k8 -- pkv_paged_decode_attention_shared_prefix
  * (prefix_tokens == 0: no shared prefix, and then partition_tokens may be 0)
  * over int8 keys: s_t = scale * scale_t * <q, code_t>, the rest as for fp16
@@ -422,6 +434,24 @@ int pkv_paged_decode_attention_k8(void* out, const void* q, const void* k_new, c
                                   int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
                                   int32_t max_context, float scale, int32_t partition_tokens, int32_t prefix_tokens,
                                   void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_paged_decode_attention_multi_k8 -- chunks of queries (as
+ * pkv_paged_decode_attention_multi: query i of sequence b at position
+ * lens[b] - n_query + i, causal within the chunk) over int8-key pages: the
+ * attention of verifying drafted tokens against a quantised cache. The
+ * chunk's keys and values must be in the pools already
+ * (pkv_kv_append_k8_chunk). prefix_tokens > 0 reads a shared prefix as
+ * pkv_paged_decode_attention_multi_shared_prefix does (workspace from
+ * pkv_decode_workspace_bytes_shared_prefix(B * n_query, ...)); 0 takes the
+ * workspace of pkv_decode_workspace_bytes. Other arguments and errors as
+ * pkv_paged_decode_attention_multi.
+ */
+int pkv_paged_decode_attention_multi_k8(void* out, const void* q, const void* k_pool8, const void* v_pool,
+                                        const int32_t* block_table, int32_t max_pages, const int32_t* lens, int32_t B,
+                                        int32_t n_query, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                                        int32_t max_context, float scale, int32_t partition_tokens,
+                                        int32_t prefix_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * pkv_probe_stream_read -- measurement aid (not part of decode): read

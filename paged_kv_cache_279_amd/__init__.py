@@ -25,10 +25,12 @@ from .binding import (  # noqa: F401
     kv_append,
     kv_append_chunk,
     kv_append_k8,
+    kv_append_k8_chunk,
     lib,
     paged_decode_attention,
     paged_decode_attention_k8,
     paged_decode_attention_multi,
+    paged_decode_attention_multi_k8,
     paged_decode_attention_shared_prefix,
     paged_decode_attention_window,
     probe_stream_read,

@@ -51,6 +51,11 @@ _SIGNATURES = {
                                                                       _i32, _i32, _i32, _i32, _i32, _i32,
                                                                       ctypes.c_float, _i32, _i32, _vp,
                                                                       ctypes.c_size_t, _vp]),
+    "pkv_kv_append_k8_chunk": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                               _vp]),
+    "pkv_paged_decode_attention_multi_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
+                                                           _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _i32, _vp,
+                                                           ctypes.c_size_t, _vp]),
     "pkv_kv_append_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_paged_decode_attention_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                                      _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _i32, _vp,
@@ -331,6 +336,50 @@ def kv_append_k8(k_new, v_new, k_pool8, v_pool, block_table, pos, stream=None):
                                   _dev_ptr(block_table, torch.int32, "block_table"), max_pages,
                                   _dev_ptr(pos, torch.int32, "pos"), B, Hkv, D, P, N, _stream(stream)),
            "pkv_kv_append_k8")
+
+
+def kv_append_k8_chunk(k_new, v_new, k_pool8, v_pool, block_table, pos, stream=None):
+    """pkv_kv_append_k8_chunk: k_new/v_new [B][n_tokens][Hkv][D]; token i of sequence b goes to
+    position pos[b] + i, its key quantised into the int8-key pool."""
+    N, Hkv, P, D = _k8_shape(k_pool8, v_pool)
+    B, max_pages = block_table.shape
+    if k_new.dim() != 4 or tuple(k_new.shape) != tuple(v_new.shape) or k_new.shape[0] != B or \
+            tuple(k_new.shape[2:]) != (Hkv, D) or tuple(pos.shape) != (B,):
+        raise ValueError("k_new/v_new must be [B][n_tokens][Hkv][D], pos [B]")
+    _check(lib().pkv_kv_append_k8_chunk(_dev_ptr(k_new, torch.float16, "k_new"),
+                                        _dev_ptr(v_new, torch.float16, "v_new"),
+                                        _dev_ptr(k_pool8, torch.uint8, "k_pool8"),
+                                        _dev_ptr(v_pool, torch.float16, "v_pool"),
+                                        _dev_ptr(block_table, torch.int32, "block_table"), max_pages,
+                                        _dev_ptr(pos, torch.int32, "pos"), B, int(k_new.shape[1]), Hkv, D, P, N,
+                                        _stream(stream)), "pkv_kv_append_k8_chunk")
+
+
+def paged_decode_attention_multi_k8(q, k_pool8, v_pool, block_table, lens, max_context, scale, partition_tokens=0,
+                                    prefix_tokens=0, out=None, workspace=None, stream=None):
+    """pkv_paged_decode_attention_multi_k8: chunks of queries q [B][n_query][Hq][D] over int8
+    keys and fp16 values; returns ``out`` [B][n_query][Hq][D]."""
+    N, Hkv, P, D = _k8_shape(k_pool8, v_pool)
+    B, nq, Hq, Dq = q.shape
+    _, max_pages = block_table.shape
+    if Dq != D or block_table.shape[0] != B or tuple(lens.shape) != (B,):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((B, nq, Hq, D), dtype=torch.float16, device=q.device)
+    if tuple(out.shape) != (B, nq, Hq, D):
+        raise ValueError("out must be [B][n_query][Hq][D]")
+    if prefix_tokens:
+        ws_bytes = decode_workspace_bytes(B * nq, Hq, D, max_context, partition_tokens, prefix_tokens)
+    else:
+        ws_bytes = decode_workspace_bytes(B, Hq, D, max_context, partition_tokens)
+    ws_ptr, ws_len = _workspace_arg(workspace, ws_bytes, q.device)
+    rc = lib().pkv_paged_decode_attention_multi_k8(
+        _dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"), _dev_ptr(k_pool8, torch.uint8, "k_pool8"),
+        _dev_ptr(v_pool, torch.float16, "v_pool"), _dev_ptr(block_table, torch.int32, "block_table"), max_pages,
+        _dev_ptr(lens, torch.int32, "lens"), B, nq, Hq, Hkv, D, P, N, int(max_context), float(scale),
+        int(partition_tokens), int(prefix_tokens), ws_ptr, ws_len, _stream(stream))
+    _check(rc, "pkv_paged_decode_attention_multi_k8")
+    return out
 
 
 def paged_decode_attention_k8(q, k_pool8, v_pool, block_table, lens, max_context, scale, partition_tokens=0,

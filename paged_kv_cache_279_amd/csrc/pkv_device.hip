@@ -318,16 +318,20 @@ __global__ __launch_bounds__(D) void kv_append_k8_kernel(const half_t* __restric
                                                          const half_t* __restrict__ v_new, uint8_t* __restrict__ k8,
                                                          half_t* __restrict__ v_pool, const int32_t* __restrict__ bt,
                                                          int32_t max_pages, const int32_t* __restrict__ pos,
-                                                         int32_t Hkv, int32_t p_shift, int32_t N) {
+                                                         int32_t Hkv, int32_t p_shift, int32_t N, int32_t n_tokens) {
   __shared__ float sm_max[D / kWave];
+  // workgroup (sequence b, token i of its chunk, KV head): token i goes to position pos[b] + i
   const int32_t kvh = blockIdx.x % Hkv;
-  const int32_t b = blockIdx.x / Hkv;
+  const int32_t bi = blockIdx.x / Hkv;
+  const int32_t b = bi / n_tokens;
   const int d = threadIdx.x;
-  const int32_t t = pos[b];
-  if (t < 0 || (t >> p_shift) >= max_pages) return;
+  const int32_t p0 = pos[b];
+  if (p0 < 0 || p0 > 0x7fffffff - n_tokens) return;
+  const int32_t t = p0 + bi % n_tokens;
+  if ((t >> p_shift) >= max_pages) return;
   const int32_t page = bt[(int64_t)b * max_pages + (t >> p_shift)];
   if (page < 0 || page >= N) return;
-  const int64_t src = ((int64_t)b * Hkv + kvh) * D;
+  const int64_t src = ((int64_t)bi * Hkv + kvh) * D;
   const float kv = (float)k_new[src + d];
   float m = fabsf(kv);
   for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -871,7 +875,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
 // step, so the slots are distinct; each slot holds 16 columns.
 template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ, bool WIN = false>
 __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodeParams p) {
-  static_assert(!MQ || (!FUSED && !K8), "chunks of queries: fp16 keys, no fused append");
+  static_assert(!MQ || !FUSED, "chunks of queries: no fused append");
   static_assert(!WIN || (!MQ && !K8), "sliding window: fp16 keys, single queries");
   static_assert(D % 32 == 0 && G >= 1 && G <= 16, "shape");
   const int lane = threadIdx.x & (kWave - 1);
@@ -891,7 +895,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
       return;
     }
     const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
-    run_range<D, 16, kKvLoadPolicy, false, false, true>(
+    run_range<D, 16, kKvLoadPolicy, false, K8, true>(
         p, smem.tile.prefix, bt_row, kvh, 0, L, 0, 0, NewToken{-1, 0, nullptr, nullptr},
         [&](int c) -> int64_t { return c < ncol ? row(c) : -1; },
         [&](int c, int d, float, float Ls, float O) {
@@ -1066,7 +1070,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
         if constexpr (MQ) {
           // columns (query i, head g) = i * G + g of the chunk of the last nq tokens
           const int32_t ncol = p.nq * G;
-          run_range<D, 16, kKvLoadPolicy, false, false, true>(
+          run_range<D, 16, kKvLoadPolicy, false, K8, true>(
               p, smem.tile.prefix, bt_row, kvh, start, end, quota, after + g1 - g - piece_n, nt,
               [&](int c) -> int64_t {
                 return c < ncol ? ((int64_t)b * p.nq + c / G) * p.Hq + (int64_t)kvh * G + c % G : -1;
@@ -1411,7 +1415,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
     return PKV_ERR_INVALID_ARG;
   const int G = Hq / Hkv;
   if (nq < 1) return PKV_ERR_INVALID_ARG;
-  if (nq > 1 && (fused || k8)) return PKV_ERR_INVALID_ARG;
+  if (nq > 1 && fused) return PKV_ERR_INVALID_ARG;
   if (window < 0 || (window > 0 && (nq > 1 || k8 || prefix_tokens > 0))) return PKV_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(nq) * G > 16) return PKV_ERR_UNSUPPORTED;     // one 16-column matrix-core tile
@@ -1496,6 +1500,9 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
     else if (window > 0)
       e = plan.split ? dispatch_d<true, false, false, false, true>(D, G, prm, s, grid)
                      : dispatch_d<false, false, false, false, true>(D, G, prm, s, grid);
+    else if (nq > 1 && k8)
+      e = plan.split ? dispatch_d<true, false, true, true>(D, G, prm, s, grid)
+                     : dispatch_d<false, false, true, true>(D, G, prm, s, grid);
     else if (nq > 1)
       e = plan.split ? dispatch_d<true, false, false, true>(D, G, prm, s, grid)
                      : dispatch_d<false, false, false, true>(D, G, prm, s, grid);
@@ -1690,10 +1697,10 @@ int pkv_k8_pool_bytes(int32_t N, int32_t Hkv, int32_t P, int32_t D, size_t* byte
   return PKV_OK;
 }
 
-int pkv_kv_append_k8(const void* k_new, const void* v_new, void* k_pool8, void* v_pool, const int32_t* block_table,
-                     int32_t max_pages, const int32_t* pos, int32_t B, int32_t Hkv, int32_t D, int32_t P, int32_t N,
-                     void* stream) {
-  if (B < 0 || Hkv <= 0 || D <= 0 || P <= 0 || N <= 0 || max_pages <= 0) return PKV_ERR_INVALID_ARG;
+int pkv_kv_append_k8_chunk(const void* k_new, const void* v_new, void* k_pool8, void* v_pool,
+                           const int32_t* block_table, int32_t max_pages, const int32_t* pos, int32_t B,
+                           int32_t n_tokens, int32_t Hkv, int32_t D, int32_t P, int32_t N, void* stream) {
+  if (B < 0 || n_tokens <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || N <= 0 || max_pages <= 0) return PKV_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
   const int p_shift = log2_page(P);
   if (p_shift < 0) return PKV_ERR_UNSUPPORTED;
@@ -1702,7 +1709,7 @@ int pkv_kv_append_k8(const void* k_new, const void* v_new, void* k_pool8, void* 
   if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pool8, 16) || !aligned(v_pool, 16) ||
       !aligned(block_table, 4) || !aligned(pos, 4))
     return PKV_ERR_INVALID_ARG;
-  const int64_t rows = static_cast<int64_t>(B) * Hkv;
+  const int64_t rows = static_cast<int64_t>(B) * n_tokens * Hkv;
   if (rows > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
   const int64_t pool_elems = static_cast<int64_t>(N) * Hkv * P * D;
   if (pool_elems / N / Hkv / P != D) return PKV_ERR_INVALID_ARG;
@@ -1713,11 +1720,18 @@ int pkv_kv_append_k8(const void* k_new, const void* v_new, void* k_pool8, void* 
   half_t* vp = static_cast<half_t*>(v_pool);
   if (D == 64)
     hipLaunchKernelGGL(kv_append_k8_kernel<64>, dim3(static_cast<uint32_t>(rows)), dim3(64), 0, s, kn, vn, k8, vp,
-                       block_table, max_pages, pos, Hkv, p_shift, N);
+                       block_table, max_pages, pos, Hkv, p_shift, N, n_tokens);
   else
     hipLaunchKernelGGL(kv_append_k8_kernel<128>, dim3(static_cast<uint32_t>(rows)), dim3(128), 0, s, kn, vn, k8, vp,
-                       block_table, max_pages, pos, Hkv, p_shift, N);
+                       block_table, max_pages, pos, Hkv, p_shift, N, n_tokens);
   return hipGetLastError() == hipSuccess ? PKV_OK : PKV_ERR_HIP;
+}
+
+int pkv_kv_append_k8(const void* k_new, const void* v_new, void* k_pool8, void* v_pool, const int32_t* block_table,
+                     int32_t max_pages, const int32_t* pos, int32_t B, int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                     void* stream) {
+  return pkv_kv_append_k8_chunk(k_new, v_new, k_pool8, v_pool, block_table, max_pages, pos, B, 1, Hkv, D, P, N,
+                                stream);
 }
 
 int pkv_paged_decode_attention_k8(void* out, const void* q, const void* k_new, const void* v_new, void* k_pool8,
@@ -1730,6 +1744,19 @@ int pkv_paged_decode_attention_k8(void* out, const void* q, const void* k_new, c
   return decode_common(out, q, k_new, v_new, k_pool8, v_pool, k_pool8, v_pool, block_table, max_pages, lens, B, Hq,
                        Hkv, D, P, N, max_context, scale, partition_tokens, prefix_tokens, workspace, workspace_bytes,
                        stream, fused, true);
+}
+
+int pkv_paged_decode_attention_multi_k8(void* out, const void* q, const void* k_pool8, const void* v_pool,
+                                        const int32_t* block_table, int32_t max_pages, const int32_t* lens, int32_t B,
+                                        int32_t n_query, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                                        int32_t max_context, float scale, int32_t partition_tokens,
+                                        int32_t prefix_tokens, void* workspace, size_t workspace_bytes,
+                                        void* stream) {
+  if (n_query < 1) return PKV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * n_query > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
+  return decode_common(out, q, nullptr, nullptr, k_pool8, v_pool, nullptr, nullptr, block_table, max_pages, lens, B,
+                       Hq, Hkv, D, P, N, max_context, scale, partition_tokens, prefix_tokens, workspace,
+                       workspace_bytes, stream, false, true, n_query);
 }
 
 int pkv_paged_decode_attention_multi(void* out, const void* q, const void* k_pool, const void* v_pool,

@@ -213,3 +213,37 @@ def test_fused_append_decode_k8_matches_oracle(number, batch, part, use_prefix):
     assert np.array_equal(host(vd).view(np.uint16), rv.view(np.uint16))
     ref = oracle.decode_attention_k8(w.q, rk, rv, w.block_table, lens, w.scale, w.P)
     check_close(got, ref, "fused k8 %s" % w.name)
+
+
+@pytest.mark.parametrize("number,batch,nq,part,use_prefix", [(2, 3, 4, 0, False), (2, 3, 4, 1024, False),
+                                                              (3, 6, 4, 512, True), (3, 6, 2, 512, False),
+                                                              (5, 5, 3, 256, False), (3, None, 4, 1024, True)])
+def test_multi_query_k8_matches_oracle(number, batch, nq, part, use_prefix):
+    """Chunks of queries over int8 keys: the chunk's tokens appended in one
+    launch (bit-exact against the oracle's quantising append, token by token),
+    then the causal chunk attention against the oracle within 4e-3."""
+    m = pkv()
+    w = workload(number, batch=batch)
+    lens = w.lens(max(0, w.steps - 1))
+    prefix = w.shared_prefix_pages * w.P if use_prefix else 0
+    rng = np.random.default_rng(300 + nq)
+    live = _live_tokens(w.N, w.P, w.block_table, lens - nq)         # the chunk's slots start poisoned
+    pool8 = random_k8_pool(rng, w.N, w.Hkv, w.P, w.D, live)
+    vp = poison_v(w.v_pool, live)
+    kn = rng.standard_normal((w.B, nq, w.Hkv, w.D)).astype(np.float16)
+    vn = rng.standard_normal((w.B, nq, w.Hkv, w.D)).astype(np.float16)
+    q = rng.standard_normal((w.B, nq, w.Hq, w.D)).astype(np.float16)
+    say("multi k8", w.name, "B=%d nq=%d part=%d prefix=%d" % (w.B, nq, part, prefix))
+    k8d, vd = dev(pool8), dev(vp)
+    m.kv_append_k8_chunk(dev(kn), dev(vn), k8d, vd, dev(w.block_table), dev(lens - nq))
+    got = m.paged_decode_attention_multi_k8(dev(q), k8d, vd, dev(w.block_table), dev(lens), int(lens.max()), w.scale,
+                                            part, prefix_tokens=prefix)
+    torch.cuda.synchronize()
+    rk, rv = pool8, vp
+    for i in range(nq):
+        rk, rv = oracle.kv_append_k8(rk, rv, kn[:, i], vn[:, i], w.block_table, (lens - nq + i).astype(np.int32), w.P)
+    assert np.array_equal(host(k8d), rk)
+    assert np.array_equal(host(vd).view(np.uint16), rv.view(np.uint16))
+    sample = np.arange(w.B) if w.B <= 8 else np.linspace(0, w.B - 1, 8).astype(int)
+    ref = oracle.decode_attention_multi_k8(q[sample], rk, rv, w.block_table[sample], lens[sample], w.scale, w.P)
+    check_close(torch.from_numpy(host(got)[sample]), ref, "multi k8 %s nq=%d" % (w.name, nq))

@@ -1,7 +1,8 @@
 """Randomised GPU parity: seeded small configurations that cross the paths
 (plain decode, fused append, shared prefix, int8 keys, chunks of queries,
 sliding windows) with random head groups, head sizes, page sizes, partition
-sizes and ragged lengths, each checked against the oracle within 4e-3; the
+sizes and ragged lengths (int8 keys also under chunks, with and without a
+prefix), each checked against the oracle within 4e-3; the
 fused appends must leave the pools byte-identical to the oracle's. Every
 slot no query attends holds NaN (NaN scales for int8 keys)."""
 
@@ -19,7 +20,7 @@ pytestmark = pytest.mark.gpu
 TOL = 4e-3
 N_CASES = 220
 MODES = ["decode", "fused", "prefix", "prefix_fused", "k8", "k8_fused", "k8_prefix", "multi", "multi_prefix",
-         "window", "window_fused"]
+         "window", "window_fused", "k8_multi", "k8_multi_prefix"]
 
 
 def say(*a):
@@ -93,7 +94,7 @@ def make_case(i):
     Hkv = int(rng.choice([1, 2, 4]))
     G = int(rng.choice([1, 2, 4, 8, 16]))
     nq = 1
-    if mode.startswith("multi"):
+    if "multi" in mode:
         nq = int(rng.integers(2, 16 // G + 1)) if G <= 8 else 1
         if nq == 1:
             G, nq = 4, int(rng.integers(2, 5))
@@ -190,8 +191,15 @@ def test_random_configuration(i):
 
     if mode.startswith("k8"):
         pool8 = k8_pool(rng, N, Hkv, P, D, live)
-        q = f16(rng, (B, Hq, D))
         k8d, vd = dev(pool8), dev(vp)
+        if nq > 1:
+            q = f16(rng, (B, nq, Hq, D))
+            got = m.paged_decode_attention_multi_k8(dev(q), k8d, vd, dev(bt), dev(lens), max_context, scale, part,
+                                                    prefix_tokens=prefix)
+            ref = oracle.decode_attention_multi_k8(q, pool8, vp, bt, lens, scale, P)
+            check(host(got), ref, what)
+            return
+        q = f16(rng, (B, Hq, D))
         if fused:
             kn, vn = f16(rng, (B, Hkv, D)), f16(rng, (B, Hkv, D))
             got = m.paged_decode_attention_k8(dev(q), k8d, vd, dev(bt), dev(lens), max_context, scale, part,
