@@ -13,11 +13,6 @@ def pytest_configure(config):
     config.addinivalue_line("markers", "slow: CPU test that takes more than a few seconds")
 
 
-def pytest_collection_modifyitems(config, items):
-    # GPU tests are only meaningful on the GPU machine; there they must run, never skip.
-    pass
-
-
 @pytest.fixture(scope="session")
 def golden_dir():
     return os.path.join(ROOT, "tests", "golden")
