@@ -48,6 +48,7 @@ from .quant_k8 import (  # noqa: F401
     k8_gather_sequence,
     decode_attention_k8,
     decode_attention_multi_k8,
+    decode_attention_window_k8,
     kv_append_k8,
 )
 from .allocator import PageAllocatorModel, OutOfPages, validate_tables  # noqa: F401

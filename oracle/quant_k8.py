@@ -180,6 +180,47 @@ def decode_attention_multi_k8(q, pool8, v_pool, block_table, lens, scale, page_s
     return out
 
 
+def decode_attention_window_k8(q, pool8, v_pool, ring_table, lens, window, scale, page_size):
+    """Sliding-window decode (the ring of pages of ``decode_attention_window``:
+    logical page ``j`` of sequence ``b`` in ``ring_table[b][j % R]``, query ``b``
+    attends tokens ``max(0, lens[b] - window) .. lens[b] - 1``) over int8 keys:
+    token ``t`` is read as ``code * scale`` from slot ``t % P`` of its ring page.
+    Returns float64 ``[B][Hq][D]``; ``lens[b] == 0`` gives zeros."""
+    from .paged_decode import _tiles, v_tile_offset
+    b_count, hq, d = q.shape
+    n, hkv, p, dim = v_pool.shape
+    ring = np.asarray(ring_table, dtype=np.int64)
+    r = ring.shape[1]
+    if window <= 0 or window > (r - 1) * page_size + 1:
+        raise ValueError("the window must fit in the ring")
+    g = _check_heads(hq, hkv)
+    s64 = _scale64(scale)
+    out = np.zeros((b_count, hq, d), dtype=np.float64)
+    for b in range(b_count):
+        length = int(lens[b])
+        if length == 0:
+            continue
+        t = np.arange(max(0, length - window), length)
+        pages = ring[b][(t // page_size) % r]
+        within = t % page_size
+        sub = _subblocks(pool8, dim)[pages, :, within // 16]            # [T][Hkv][sb]
+        u = within % 16
+        for kvh in range(hkv):
+            blk = sub[:, kvh]
+            codes = np.take_along_axis(blk, k8_code_offset(u[:, None], np.arange(dim)[None, :], dim), 1)
+            so = k8_scale_offset(u, dim)[:, None] + np.arange(4)[None, :]
+            scales = np.take_along_axis(blk, so, 1).copy().view(np.float32)[:, 0]
+            keys = codes.view(np.int8).astype(np.float64) * scales.astype(np.float64)[:, None]
+            vals = _tiles(v_pool)[pages[:, None], kvh, v_tile_offset(within[:, None], np.arange(dim)[None, :], p,
+                                                                       dim)].astype(np.float64)
+            for i in range(g):
+                h = kvh * g + i
+                sc = s64 * (keys @ q[b, h].astype(np.float64))
+                w = np.exp(sc - sc.max())
+                out[b, h] = (w @ vals) / w.sum()
+    return out
+
+
 def kv_append_k8(pool8, v_pool, k_new, v_new, block_table, pos, page_size):
     """Copies of the pools with each sequence's new token written: its key
     quantised (``quantize_k``) into the int8 pool, its value as fp16 (the

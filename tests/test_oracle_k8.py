@@ -186,8 +186,9 @@ K8_MUTANTS = [
     ("codes = np.rint(k / scale)", "codes = np.trunc(k / scale)"),                    # truncation
     ("scale = np.float32(amax / np.float32(127.0))", "scale = np.float32(amax / np.float32(128.0))"),
     ("return codes.view(np.int8).astype(np.float64)", "return codes.astype(np.float64)"),   # unsigned codes
-    ("* scales.astype(np.float64)[:, None]", "* scales.astype(np.float64)[::-1, None]"),   # scales of other tokens
-    ("within = t % page_size", "within = (t + 1) % page_size"),                       # slot off by one
+    ("return codes.view(np.int8).astype(np.float64) * scales.astype(np.float64)[:, None]",
+     "return codes.view(np.int8).astype(np.float64) * scales.astype(np.float64)[::-1, None]"),   # other tokens' scales
+    ("within = t % page_size\n    sub = pool8[pages", "within = (t + 1) % page_size\n    sub = pool8[pages"),  # slot off by one
     ("p = np.exp(s - s.max())", "p = np.exp(s.max() - s)"),                          # sign
     ("s = s64 * (keys @ q[b, h].astype(np.float64))", "s = keys @ q[b, h].astype(np.float64)"),  # dropped scale
 ]
@@ -273,3 +274,76 @@ def test_multi_k8_planted_mistake_is_caught(old, new):
     exec(compile(src.replace(old, new), "<mutant>", "exec"), mutant.__dict__)
     with pytest.raises(AssertionError):
         _check_multi_k8(mutant.decode_attention_multi_k8)
+
+
+# ---------------------------------------------------------------------------
+# sliding window over a ring of int8-key pages
+# ---------------------------------------------------------------------------
+
+def _check_window_k8(fn, seed=31):
+    """Brute force: tokens written in order into a ring of R pages (later ones
+    overwrite earlier ones), keys quantised by the quantiser; the textbook
+    attention over the last W tokens' dequantised keys against the oracle;
+    then a window covering a ring that never wrapped is int8 decode itself."""
+    rng = np.random.default_rng(seed)
+    B, Hq, Hkv, D, P, R, W = 2, 4, 2, 64, 16, 3, 33
+    G = Hq // Hkv
+    N = B * R + 2
+    ring = rng.permutation(N)[:B * R].reshape(B, R).astype(np.int32)
+    lens = np.array([W - 5, 4 * R * P + 7], np.int32)
+    pool8 = np.zeros((N, Hkv, P // 16, oracle.k8_subblock_bytes(D)), np.uint8)
+    vp = _paged_fp16_pool(rng, N, Hkv, P, D)
+    K, V = [], []
+    for b in range(B):
+        kb, vb = [], []
+        for t in range(int(lens[b])):
+            page = int(ring[b, (t // P) % R])
+            kt, vt = [], []
+            for h in range(Hkv):
+                key = _fp16(rng.standard_normal(D))
+                codes, sc = oracle.quantize_k(key)
+                oracle.k8_write_token(pool8, page, h, t % P, codes, sc, D)
+                val = _fp16(rng.standard_normal(D))
+                oracle.write_token(vp, page, h, t % P, val, "v")
+                kt.append(codes.astype(np.float64) * float(sc))
+                vt.append(val.astype(np.float64))
+            kb.append(kt)
+            vb.append(vt)
+        K.append(kb)
+        V.append(vb)
+    q = _fp16(rng.standard_normal((B, Hq, D)))
+    got = fn(q, pool8, vp, ring, lens, W, 0.125, P)
+    for b in range(B):
+        lo = max(0, int(lens[b]) - W)
+        for h in range(Hq):
+            kvh = h // G
+            keys = [K[b][t][kvh].tolist() for t in range(lo, int(lens[b]))]
+            vals = [V[b][t][kvh].tolist() for t in range(lo, int(lens[b]))]
+            ref = _textbook(q[b, h].astype(np.float64).tolist(), keys, vals, float(np.float32(0.125)))
+            np.testing.assert_allclose(got[b, h], ref, rtol=0, atol=1e-12)
+    # a ring that never wrapped, the window covering everything: int8 decode over the ring as a table
+    short = np.array([20, (R - 1) * P + 1], np.int32)
+    whole = fn(q, pool8, vp, ring, short, (R - 1) * P + 1, 0.125, P)
+    np.testing.assert_array_equal(whole, oracle.decode_attention_k8(q, pool8, vp, ring, short, 0.125, P))
+
+
+def test_window_k8_brute_force():
+    _check_window_k8(oracle.decode_attention_window_k8)
+
+
+@pytest.mark.parametrize("old,new", [
+    ("t = np.arange(max(0, length - window), length)\n        pages = ring[b][(t // page_size) % r]\n        within",
+     "t = np.arange(max(0, length - window + 1), length)\n        pages = ring[b][(t // page_size) % r]\n        within"),
+    ("pages = ring[b][(t // page_size) % r]\n        within", "pages = ring[b][(t // page_size) % (r - 1)]\n        within"),
+    ("codes.view(np.int8).astype(np.float64) * scales.astype(np.float64)[:, None]\n            vals",
+     "codes.astype(np.float64) * scales.astype(np.float64)[:, None]\n            vals"),
+])
+def test_window_k8_planted_mistake_is_caught(old, new):
+    src = open(quant_k8.__file__).read()
+    assert src.count(old) == 1, old
+    mutant = types.ModuleType("oracle.quant_k8_mutant")
+    mutant.__dict__["__file__"] = "<mutant>"
+    mutant.__dict__["__package__"] = "oracle"
+    exec(compile(src.replace(old, new), "<mutant>", "exec"), mutant.__dict__)
+    with pytest.raises((AssertionError, IndexError)):
+        _check_window_k8(mutant.decode_attention_window_k8)
