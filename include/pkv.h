@@ -454,6 +454,21 @@ int pkv_paged_decode_attention_multi_k8(void* out, const void* q, const void* k_
                                         int32_t prefix_tokens, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_paged_decode_attention_window_k8 -- pkv_paged_decode_attention_window
+ * over int8-key pages: the last `window` tokens of each sequence through its
+ * ring of pages, keys dequantised as code * scale, values fp16; with k_new and
+ * v_new the new token is appended into its ring page in the same launch, its
+ * key quantised exactly as pkv_kv_append_k8 does. Arguments, workspace and
+ * errors as pkv_paged_decode_attention_window, the key pool being the int8
+ * pool above (D in {64, 128}).
+ */
+int pkv_paged_decode_attention_window_k8(void* out, const void* q, const void* k_new, const void* v_new,
+                                         void* k_pool8, void* v_pool, const int32_t* ring_table, int32_t ring_pages,
+                                         const int32_t* lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                                         int32_t N, int32_t window, float scale, int32_t partition_tokens,
+                                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pkv_probe_stream_read -- measurement aid (not part of decode): read
  * n_tiles 4 KiB tiles of `base` in the order tile_order gives, with the decode
  * kernel's access pattern (16-byte non-temporal loads per lane, two tiles in

@@ -56,6 +56,9 @@ _SIGNATURES = {
     "pkv_paged_decode_attention_multi_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32,
                                                            _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _i32, _vp,
                                                            ctypes.c_size_t, _vp]),
+    "pkv_paged_decode_attention_window_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
+                                                            _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _vp,
+                                                            ctypes.c_size_t, _vp]),
     "pkv_kv_append_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_paged_decode_attention_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                                      _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _i32, _vp,
@@ -379,6 +382,36 @@ def paged_decode_attention_multi_k8(q, k_pool8, v_pool, block_table, lens, max_c
         _dev_ptr(lens, torch.int32, "lens"), B, nq, Hq, Hkv, D, P, N, int(max_context), float(scale),
         int(partition_tokens), int(prefix_tokens), ws_ptr, ws_len, _stream(stream))
     _check(rc, "pkv_paged_decode_attention_multi_k8")
+    return out
+
+
+def paged_decode_attention_window_k8(q, k_pool8, v_pool, ring_table, lens, window, scale, partition_tokens=0,
+                                     k_new=None, v_new=None, out=None, workspace=None, stream=None):
+    """pkv_paged_decode_attention_window_k8: the sliding-window call over an int8-key pool
+    (logical page j in ring_table[b][j % ring_pages]); optional fused quantising append."""
+    N, Hkv, P, D = _k8_shape(k_pool8, v_pool)
+    B, Hq, Dq = q.shape
+    _, ring_pages = ring_table.shape
+    if Dq != D or ring_table.shape[0] != B or tuple(lens.shape) != (B,):
+        raise ValueError("shape mismatch")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("k_new and v_new go together")
+    if k_new is not None and (tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D)):
+        raise ValueError("k_new / v_new must be [B][Hkv][D]")
+    if out is None:
+        out = torch.empty((B, Hq, D), dtype=torch.float16, device=q.device)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B][Hq][D]")
+    ws_ptr, ws_len = _workspace_arg(workspace, decode_workspace_bytes(B, Hq, D, int(window), partition_tokens),
+                                    q.device)
+    kn = _dev_ptr(k_new, torch.float16, "k_new") if k_new is not None else ctypes.c_void_p(0)
+    vn = _dev_ptr(v_new, torch.float16, "v_new") if v_new is not None else ctypes.c_void_p(0)
+    rc = lib().pkv_paged_decode_attention_window_k8(
+        _dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"), kn, vn,
+        _dev_ptr(k_pool8, torch.uint8, "k_pool8"), _dev_ptr(v_pool, torch.float16, "v_pool"),
+        _dev_ptr(ring_table, torch.int32, "ring_table"), ring_pages, _dev_ptr(lens, torch.int32, "lens"),
+        B, Hq, Hkv, D, P, N, int(window), float(scale), int(partition_tokens), ws_ptr, ws_len, _stream(stream))
+    _check(rc, "pkv_paged_decode_attention_window_k8")
     return out
 
 

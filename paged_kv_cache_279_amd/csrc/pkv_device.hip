@@ -402,9 +402,10 @@ __device__ __forceinline__ void set_priority(int32_t remaining, int32_t quota) {
 // the codes widen exactly to fp16 for the score MFMA and each score is then
 // multiplied by its token's scale (s_t = scale_t * <codes_t, q>).
 //
-// kWin: the pages of a sequence form a ring (logical page j is table entry
-// j % ring) and tokens below win_lo, the window start, are masked, scores and
-// values (start <= win_lo < start + 16).
+// Sliding window (p.ring > 0, decided at run time): the pages of a sequence
+// form a ring (logical page j is table entry j % ring) and tokens below
+// win_lo, the window start, are masked, scores and values
+// (start <= win_lo < start + 16; win_lo = 0 without a window).
 //
 // kMQ: the column of lane (col, quad) may see tokens up to clim only (the
 // causal bound of its query within a chunk); clim_min is the smallest bound of
@@ -415,7 +416,7 @@ __device__ __forceinline__ void set_priority(int32_t remaining, int32_t quota) {
 // other loads, patches them into the block's registers before use, and writes
 // them to the pool from there. No other wave reads that row, so the write
 // needs no ordering against the loads.
-template <int D, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ, bool kWin>
+template <int D, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ>
 __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32_t* bt_row, int32_t kvh,
                                               int32_t start, int32_t end, int32_t first, int32_t stride,
                                               int32_t quota, int32_t after, const NewToken& nt,
@@ -444,7 +445,7 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     bool bad = false;
     if (blk < nblocks) {
       int32_t entry = (start + blk * kBlk) >> p.p_shift;
-      if constexpr (kWin) entry %= p.ring;
+      if (p.ring > 0) entry %= p.ring;
       page = bt_row[entry];
       bad = page < 0 || page >= p.N;
     }
@@ -652,21 +653,19 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
 #pragma unroll
       for (int j = 0; j < KL; ++j) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kr[j]), qb[j], s, 0, 0, 0);
     }
-    if constexpr (kWin) {
-      if (t0 < win_lo) {
-        // tokens before the window: masked scores, zeroed values (never 0 * NaN)
-        const int32_t tq = t0 + 4 * quad;
+    if (t0 < win_lo) {
+      // sliding window: tokens before its start get masked scores and zeroed values (never 0 * NaN)
+      const int32_t tq = t0 + 4 * quad;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] = tq + i >= win_lo ? s[i] : kNegInf();
-        const uint32_t m0 = (tq + 0 >= win_lo ? 0x0000FFFFu : 0u) | (tq + 1 >= win_lo ? 0xFFFF0000u : 0u);
-        const uint32_t m1 = (tq + 2 >= win_lo ? 0x0000FFFFu : 0u) | (tq + 3 >= win_lo ? 0xFFFF0000u : 0u);
+      for (int i = 0; i < 4; ++i) s[i] = tq + i >= win_lo ? s[i] : kNegInf();
+      const uint32_t m0 = (tq + 0 >= win_lo ? 0x0000FFFFu : 0u) | (tq + 1 >= win_lo ? 0xFFFF0000u : 0u);
+      const uint32_t m1 = (tq + 2 >= win_lo ? 0x0000FFFFu : 0u) | (tq + 3 >= win_lo ? 0xFFFF0000u : 0u);
 #pragma unroll
-        for (int j = 0; j < KL; ++j) {
-          vr[j].x &= m0;
-          vr[j].y &= m1;
-          vr[j].z &= m0;
-          vr[j].w &= m1;
-        }
+      for (int j = 0; j < KL; ++j) {
+        vr[j].x &= m0;
+        vr[j].y &= m1;
+        vr[j].z &= m0;
+        vr[j].w &= m1;
       }
     }
     if constexpr (kMQ) {
@@ -786,7 +785,7 @@ struct KernelShared {
 // and unnormalised output. Callers must be workgroup-uniform.
 // kMQ: column c is query c / g of the chunk (g = mq_g heads per query); query
 // i may see tokens up to mq_last0 + i.
-template <int D, int NC, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ = false, bool kWin = false, class RowFn,
+template <int D, int NC, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ = false, class RowFn,
           class EmitFn>
 __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>& sh, const int32_t* bt_row,
                                           int32_t kvh, int32_t start, int32_t end, int32_t quota, int32_t after,
@@ -812,7 +811,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
     const int32_t qi = col / mq_g;
     clim = qi < p.nq ? mq_last0 + qi : 0x7fffffff;
   }
-  stream_blocks<D, kPolicy, kAppend, kK8, kMQ, kWin>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, nt,
+  stream_blocks<D, kPolicy, kAppend, kK8, kMQ>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, nt,
                                                      clim, mq_last0, lo, qb, st, lane);
   // per-column denominators of this wave: sum the 4 quads of column col
   st.l_part += __shfl_xor(st.l_part, 16);
@@ -873,10 +872,9 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
 // writes slot kvh * (NT + B + 2 Wk) + s + j, private segments numbered after
 // NT + Wk: walking a list in order increases s or j (or both) by one each
 // step, so the slots are distinct; each slot holds 16 columns.
-template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ, bool WIN = false>
+template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ>
 __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodeParams p) {
   static_assert(!MQ || !FUSED, "chunks of queries: no fused append");
-  static_assert(!WIN || (!MQ && !K8), "sliding window: fp16 keys, single queries");
   static_assert(D % 32 == 0 && G >= 1 && G <= 16, "shape");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -910,7 +908,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
     const int32_t kvh = blockIdx.x % p.Hkv;
     const int32_t b = blockIdx.x / p.Hkv;
     const int32_t L = p.lens[b];
-    const bool bad_len = L < 0 || L > p.max_context || (!WIN && L > (p.max_pages << p.p_shift));
+    const bool bad_len = L < 0 || L > p.max_context || (p.ring == 0 && L > (p.max_pages << p.p_shift));
     const int32_t Lc = bad_len ? 0 : L;
     const int64_t head_row0 = (int64_t)b * p.Hq + (int64_t)kvh * G;
     if (Lc == 0) {
@@ -920,14 +918,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
     }
     const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
     // sliding window: attend [lo, L), streamed from the 16-aligned block below lo
-    const int32_t lo = WIN ? max(0, Lc - p.window) : 0;
+    const int32_t lo = p.window > 0 ? max(0, Lc - p.window) : 0;
     const int32_t s0 = lo & ~(kBlk - 1);
     NewToken nt{-1, 0, nullptr, nullptr};
     if constexpr (FUSED) {
       const int64_t src = ((int64_t)b * p.Hkv + kvh) * D;
       nt = NewToken{(Lc - 1 - s0) >> 4, (Lc - 1) & 15, p.k_new + src, p.v_new + src};
     }
-    run_range<D, G, kKvLoadPolicy, FUSED, K8, false, WIN>(
+    run_range<D, G, kKvLoadPolicy, FUSED, K8>(
         p, sh, bt_row, kvh, s0, Lc, 0, 0, nt, [&](int c) -> int64_t { return head_row0 + c; },
         [&](int c, int d, float, float Ls, float O) {
           const float r = Ls > 0.f ? O / Ls : (Ls == 0.f ? 0.f : __builtin_nanf(""));
@@ -944,12 +942,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
     // first streamed token of a sequence: after the shared prefix, or the
     // 16-aligned block below the window start
     auto first_token = [&](int32_t L) -> int32_t {
-      return WIN ? max(0, L - p.window) & ~(kBlk - 1) : p.prefix_tokens;
+      return p.window > 0 ? max(0, L - p.window) & ~(kBlk - 1) : p.prefix_tokens;
     };
     auto priv_blocks = [&](int32_t bb) -> int32_t {
       const int32_t L = p.lens[bb];
       sm_len[bb] = L;
-      const bool bad = L < p.min_len || L > p.max_context || (!WIN && L > (p.max_pages << p.p_shift));
+      const bool bad = L < p.min_len || L > p.max_context || (p.ring == 0 && L > (p.max_pages << p.p_shift));
       return bad ? 0 : (L - first_token(L) + kBlk - 1) / kBlk;
     };
     int32_t local = 0;
@@ -1077,10 +1075,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
               },
               emit, lane, wave, L - p.nq, G);
         } else {
-          run_range<D, G, kKvLoadPolicy, FUSED, K8, false, WIN>(
+          run_range<D, G, kKvLoadPolicy, FUSED, K8>(
               p, smem.tile.priv, bt_row, kvh, start, end, quota, after + g1 - g - piece_n, nt,
               [&](int c) -> int64_t { return c < G ? head_row0 + c : -1; }, emit, lane, wave, 0, 1,
-              WIN ? max(0, L - p.window) : 0);
+              p.window > 0 ? max(0, L - p.window) : 0);
         }
         g += piece_n;
       }
@@ -1364,9 +1362,9 @@ int64_t max_slots(int32_t B, int32_t Hq, bool prefix) {
 thread_local hipEvent_t t_prof_armed[2] = {nullptr, nullptr};
 thread_local hipEvent_t t_prof_call[2] = {nullptr, nullptr};
 
-template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ, bool WIN>
+template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ>
 hipError_t launch_partition(const DecodeParams& p, hipStream_t stream, int64_t grid) {
-  const void* fn = reinterpret_cast<const void*>(&decode_partition_kernel<D, G, SPLIT, FUSED, K8, MQ, WIN>);
+  const void* fn = reinterpret_cast<const void*>(&decode_partition_kernel<D, G, SPLIT, FUSED, K8, MQ>);
   if (t_prof_call[0] || t_prof_call[1]) {
     // the start and stop of this kernel alone go into the caller's events
     DecodeParams arg = p;
@@ -1375,26 +1373,26 @@ hipError_t launch_partition(const DecodeParams& p, hipStream_t stream, int64_t g
                                             t_prof_call[0], t_prof_call[1], 0);
     return e != hipSuccess ? e : hipGetLastError();
   }
-  hipLaunchKernelGGL((decode_partition_kernel<D, G, SPLIT, FUSED, K8, MQ, WIN>), dim3(static_cast<uint32_t>(grid)),
+  hipLaunchKernelGGL((decode_partition_kernel<D, G, SPLIT, FUSED, K8, MQ>), dim3(static_cast<uint32_t>(grid)),
                      dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool SPLIT, bool FUSED, bool K8, bool MQ = false, bool WIN = false>
+template <int D, bool SPLIT, bool FUSED, bool K8, bool MQ = false>
 hipError_t dispatch_g(int G, const DecodeParams& p, hipStream_t s, int64_t grid) {
   switch (G) {
-    case 1: return launch_partition<D, 1, SPLIT, FUSED, K8, MQ, WIN>(p, s, grid);
-    case 2: return launch_partition<D, 2, SPLIT, FUSED, K8, MQ, WIN>(p, s, grid);
-    case 4: return launch_partition<D, 4, SPLIT, FUSED, K8, MQ, WIN>(p, s, grid);
-    case 8: return launch_partition<D, 8, SPLIT, FUSED, K8, MQ, WIN>(p, s, grid);
-    default: return launch_partition<D, 16, SPLIT, FUSED, K8, MQ, WIN>(p, s, grid);
+    case 1: return launch_partition<D, 1, SPLIT, FUSED, K8, MQ>(p, s, grid);
+    case 2: return launch_partition<D, 2, SPLIT, FUSED, K8, MQ>(p, s, grid);
+    case 4: return launch_partition<D, 4, SPLIT, FUSED, K8, MQ>(p, s, grid);
+    case 8: return launch_partition<D, 8, SPLIT, FUSED, K8, MQ>(p, s, grid);
+    default: return launch_partition<D, 16, SPLIT, FUSED, K8, MQ>(p, s, grid);
   }
 }
 
-template <bool SPLIT, bool FUSED, bool K8, bool MQ = false, bool WIN = false>
+template <bool SPLIT, bool FUSED, bool K8, bool MQ = false>
 hipError_t dispatch_d(int D, int G, const DecodeParams& p, hipStream_t s, int64_t grid) {
-  return D == 64 ? dispatch_g<64, SPLIT, FUSED, K8, MQ, WIN>(G, p, s, grid)
-                 : dispatch_g<128, SPLIT, FUSED, K8, MQ, WIN>(G, p, s, grid);
+  return D == 64 ? dispatch_g<64, SPLIT, FUSED, K8, MQ>(G, p, s, grid)
+                 : dispatch_g<128, SPLIT, FUSED, K8, MQ>(G, p, s, grid);
 }
 
 int decode_common(void* out, const void* q, const void* k_new, const void* v_new, const void* k_pool,
@@ -1416,7 +1414,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   const int G = Hq / Hkv;
   if (nq < 1) return PKV_ERR_INVALID_ARG;
   if (nq > 1 && fused) return PKV_ERR_INVALID_ARG;
-  if (window < 0 || (window > 0 && (nq > 1 || k8 || prefix_tokens > 0))) return PKV_ERR_INVALID_ARG;
+  if (window < 0 || (window > 0 && (nq > 1 || prefix_tokens > 0))) return PKV_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(nq) * G > 16) return PKV_ERR_UNSUPPORTED;     // one 16-column matrix-core tile
   if (static_cast<int64_t>(B) * nq * Hq > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
@@ -1494,13 +1492,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   const int64_t grid = plan.grid;
   hipError_t e = hipSuccess;
   if (grid > 0) {
-    if (window > 0 && fused)
-      e = plan.split ? dispatch_d<true, true, false, false, true>(D, G, prm, s, grid)
-                     : dispatch_d<false, true, false, false, true>(D, G, prm, s, grid);
-    else if (window > 0)
-      e = plan.split ? dispatch_d<true, false, false, false, true>(D, G, prm, s, grid)
-                     : dispatch_d<false, false, false, false, true>(D, G, prm, s, grid);
-    else if (nq > 1 && k8)
+    if (nq > 1 && k8)
       e = plan.split ? dispatch_d<true, false, true, true>(D, G, prm, s, grid)
                      : dispatch_d<false, false, true, true>(D, G, prm, s, grid);
     else if (nq > 1)
@@ -1782,6 +1774,19 @@ int pkv_paged_decode_attention_window(void* out, const void* q, const void* k_ne
   return decode_common(out, q, k_new, v_new, k_pool, v_pool, k_pool, v_pool, ring_table, ring_pages, lens, B, Hq, Hkv,
                        D, P, N, kWindowMaxLen, scale, partition_tokens, 0, workspace, workspace_bytes, stream, fused,
                        false, 1, window);
+}
+
+int pkv_paged_decode_attention_window_k8(void* out, const void* q, const void* k_new, const void* v_new,
+                                         void* k_pool8, void* v_pool, const int32_t* ring_table, int32_t ring_pages,
+                                         const int32_t* lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                                         int32_t N, int32_t window, float scale, int32_t partition_tokens,
+                                         void* workspace, size_t workspace_bytes, void* stream) {
+  if ((k_new == nullptr) != (v_new == nullptr)) return PKV_ERR_INVALID_ARG;
+  if (window <= 0 || ring_pages <= 0) return PKV_ERR_INVALID_ARG;
+  const bool fused = k_new != nullptr;
+  return decode_common(out, q, k_new, v_new, k_pool8, v_pool, k_pool8, v_pool, ring_table, ring_pages, lens, B, Hq,
+                       Hkv, D, P, N, kWindowMaxLen, scale, partition_tokens, 0, workspace, workspace_bytes, stream,
+                       fused, true, 1, window);
 }
 
 int pkv_paged_decode_attention_multi_shared_prefix(void* out, const void* q, const void* k_pool, const void* v_pool,

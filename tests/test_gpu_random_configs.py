@@ -2,7 +2,7 @@
 (plain decode, fused append, shared prefix, int8 keys, chunks of queries,
 sliding windows) with random head groups, head sizes, page sizes, partition
 sizes and ragged lengths (int8 keys also under chunks, with and without a
-prefix), each checked against the oracle within 4e-3; the
+prefix, and under sliding windows), each checked against the oracle within 4e-3; the
 fused appends must leave the pools byte-identical to the oracle's. Every
 slot no query attends holds NaN (NaN scales for int8 keys)."""
 
@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 TOL = 4e-3
 N_CASES = 220
 MODES = ["decode", "fused", "prefix", "prefix_fused", "k8", "k8_fused", "k8_prefix", "multi", "multi_prefix",
-         "window", "window_fused", "k8_multi", "k8_multi_prefix"]
+         "window", "window_fused", "k8_multi", "k8_multi_prefix", "k8_window", "k8_window_fused"]
 
 
 def say(*a):
@@ -153,7 +153,7 @@ def test_random_configuration(i):
     m = pkv()
     max_context = int(max(int(lens.max()), prefix, 1))
 
-    if mode.startswith("window"):
+    if "window" in mode:
         R = int(rng.integers(2, 6))
         W = int(rng.integers(1, (R - 1) * P + 2))
         lens = rng.integers(1 if fused else 0, 3 * R * P, size=B).astype(np.int32)
@@ -162,16 +162,32 @@ def test_random_configuration(i):
         attended = lens - 1 if fused else lens
         lo = np.maximum(lens - W, 0)
         live = live_slots(N, P, ring, attended, lo)
-        kp = poison(f16(rng, (N, Hkv, P, D)), live, "k")
         vp = poison(f16(rng, (N, Hkv, P, D)), live, "v")
         q = f16(rng, (B, Hq, D))
+        width = max(1, -(-int(lens.max()) // P))
+        logical = np.ascontiguousarray(ring[:, np.arange(width) % R])
+        if mode.startswith("k8"):
+            pool8 = k8_pool(rng, N, Hkv, P, D, live)
+            k8d, vd = dev(pool8), dev(vp)
+            if fused:
+                kn, vn = f16(rng, (B, Hkv, D)), f16(rng, (B, Hkv, D))
+                got = m.paged_decode_attention_window_k8(dev(q), k8d, vd, dev(ring), dev(lens), W, scale, part,
+                                                         k_new=dev(kn), v_new=dev(vn))
+                pool8, vp = oracle.kv_append_k8(pool8, vp, kn, vn, logical, lens - 1, P)
+                torch.cuda.synchronize()
+                assert np.array_equal(host(k8d), pool8)
+                assert np.array_equal(host(vd).view(np.uint16), vp.view(np.uint16))
+            else:
+                got = m.paged_decode_attention_window_k8(dev(q), k8d, vd, dev(ring), dev(lens), W, scale, part)
+            ref = oracle.decode_attention_window_k8(q, pool8, vp, ring, lens, W, scale, P)
+            check(host(got), ref, what + " R=%d W=%d" % (R, W))
+            return
+        kp = poison(f16(rng, (N, Hkv, P, D)), live, "k")
         kd, vd = dev(kp), dev(vp)
         if fused:
             kn, vn = f16(rng, (B, Hkv, D)), f16(rng, (B, Hkv, D))
             got = m.paged_decode_attention_window(dev(q), kd, vd, dev(ring), dev(lens), W, scale, part,
                                                   k_new=dev(kn), v_new=dev(vn))
-            width = max(1, -(-int(lens.max()) // P))
-            logical = np.ascontiguousarray(ring[:, np.arange(width) % R])
             kp, vp = oracle.kv_append(kp, vp, kn, vn, logical, lens - 1, P)
             torch.cuda.synchronize()
             assert np.array_equal(host(kd).view(np.uint16), kp.view(np.uint16))

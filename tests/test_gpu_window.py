@@ -165,3 +165,51 @@ def test_window_full_size_sampled(part):
     ref = oracle.decode_attention_window(q[sample], kp, vp, ring[sample], lens[sample], W, scale, P)
     check_close(got[sample], ref, "window full size")
     assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("part,fused", [(0, False), (64, False), (0, True), (512, True)])
+def test_window_k8_matches_oracle(part, fused):
+    """Sliding window over int8-key pages (wrapped rings, stale slots with NaN
+    scales and values), with and without the fused quantising append."""
+    import oracle as orc
+    D, Hq, Hkv, P, R, W = 128, 32, 8, 16, 9, 129
+    lens = window_lens(P, R, W)
+    if fused:
+        lens = lens[lens > 0]
+    B = len(lens)
+    rng = np.random.default_rng(40 + part + fused)
+    N = B * R + 3
+    ring = rng.permutation(N)[:B * R].reshape(B, R).astype(np.int32)
+    attended = lens - 1 if fused else lens
+    live = np.zeros((N, P), dtype=bool)
+    for b in range(B):
+        t = np.arange(max(0, int(lens[b]) - W), max(int(attended[b]), 0))
+        live[ring[b, (t // P) % R], t % P] = True
+    codes = rng.integers(-127, 128, size=(N, Hkv, P // 16, 16 * D)).astype(np.int8).view(np.uint8)
+    scales = (np.abs(rng.standard_normal((N, Hkv, P // 16, 16))) * 0.05 + 0.005).astype(np.float32)
+    scales = np.where(np.broadcast_to(~live.reshape(N, 1, P // 16, 16), scales.shape), np.float32(np.nan), scales)
+    pool8 = np.ascontiguousarray(np.concatenate([codes, scales.view(np.uint8)], axis=-1))
+    vp = rng.standard_normal((N, Hkv, P, D), dtype=np.float32).astype(np.float16)
+    pages, slots = np.nonzero(~live)
+    tiles = vp.reshape(N, Hkv, P * D)
+    off = orc.v_tile_offset(slots[:, None], np.arange(D)[None, :], P, D)
+    for kvh in range(Hkv):
+        tiles[pages[:, None], kvh, off] = np.nan
+    q = rng.standard_normal((B, Hq, D), dtype=np.float32).astype(np.float16)
+    scale = 1.0 / math.sqrt(D)
+    k8d, vd = dev(pool8), dev(vp)
+    say("window k8 part=%d fused=%s" % (part, fused))
+    if fused:
+        kn = rng.standard_normal((B, Hkv, D), dtype=np.float32).astype(np.float16)
+        vn = rng.standard_normal((B, Hkv, D), dtype=np.float32).astype(np.float16)
+        got = pkv().paged_decode_attention_window_k8(dev(q), k8d, vd, dev(ring), dev(lens), W, scale, part,
+                                                     k_new=dev(kn), v_new=dev(vn))
+        torch.cuda.synchronize()
+        pool8, vp = orc.kv_append_k8(pool8, vp, kn, vn, _logical_table(ring, lens.max(), P), lens - 1, P)
+        assert np.array_equal(host(k8d), pool8)
+        assert np.array_equal(host(vd).view(np.uint16), vp.view(np.uint16))
+    else:
+        got = pkv().paged_decode_attention_window_k8(dev(q), k8d, vd, dev(ring), dev(lens), W, scale, part)
+        torch.cuda.synchronize()
+    ref = orc.decode_attention_window_k8(q, pool8, vp, ring, lens, W, scale, P)
+    check_close(host(got), ref, "window k8 part=%d fused=%s" % (part, fused))
