@@ -116,16 +116,18 @@ def algorithmic_bytes(lens, B, Hq, Hkv, D, P, shared_tokens, k_bytes=None, n_que
     return kv + q_out + new_kv + table, kv
 
 
-def algorithmic_bytes_window(lens, B, Hq, Hkv, D, P, window):
+def algorithmic_bytes_window(lens, B, Hq, Hkv, D, P, window, k_bytes=None):
     """Unique bytes of one sliding-window layer-step: the K/V of the last
     ``window`` tokens of each sequence, q in, out, the new K/V read and
-    written, the ring entries the window touches and the lengths."""
+    written, the ring entries the window touches and the lengths. ``k_bytes``:
+    stored bytes of one token's key per KV head (2 D for fp16, D + 4 for int8)."""
+    kb = 2 * D if k_bytes is None else k_bytes
     lens = np.asarray(lens, dtype=np.int64)
     lo = np.maximum(lens - window, 0)
     kv_tokens = int((lens - lo).sum())
-    kv = kv_tokens * Hkv * 4 * D
+    kv = kv_tokens * Hkv * (kb + 2 * D)
     q_out = 2 * B * Hq * D * 2
-    new_kv = B * Hkv * 2 * 2 * D * 2
+    new_kv = B * Hkv * (2 * 2 * D + kb + 2 * D)
     table = int(((lens - 1) // P - lo // P + 1).clip(min=0).sum()) * 4 + B * 4
     return kv + q_out + new_kv + table, kv
 
@@ -266,8 +268,8 @@ def main():
     fused = not args.separate_append and KQ == 1
     prefix_tokens = 0 if args.no_shared_prefix else w.shared_prefix_pages * w.P
     W = w.window
-    if W and (k8 or KQ > 1 or not fused or args.graph):
-        raise SystemExit("the sliding-window workload runs fp16 keys, one query, the fused append, eagerly")
+    if W and (KQ > 1 or not fused or args.graph):
+        raise SystemExit("the sliding-window workload runs one query, the fused append, eagerly")
     if w.steps == 0:
         raise SystemExit("workload %d has no append; pick 2-5" % args.workload)
     if KQ > 1 and args.graph:
@@ -363,15 +365,17 @@ def main():
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
     torch.cuda.synchronize()
-    mem_gb = (2 * R * N * Hkv * P * D * 2) / 1e9
+    k_pool_bytes = pkv.k8_pool_bytes(N, Hkv, P, D) if k8 else N * Hkv * P * D * 2
+    mem_gb = R * (k_pool_bytes + N * Hkv * P * D * 2) / 1e9
     log("pools: N=%d pages/layer, %.2f GB over %d layers" % (N, mem_gb, R))
 
     scale = w.scale
 
     def layer_call(layer, lens, pos, kn, vn, s):
         if W:
-            pkv.paged_decode_attention_window(q, k_pools[layer], v_pools[layer], bt_dev, lens, W, scale, part,
-                                              k_new=kn, v_new=vn, out=out, workspace=workspace, stream=s)
+            window_call = pkv.paged_decode_attention_window_k8 if k8 else pkv.paged_decode_attention_window
+            window_call(q, k_pools[layer], v_pools[layer], bt_dev, lens, W, scale, part, k_new=kn, v_new=vn,
+                        out=out, workspace=workspace, stream=s)
         elif KQ > 1:
             # pos [B], kn / vn [B][K][Hkv][D]: the chunk's K tokens in one append launch, then its attention
             if k8:
@@ -468,10 +472,15 @@ def main():
         ref = chunk(q_mq.cpu().numpy()[sample], kpool_full, vpool_full, bt0[sample],
                     (w.context + KQ).astype(np.int32)[sample], scale, P)
     elif W:
-        kp0, vp0 = oracle.kv_append(w.k_pool, w.v_pool, w.k_new[0], w.v_new[0],
-                                    logical_table(w.block_table, int(w.lens(0).max()), P), w.pos(0), P)
-        ref = oracle.decode_attention_window(w.q[sample], kp0, vp0, w.block_table[sample], w.lens(0)[sample], W,
-                                             scale, P)
+        logical = logical_table(w.block_table, int(w.lens(0).max()), P)
+        if k8:
+            kp0, vp0 = oracle.kv_append_k8(k8_layer0[:w.N], w.v_pool, w.k_new[0], w.v_new[0], logical, w.pos(0), P)
+            ref = oracle.decode_attention_window_k8(w.q[sample], kp0, vp0, w.block_table[sample], w.lens(0)[sample],
+                                                    W, scale, P)
+        else:
+            kp0, vp0 = oracle.kv_append(w.k_pool, w.v_pool, w.k_new[0], w.v_new[0], logical, w.pos(0), P)
+            ref = oracle.decode_attention_window(w.q[sample], kp0, vp0, w.block_table[sample], w.lens(0)[sample], W,
+                                                 scale, P)
     elif k8:
         kp0, vp0 = oracle.kv_append_k8(k8_layer0[:w.N], w.v_pool, w.k_new[0], w.v_new[0], w.block_table, w.pos(0), P)
         ref = oracle.decode_attention_k8(w.q[sample], kp0, vp0, w.block_table[sample], w.lens(0)[sample], scale, P)
@@ -602,7 +611,8 @@ def main():
     for i in range(args.steps):
         step = args.warmup + i
         if W:
-            tot, kv = algorithmic_bytes_window(w.context + step + 1, B, Hq, Hkv, D, P, W)
+            tot, kv = algorithmic_bytes_window(w.context + step + 1, B, Hq, Hkv, D, P, W,
+                                               k_bytes=(D + 4) if k8 else None)
         else:
             tot, kv = algorithmic_bytes(w.context + KQ * (step + 1), B, Hq, Hkv, D, P, prefix_pages * P,
                                         k_bytes=(D + 4) if k8 else None, n_query=KQ)
