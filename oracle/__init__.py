@@ -32,6 +32,7 @@ from .paged_decode import (  # noqa: F401
     decode_attention,
     decode_attention_multi,
     decode_attention_window,
+    decode_attention_window_multi,
     kv_append,
     decode_partials,
     lse_merge,
@@ -49,6 +50,7 @@ from .quant_k8 import (  # noqa: F401
     decode_attention_k8,
     decode_attention_multi_k8,
     decode_attention_window_k8,
+    decode_attention_window_multi_k8,
     kv_append_k8,
 )
 from .allocator import PageAllocatorModel, OutOfPages, validate_tables  # noqa: F401

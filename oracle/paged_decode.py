@@ -265,6 +265,29 @@ def decode_attention_multi(q, k_pool, v_pool, block_table, lens, scale, page_siz
     return out
 
 
+def decode_attention_window_multi(q, k_pool, v_pool, ring_table, lens, window, scale, page_size):
+    """Chunks of queries over a sliding window in a ring of pages: query ``i``
+    of sequence ``b`` sits at position ``p = lens[b] - k + i`` (the chunk
+    reading of ``decode_attention_multi``) and attends the last ``window``
+    tokens up to itself, ``max(0, p + 1 - window) .. p`` (the window reading of
+    ``decode_attention_window``), each query being the window decode step of
+    its own prefix. All of the chunk's tokens must still be in the ring:
+    ``window + k - 1 <= (R - 1) * P + 1``. Returns float64 ``[B][k][Hq][D]``; a
+    row with ``lens[b] < k`` is all NaN."""
+    b_count, k, hq, d = q.shape
+    r = np.asarray(ring_table).shape[1]
+    if window + k - 1 > (r - 1) * page_size + 1:
+        raise ValueError("the chunk's windows must fit in the ring")
+    out = np.zeros((b_count, k, hq, d), dtype=np.float64)
+    lens64 = np.asarray(lens, dtype=np.int64)
+    short = lens64 < k
+    for i in range(k):
+        li = np.where(short, 0, lens64 - k + i + 1)
+        out[:, i] = decode_attention_window(q[:, i], k_pool, v_pool, ring_table, li, window, scale, page_size)
+    out[short] = np.nan
+    return out
+
+
 def kv_append(k_pool, v_pool, k_new, v_new, block_table, pos, page_size):
     """Return copies of the pools with each sequence's new token written.
 

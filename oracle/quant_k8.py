@@ -221,6 +221,25 @@ def decode_attention_window_k8(q, pool8, v_pool, ring_table, lens, window, scale
     return out
 
 
+def decode_attention_window_multi_k8(q, pool8, v_pool, ring_table, lens, window, scale, page_size):
+    """``decode_attention_window_multi`` over int8 keys: query ``i`` of sequence
+    ``b`` is the int8-key window decode step (``decode_attention_window_k8``)
+    of its own prefix ``lens[b] - k + i + 1``; a row with ``lens[b] < k`` is all
+    NaN; ``window + k - 1 <= (R - 1) * P + 1``."""
+    b_count, k, hq, d = q.shape
+    r = np.asarray(ring_table).shape[1]
+    if window + k - 1 > (r - 1) * page_size + 1:
+        raise ValueError("the chunk's windows must fit in the ring")
+    out = np.zeros((b_count, k, hq, d), dtype=np.float64)
+    lens64 = np.asarray(lens, dtype=np.int64)
+    short = lens64 < k
+    for i in range(k):
+        li = np.where(short, 0, lens64 - k + i + 1)
+        out[:, i] = decode_attention_window_k8(q[:, i], pool8, v_pool, ring_table, li, window, scale, page_size)
+    out[short] = np.nan
+    return out
+
+
 def kv_append_k8(pool8, v_pool, k_new, v_new, block_table, pos, page_size):
     """Copies of the pools with each sequence's new token written: its key
     quantised (``quantize_k``) into the int8 pool, its value as fp16 (the

@@ -347,3 +347,24 @@ def test_window_k8_planted_mistake_is_caught(old, new):
     exec(compile(src.replace(old, new), "<mutant>", "exec"), mutant.__dict__)
     with pytest.raises((AssertionError, IndexError)):
         _check_window_k8(mutant.decode_attention_window_k8)
+
+
+def test_window_chunks_k8_are_per_query_window_decodes():
+    """Chunks over an int8-key ring: query i equals the int8 window decode of
+    its own prefix (checked against the pinned window oracle), short rows NaN."""
+    rng = np.random.default_rng(44)
+    B, Hq, Hkv, D, P, R, W, k = 2, 4, 2, 64, 16, 4, 40, 3
+    N = B * R + 2
+    ring = rng.permutation(N)[:B * R].reshape(B, R).astype(np.int32)
+    kp = _paged_fp16_pool(rng, N, Hkv, P, D)
+    vp = _paged_fp16_pool(rng, N, Hkv, P, D)
+    pool8 = oracle.quantize_k_pool(kp)
+    lens = np.array([k + 1, 5 * R * P + 3], np.int32)
+    q = _fp16(rng.standard_normal((B, k, Hq, D)))
+    got = oracle.decode_attention_window_multi_k8(q, pool8, vp, ring, lens, W, 0.125, P)
+    for i in range(k):
+        li = lens - k + i + 1
+        np.testing.assert_array_equal(got[:, i], oracle.decode_attention_window_k8(q[:, i], pool8, vp, ring, li, W,
+                                                                                   0.125, P))
+    short = oracle.decode_attention_window_multi_k8(q, pool8, vp, ring, np.array([k - 1, 50], np.int32), W, 0.125, P)
+    assert np.all(np.isnan(short[0])) and np.all(np.isfinite(short[1]))

@@ -88,3 +88,44 @@ def test_tokens_outside_the_window_do_not_matter():
     assert np.array_equal(oracle.decode_attention_window(q, kp2, vp2, ring, lens, W, 0.3, P), base)
     with pytest.raises(ValueError):
         oracle.decode_attention_window(q, kp, vp, ring, lens, (R - 1) * P + 2, 0.3, P)
+
+
+def _window_causal_textbook(Q, K, V, scale, W):
+    """Q [k][D], K/V [L][D] contiguous: query i sits at p = L - k + i and sees
+    keys max(0, p + 1 - W) .. p only."""
+    k, L = len(Q), len(K)
+    out = []
+    for i in range(k):
+        p = L - k + i
+        lo = max(0, p + 1 - W)
+        scores = [scale * math.fsum(a * b for a, b in zip(Q[i], K[j])) for j in range(lo, p + 1)]
+        top = max(scores)
+        w = [math.exp(s - top) for s in scores]
+        z = math.fsum(w)
+        out.append([math.fsum(w[j] * V[lo + j][d] for j in range(len(w))) / z for d in range(len(V[0]))])
+    return out
+
+
+@pytest.mark.parametrize("k,W,R", [(1, 33, 3), (4, 30, 3), (3, 47, 4), (2, 1, 2)])
+def test_window_chunks_brute_force(k, W, R):
+    """Each query of a chunk over a wrapped ring sees only the window ending at
+    itself: the textbook with per-query bounds on the contiguous K/V."""
+    rng = np.random.default_rng(7 * k + W)
+    B, Hkv, G, D, P = 2, 2, 2, 32, 16
+    Hq = Hkv * G
+    lens = np.array([k + 3, R * P * 3 + 9], np.int32)
+    ring, kp, vp, K, V = _ring_case(rng, B, Hkv, D, P, R, lens)
+    q = rng.standard_normal((B, k, Hq, D)).astype(np.float16)
+    got = oracle.decode_attention_window_multi(q, kp, vp, ring, lens, W, 0.2, P)
+    s32 = float(np.float32(0.2))
+    for b in range(B):
+        for h in range(Hq):
+            kvh = h // G
+            ref = _window_causal_textbook(q[b, :, h].astype(float).tolist(), K[b][kvh].astype(float).tolist(),
+                                          V[b][kvh].astype(float).tolist(), s32, W)
+            np.testing.assert_allclose(got[b, :, h], ref, rtol=0, atol=1e-12)
+    one = oracle.decode_attention_window_multi(q[:, -1:], kp, vp, ring, lens, W, 0.2, P)
+    np.testing.assert_array_equal(one[:, 0], oracle.decode_attention_window(q[:, -1], kp, vp, ring, lens, W, 0.2, P))
+    short = oracle.decode_attention_window_multi(q, kp, vp, ring, np.array([k - 1, 40], np.int32), W, 0.2, P)
+    if k > 1:
+        assert np.all(np.isnan(short[0])) and np.all(np.isfinite(short[1]))
