@@ -338,6 +338,32 @@ int pkv_paged_decode_attention_window(void* out, const void* q, const void* k_ne
                                       size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_paged_decode_attention_window_multi -- chunks of queries (as
+ * pkv_paged_decode_attention_multi: query i of sequence b at position
+ * p = lens[b] - n_query + i) over a sliding window in a ring of pages (as
+ * pkv_paged_decode_attention_window): query i attends the last `window`
+ * tokens ending at itself, max(0, p + 1 - window) .. p. Drafted tokens of a
+ * sliding-window model verified in one call; their keys and values must be in
+ * the ring already (pkv_kv_append_chunk through the ring table's logical
+ * pages).
+ *
+ *   q, out       : fp16 [B][n_query][Hq][D] device.
+ *   ring_pages   : window + n_query - 1 <= (ring_pages - 1) * P + 1, so that
+ *                  every token the chunk's windows reach is still in the ring.
+ *   lens[b]      : tokens so far, the chunk included; lens[b] < n_query (or
+ *                  negative, or above 2^31 - 65) makes the row NaN.
+ *   workspace    : pkv_decode_workspace_bytes(B, Hq, D, window,
+ *                  partition_tokens, ...) bytes when partition_tokens > 0.
+ * n_query * (Hq / Hkv) <= 16 as in pkv_paged_decode_attention_multi. Errors
+ * as pkv_paged_decode_attention_window and pkv_paged_decode_attention_multi.
+ */
+int pkv_paged_decode_attention_window_multi(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                            const int32_t* ring_table, int32_t ring_pages, const int32_t* lens,
+                                            int32_t B, int32_t n_query, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                                            int32_t N, int32_t window, float scale, int32_t partition_tokens,
+                                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * pkv_paged_decode_attention_multi_shared_prefix -- the chunked attention of
  * pkv_paged_decode_attention_multi for a batch whose sequences all begin with
  * the same prefix_tokens tokens in the same pages (drafted tokens verified
@@ -467,6 +493,19 @@ int pkv_paged_decode_attention_window_k8(void* out, const void* q, const void* k
                                          const int32_t* lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
                                          int32_t N, int32_t window, float scale, int32_t partition_tokens,
                                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_paged_decode_attention_window_multi_k8 --
+ * pkv_paged_decode_attention_window_multi over int8-key pages (keys
+ * dequantised as code * scale, values fp16). Arguments and errors as there,
+ * the key pool being the int8 pool above.
+ */
+int pkv_paged_decode_attention_window_multi_k8(void* out, const void* q, const void* k_pool8, const void* v_pool,
+                                               const int32_t* ring_table, int32_t ring_pages, const int32_t* lens,
+                                               int32_t B, int32_t n_query, int32_t Hq, int32_t Hkv, int32_t D,
+                                               int32_t P, int32_t N, int32_t window, float scale,
+                                               int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                                               void* stream);
 
 /*
  * pkv_probe_stream_read -- measurement aid (not part of decode): read

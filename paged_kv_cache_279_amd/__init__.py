@@ -33,6 +33,7 @@ from .binding import (  # noqa: F401
     paged_decode_attention_multi_k8,
     paged_decode_attention_shared_prefix,
     paged_decode_attention_window,
+    paged_decode_attention_window_multi,
     paged_decode_attention_window_k8,
     probe_stream_read,
     profile_next_partition_kernel,

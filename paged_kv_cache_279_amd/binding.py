@@ -59,6 +59,8 @@ _SIGNATURES = {
     "pkv_paged_decode_attention_window_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32,
                                                             _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _vp,
                                                             ctypes.c_size_t, _vp]),
+    "pkv_paged_decode_attention_window_multi": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]),
+    "pkv_paged_decode_attention_window_multi_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _vp, ctypes.c_size_t, _vp]),
     "pkv_kv_append_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32, _i32, _i32, _vp]),
     "pkv_paged_decode_attention_k8": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _i32, _i32,
                                                      _i32, _i32, _i32, _i32, ctypes.c_float, _i32, _i32, _vp,
@@ -311,6 +313,38 @@ def paged_decode_attention_window(q, k_pool, v_pool, ring_table, lens, window, s
         _dev_ptr(ring_table, torch.int32, "ring_table"), ring_pages, _dev_ptr(lens, torch.int32, "lens"),
         B, Hq, Hkv, D, P, N, int(window), float(scale), int(partition_tokens), ws_ptr, ws_len, _stream(stream))
     _check(rc, "pkv_paged_decode_attention_window")
+    return out
+
+
+def paged_decode_attention_window_multi(q, k_pool, v_pool, ring_table, lens, window, scale, partition_tokens=0,
+                                        out=None, workspace=None, stream=None):
+    """pkv_paged_decode_attention_window_multi (fp16 keys) or, when ``k_pool`` is an int8-key pool
+    (uint8 [N][Hkv][P/16][16 D + 64]), pkv_paged_decode_attention_window_multi_k8: chunks of
+    queries q [B][n_query][Hq][D], each attending the window ending at itself through the ring."""
+    k8 = k_pool.dtype == torch.uint8
+    if k8:
+        N, Hkv, P, D = _k8_shape(k_pool, v_pool)
+    else:
+        N, Hkv, P, D = k_pool.shape
+        if tuple(v_pool.shape) != tuple(k_pool.shape):
+            raise ValueError("shape mismatch")
+    B, nq, Hq, Dq = q.shape
+    _, ring_pages = ring_table.shape
+    if Dq != D or ring_table.shape[0] != B or tuple(lens.shape) != (B,):
+        raise ValueError("shape mismatch")
+    if out is None:
+        out = torch.empty((B, nq, Hq, D), dtype=torch.float16, device=q.device)
+    if tuple(out.shape) != (B, nq, Hq, D):
+        raise ValueError("out must be [B][n_query][Hq][D]")
+    ws_ptr, ws_len = _workspace_arg(workspace, decode_workspace_bytes(B, Hq, D, int(window), partition_tokens),
+                                    q.device)
+    fn = lib().pkv_paged_decode_attention_window_multi_k8 if k8 else lib().pkv_paged_decode_attention_window_multi
+    rc = fn(_dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"),
+            _dev_ptr(k_pool, torch.uint8 if k8 else torch.float16, "k_pool"), _dev_ptr(v_pool, torch.float16, "v_pool"),
+            _dev_ptr(ring_table, torch.int32, "ring_table"), ring_pages, _dev_ptr(lens, torch.int32, "lens"),
+            B, nq, Hq, Hkv, D, P, N, int(window), float(scale), int(partition_tokens), ws_ptr, ws_len,
+            _stream(stream))
+    _check(rc, "pkv_paged_decode_attention_window_multi" + ("_k8" if k8 else ""))
     return out
 
 

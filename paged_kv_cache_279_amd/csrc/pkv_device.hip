@@ -408,8 +408,10 @@ __device__ __forceinline__ void set_priority(int32_t remaining, int32_t quota) {
 // (start <= win_lo < start + 16; win_lo = 0 without a window).
 //
 // kMQ: the column of lane (col, quad) may see tokens up to clim only (the
-// causal bound of its query within a chunk); clim_min is the smallest bound of
-// the wave, so blocks wholly below it skip the mask.
+// causal bound of its query within a chunk) and, with a sliding window, from
+// clo on (its query's own window start); clim_min is the smallest upper bound
+// and clo_max the largest lower bound of the wave, so blocks wholly inside
+// both skip the mask.
 //
 // kAppend: the new token nt is taken from k_new / v_new instead of the pool:
 // the wave that streams its block loads the token's operand slices with its
@@ -420,7 +422,8 @@ template <int D, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ>
 __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32_t* bt_row, int32_t kvh,
                                               int32_t start, int32_t end, int32_t first, int32_t stride,
                                               int32_t quota, int32_t after, const NewToken& nt,
-                                              int32_t clim, int32_t clim_min, int32_t win_lo,
+                                              int32_t clim, int32_t clim_min, int32_t clo, int32_t clo_max,
+                                              int32_t win_lo,
                                               const half8_t (&qb)[D / 32], WaveState<D>& st, int lane) {
   constexpr int KL = D / 32;           // 16-byte loads per lane per block, for K and for V
   constexpr int NT = D / 16;           // 16-dim output tiles
@@ -669,9 +672,13 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
       }
     }
     if constexpr (kMQ) {
-      if (t0 + kBlk - 1 > clim_min) {
+      // causal bound of each query, and with a sliding window its own window start
+      if (t0 + kBlk - 1 > clim_min || t0 < clo_max) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) s[i] = t0 + 4 * quad + i <= clim ? s[i] : kNegInf();
+        for (int i = 0; i < 4; ++i) {
+          const int32_t t = t0 + 4 * quad + i;
+          s[i] = t <= clim && t >= clo ? s[i] : kNegInf();
+        }
       }
     }
     const int32_t rem = end - t0;      // valid tokens in this block (>= 1)
@@ -807,12 +814,18 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
   WaveState<D> st;
   init_state<D>(st);
   int32_t clim = 0x7fffffff;
+  int32_t clo = 0, clo_max = 0;
   if constexpr (kMQ) {
+    // query qi sits at mq_last0 + qi; with a window it sees window tokens ending there
     const int32_t qi = col / mq_g;
     clim = qi < p.nq ? mq_last0 + qi : 0x7fffffff;
+    if (p.window > 0) {
+      clo = qi < p.nq ? max(0, mq_last0 + qi + 1 - p.window) : 0;
+      clo_max = max(0, mq_last0 + p.nq - p.window);
+    }
   }
   stream_blocks<D, kPolicy, kAppend, kK8, kMQ>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, nt,
-                                                     clim, mq_last0, lo, qb, st, lane);
+                                                     clim, mq_last0, clo, clo_max, lo, qb, st, lane);
   // per-column denominators of this wave: sum the 4 quads of column col
   st.l_part += __shfl_xor(st.l_part, 16);
   st.l_part += __shfl_xor(st.l_part, 32);
@@ -885,7 +898,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
     const int32_t kvh = blockIdx.x % p.Hkv;
     const int32_t b = blockIdx.x / p.Hkv;
     const int32_t L = p.lens[b];
-    const bool bad_len = L < p.nq || L > p.max_context || L > (p.max_pages << p.p_shift);
+    const bool bad_len = L < p.nq || L > p.max_context || (p.ring == 0 && L > (p.max_pages << p.p_shift));
     const int32_t ncol = p.nq * G;
     auto row = [&](int c) -> int64_t { return ((int64_t)b * p.nq + c / G) * p.Hq + (int64_t)kvh * G + c % G; };
     if (bad_len) {
@@ -893,8 +906,10 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
       return;
     }
     const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
+    // sliding window: from the block holding the first query's window start
+    const int32_t lo = p.window > 0 ? max(0, L - p.nq + 1 - p.window) : 0;
     run_range<D, 16, kKvLoadPolicy, false, K8, true>(
-        p, smem.tile.prefix, bt_row, kvh, 0, L, 0, 0, NewToken{-1, 0, nullptr, nullptr},
+        p, smem.tile.prefix, bt_row, kvh, lo & ~(kBlk - 1), L, 0, 0, NewToken{-1, 0, nullptr, nullptr},
         [&](int c) -> int64_t { return c < ncol ? row(c) : -1; },
         [&](int c, int d, float, float Ls, float O) {
           if (c < ncol) {
@@ -902,7 +917,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
             p.out[row(c) * D + d] = (half_t)(Ls != Ls ? __builtin_nanf("") : r);
           }
         },
-        lane, wave, L - p.nq, G);
+        lane, wave, L - p.nq, G, lo);
   } else if constexpr (!SPLIT) {
     WgShared<D, G>& sh = smem.tile.priv;
     const int32_t kvh = blockIdx.x % p.Hkv;
@@ -939,10 +954,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
     const int32_t wg = blockIdx.x;
     const int32_t per = (p.B + kThreads - 1) / kThreads;
     const int32_t b0 = threadIdx.x * per;
-    // first streamed token of a sequence: after the shared prefix, or the
-    // 16-aligned block below the window start
+    // first token of a sequence's window (that of its first query), and the
+    // first streamed token: after the shared prefix, or the 16-aligned block
+    // holding the window start
+    auto window_lo = [&](int32_t L) -> int32_t { return p.window > 0 ? max(0, L - p.nq + 1 - p.window) : 0; };
     auto first_token = [&](int32_t L) -> int32_t {
-      return p.window > 0 ? max(0, L - p.window) & ~(kBlk - 1) : p.prefix_tokens;
+      return p.window > 0 ? window_lo(L) & ~(kBlk - 1) : p.prefix_tokens;
     };
     auto priv_blocks = [&](int32_t bb) -> int32_t {
       const int32_t L = p.lens[bb];
@@ -1073,12 +1090,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
               [&](int c) -> int64_t {
                 return c < ncol ? ((int64_t)b * p.nq + c / G) * p.Hq + (int64_t)kvh * G + c % G : -1;
               },
-              emit, lane, wave, L - p.nq, G);
+              emit, lane, wave, L - p.nq, G, window_lo(L));
         } else {
           run_range<D, G, kKvLoadPolicy, FUSED, K8>(
               p, smem.tile.priv, bt_row, kvh, start, end, quota, after + g1 - g - piece_n, nt,
               [&](int c) -> int64_t { return c < G ? head_row0 + c : -1; }, emit, lane, wave, 0, 1,
-              p.window > 0 ? max(0, L - p.window) : 0);
+              window_lo(L));
         }
         g += piece_n;
       }
@@ -1414,7 +1431,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   const int G = Hq / Hkv;
   if (nq < 1) return PKV_ERR_INVALID_ARG;
   if (nq > 1 && fused) return PKV_ERR_INVALID_ARG;
-  if (window < 0 || (window > 0 && (nq > 1 || prefix_tokens > 0))) return PKV_ERR_INVALID_ARG;
+  if (window < 0 || (window > 0 && prefix_tokens > 0)) return PKV_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(nq) * G > 16) return PKV_ERR_UNSUPPORTED;     // one 16-column matrix-core tile
   if (static_cast<int64_t>(B) * nq * Hq > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
@@ -1424,8 +1441,8 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   if (prefix_tokens % P != 0) return PKV_ERR_INVALID_ARG;       // shared pages hold prefix tokens only
   if (window == 0 && static_cast<int64_t>(max_context) > (static_cast<int64_t>(max_pages) << p_shift))
     return PKV_ERR_INVALID_ARG;
-  // a ring of max_pages pages holds every page a window of this many tokens touches
-  if (window > 0 && static_cast<int64_t>(window) > (static_cast<int64_t>(max_pages) - 1) * P + 1)
+  // a ring of max_pages pages holds every page the windows of a chunk touch
+  if (window > 0 && static_cast<int64_t>(window) + nq - 1 > (static_cast<int64_t>(max_pages) - 1) * P + 1)
     return PKV_ERR_INVALID_ARG;
   Plan plan;
   const int rc = make_plan(B, Hq, Hkv, max_context, partition_tokens, prefix_tokens, &plan, nq);
@@ -1787,6 +1804,31 @@ int pkv_paged_decode_attention_window_k8(void* out, const void* q, const void* k
   return decode_common(out, q, k_new, v_new, k_pool8, v_pool, k_pool8, v_pool, ring_table, ring_pages, lens, B, Hq,
                        Hkv, D, P, N, kWindowMaxLen, scale, partition_tokens, 0, workspace, workspace_bytes, stream,
                        fused, true, 1, window);
+}
+
+int pkv_paged_decode_attention_window_multi(void* out, const void* q, const void* k_pool, const void* v_pool,
+                                            const int32_t* ring_table, int32_t ring_pages, const int32_t* lens,
+                                            int32_t B, int32_t n_query, int32_t Hq, int32_t Hkv, int32_t D, int32_t P,
+                                            int32_t N, int32_t window, float scale, int32_t partition_tokens,
+                                            void* workspace, size_t workspace_bytes, void* stream) {
+  if (n_query < 1 || window <= 0 || ring_pages <= 0) return PKV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * n_query > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
+  return decode_common(out, q, nullptr, nullptr, k_pool, v_pool, nullptr, nullptr, ring_table, ring_pages, lens, B,
+                       Hq, Hkv, D, P, N, kWindowMaxLen, scale, partition_tokens, 0, workspace, workspace_bytes,
+                       stream, false, false, n_query, window);
+}
+
+int pkv_paged_decode_attention_window_multi_k8(void* out, const void* q, const void* k_pool8, const void* v_pool,
+                                               const int32_t* ring_table, int32_t ring_pages, const int32_t* lens,
+                                               int32_t B, int32_t n_query, int32_t Hq, int32_t Hkv, int32_t D,
+                                               int32_t P, int32_t N, int32_t window, float scale,
+                                               int32_t partition_tokens, void* workspace, size_t workspace_bytes,
+                                               void* stream) {
+  if (n_query < 1 || window <= 0 || ring_pages <= 0) return PKV_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(B) * n_query > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
+  return decode_common(out, q, nullptr, nullptr, k_pool8, v_pool, nullptr, nullptr, ring_table, ring_pages, lens, B,
+                       Hq, Hkv, D, P, N, kWindowMaxLen, scale, partition_tokens, 0, workspace, workspace_bytes,
+                       stream, false, true, n_query, window);
 }
 
 int pkv_paged_decode_attention_multi_shared_prefix(void* out, const void* q, const void* k_pool, const void* v_pool,

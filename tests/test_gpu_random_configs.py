@@ -2,7 +2,7 @@
 (plain decode, fused append, shared prefix, int8 keys, chunks of queries,
 sliding windows) with random head groups, head sizes, page sizes, partition
 sizes and ragged lengths (int8 keys also under chunks, with and without a
-prefix, and under sliding windows), each checked against the oracle within 4e-3; the
+prefix, and under sliding windows, also with chunks), each checked against the oracle within 4e-3; the
 fused appends must leave the pools byte-identical to the oracle's. Every
 slot no query attends holds NaN (NaN scales for int8 keys)."""
 
@@ -20,7 +20,8 @@ pytestmark = pytest.mark.gpu
 TOL = 4e-3
 N_CASES = 220
 MODES = ["decode", "fused", "prefix", "prefix_fused", "k8", "k8_fused", "k8_prefix", "multi", "multi_prefix",
-         "window", "window_fused", "k8_multi", "k8_multi_prefix", "k8_window", "k8_window_fused"]
+         "window", "window_fused", "k8_multi", "k8_multi_prefix", "k8_window", "k8_window_fused", "window_multi",
+         "k8_window_multi"]
 
 
 def say(*a):
@@ -155,17 +156,32 @@ def test_random_configuration(i):
 
     if "window" in mode:
         R = int(rng.integers(2, 6))
-        W = int(rng.integers(1, (R - 1) * P + 2))
-        lens = rng.integers(1 if fused else 0, 3 * R * P, size=B).astype(np.int32)
+        W = int(rng.integers(1, (R - 1) * P + 2 - (nq - 1)))        # the chunk's windows fit the ring
+        low = nq if nq > 1 else (1 if fused else 0)
+        lens = rng.integers(low, 3 * R * P + low, size=B).astype(np.int32)
         N = B * R + 2
         ring = rng.permutation(N)[:B * R].reshape(B, R).astype(np.int32)
         attended = lens - 1 if fused else lens
-        lo = np.maximum(lens - W, 0)
+        lo = np.maximum(lens - nq + 1 - W, 0)                        # the first query's window start
         live = live_slots(N, P, ring, attended, lo)
         vp = poison(f16(rng, (N, Hkv, P, D)), live, "v")
         q = f16(rng, (B, Hq, D))
         width = max(1, -(-int(lens.max()) // P))
         logical = np.ascontiguousarray(ring[:, np.arange(width) % R])
+        if nq > 1:
+            q = f16(rng, (B, nq, Hq, D))
+            if mode.startswith("k8"):
+                pool8 = k8_pool(rng, N, Hkv, P, D, live)
+                got = m.paged_decode_attention_window_multi(dev(q), dev(pool8), dev(vp), dev(ring), dev(lens), W,
+                                                            scale, part)
+                ref = oracle.decode_attention_window_multi_k8(q, pool8, vp, ring, lens, W, scale, P)
+            else:
+                kp = poison(f16(rng, (N, Hkv, P, D)), live, "k")
+                got = m.paged_decode_attention_window_multi(dev(q), dev(kp), dev(vp), dev(ring), dev(lens), W,
+                                                            scale, part)
+                ref = oracle.decode_attention_window_multi(q, kp, vp, ring, lens, W, scale, P)
+            check(host(got), ref, what + " R=%d W=%d" % (R, W))
+            return
         if mode.startswith("k8"):
             pool8 = k8_pool(rng, N, Hkv, P, D, live)
             k8d, vd = dev(pool8), dev(vp)

@@ -213,3 +213,66 @@ def test_window_k8_matches_oracle(part, fused):
         torch.cuda.synchronize()
     ref = orc.decode_attention_window_k8(q, pool8, vp, ring, lens, W, scale, P)
     check_close(host(got), ref, "window k8 part=%d fused=%s" % (part, fused))
+
+
+@pytest.mark.parametrize("nq,part,k8", [(4, 0, False), (4, 64, False), (2, 512, False), (4, 0, True), (3, 64, True)])
+def test_window_chunks_match_oracle(nq, part, k8):
+    """Chunks of queries over a wrapped ring: the chunk's tokens appended in
+    one launch through the ring's logical pages (bit-exact), then each query
+    attending the window ending at itself; stale slots NaN."""
+    import oracle as orc
+    D, Hq, Hkv, P, R = 128, 16, 4, 16, 9
+    W = (R - 1) * P + 1 - (nq - 1)
+    cap = R * P
+    lens = np.array([nq, nq + 5, W, W + nq + 3, cap + 1, 3 * cap + P, 37 * cap + 11, 5 * cap + W + 9], np.int32)
+    B = len(lens)
+    rng = np.random.default_rng(60 + nq + part + k8)
+    N = B * R + 3
+    ring = rng.permutation(N)[:B * R].reshape(B, R).astype(np.int32)
+    before = lens - nq                                   # tokens before the chunk
+    lo = np.maximum(lens - nq + 1 - W, 0)
+    live = np.zeros((N, P), dtype=bool)
+    for b in range(B):
+        t = np.arange(lo[b], before[b])
+        live[ring[b, (t // P) % R], t % P] = True
+    vp = rng.standard_normal((N, Hkv, P, D), dtype=np.float32).astype(np.float16)
+    kp = rng.standard_normal((N, Hkv, P, D), dtype=np.float32).astype(np.float16)
+    pages, slots = np.nonzero(~live)
+    for pool, f in ((kp, orc.k_tile_offset), (vp, orc.v_tile_offset)):
+        tiles = pool.reshape(N, Hkv, P * D)
+        off = f(slots[:, None], np.arange(D)[None, :], P, D)
+        for kvh in range(Hkv):
+            tiles[pages[:, None], kvh, off] = np.nan
+    kn = rng.standard_normal((B, nq, Hkv, D), dtype=np.float32).astype(np.float16)
+    vn = rng.standard_normal((B, nq, Hkv, D), dtype=np.float32).astype(np.float16)
+    q = rng.standard_normal((B, nq, Hq, D), dtype=np.float32).astype(np.float16)
+    logical = _logical_table(ring, lens.max(), P)
+    scale = 1.0 / math.sqrt(D)
+    say("window chunks nq=%d part=%d k8=%s" % (nq, part, k8))
+    m = pkv()
+    if k8:
+        codes = rng.integers(-127, 128, size=(N, Hkv, P // 16, 16 * D)).astype(np.int8).view(np.uint8)
+        sc = (np.abs(rng.standard_normal((N, Hkv, P // 16, 16))) * 0.05 + 0.005).astype(np.float32)
+        sc = np.where(np.broadcast_to(~live.reshape(N, 1, P // 16, 16), sc.shape), np.float32(np.nan), sc)
+        pool8 = np.ascontiguousarray(np.concatenate([codes, sc.view(np.uint8)], axis=-1))
+        kd, vd = dev(pool8), dev(vp)
+        m.kv_append_k8_chunk(dev(kn), dev(vn), kd, vd, dev(logical), dev(before))
+        rk, rv = pool8, vp
+        for i in range(nq):
+            rk, rv = orc.kv_append_k8(rk, rv, kn[:, i], vn[:, i], logical, (before + i).astype(np.int32), P)
+        got = m.paged_decode_attention_window_multi(dev(q), kd, vd, dev(ring), dev(lens), W, scale, part)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(kd), rk)
+        ref = orc.decode_attention_window_multi_k8(q, rk, rv, ring, lens, W, scale, P)
+    else:
+        kd, vd = dev(kp), dev(vp)
+        m.kv_append_chunk(dev(kn), dev(vn), kd, vd, dev(logical), dev(before))
+        rk, rv = kp, vp
+        for i in range(nq):
+            rk, rv = orc.kv_append(rk, rv, kn[:, i], vn[:, i], logical, (before + i).astype(np.int32), P)
+        got = m.paged_decode_attention_window_multi(dev(q), kd, vd, dev(ring), dev(lens), W, scale, part)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(kd).view(np.uint16), rk.view(np.uint16))
+        ref = orc.decode_attention_window_multi(q, rk, rv, ring, lens, W, scale, P)
+    assert np.array_equal(host(vd).view(np.uint16), rv.view(np.uint16))
+    check_close(host(got), ref, "window chunks nq=%d part=%d k8=%s" % (nq, part, k8))
