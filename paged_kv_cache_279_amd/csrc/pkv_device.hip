@@ -142,6 +142,21 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 
 __device__ __forceinline__ half8_t as_h8(const uint4& v) { return __builtin_bit_cast(half8_t, v); }
 
+// Maximum of x over the four lanes col, col + 16, col + 32, col + 48 (the four
+// quads of an MFMA column), in every one of them. gfx950's lane-swap
+// instructions exchange 32-lane halves and odd/even 16-lane rows between two
+// registers; swapping x with a copy of itself leaves lane j holding x[j] in one
+// register and x[j ^ 32] (then x[j ^ 16]) in the other. VALU only: no LDS
+// round trip, unlike a bpermute shuffle.
+__device__ __forceinline__ float col_max4(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto h = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float y = fmaxf(__builtin_bit_cast(float, (uint32_t)h[0]), __builtin_bit_cast(float, (uint32_t)h[1]));
+  const uint32_t v = __builtin_bit_cast(uint32_t, y);
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return fmaxf(__builtin_bit_cast(float, (uint32_t)r[0]), __builtin_bit_cast(float, (uint32_t)r[1]));
+}
+
 __device__ __forceinline__ half4_t lo4(const uint4& v) {
   return __builtin_bit_cast(half4_t, make_uint2(v.x, v.y));
 }
@@ -696,9 +711,7 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
         vr[j].w &= m1;
       }
     }
-    float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    bm = fmaxf(bm, __shfl_xor(bm, 16));
-    bm = fmaxf(bm, __shfl_xor(bm, 32));
+    float bm = col_max4(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
     bm *= c;                            // block max of column col, base-2 units (c > 0)
     if (__builtin_amdgcn_ballot_w64(bm > st.m_ref + kRescaleSlack) != 0) {
       const float m_new = fmaxf(st.m_ref, bm);
