@@ -4,7 +4,10 @@ sliding windows) with random head groups, head sizes, page sizes, partition
 sizes and ragged lengths (int8 keys also under chunks, with and without a
 prefix, and under sliding windows, also with chunks), each checked against the oracle within 4e-3; the
 fused appends must leave the pools byte-identical to the oracle's. Every
-slot no query attends holds NaN (NaN scales for int8 keys)."""
+slot no query attends holds NaN (NaN scales for int8 keys). A second set of
+seeded cases takes 8 or 16 KV heads, one- or two-block minimum pieces and
+contexts of several hundred tokens, so the split schedule cuts every
+sequence into many pieces across many workgroups."""
 
 import math
 import sys
@@ -142,13 +145,47 @@ def check(got, ref, what):
     assert err <= TOL, "%s: max abs error %.3e" % (what, err)
 
 
+def make_many_heads_case(i):
+    """Many KV heads and tiny pieces: 8 or 16 KV heads (64 or 32 workgroups
+    per head), minimum pieces of one or two blocks and a few hundred blocks
+    per KV head, so every workgroup's share crosses several sequences and
+    every sequence is cut into many pieces; long sliding windows over rings of
+    24-47 pages."""
+    rng = np.random.default_rng(17000 + i)
+    mode = MODES[i % len(MODES)]
+    D = int(rng.choice([64, 128]))
+    P = int(rng.choice([16, 32, 64]))
+    Hkv = int(rng.choice([8, 16]))
+    G = int(rng.choice([1, 2, 4]))
+    nq = 1
+    if "multi" in mode:
+        nq = int(rng.integers(2, 16 // G + 1))
+    B = int(rng.integers(6, 13))
+    part = int(rng.choice([16, 32]))
+    prefix = int(rng.integers(1, 4)) * P if "prefix" in mode else 0
+    fused = mode.endswith("fused")
+    floor = prefix + (nq if nq > 1 else (1 if fused else 0))
+    lens = rng.integers(floor + 400, floor + 1400, size=B)
+    lens[0] = floor + int(rng.integers(0, 17))                  # one short row among long ones
+    return dict(rng=rng, mode=mode, D=D, P=P, Hkv=Hkv, G=G, Hq=Hkv * G, nq=nq, B=B, part=part, prefix=prefix,
+                fused=fused, lens=lens.astype(np.int32), many=True)
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_configuration(i):
-    c = make_case(i)
+    run_case(make_case(i), i)
+
+
+@pytest.mark.parametrize("i", range(4 * len(MODES)))
+def test_many_heads_configuration(i):
+    run_case(make_many_heads_case(i), i)
+
+
+def run_case(c, i):
     rng, mode, D, P, Hkv, Hq, nq, B = c["rng"], c["mode"], c["D"], c["P"], c["Hkv"], c["Hq"], c["nq"], c["B"]
     part, prefix, fused, lens = c["part"], c["prefix"], c["fused"], c["lens"]
     scale = 1.0 / math.sqrt(D)
-    what = "case %d %s D=%d P=%d Hkv=%d G=%d nq=%d B=%d part=%d prefix=%d lens=%s" % (
+    what = ("many-heads " if c.get("many") else "") + "case %d %s D=%d P=%d Hkv=%d G=%d nq=%d B=%d part=%d prefix=%d lens=%s" % (
         i, mode, D, P, Hkv, Hq // Hkv, nq, B, part, prefix, lens.tolist())
     say(what)
     m = pkv()
@@ -159,6 +196,11 @@ def test_random_configuration(i):
         W = int(rng.integers(1, (R - 1) * P + 2 - (nq - 1)))        # the chunk's windows fit the ring
         low = nq if nq > 1 else (1 if fused else 0)
         lens = rng.integers(low, 3 * R * P + low, size=B).astype(np.int32)
+        if c.get("many"):
+            # long windows over rings of many pages
+            R = int(rng.integers(24, 48))
+            W = int(rng.integers(((R - 1) * P) // 2, (R - 1) * P + 2 - (nq - 1)))
+            lens = rng.integers(W + low, 3 * R * P + low, size=B).astype(np.int32)
         N = B * R + 2
         ring = rng.permutation(N)[:B * R].reshape(B, R).astype(np.int32)
         attended = lens - 1 if fused else lens
