@@ -489,34 +489,6 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
         const uint32_t hi = reinterpret_cast<const uint16_t*>(nt.v)[32 * j + 16 + col];
         vn[j] = lo | (hi << 16);
       }
-      if constexpr (kK8) {
-        // quantise as the append kernel does: the 4 quads of a column hold all
-        // D dims between them, so two shuffles give amax; then
-        // scale = amax / 127 and code = rint(k / scale) in IEEE fp32
-        float amax = 0.f;
-#pragma unroll
-        for (int j = 0; j < KL; ++j) {
-          const half8_t h = as_h8(kn[j]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)h[e]));
-        }
-        amax = fmaxf(amax, __shfl_xor(amax, 16));
-        amax = fmaxf(amax, __shfl_xor(amax, 32));
-        const float qs = amax / 127.0f;
-        kq = amax > 0.f ? qs : 0.f;
-#pragma unroll
-        for (int j = 0; j < KL; ++j) {
-          const half8_t h = as_h8(kn[j]);
-          uint32_t w[2] = {0u, 0u};
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            int32_t c = 0;
-            if (amax > 0.f) c = max(-127, min(127, (int32_t)rintf((float)h[e] / qs)));
-            w[e / 4] |= ((uint32_t)c & 0xFFu) << (8 * (e % 4));
-          }
-          kc[j] = make_uint2(w[0], w[1]);
-        }
-      }
     }
   }
 
@@ -751,6 +723,39 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
   uint4 kr[kDepth + 1][KL], vr[kDepth + 1][KL];
 #pragma unroll
   for (int r = 0; r < kDepth; ++r) load_block(r, kr[r], vr[r]);
+  if constexpr (kAppend && kK8) {
+    // Quantise the new key once the first blocks' loads are in flight (it
+    // waits for the token's own loads; done before them, it would hold back
+    // the whole pipeline). As the append kernel does: the 4 quads of a
+    // column hold all D dims between them, so two shuffles give amax; then
+    // scale = amax / 127 and code = rint(k / scale) in IEEE fp32.
+    __builtin_amdgcn_sched_barrier(0);
+    if (nt.blk >= 0) {
+      float amax = 0.f;
+#pragma unroll
+      for (int j = 0; j < KL; ++j) {
+        const half8_t h = as_h8(kn[j]);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf((float)h[e]));
+      }
+      amax = fmaxf(amax, __shfl_xor(amax, 16));
+      amax = fmaxf(amax, __shfl_xor(amax, 32));
+      const float qs = amax / 127.0f;
+      kq = amax > 0.f ? qs : 0.f;
+#pragma unroll
+      for (int j = 0; j < KL; ++j) {
+        const half8_t h = as_h8(kn[j]);
+        uint32_t w[2] = {0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          int32_t c = 0;
+          if (amax > 0.f) c = max(-127, min(127, (int32_t)rintf((float)h[e] / qs)));
+          w[e / 4] |= ((uint32_t)c & 0xFFu) << (8 * (e % 4));
+        }
+        kc[j] = make_uint2(w[0], w[1]);
+      }
+    }
+  }
   int32_t k = 0;
   while (true) {
 #pragma unroll
