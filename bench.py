@@ -316,11 +316,11 @@ def main():
         return torch.cat([codes.view(torch.uint8), scales.view(torch.uint8)], dim=-1).contiguous()
 
     for layer in range(R):
-        vp = torch.empty((N, Hkv, P, D), dtype=torch.float16, device=dev)
+        vp = pkv.empty_pool(N, Hkv, P, D, device=dev)
         if k8:
             kp = random_k8_pool()
         else:
-            kp = torch.empty((N, Hkv, P, D), dtype=torch.float16, device=dev)
+            kp = pkv.empty_pool(N, Hkv, P, D, device=dev)
         if layer == 0:
             if not k8:
                 kp[:w.N].copy_(put(w.k_pool))
@@ -359,9 +359,7 @@ def main():
         q_mq.normal_(generator=gen)
         out_mq = torch.empty((B, KQ, Hq, D), dtype=torch.float16, device=dev)
     max_context = int(final_ctx.max())
-    # chunks of queries with a shared prefix: the chunk rows count as sequences in the workspace query
-    ws_rows = B * KQ if KQ > 1 and prefix_tokens else B
-    ws_bytes = pkv.decode_workspace_bytes(ws_rows, Hq, D, W or max_context, part, prefix_tokens)
+    ws_bytes = pkv.decode_workspace_bytes_multi(B, KQ, Hq, D, W or max_context, part, prefix_tokens)
     workspace = torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float16, device=dev)
     torch.cuda.synchronize()

@@ -10,13 +10,15 @@
  *
  * Data layout shared by every device entry point
  * ----------------------------------------------
- *   K pool, V pool : fp16, N pages x Hkv KV heads x one tile of P*D halves;
- *                    the tile of (page, KV head) is contiguous. A page holds P
- *                    tokens of every KV head (hotelren §3.2 and pgsm §3.2
- *                    describe a page as tokens x heads x dims in fp16; the
- *                    order inside a tile is this library's choice). A tile is
- *                    P/16 sub-blocks of 16 tokens (16*D halves each); token
- *                    u = t % 16 of sub-block t / 16, dim d, sits at
+ *   K pool, V pool : fp16 storage of shape [N][Hkv][P / 16][16 * D]: N pages
+ *                    x Hkv KV heads x P / 16 sub-blocks of 16 tokens, each
+ *                    sub-block 16 * D halves; the P * D halves of a (page, KV
+ *                    head) tile are contiguous. A page holds P tokens of
+ *                    every KV head (hotelren §3.2 and pgsm §3.2 describe a
+ *                    page as tokens x heads x dims in fp16; the order inside a
+ *                    tile is this library's choice). The storage is NOT a
+ *                    [token][dim] array: token u = t % 16 of sub-block t / 16,
+ *                    dim d, sits at
  *                      K: ((d / 8) * 16 + u) * 8 + d % 8
  *                      V: (((d / 32) * 4 + u / 4) * 16 + d % 16) * 8
  *                         + ((d / 16) % 2) * 4 + u % 4
@@ -46,6 +48,8 @@
  *     a page id outside [0, N) or a length beyond the table width /
  *     max_context turns the affected output row into NaN, and an append whose
  *     slot is out of range is skipped. pkv_validate_tables checks host copies.
+ *   - lens[b] == 0 marks an idle batch slot on every decode path: its output
+ *     rows are zero, none of its pages is read and nothing is appended.
  *   - Supported: D in {64, 128}; P in {16, 32, 64, 128}; Hq / Hkv in
  *     {1, 2, 4, 8, 16}. Other values return PKV_ERR_UNSUPPORTED.
  */
@@ -74,7 +78,7 @@ typedef enum pkv_status {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* pkv_status_string(int status);
 
-/* ABI version of this header: 1. */
+/* ABI version of this header: 2. */
 int pkv_abi_version(void);
 
 /* ------------------------------------------------------------------------ */
@@ -157,6 +161,7 @@ int pkv_kv_append_chunk(const void* k_new, const void* v_new, void* k_pool, void
  * partition_tokens == 0 needs no workspace (*bytes = 0).
  * Errors: PKV_ERR_INVALID_ARG (negative sizes, partition_tokens not a
  * multiple of 16, B > 4096 with partition_tokens > 0, null `bytes`).
+ * The size holds for every Hkv dividing Hq and every device.
  */
 int pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context,
                                int32_t partition_tokens, size_t* bytes);
@@ -181,13 +186,15 @@ int pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_con
  *                  included). lens[b] == 0 writes a zero row.
  *   max_context  : host upper bound on every lens[b]; sizes the launch and
  *                  the workspace; must be <= max_pages * P.
- *   scale        : softmax scale, normally 1/sqrt(D).
+ *   scale        : softmax scale, normally 1/sqrt(D); positive and finite
+ *                  (else PKV_ERR_INVALID_ARG).
  *   partition_tokens: 0 = one workgroup per (sequence, KV head) over the whole
  *                  context, writing the output directly. Otherwise a positive
  *                  multiple of 16 (split mode, at most 4096 sequences): the
  *                  16-token blocks of all (KV head, sequence) contexts form
  *                  one list that is divided evenly among a fixed set of
- *                  workgroups, each taking at least partition_tokens tokens
+ *                  workgroups (two per compute unit of the current device),
+ *                  each taking at least partition_tokens tokens
  *                  (pieces may cross from one sequence into the next); a
  *                  log-sum-exp reduction kernel then merges the pieces of
  *                  every sequence. This balances batches of mixed lengths.
@@ -235,6 +242,20 @@ int pkv_decode_workspace_bytes_shared_prefix(int32_t B, int32_t Hq, int32_t D, i
                                              int32_t partition_tokens, int32_t prefix_tokens, size_t* bytes);
 
 /*
+ * pkv_decode_workspace_bytes_multi -- workspace size for the chunked calls
+ * (pkv_paged_decode_attention_multi, _multi_shared_prefix, _multi_k8,
+ * _window_multi, _window_multi_k8) with n_query queries per sequence: one
+ * private segment per sequence and 16-column query tile (chunks of pgsm
+ * §3.2's draft verification and chunked prefill), one prefix segment per 16
+ * chunk rows of a KV head when prefix_tokens > 0. n_query == 1 gives the
+ * single-query sizes. Errors: PKV_ERR_INVALID_ARG (as
+ * pkv_decode_workspace_bytes_shared_prefix; n_query < 1; more than 4096
+ * segments for every allowed Hkv).
+ */
+int pkv_decode_workspace_bytes_multi(int32_t B, int32_t n_query, int32_t Hq, int32_t D, int32_t max_context,
+                                     int32_t partition_tokens, int32_t prefix_tokens, size_t* bytes);
+
+/*
  * pkv_paged_decode_attention_shared_prefix -- decode for a batch whose
  * sequences all begin with the same prefix_tokens tokens held in the same
  * physical pages (a system prompt stored once and shared by every request:
@@ -249,9 +270,11 @@ int pkv_decode_workspace_bytes_shared_prefix(int32_t B, int32_t Hq, int32_t D, i
  * log-sum-exp reduction merges both.
  *
  *   prefix_tokens: multiple of P, 0 <= prefix_tokens <= max_context; entries
- *                  0 .. prefix_tokens / P - 1 of every block-table row must be
- *                  identical (they are read from row 0). lens[b] <
- *                  prefix_tokens makes row b NaN.
+ *                  0 .. prefix_tokens / P - 1 must be identical in every
+ *                  attended row (lens[b] > 0): they are read from the first
+ *                  such row, and an idle row's entries are never read
+ *                  (pkv_validate_tables with prefix_tokens checks this on host
+ *                  copies). 0 < lens[b] < prefix_tokens makes row b NaN.
  *   k_new, v_new : both NULL (no append) or both fp16 [B][Hkv][D]: append
  *                  each sequence's new token at lens[b] - 1 first, as in
  *                  pkv_append_paged_decode_attention. That position must lie
@@ -281,13 +304,16 @@ int pkv_paged_decode_attention_shared_prefix(void* out, const void* q, const voi
  *
  *   out          : fp16 [B][n_query][Hq][D] device, written.
  *   q            : fp16 [B][n_query][Hq][D] device, read.
- *   n_query      : >= 1, with n_query * (Hq / Hkv) <= 16 (the query rows of a
- *                  KV head fill one 16-column matrix-core tile; otherwise
- *                  PKV_ERR_UNSUPPORTED).
+ *   n_query      : >= 1. The n_query * (Hq / Hkv) query rows of a (sequence,
+ *                  KV head) are cut into 16-column matrix-core tiles of 16 /
+ *                  (Hq / Hkv) consecutive queries; each tile streams the
+ *                  sequence's tokens up to its last query. In split mode
+ *                  B * ceil(n_query * (Hq / Hkv) / 16) <= 4096.
  *   lens[b]      : tokens in the cache including the whole chunk; a row with
- *                  lens[b] < n_query (or beyond max_context / the table) is NaN.
- * Other arguments, the workspace (pkv_decode_workspace_bytes) and errors as
- * pkv_paged_decode_attention.
+ *                  0 < lens[b] < n_query (or beyond max_context / the table)
+ *                  is NaN; lens[b] == 0 gives zero rows.
+ *   workspace    : pkv_decode_workspace_bytes_multi bytes.
+ * Other arguments and errors as pkv_paged_decode_attention.
  */
 int pkv_paged_decode_attention_multi(void* out, const void* q, const void* k_pool, const void* v_pool,
                                      const int32_t* block_table, int32_t max_pages, const int32_t* lens, int32_t B,
@@ -350,12 +376,12 @@ int pkv_paged_decode_attention_window(void* out, const void* q, const void* k_ne
  *   q, out       : fp16 [B][n_query][Hq][D] device.
  *   ring_pages   : window + n_query - 1 <= (ring_pages - 1) * P + 1, so that
  *                  every token the chunk's windows reach is still in the ring.
- *   lens[b]      : tokens so far, the chunk included; lens[b] < n_query (or
- *                  negative, or above 2^31 - 65) makes the row NaN.
- *   workspace    : pkv_decode_workspace_bytes(B, Hq, D, window,
- *                  partition_tokens, ...) bytes when partition_tokens > 0.
- * n_query * (Hq / Hkv) <= 16 as in pkv_paged_decode_attention_multi. Errors
- * as pkv_paged_decode_attention_window and pkv_paged_decode_attention_multi.
+ *   lens[b]      : tokens so far, the chunk included; 0 < lens[b] < n_query
+ *                  (or negative, or above 2^31 - 65) makes the row NaN.
+ *   workspace    : pkv_decode_workspace_bytes_multi(B, n_query, Hq, D, window,
+ *                  partition_tokens, 0, ...) bytes when partition_tokens > 0.
+ * Query tiles as in pkv_paged_decode_attention_multi. Errors as
+ * pkv_paged_decode_attention_window and pkv_paged_decode_attention_multi.
  */
 int pkv_paged_decode_attention_window_multi(void* out, const void* q, const void* k_pool, const void* v_pool,
                                             const int32_t* ring_table, int32_t ring_pages, const int32_t* lens,
@@ -377,13 +403,11 @@ int pkv_paged_decode_attention_window_multi(void* out, const void* q, const void
  * needs no causal mask.
  *
  *   prefix_tokens: as in pkv_paged_decode_attention_shared_prefix; a row with
- *                  lens[b] < prefix_tokens + n_query (a chunk reaching into
- *                  the prefix) is NaN.
+ *                  0 < lens[b] < prefix_tokens + n_query (a chunk reaching
+ *                  into the prefix) is NaN.
  *   partition_tokens: > 0 (this path always splits).
- *   workspace    : at least pkv_decode_workspace_bytes_shared_prefix(
- *                  B * n_query, Hq, D, max_context, partition_tokens,
- *                  prefix_tokens) bytes (the chunk rows count as sequences
- *                  there; B * n_query <= 4096).
+ *   workspace    : at least pkv_decode_workspace_bytes_multi(B, n_query, Hq,
+ *                  D, max_context, partition_tokens, prefix_tokens) bytes.
  * Other arguments and errors as pkv_paged_decode_attention_multi.
  */
 int pkv_paged_decode_attention_multi_shared_prefix(void* out, const void* q, const void* k_pool, const void* v_pool,
@@ -468,10 +492,9 @@ int pkv_paged_decode_attention_k8(void* out, const void* q, const void* k_new, c
  * attention of verifying drafted tokens against a quantised cache. The
  * chunk's keys and values must be in the pools already
  * (pkv_kv_append_k8_chunk). prefix_tokens > 0 reads a shared prefix as
- * pkv_paged_decode_attention_multi_shared_prefix does (workspace from
- * pkv_decode_workspace_bytes_shared_prefix(B * n_query, ...)); 0 takes the
- * workspace of pkv_decode_workspace_bytes. Other arguments and errors as
- * pkv_paged_decode_attention_multi.
+ * pkv_paged_decode_attention_multi_shared_prefix does. Workspace:
+ * pkv_decode_workspace_bytes_multi(B, n_query, ..., prefix_tokens). Other
+ * arguments and errors as pkv_paged_decode_attention_multi.
  */
 int pkv_paged_decode_attention_multi_k8(void* out, const void* q, const void* k_pool8, const void* v_pool,
                                         const int32_t* block_table, int32_t max_pages, const int32_t* lens, int32_t B,
@@ -679,18 +702,33 @@ int pkv_copy_pages(void* pool, size_t page_bytes, int32_t N, const int32_t* src,
                    void* stream);
 
 /*
- * pkv_validate_tables -- check host copies of a block table and lengths.
- * Rules: lens[b] >= 0; ceil(lens[b] / P) <= max_pages; every entry a token
- * reaches is in [0, N); no page twice within a row; with exclusive_tail != 0
- * the page of each sequence's last token (where an append writes) appears in
- * no other row. Returns PKV_OK or PKV_ERR_INVALID_TABLE with the first
- * offending row and entry in *bad_row / *bad_entry (entry -1 for a length
- * problem) and the rule number (1..5, in the order above) in *rule.
- * Errors: PKV_ERR_INVALID_ARG for null pointers or bad sizes.
+ * pkv_validate_tables -- check host copies of a block table and lengths
+ * against what the decode entry points assume of device-resident contents.
+ * Rules, checked row by row (1-4), then 5, then 6 and 7:
+ *   1 lens[b] >= 0;
+ *   2 without a window, ceil(lens[b] / P) <= max_pages;
+ *   3 every entry a token reaches is in [0, N);
+ *   4 no page twice among a row's reached entries;
+ *   5 with exclusive_tail != 0, the page of each sequence's last token (where
+ *     an append writes) appears in no other row;
+ *   6 with prefix_tokens > 0, entries 0 .. prefix_tokens / P - 1 of every
+ *     attended row (lens[b] > 0) equal those of the first attended row (the
+ *     shared pages of dpshk §4.2, read once for the batch);
+ *   7 with prefix_tokens > 0, no attended row is shorter than the prefix.
+ * window > 0 reads the table as rings of max_pages pages (the sliding-window
+ * entry points): the entries a row reaches are (j % max_pages) for the
+ * logical pages j holding tokens max(0, lens[b] - window) .. lens[b] - 1
+ * (hotelren §3.2's fixed-capacity buffer), and rule 2 does not apply.
+ * Returns PKV_OK or PKV_ERR_INVALID_TABLE with the first offending row and
+ * entry in *bad_row / *bad_entry (entry -1 for a length problem) and the rule
+ * number in *rule.
+ * Errors: PKV_ERR_INVALID_ARG for null pointers, bad sizes, a prefix that is
+ * not whole pages, a window with a prefix, or a window that does not fit the
+ * ring (window > (max_pages - 1) * P + 1).
  */
 int pkv_validate_tables(const int32_t* block_table, const int32_t* lens, int32_t B, int32_t max_pages,
-                        int32_t P, int32_t N, int32_t exclusive_tail, int32_t* bad_row,
-                        int32_t* bad_entry, int32_t* rule);
+                        int32_t P, int32_t N, int32_t exclusive_tail, int32_t prefix_tokens, int32_t window,
+                        int32_t* bad_row, int32_t* bad_entry, int32_t* rule);
 
 #ifdef __cplusplus
 }

@@ -23,6 +23,8 @@ from .paged_decode import (  # noqa: F401
     kv_cache_bytes,
     pages_for_tokens,
     pool_bytes,
+    pool_dims,
+    pool_shape,
     token_slot,
     k_tile_offset,
     v_tile_offset,

@@ -202,16 +202,42 @@ class PageAllocatorModel:
         return copies
 
 
-def validate_tables(block_table, lens, page_size, num_pages, exclusive_tail=False):
+def _reached_entries(n, page_size, width, window):
+    """Block-table entries the tokens of a length-``n`` row reach, in token
+    order: logical pages ``0 .. ceil(n / P) - 1``; under a sliding window over a
+    ring of ``width`` pages, the ring entries ``j % width`` of the logical pages
+    holding tokens ``max(0, n - window) .. n - 1`` (hotelren §3.2's ring of
+    preallocated pages, expressed through the page table)."""
+    if n <= 0:
+        return []
+    if window:
+        lo = max(0, n - window)
+        return [j % width for j in range(lo // page_size, (n - 1) // page_size + 1)]
+    return list(range(pages_for_tokens(n, page_size)))
+
+
+def validate_tables(block_table, lens, page_size, num_pages, exclusive_tail=False, prefix_tokens=0, window=0):
     """Return a list of problems with a block table (empty when valid).
 
-    Checks, on host copies: lengths non-negative and within the row width;
-    every entry a token can reach is a page id in ``[0, num_pages)``; no page
-    twice in one row; with ``exclusive_tail`` the page holding each sequence's
-    last token (the one an append writes) appears in no other row.
+    Checks, on host copies: lengths non-negative and (without a window) within
+    the row width; every entry a token can reach is a page id in
+    ``[0, num_pages)``; no page twice among a row's reached entries; with
+    ``exclusive_tail`` the page holding each sequence's last token (the one an
+    append writes) appears in no other row; with ``prefix_tokens`` every
+    attended row (length > 0) is at least that long and holds the shared
+    prefix in the same pages as the first attended row (dpshk §4.2: one copy
+    of a shared prompt serves every request that starts with it). ``window``
+    reads the rows as rings (``_reached_entries``); it must fit the ring.
     """
     bt = np.asarray(block_table)
     lens = np.asarray(lens)
+    width = bt.shape[1]
+    if window and prefix_tokens:
+        raise ValueError("a window leaves no shared prefix")
+    if prefix_tokens % page_size:
+        raise ValueError("the shared prefix is whole pages")
+    if window and window > (width - 1) * page_size + 1:
+        raise ValueError("the window must fit in the ring")
     problems = []
     owners = {}
     tails = []
@@ -220,12 +246,12 @@ def validate_tables(block_table, lens, page_size, num_pages, exclusive_tail=Fals
         if n < 0:
             problems.append(("negative_length", b, -1))
             continue
-        used = pages_for_tokens(n, page_size)
-        if used > bt.shape[1]:
+        if not window and pages_for_tokens(n, page_size) > width:
             problems.append(("length_exceeds_table", b, -1))
             continue
         seen = set()
-        for j in range(used):
+        entries = _reached_entries(n, page_size, width, window)
+        for j in entries:
             p = int(bt[b, j])
             if not (0 <= p < num_pages):
                 problems.append(("page_out_of_range", b, j))
@@ -234,10 +260,26 @@ def validate_tables(block_table, lens, page_size, num_pages, exclusive_tail=Fals
                 problems.append(("duplicate_in_row", b, j))
             seen.add(p)
             owners.setdefault(p, set()).add(b)
-        if used:
-            tails.append((b, used - 1, int(bt[b, used - 1])))
+        if entries:
+            tails.append((b, entries[-1], int(bt[b, entries[-1]])))
     if exclusive_tail:
         for b, j, p in tails:
             if p in owners and len(owners[p]) > 1:
                 problems.append(("shared_tail_page", b, j))
+    if prefix_tokens:
+        first = None
+        for b in range(bt.shape[0]):
+            n = int(lens[b])
+            if n == 0:
+                continue
+            if n < prefix_tokens:
+                problems.append(("shorter_than_prefix", b, -1))
+                continue
+            if first is None:
+                first = b
+                continue
+            for j in range(prefix_tokens // page_size):
+                if int(bt[b, j]) != int(bt[first, j]):
+                    problems.append(("prefix_differs", b, j))
+                    break
     return problems

@@ -7,12 +7,13 @@ Data format (the pages give a page as "tokens x heads x dims" in fp16 without
 fixing the axis order -- hotelren §3.2, pgsm §3.2; the order below is this
 library's reading):
 
-* ``k_pool``, ``v_pool``: fp16 arrays of shape ``[N][Hkv][P][D]``; the ``P*D``
-  halves of one (page, kv head) tile are contiguous. Inside a tile, token ``t``
-  and dim ``d`` sit at the offset given by ``k_tile_offset`` / ``v_tile_offset``
-  (the tile is cut into 16-token sub-blocks; K keeps 8-dim chunks with the
-  token index minor, V keeps 4-token groups with the token index minor). The
-  pool's two last axes are therefore storage, not (token, dim).
+* ``k_pool``, ``v_pool``: fp16 arrays of storage shape ``[N][Hkv][P/16][16*D]``
+  (``pool_shape``): N pages x Hkv KV heads x P/16 sub-blocks of 16 tokens; the
+  ``P*D`` halves of one (page, kv head) tile are contiguous. Inside a tile,
+  token ``t`` and dim ``d`` sit at the offset given by ``k_tile_offset`` /
+  ``v_tile_offset`` (K keeps 8-dim chunks with the token index minor, V keeps
+  4-token groups with the token index minor), so a sub-block is storage, not a
+  (token, dim) array.
 * ``block_table``: int32 ``[B][max_pages]``; entry ``j`` of row ``b`` is the
   physical page holding logical tokens ``j*P .. j*P+P-1`` of sequence ``b``
   (pgsm §3.2 and §4.1: a page table maps each sequence's pages).
@@ -113,20 +114,34 @@ def _tile_offset(kind, t, d, page_size, head_dim):
     raise ValueError("kind must be 'k' or 'v'")
 
 
+def pool_shape(num_pages, kv_heads, page_size, head_dim):
+    """Storage shape of a K or V pool: ``[N][Hkv][P/16][16*D]``."""
+    _check_tile(page_size, head_dim)
+    return (num_pages, kv_heads, page_size // 16, 16 * head_dim)
+
+
+def pool_dims(pool):
+    """``(N, Hkv, P, D)`` of a pool of storage shape ``[N][Hkv][P/16][16*D]``."""
+    n, hkv, nsub, width = pool.shape
+    if width % 16:
+        raise ValueError("a pool's last axis holds 16 tokens x D halves")
+    return n, hkv, 16 * nsub, width // 16
+
+
 def _tiles(pool):
-    n, hkv, p, d = pool.shape
+    n, hkv, p, d = pool_dims(pool)
     return pool.reshape(n, hkv, p * d)
 
 
 def read_token(pool, page, kv_head, t, kind):
     """The ``D`` halves of token ``t`` (within ``page``) of one KV head."""
-    n, hkv, p, dim = pool.shape
+    n, hkv, p, dim = pool_dims(pool)
     return _tiles(pool)[page, kv_head, _tile_offset(kind, t, np.arange(dim), p, dim)]
 
 
 def write_token(pool, page, kv_head, t, vec, kind):
     """Store the ``D`` halves ``vec`` as token ``t`` of ``page`` (in place)."""
-    n, hkv, p, dim = pool.shape
+    n, hkv, p, dim = pool_dims(pool)
     _tiles(pool)[page, kv_head, _tile_offset(kind, t, np.arange(dim), p, dim)] = vec
 
 
@@ -138,7 +153,7 @@ def gather_sequence(pool, block_table_row, length, kv_head, page_size, kind):
     ``kind``, so the result is exactly the contiguous cache a non-paged
     implementation would hold.
     """
-    n, hkv, p, dim = pool.shape
+    n, hkv, p, dim = pool_dims(pool)
     if p != page_size:
         raise ValueError("pool page size differs from page_size")
     t = np.arange(length)
@@ -211,7 +226,7 @@ def decode_attention_window(q, k_pool, v_pool, ring_table, lens, window, scale, 
     Returns float64 ``[B][Hq][D]``; ``lens[b] == 0`` gives zeros.
     """
     b_count, hq, d = q.shape
-    n, hkv, p, dim = k_pool.shape
+    n, hkv, p, dim = pool_dims(k_pool)
     ring = np.asarray(ring_table, dtype=np.int64)
     r = ring.shape[1]
     if window <= 0 or window > (r - 1) * page_size + 1:
@@ -252,14 +267,16 @@ def decode_attention_multi(q, k_pool, v_pool, block_table, lens, scale, page_siz
     query is exactly a single-token decode step over its own prefix, so it is
     computed as one (``decode_attention`` with length ``lens[b] - k + i + 1``).
     Returns float64 ``[B][k][Hq][D]``; a row whose query would start before
-    token 0 (``lens[b] < k``) is all NaN.
+    token 0 (``0 < lens[b] < k``) is all NaN; ``lens[b] == 0`` (an idle batch
+    slot) gives zeros.
     """
     b_count, k, hq, d = q.shape
     out = np.zeros((b_count, k, hq, d), dtype=np.float64)
     lens64 = np.asarray(lens, dtype=np.int64)
-    short = lens64 < k                  # the chunk would reach before token 0: the whole row is invalid
+    # the chunk would reach before token 0: the whole row is invalid; length 0 is an idle slot (zeros)
+    short = (lens64 < k) & (lens64 != 0)
     for i in range(k):
-        li = np.where(short, 0, lens64 - k + i + 1)
+        li = np.where(lens64 < k, 0, lens64 - k + i + 1)
         out[:, i] = decode_attention(q[:, i], k_pool, v_pool, block_table, li, scale, page_size)
     out[short] = np.nan
     return out
@@ -273,16 +290,16 @@ def decode_attention_window_multi(q, k_pool, v_pool, ring_table, lens, window, s
     ``decode_attention_window``), each query being the window decode step of
     its own prefix. All of the chunk's tokens must still be in the ring:
     ``window + k - 1 <= (R - 1) * P + 1``. Returns float64 ``[B][k][Hq][D]``; a
-    row with ``lens[b] < k`` is all NaN."""
+    row with ``0 < lens[b] < k`` is all NaN; ``lens[b] == 0`` gives zeros."""
     b_count, k, hq, d = q.shape
     r = np.asarray(ring_table).shape[1]
     if window + k - 1 > (r - 1) * page_size + 1:
         raise ValueError("the chunk's windows must fit in the ring")
     out = np.zeros((b_count, k, hq, d), dtype=np.float64)
     lens64 = np.asarray(lens, dtype=np.int64)
-    short = lens64 < k
+    short = (lens64 < k) & (lens64 != 0)        # length 0: an idle slot (zeros)
     for i in range(k):
-        li = np.where(short, 0, lens64 - k + i + 1)
+        li = np.where(lens64 < k, 0, lens64 - k + i + 1)
         out[:, i] = decode_attention_window(q[:, i], k_pool, v_pool, ring_table, li, window, scale, page_size)
     out[short] = np.nan
     return out

@@ -107,8 +107,8 @@ def k8_read_token(pool8, page, kv_head, t, head_dim):
 def quantize_k_pool(k_pool):
     """int8 K pool of an fp16 K pool (every slot quantised, tile layout read
     through ``read_token``): ``[N][Hkv][P / 16][16 D + 64]`` bytes."""
-    from .paged_decode import read_token
-    n, hkv, p, dim = k_pool.shape
+    from .paged_decode import pool_dims, read_token
+    n, hkv, p, dim = pool_dims(k_pool)
     pool8 = np.zeros((n, hkv, p // 16, k8_subblock_bytes(dim)), np.uint8)
     for page in range(n):
         for h in range(hkv):
@@ -168,13 +168,14 @@ def decode_attention_multi_k8(q, pool8, v_pool, block_table, lens, scale, page_s
     keys in ``decode_attention_multi``), each query computed as the int8-key
     decode step over its own prefix (``decode_attention_k8`` with length
     ``lens[b] - k + i + 1``). Returns float64 ``[B][k][Hq][D]``; a row with
-    ``lens[b] < k`` is all NaN."""
+    ``0 < lens[b] < k`` is all NaN; ``lens[b] == 0`` gives zeros."""
     b_count, k, hq, d = q.shape
     out = np.zeros((b_count, k, hq, d), dtype=np.float64)
     lens64 = np.asarray(lens, dtype=np.int64)
-    short = lens64 < k                  # the chunk would reach before token 0: the whole row is invalid
+    # the chunk would reach before token 0: the whole row is invalid; length 0 is an idle slot (zeros)
+    short = (lens64 < k) & (lens64 != 0)
     for i in range(k):
-        li = np.where(short, 0, lens64 - k + i + 1)
+        li = np.where(lens64 < k, 0, lens64 - k + i + 1)
         out[:, i] = decode_attention_k8(q[:, i], pool8, v_pool, block_table, li, scale, page_size)
     out[short] = np.nan
     return out
@@ -186,9 +187,9 @@ def decode_attention_window_k8(q, pool8, v_pool, ring_table, lens, window, scale
     attends tokens ``max(0, lens[b] - window) .. lens[b] - 1``) over int8 keys:
     token ``t`` is read as ``code * scale`` from slot ``t % P`` of its ring page.
     Returns float64 ``[B][Hq][D]``; ``lens[b] == 0`` gives zeros."""
-    from .paged_decode import _tiles, v_tile_offset
+    from .paged_decode import _tiles, pool_dims, v_tile_offset
     b_count, hq, d = q.shape
-    n, hkv, p, dim = v_pool.shape
+    n, hkv, p, dim = pool_dims(v_pool)
     ring = np.asarray(ring_table, dtype=np.int64)
     r = ring.shape[1]
     if window <= 0 or window > (r - 1) * page_size + 1:
@@ -224,17 +225,17 @@ def decode_attention_window_k8(q, pool8, v_pool, ring_table, lens, window, scale
 def decode_attention_window_multi_k8(q, pool8, v_pool, ring_table, lens, window, scale, page_size):
     """``decode_attention_window_multi`` over int8 keys: query ``i`` of sequence
     ``b`` is the int8-key window decode step (``decode_attention_window_k8``)
-    of its own prefix ``lens[b] - k + i + 1``; a row with ``lens[b] < k`` is all
-    NaN; ``window + k - 1 <= (R - 1) * P + 1``."""
+    of its own prefix ``lens[b] - k + i + 1``; a row with ``0 < lens[b] < k``
+    is all NaN, ``lens[b] == 0`` gives zeros; ``window + k - 1 <= (R - 1) * P + 1``."""
     b_count, k, hq, d = q.shape
     r = np.asarray(ring_table).shape[1]
     if window + k - 1 > (r - 1) * page_size + 1:
         raise ValueError("the chunk's windows must fit in the ring")
     out = np.zeros((b_count, k, hq, d), dtype=np.float64)
     lens64 = np.asarray(lens, dtype=np.int64)
-    short = lens64 < k
+    short = (lens64 < k) & (lens64 != 0)        # length 0: an idle slot (zeros)
     for i in range(k):
-        li = np.where(short, 0, lens64 - k + i + 1)
+        li = np.where(lens64 < k, 0, lens64 - k + i + 1)
         out[:, i] = decode_attention_window_k8(q[:, i], pool8, v_pool, ring_table, li, window, scale, page_size)
     out[short] = np.nan
     return out

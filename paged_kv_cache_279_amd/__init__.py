@@ -21,6 +21,8 @@ from .binding import (  # noqa: F401
     block_table_patch,
     copy_pages,
     decode_workspace_bytes,
+    decode_workspace_bytes_multi,
+    empty_pool,
     k8_pool_bytes,
     kv_append,
     kv_append_chunk,
@@ -35,6 +37,7 @@ from .binding import (  # noqa: F401
     paged_decode_attention_window,
     paged_decode_attention_window_multi,
     paged_decode_attention_window_k8,
+    pool_shape,
     probe_stream_read,
     profile_next_partition_kernel,
     status_string,

@@ -73,6 +73,8 @@ _SIGNATURES = {
                                                          ctypes.c_size_t, _vp]),
     "pkv_decode_workspace_bytes_shared_prefix": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32,
                                                                  ctypes.POINTER(ctypes.c_size_t)]),
+    "pkv_decode_workspace_bytes_multi": (ctypes.c_int, [_i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                         ctypes.POINTER(ctypes.c_size_t)]),
     "pkv_paged_decode_attention_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
                                                                 _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
                                                                 _i32, _i32, _vp, ctypes.c_size_t, _vp]),
@@ -91,7 +93,7 @@ _SIGNATURES = {
     "pkv_alloc_cache_entries": (ctypes.c_int32, [_vp]),
     "pkv_alloc_prepare_append": (ctypes.c_int, [_vp, _i32, _ip, _ip, _ip, _ip, _ip, _ip, _i32]),
     "pkv_copy_pages": (ctypes.c_int, [_vp, ctypes.c_size_t, _i32, _ip, _ip, _i32, _vp]),
-    "pkv_validate_tables": (ctypes.c_int, [_ip, _ip, _i32, _i32, _i32, _i32, _i32, _ip, _ip, _ip]),
+    "pkv_validate_tables": (ctypes.c_int, [_ip, _ip, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _ip, _ip, _ip]),
 }
 
 _LIB = None
@@ -139,6 +141,32 @@ def _dev_ptr(t, dtype, name, ndim=None):
     if ndim is not None and t.dim() != ndim:
         raise ValueError("%s must have %d dims, got %d" % (name, ndim, t.dim()))
     return ctypes.c_void_p(t.data_ptr())
+
+
+def pool_shape(N, Hkv, P, D):
+    """Storage shape of an fp16 K or V pool: N pages x Hkv KV heads x P/16
+    sub-blocks of 16 tokens x 16*D halves. A sub-block is in the library's
+    matrix-core operand order (``include/pkv.h``), not [token][dim]: write
+    tokens with kv_append, never by indexing."""
+    if P % 16 or P <= 0 or D <= 0:
+        raise ValueError("P must be a positive multiple of 16")
+    return (N, Hkv, P // 16, 16 * D)
+
+
+def empty_pool(N, Hkv, P, D, device="cuda"):
+    """An uninitialised fp16 pool of ``pool_shape(N, Hkv, P, D)`` on ``device``."""
+    return torch.empty(pool_shape(N, Hkv, P, D), dtype=torch.float16, device=device)
+
+
+def _f16_pool(pool, name, head_dim):
+    """(N, Hkv, P, D) of an fp16 pool tensor of storage shape [N][Hkv][P/16][16*D],
+    D = ``head_dim`` (taken from the queries or new tokens)."""
+    if not isinstance(pool, torch.Tensor) or pool.dim() != 4 or pool.dtype != torch.float16 or \
+            pool.shape[3] != 16 * head_dim:
+        raise ValueError("%s must be an fp16 pool of storage shape [N][Hkv][P/16][16*D] (pool_shape), D = %d; got %s"
+                         % (name, head_dim, tuple(pool.shape) if isinstance(pool, torch.Tensor) else type(pool)))
+    N, Hkv, nsub, w = pool.shape
+    return N, Hkv, 16 * nsub, w // 16
 
 
 def _workspace_arg(workspace, ws_bytes, device):
@@ -219,7 +247,7 @@ def copy_pages(pool, src, dst, stream=None):
 
 def kv_append(k_new, v_new, k_pool, v_pool, block_table, pos, stream=None):
     """pkv_kv_append: write k_new/v_new [B][Hkv][D] at slot pos[b] of each sequence."""
-    N, Hkv, P, D = k_pool.shape
+    N, Hkv, P, D = _f16_pool(k_pool, "k_pool", int(k_new.shape[-1]))
     B, max_pages = block_table.shape
     if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D) or tuple(v_pool.shape) != tuple(k_pool.shape):
         raise ValueError("shape mismatch")
@@ -235,7 +263,7 @@ def kv_append(k_new, v_new, k_pool, v_pool, block_table, pos, stream=None):
 def kv_append_chunk(k_new, v_new, k_pool, v_pool, block_table, pos, stream=None):
     """pkv_kv_append_chunk: write k_new/v_new [B][n_tokens][Hkv][D]; token i of sequence b
     goes to position pos[b] + i."""
-    N, Hkv, P, D = k_pool.shape
+    N, Hkv, P, D = _f16_pool(k_pool, "k_pool", int(k_new.shape[-1]))
     B, max_pages = block_table.shape
     if k_new.dim() != 4 or tuple(k_new.shape) != tuple(v_new.shape) or k_new.shape[0] != B or \
             tuple(k_new.shape[2:]) != (Hkv, D) or tuple(v_pool.shape) != tuple(k_pool.shape):
@@ -257,7 +285,7 @@ def paged_decode_attention_multi(q, k_pool, v_pool, block_table, lens, max_conte
     prefix_tokens > 0 the batch shares its first prefix_tokens tokens
     (pkv_paged_decode_attention_multi_shared_prefix)."""
     B, nq, Hq, D = q.shape
-    N, Hkv, P, Dk = k_pool.shape
+    N, Hkv, P, Dk = _f16_pool(k_pool, "k_pool", int(q.shape[-1]))
     _, max_pages = block_table.shape
     if Dk != D or tuple(v_pool.shape) != tuple(k_pool.shape) or block_table.shape[0] != B or tuple(lens.shape) != (B,):
         raise ValueError("shape mismatch")
@@ -265,11 +293,7 @@ def paged_decode_attention_multi(q, k_pool, v_pool, block_table, lens, max_conte
         out = torch.empty((B, nq, Hq, D), dtype=torch.float16, device=q.device)
     if tuple(out.shape) != (B, nq, Hq, D):
         raise ValueError("out must be [B][n_query][Hq][D]")
-    if prefix_tokens:
-        # the chunk rows count as sequences in the workspace query
-        ws_bytes = decode_workspace_bytes(B * nq, Hq, D, max_context, partition_tokens, prefix_tokens)
-    else:
-        ws_bytes = decode_workspace_bytes(B, Hq, D, max_context, partition_tokens)
+    ws_bytes = decode_workspace_bytes_multi(B, nq, Hq, D, max_context, partition_tokens, prefix_tokens)
     ws_ptr, ws_len = _workspace_arg(workspace, ws_bytes, q.device)
     ptrs = (_dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"),
             _dev_ptr(k_pool, torch.float16, "k_pool"), _dev_ptr(v_pool, torch.float16, "v_pool"),
@@ -291,7 +315,7 @@ def paged_decode_attention_window(q, k_pool, v_pool, ring_table, lens, window, s
     logical page j in ``ring_table[b][j % ring_pages]``; with k_new / v_new the new token is
     appended at lens[b] - 1 in the same launch. Returns ``out`` [B][Hq][D]."""
     B, Hq, D = q.shape
-    N, Hkv, P, Dk = k_pool.shape
+    N, Hkv, P, Dk = _f16_pool(k_pool, "k_pool", int(q.shape[-1]))
     _, ring_pages = ring_table.shape
     if Dk != D or tuple(v_pool.shape) != tuple(k_pool.shape) or ring_table.shape[0] != B or tuple(lens.shape) != (B,):
         raise ValueError("shape mismatch")
@@ -323,9 +347,9 @@ def paged_decode_attention_window_multi(q, k_pool, v_pool, ring_table, lens, win
     queries q [B][n_query][Hq][D], each attending the window ending at itself through the ring."""
     k8 = k_pool.dtype == torch.uint8
     if k8:
-        N, Hkv, P, D = _k8_shape(k_pool, v_pool)
+        N, Hkv, P, D = _k8_shape(k_pool, v_pool, int(q.shape[-1]))
     else:
-        N, Hkv, P, D = k_pool.shape
+        N, Hkv, P, D = _f16_pool(k_pool, "k_pool", int(q.shape[-1]))
         if tuple(v_pool.shape) != tuple(k_pool.shape):
             raise ValueError("shape mismatch")
     B, nq, Hq, Dq = q.shape
@@ -336,8 +360,8 @@ def paged_decode_attention_window_multi(q, k_pool, v_pool, ring_table, lens, win
         out = torch.empty((B, nq, Hq, D), dtype=torch.float16, device=q.device)
     if tuple(out.shape) != (B, nq, Hq, D):
         raise ValueError("out must be [B][n_query][Hq][D]")
-    ws_ptr, ws_len = _workspace_arg(workspace, decode_workspace_bytes(B, Hq, D, int(window), partition_tokens),
-                                    q.device)
+    ws_ptr, ws_len = _workspace_arg(workspace, decode_workspace_bytes_multi(B, nq, Hq, D, int(window),
+                                                                            partition_tokens), q.device)
     fn = lib().pkv_paged_decode_attention_window_multi_k8 if k8 else lib().pkv_paged_decode_attention_window_multi
     rc = fn(_dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"),
             _dev_ptr(k_pool, torch.uint8 if k8 else torch.float16, "k_pool"), _dev_ptr(v_pool, torch.float16, "v_pool"),
@@ -355,16 +379,16 @@ def k8_pool_bytes(N, Hkv, P, D):
     return out.value
 
 
-def _k8_shape(k_pool8, v_pool):
-    N, Hkv, P, D = v_pool.shape
+def _k8_shape(k_pool8, v_pool, head_dim):
+    N, Hkv, P, D = _f16_pool(v_pool, "v_pool", head_dim)
     if k_pool8.dtype != torch.uint8 or tuple(k_pool8.shape) != (N, Hkv, P // 16, 16 * D + 64):
-        raise ValueError("k_pool8 must be uint8 [N][Hkv][P/16][16 D + 64] matching v_pool [N][Hkv][P][D]")
+        raise ValueError("k_pool8 must be uint8 [N][Hkv][P/16][16 D + 64] matching v_pool [N][Hkv][P/16][16 D]")
     return N, Hkv, P, D
 
 
 def kv_append_k8(k_new, v_new, k_pool8, v_pool, block_table, pos, stream=None):
     """pkv_kv_append_k8: quantise k_new into the int8-key pool, write v_new into the fp16 V pool."""
-    N, Hkv, P, D = _k8_shape(k_pool8, v_pool)
+    N, Hkv, P, D = _k8_shape(k_pool8, v_pool, int(k_new.shape[-1]))
     B, max_pages = block_table.shape
     if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D) or tuple(pos.shape) != (B,):
         raise ValueError("shape mismatch")
@@ -378,7 +402,7 @@ def kv_append_k8(k_new, v_new, k_pool8, v_pool, block_table, pos, stream=None):
 def kv_append_k8_chunk(k_new, v_new, k_pool8, v_pool, block_table, pos, stream=None):
     """pkv_kv_append_k8_chunk: k_new/v_new [B][n_tokens][Hkv][D]; token i of sequence b goes to
     position pos[b] + i, its key quantised into the int8-key pool."""
-    N, Hkv, P, D = _k8_shape(k_pool8, v_pool)
+    N, Hkv, P, D = _k8_shape(k_pool8, v_pool, int(k_new.shape[-1]))
     B, max_pages = block_table.shape
     if k_new.dim() != 4 or tuple(k_new.shape) != tuple(v_new.shape) or k_new.shape[0] != B or \
             tuple(k_new.shape[2:]) != (Hkv, D) or tuple(pos.shape) != (B,):
@@ -396,7 +420,7 @@ def paged_decode_attention_multi_k8(q, k_pool8, v_pool, block_table, lens, max_c
                                     prefix_tokens=0, out=None, workspace=None, stream=None):
     """pkv_paged_decode_attention_multi_k8: chunks of queries q [B][n_query][Hq][D] over int8
     keys and fp16 values; returns ``out`` [B][n_query][Hq][D]."""
-    N, Hkv, P, D = _k8_shape(k_pool8, v_pool)
+    N, Hkv, P, D = _k8_shape(k_pool8, v_pool, int(q.shape[-1]))
     B, nq, Hq, Dq = q.shape
     _, max_pages = block_table.shape
     if Dq != D or block_table.shape[0] != B or tuple(lens.shape) != (B,):
@@ -405,10 +429,7 @@ def paged_decode_attention_multi_k8(q, k_pool8, v_pool, block_table, lens, max_c
         out = torch.empty((B, nq, Hq, D), dtype=torch.float16, device=q.device)
     if tuple(out.shape) != (B, nq, Hq, D):
         raise ValueError("out must be [B][n_query][Hq][D]")
-    if prefix_tokens:
-        ws_bytes = decode_workspace_bytes(B * nq, Hq, D, max_context, partition_tokens, prefix_tokens)
-    else:
-        ws_bytes = decode_workspace_bytes(B, Hq, D, max_context, partition_tokens)
+    ws_bytes = decode_workspace_bytes_multi(B, nq, Hq, D, max_context, partition_tokens, prefix_tokens)
     ws_ptr, ws_len = _workspace_arg(workspace, ws_bytes, q.device)
     rc = lib().pkv_paged_decode_attention_multi_k8(
         _dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"), _dev_ptr(k_pool8, torch.uint8, "k_pool8"),
@@ -423,7 +444,7 @@ def paged_decode_attention_window_k8(q, k_pool8, v_pool, ring_table, lens, windo
                                      k_new=None, v_new=None, out=None, workspace=None, stream=None):
     """pkv_paged_decode_attention_window_k8: the sliding-window call over an int8-key pool
     (logical page j in ring_table[b][j % ring_pages]); optional fused quantising append."""
-    N, Hkv, P, D = _k8_shape(k_pool8, v_pool)
+    N, Hkv, P, D = _k8_shape(k_pool8, v_pool, int(q.shape[-1]))
     B, Hq, Dq = q.shape
     _, ring_pages = ring_table.shape
     if Dq != D or ring_table.shape[0] != B or tuple(lens.shape) != (B,):
@@ -453,7 +474,7 @@ def paged_decode_attention_k8(q, k_pool8, v_pool, block_table, lens, max_context
                               prefix_tokens=0, k_new=None, v_new=None, out=None, workspace=None, stream=None):
     """pkv_paged_decode_attention_k8: decode over int8 keys and fp16 values, with the
     new token appended (and its key quantised) first when k_new/v_new are given; returns ``out``."""
-    N, Hkv, P, D = _k8_shape(k_pool8, v_pool)
+    N, Hkv, P, D = _k8_shape(k_pool8, v_pool, int(q.shape[-1]))
     out, (_, _, _, _, B, Hq, max_pages), ws_ptr, ws_len = _decode_args(
         out, q, v_pool, v_pool, block_table, lens, max_context, partition_tokens, workspace, prefix_tokens)
     if (k_new is None) != (v_new is None):
@@ -486,9 +507,17 @@ def decode_workspace_bytes(B, Hq, D, max_context, partition_tokens, prefix_token
     return out.value
 
 
+def decode_workspace_bytes_multi(B, n_query, Hq, D, max_context, partition_tokens, prefix_tokens=0):
+    """pkv_decode_workspace_bytes_multi: workspace of the chunked calls (n_query queries per sequence)."""
+    out = ctypes.c_size_t(0)
+    _check(lib().pkv_decode_workspace_bytes_multi(B, n_query, Hq, D, max_context, partition_tokens, prefix_tokens,
+                                                  ctypes.byref(out)), "pkv_decode_workspace_bytes_multi")
+    return out.value
+
+
 def _decode_args(out, q, k_pool, v_pool, block_table, lens, max_context, partition_tokens, workspace,
                  prefix_tokens=0):
-    N, Hkv, P, D = k_pool.shape
+    N, Hkv, P, D = _f16_pool(k_pool, "k_pool", int(q.shape[-1]))
     B, Hq, Dq = q.shape
     _, max_pages = block_table.shape
     if Dq != D or tuple(v_pool.shape) != tuple(k_pool.shape) or block_table.shape[0] != B or tuple(lens.shape) != (B,):
@@ -683,12 +712,12 @@ class PageAllocator:
         return c.value
 
 
-def validate_tables(block_table, lens, page_size, num_pages, exclusive_tail=False):
+def validate_tables(block_table, lens, page_size, num_pages, exclusive_tail=False, prefix_tokens=0, window=0):
     """pkv_validate_tables on host copies; returns ``(status, row, entry, rule)``."""
     bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
     ln, lp = _host_i32(lens, "lens")
     row, entry, rule = ctypes.c_int32(-1), ctypes.c_int32(-1), ctypes.c_int32(0)
     rc = lib().pkv_validate_tables(bt.ctypes.data_as(_ip), lp, bt.shape[0], bt.shape[1], page_size, num_pages,
-                                   1 if exclusive_tail else 0, ctypes.byref(row), ctypes.byref(entry),
-                                   ctypes.byref(rule))
+                                   1 if exclusive_tail else 0, int(prefix_tokens), int(window), ctypes.byref(row),
+                                   ctypes.byref(entry), ctypes.byref(rule))
     return rc, row.value, entry.value, rule.value

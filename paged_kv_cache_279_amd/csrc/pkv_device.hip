@@ -39,6 +39,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <atomic>
 #include <vector>
 
 #include "pkv.h"
@@ -52,39 +53,19 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t v4u32_t __attribute__((ext_vector_type(4)));
 
-// Tuning knobs (compile-time; the defaults are the measured best on MI355X).
-#ifndef PKV_PREFETCH_DEPTH
-#define PKV_PREFETCH_DEPTH 2
-#endif
-#ifndef PKV_KV_LOAD_POLICY
-#define PKV_KV_LOAD_POLICY 2
-#endif
-// Order of the (partition, sequence) work items in the grid: 0 = partition
-// major (every sequence's first partition first), 1 = sequence major.
-// Private workgroups of the balanced split schedule (2 per CU on 256 CUs).
-#ifndef PKV_PRIO_BALANCE
-#define PKV_PRIO_BALANCE 1
-#endif
-constexpr bool kPrioBalance = PKV_PRIO_BALANCE != 0;   // level workgroups sharing a CU by issue priority
-#ifndef PKV_FLAT_WORKGROUPS
-#define PKV_FLAT_WORKGROUPS 512
-#endif
-
 constexpr int kWave = 64;
-#ifndef PKV_WAVES
-#define PKV_WAVES 4
-#endif
-constexpr int kWaves = PKV_WAVES;          // waves per workgroup
+constexpr int kWaves = 4;                  // waves per workgroup
 constexpr int kThreads = kWave * kWaves;
 constexpr int kBlk = 16;                   // tokens per block (= one sub-block)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr size_t kWsAlign = 256;
 constexpr int32_t kMaxPartitions = 1024;   // partial slots per (sequence, head) (reduce kernel LDS)
 constexpr uint32_t kWaveMergeRows = 4096;  // output rows from which the one-wave-per-row merge runs
-#ifndef PKV_MAX_FLAT_BATCH
-#define PKV_MAX_FLAT_BATCH 4096
-#endif
-constexpr int32_t kMaxFlatBatch = PKV_MAX_FLAT_BATCH;    // sequences per split call (LDS prefix sums)
+// work segments per split call (one per sequence, or per sequence and 16-column
+// query tile for chunks of queries): their block prefix sums sit in LDS
+constexpr int32_t kMaxSegments = 4096;
+// Split-mode workgroups per compute unit: two stream side by side (<= 256 VGPRs each)
+constexpr int kWgsPerCu = 2;
 // sliding window: longest sequence (its token positions plus a block stay in int32)
 constexpr int32_t kWindowMaxLen = 0x7fffffff - 64;
 // Online-softmax rescaling is deferred until a head's block maximum exceeds
@@ -92,16 +73,14 @@ constexpr int32_t kWindowMaxLen = 0x7fffffff - 64;
 // then stay below 2^8 and fp16/fp32 ranges are never approached.
 constexpr float kRescaleSlack = 8.0f;
 // Blocks each wave keeps in flight ahead of the one it is consuming.
-constexpr int kDepth = PKV_PREFETCH_DEPTH;
+constexpr int kDepth = 2;
 // Word 3 of a raw gfx9 buffer descriptor (32-bit data format, no swizzle).
 constexpr int32_t kBufferFlags = 0x00020000;
 // Cache policy of the K/V loads: 2 = non-temporal (private pages are streamed
-// once per step); shared-prefix pages use the default policy so they stay in L2.
-constexpr int32_t kKvLoadPolicy = PKV_KV_LOAD_POLICY;
-#ifndef PKV_PREFIX_LOAD_POLICY
-#define PKV_PREFIX_LOAD_POLICY 0
-#endif
-constexpr int32_t kPrefixLoadPolicy = PKV_PREFIX_LOAD_POLICY;
+// once per step); shared-prefix pages use the default policy (0) so that they
+// stay in L2 for the other query tiles that read them.
+constexpr int32_t kKvLoadPolicy = 2;
+constexpr int32_t kPrefixLoadPolicy = 0;
 
 struct DecodeParams {
   half_t* out;               // [B][Hq][D]
@@ -121,15 +100,17 @@ struct DecodeParams {
   int32_t p_shift;           // log2(P)
   int32_t max_context;
   int32_t prefix_tokens;     // shared leading tokens (0 = none), multiple of P
-  int32_t min_len;           // split mode: shorter sequences are invalid (NaN rows)
+  int32_t min_len;           // a positive length below this is invalid (NaN rows)
   int32_t nq;                // queries per sequence (1 = decode; > 1: the chunk of the last nq tokens)
+  int32_t n_qt;              // 16-column query tiles per (sequence, KV head): ceil(nq * G / 16) for chunks, else 1
+  int32_t qpt;               // queries per query tile (16 / G for chunks)
   int32_t ring;              // sliding window: pages per sequence in its ring (logical page j -> entry j % ring)
   int32_t window;            // sliding window: tokens attended (the last `window`)
   int32_t n_tiles;           // 16-row query tiles per KV head that read the prefix (0 = none)
   int32_t n_flat_wgs;        // workgroups of the balanced split schedule
   int32_t min_piece;         // minimum blocks per piece
   int32_t* flat_hdr;         // [3]: private blocks per KV head, private and prefix units per workgroup
-  int32_t* flat_cum;         // [B]: inclusive prefix sums of private blocks
+  int32_t* flat_cum;         // [B * n_qt]: inclusive prefix sums of private blocks per segment
   float* flat_m;             // [slots][16]: piece partials, base-2 scaled score max
   float* flat_l;             // [slots][16]: softmax denominators
   float* flat_o;             // [slots][16][D]: unnormalised outputs
@@ -137,6 +118,16 @@ struct DecodeParams {
 };
 
 __device__ __forceinline__ float kNegInf() { return -__builtin_huge_valf(); }
+
+// What a sequence of length L gives: 0 = an idle batch slot (L == 0: zero
+// rows, no page read, nothing appended), 1 = attended, -1 = invalid (NaN rows:
+// negative, beyond max_context or the table, or shorter than the call needs --
+// the shared prefix, plus the appended token or the chunk of queries).
+__device__ __forceinline__ int len_state(const DecodeParams& p, int32_t L) {
+  if (L == 0) return 0;
+  const bool bad = L < 0 || L < p.min_len || L > p.max_context || (p.ring == 0 && L > (p.max_pages << p.p_shift));
+  return bad ? -1 : 1;
+}
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -707,8 +698,12 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     if constexpr (kMQ) mref = mref == kNegInf() ? 0.f : mref;   // all its scores are -inf then: p = 0
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(s[i], c, -mref));
-    st.l_part += (pr[0] + pr[1]) + (pr[2] + pr[3]);
+    // The P.V product takes the weights rounded to fp16; the denominator sums
+    // exactly those rounded weights, so that numerator and denominator weigh
+    // every token alike (with fp32 weights in the denominator a dominant token
+    // whose weight is not exactly 1 would bias the output by ~2^-11 |v|).
     const half4_t pa = {(half_t)pr[0], (half_t)pr[1], (half_t)pr[2], (half_t)pr[3]};
+    st.l_part += ((float)pa[0] + (float)pa[1]) + ((float)pa[2] + (float)pa[3]);
 #pragma unroll
     for (int j = 0; j < KL; ++j) {
       st.o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, lo4(vr[j]), st.o[2 * j], 0, 0, 0);
@@ -762,7 +757,7 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     for (int r = 0; r <= kDepth; ++r) {
       const int32_t blk = first + k * stride;
       if (blk >= nblocks) return;
-      if (kPrioBalance && quota > 0) set_priority(after + nblocks - blk, quota);
+      if (quota > 0) set_priority(after + nblocks - blk, quota);
       load_block(k + kDepth, kr[(r + kDepth) % (kDepth + 1)], vr[(r + kDepth) % (kDepth + 1)]);
       __builtin_amdgcn_sched_barrier(0);
       consume(blk, kr[r], vr[r]);
@@ -789,17 +784,18 @@ struct WgShared {
 };
 
 // LDS of the partition kernel: the merge area of one range (16 columns for a
-// prefix tile, G for a private segment; one at a time) and the per-sequence
-// block prefix sums of the split schedule.
+// prefix tile or a tile of a chunk of queries, G for a private segment; one at
+// a time) and the per-segment block prefix sums of the split schedule.
 template <int D, int G>
 struct KernelShared {
   union {
     WgShared<D, 16> prefix;
     WgShared<D, G> priv;
   } tile;
-  int32_t cum[kMaxFlatBatch];    // inclusive prefix sums of private blocks per sequence
-  int32_t len[kMaxFlatBatch];    // lens
+  int32_t cum[kMaxSegments];     // inclusive prefix sums of private blocks per segment
+  int32_t len[kMaxSegments];     // the length of each segment's sequence
   int32_t wsum[kWaves];
+  int32_t wmin[kWaves];
 };
 
 // The 4 waves of a workgroup stream tokens [start, end) of KV head kvh through
@@ -808,14 +804,15 @@ struct KernelShared {
 // waves merge through LDS and every (column c, dim d) goes to
 // emit(c, d, M, Ls, O): the column's base-2 score max, softmax denominator
 // and unnormalised output. Callers must be workgroup-uniform.
-// kMQ: column c is query c / g of the chunk (g = mq_g heads per query); query
-// i may see tokens up to mq_last0 + i.
+// kMQ: column c is query c / g of a tile of mq_n queries of a chunk (g = mq_g
+// heads per query); query i of the tile sits at position mq_last0 + i and may
+// see tokens up to there (with a sliding window, the window ending there).
 template <int D, int NC, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ = false, class RowFn,
           class EmitFn>
 __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>& sh, const int32_t* bt_row,
                                           int32_t kvh, int32_t start, int32_t end, int32_t quota, int32_t after,
                                           const NewToken& nt, RowFn qrow, EmitFn emit, int lane, int wave,
-                                          int32_t mq_last0 = 0, int32_t mq_g = 1, int32_t lo = 0) {
+                                          int32_t mq_last0 = 0, int32_t mq_g = 1, int32_t lo = 0, int32_t mq_n = 0) {
   constexpr int KL = D / 32;
   constexpr int NT = D / 16;
   const int col = lane & 15;
@@ -836,10 +833,10 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
   if constexpr (kMQ) {
     // query qi sits at mq_last0 + qi; with a window it sees window tokens ending there
     const int32_t qi = col / mq_g;
-    clim = qi < p.nq ? mq_last0 + qi : 0x7fffffff;
+    clim = qi < mq_n ? mq_last0 + qi : 0x7fffffff;
     if (p.window > 0) {
-      clo = qi < p.nq ? max(0, mq_last0 + qi + 1 - p.window) : 0;
-      clo_max = max(0, mq_last0 + p.nq - p.window);
+      clo = qi < mq_n ? max(0, mq_last0 + qi + 1 - p.window) : 0;
+      clo_max = max(0, mq_last0 + mq_n - p.window);
     }
   }
   stream_blocks<D, kPolicy, kAppend, kK8, kMQ>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, nt,
@@ -884,15 +881,18 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
 
 // Unsplit (partition_tokens == 0): workgroup (KV head, sequence) over the
 // whole context; columns are the G heads of the group (zero-padded to 16);
-// fp16 output.
+// fp16 output. A chunk of queries: workgroup (KV head, query tile,
+// sequence), the tile's queries and heads as columns.
 //
 // Split: a balanced schedule per KV head over two work lists,
 //   prefix:  [tile 0: PB blocks] ... [tile NT-1: PB blocks]
-//   private: [seq 0 private blocks] ... [seq B-1 private blocks]
+//   private: [segment 0 blocks] ... [segment S-1 blocks]
 // A prefix segment is the PB = prefix_tokens / 16 shared blocks read for one
 // tile of 16 query rows (row r = sequence r / G, head kvh * G + r % G: a full
 // 16-column MFMA tile, the shared pages read once for all 16); a private
-// segment is a sequence's own blocks after the prefix, read for its G heads.
+// segment is a sequence's own blocks after the prefix, read for its G heads
+// (for a chunk of queries, segment b * n_qt + t is sequence b's blocks up to
+// the last query of its query tile t, read for that tile's columns).
 // Workgroup w serves KV head w % Hkv (under round-robin dispatch an XCD keeps
 // to the same heads, so their shared pages stay in its L2); its index j =
 // w / Hkv among the head's Wk = W / Hkv workgroups selects units
@@ -900,7 +900,7 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
 // list, Qx = max(ceil(list length / Wk), minimum piece). Every workgroup thus
 // gets the same mix of L2-resident prefix reads and HBM-bound private reads;
 // pieces cross segment boundaries. The piece of (segment s, workgroup j)
-// writes slot kvh * (NT + B + 2 Wk) + s + j, private segments numbered after
+// writes slot kvh * (NT + S + 2 Wk) + s + j, private segments numbered after
 // NT + Wk: walking a list in order increases s or j (or both) by one each
 // step, so the slots are distinct; each slot holds 16 columns.
 template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ>
@@ -912,22 +912,28 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
   __shared__ KernelShared<D, G> smem;
 
   if constexpr (!SPLIT && MQ) {
-    // a chunk of nq queries per sequence: columns (query i, head g) = i * G + g
+    // query tile t of a chunk of nq queries: columns (query q0 + i, head g) = i * G + g
     const int32_t kvh = blockIdx.x % p.Hkv;
-    const int32_t b = blockIdx.x / p.Hkv;
+    const int32_t bt_i = blockIdx.x / p.Hkv;
+    const int32_t t = bt_i % p.n_qt;
+    const int32_t b = bt_i / p.n_qt;
     const int32_t L = p.lens[b];
-    const bool bad_len = L < p.nq || L > p.max_context || (p.ring == 0 && L > (p.max_pages << p.p_shift));
-    const int32_t ncol = p.nq * G;
-    auto row = [&](int c) -> int64_t { return ((int64_t)b * p.nq + c / G) * p.Hq + (int64_t)kvh * G + c % G; };
-    if (bad_len) {
-      for (int i = threadIdx.x; i < ncol * D; i += kThreads) p.out[row(i / D) * D + i % D] = (half_t)__builtin_nanf("");
+    const int ls = len_state(p, L);
+    const int32_t q0 = t * p.qpt;
+    const int32_t nqt = min(p.nq - q0, p.qpt);
+    const int32_t ncol = nqt * G;
+    auto row = [&](int c) -> int64_t { return ((int64_t)b * p.nq + q0 + c / G) * p.Hq + (int64_t)kvh * G + c % G; };
+    if (ls != 1) {
+      const half_t fill = ls == 0 ? (half_t)0.0f : (half_t)__builtin_nanf("");
+      for (int i = threadIdx.x; i < ncol * D; i += kThreads) p.out[row(i / D) * D + i % D] = fill;
       return;
     }
     const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
+    const int32_t pos0 = L - p.nq + q0;            // position of the tile's first query
     // sliding window: from the block holding the first query's window start
-    const int32_t lo = p.window > 0 ? max(0, L - p.nq + 1 - p.window) : 0;
+    const int32_t lo = p.window > 0 ? max(0, pos0 + 1 - p.window) : 0;
     run_range<D, 16, kKvLoadPolicy, false, K8, true>(
-        p, smem.tile.prefix, bt_row, kvh, lo & ~(kBlk - 1), L, 0, 0, NewToken{-1, 0, nullptr, nullptr},
+        p, smem.tile.prefix, bt_row, kvh, lo & ~(kBlk - 1), pos0 + nqt, 0, 0, NewToken{-1, 0, nullptr, nullptr},
         [&](int c) -> int64_t { return c < ncol ? row(c) : -1; },
         [&](int c, int d, float, float Ls, float O) {
           if (c < ncol) {
@@ -935,31 +941,30 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
             p.out[row(c) * D + d] = (half_t)(Ls != Ls ? __builtin_nanf("") : r);
           }
         },
-        lane, wave, L - p.nq, G, lo);
+        lane, wave, pos0, G, lo, nqt);
   } else if constexpr (!SPLIT) {
     WgShared<D, G>& sh = smem.tile.priv;
     const int32_t kvh = blockIdx.x % p.Hkv;
     const int32_t b = blockIdx.x / p.Hkv;
     const int32_t L = p.lens[b];
-    const bool bad_len = L < 0 || L > p.max_context || (p.ring == 0 && L > (p.max_pages << p.p_shift));
-    const int32_t Lc = bad_len ? 0 : L;
+    const int ls = len_state(p, L);
     const int64_t head_row0 = (int64_t)b * p.Hq + (int64_t)kvh * G;
-    if (Lc == 0) {
-      const half_t fill = bad_len ? (half_t)__builtin_nanf("") : (half_t)0.0f;
+    if (ls != 1) {
+      const half_t fill = ls == 0 ? (half_t)0.0f : (half_t)__builtin_nanf("");
       for (int i = threadIdx.x; i < G * D; i += kThreads) p.out[head_row0 * D + i] = fill;
       return;
     }
     const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
     // sliding window: attend [lo, L), streamed from the 16-aligned block below lo
-    const int32_t lo = p.window > 0 ? max(0, Lc - p.window) : 0;
+    const int32_t lo = p.window > 0 ? max(0, L - p.window) : 0;
     const int32_t s0 = lo & ~(kBlk - 1);
     NewToken nt{-1, 0, nullptr, nullptr};
     if constexpr (FUSED) {
       const int64_t src = ((int64_t)b * p.Hkv + kvh) * D;
-      nt = NewToken{(Lc - 1 - s0) >> 4, (Lc - 1) & 15, p.k_new + src, p.v_new + src};
+      nt = NewToken{(L - 1 - s0) >> 4, (L - 1) & 15, p.k_new + src, p.v_new + src};
     }
     run_range<D, G, kKvLoadPolicy, FUSED, K8>(
-        p, sh, bt_row, kvh, s0, Lc, 0, 0, nt, [&](int c) -> int64_t { return head_row0 + c; },
+        p, sh, bt_row, kvh, s0, L, 0, 0, nt, [&](int c) -> int64_t { return head_row0 + c; },
         [&](int c, int d, float, float Ls, float O) {
           const float r = Ls > 0.f ? O / Ls : (Ls == 0.f ? 0.f : __builtin_nanf(""));
           p.out[(head_row0 + c) * D + d] = (half_t)(Ls != Ls ? __builtin_nanf("") : r);
@@ -968,29 +973,39 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
   } else {
     int32_t* sm_cum = smem.cum;
     int32_t* sm_len = smem.len;
-    int32_t* sm_wsum = smem.wsum;
     const int32_t wg = blockIdx.x;
-    const int32_t per = (p.B + kThreads - 1) / kThreads;
-    const int32_t b0 = threadIdx.x * per;
-    // first token of a sequence's window (that of its first query), and the
-    // first streamed token: after the shared prefix, or the 16-aligned block
-    // holding the window start
-    auto window_lo = [&](int32_t L) -> int32_t { return p.window > 0 ? max(0, L - p.nq + 1 - p.window) : 0; };
-    auto first_token = [&](int32_t L) -> int32_t {
-      return p.window > 0 ? window_lo(L) & ~(kBlk - 1) : p.prefix_tokens;
+    const int32_t S = p.B * p.n_qt;                   // private segments
+    const int32_t per = (S + kThreads - 1) / kThreads;
+    const int32_t s_first = threadIdx.x * per;
+    // queries of tile t of a chunk (a single query: tile 0, one query)
+    auto tile_q0 = [&](int32_t t) -> int32_t { return MQ ? t * p.qpt : 0; };
+    auto tile_nq = [&](int32_t t) -> int32_t { return MQ ? min(p.nq - t * p.qpt, p.qpt) : 1; };
+    // window start of the first query of tile t, and the first streamed
+    // token: after the shared prefix, or the 16-aligned block holding the
+    // window start
+    auto window_lo = [&](int32_t L, int32_t t) -> int32_t {
+      return p.window > 0 ? max(0, L - p.nq + tile_q0(t) + 1 - p.window) : 0;
     };
-    auto priv_blocks = [&](int32_t bb) -> int32_t {
-      const int32_t L = p.lens[bb];
-      sm_len[bb] = L;
-      const bool bad = L < p.min_len || L > p.max_context || (p.ring == 0 && L > (p.max_pages << p.p_shift));
-      return bad ? 0 : (L - first_token(L) + kBlk - 1) / kBlk;
+    auto first_token = [&](int32_t L, int32_t t) -> int32_t {
+      return p.window > 0 ? window_lo(L, t) & ~(kBlk - 1) : p.prefix_tokens;
     };
+    // one past the last token segment (b, t) attends: its tile's last query
+    auto seg_end = [&](int32_t L, int32_t t) -> int32_t { return L - p.nq + tile_q0(t) + tile_nq(t); };
     int32_t local = 0;
+    int32_t first_live = 0x7fffffff;                  // first attended sequence (shared prefix page ids)
     for (int32_t i = 0; i < per; ++i) {
-      const int32_t bb = b0 + i;
-      if (bb < p.B) {
-        const int32_t nb = priv_blocks(bb);
-        sm_cum[bb] = nb;
+      const int32_t s = s_first + i;
+      if (s < S) {
+        const int32_t b = s / p.n_qt;
+        const int32_t t = s - b * p.n_qt;
+        const int32_t L = p.lens[b];
+        sm_len[s] = L;
+        int32_t nb = 0;
+        if (len_state(p, L) == 1) {
+          nb = (seg_end(L, t) - first_token(L, t) + kBlk - 1) / kBlk;
+          first_live = min(first_live, b);
+        }
+        sm_cum[s] = nb;
         local += nb;
       }
     }
@@ -1000,19 +1015,27 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
       const int32_t y = __shfl_up(incl, off);
       if (lane >= off) incl += y;
     }
-    if (lane == kWave - 1) sm_wsum[wave] = incl;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) first_live = min(first_live, __shfl_xor(first_live, off));
+    if (lane == kWave - 1) smem.wsum[wave] = incl;
+    if (lane == 0) smem.wmin[wave] = first_live;
     __syncthreads();
     int32_t run = incl - local;
-    for (int w = 0; w < wave; ++w) run += sm_wsum[w];
+    for (int w = 0; w < wave; ++w) run += smem.wsum[w];
     for (int32_t i = 0; i < per; ++i) {
-      const int32_t bb = b0 + i;
-      if (bb < p.B) {
-        run += sm_cum[bb];
-        sm_cum[bb] = run;
+      const int32_t s = s_first + i;
+      if (s < S) {
+        run += sm_cum[s];
+        sm_cum[s] = run;
       }
     }
+    int32_t prefix_row = smem.wmin[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) prefix_row = min(prefix_row, smem.wmin[w]);
+    // no attended sequence: the prefix pieces feed no output row
+    if (prefix_row == 0x7fffffff) prefix_row = 0;
     __syncthreads();
-    const int32_t NB = sm_cum[p.B - 1];               // private blocks per KV head
+    const int32_t NB = sm_cum[S - 1];                 // private blocks per KV head
     const int32_t PB = p.prefix_tokens / kBlk;        // prefix blocks per tile
     const int32_t NTP = p.n_tiles * PB;               // prefix units per KV head
     const int32_t Wk = p.n_flat_wgs / p.Hkv;          // workgroups per KV head
@@ -1025,14 +1048,17 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
         p.flat_hdr[1] = Qv;
         p.flat_hdr[2] = Qp;
       }
-      for (int32_t bb = threadIdx.x; bb < p.B; bb += kThreads) p.flat_cum[bb] = sm_cum[bb];
+      for (int32_t s = threadIdx.x; s < S; s += kThreads) p.flat_cum[s] = sm_cum[s];
     }
     const int32_t kvh = wg % p.Hkv;
     const int32_t jw = wg / p.Hkv;
-    const int64_t slot_base = (int64_t)kvh * (p.n_tiles + p.B + 2 * Wk) + jw;
+    const int64_t slot_base = (int64_t)kvh * (p.n_tiles + S + 2 * Wk) + jw;
     const int32_t gp0 = min(jw * Qp, NTP), gp1 = min(gp0 + Qp, NTP);
     const int32_t gv0 = min(jw * Qv, NB), gv1 = min(gv0 + Qv, NB);
     const int32_t quota = (gp1 - gp0) + (gv1 - gv0);
+    // the prefix pages are the same in every attended row of the table: read
+    // them from the first such row (an idle slot's row may hold anything)
+    const int32_t* prefix_bt = p.bt + (int64_t)prefix_row * p.max_pages;
 
     // shared prefix, units [g0, g1): 16 query rows of tile rt per piece
     auto prefix_part = [&](int32_t g0, int32_t g1, int32_t after) {
@@ -1047,40 +1073,42 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
           return r < rows ? (int64_t)(r / G) * p.Hq + (int64_t)kvh * G + r % G : -1;
         };
         const int64_t slot = slot_base + rt;
-        // the prefix pages are the same in every row of the table: read row 0
-        run_range<D, 16, kPrefixLoadPolicy, false, K8>(p, smem.tile.prefix, p.bt, kvh, blk0 * kBlk, (blk0 + piece_n) * kBlk,
-                                                   quota, after + g1 - g - piece_n, NewToken{-1, 0, nullptr, nullptr}, qrow,
-                                            [&](int c, int d, float M, float Ls, float O) {
-                                              const int64_t ps = slot * 16 + c;
-                                              p.flat_o[ps * D + d] = O;
-                                              if (d == 0) {
-                                                p.flat_m[ps] = M;
-                                                p.flat_l[ps] = Ls;
-                                              }
-                                            },
-                                            lane, wave);
+        run_range<D, 16, kPrefixLoadPolicy, false, K8>(
+            p, smem.tile.prefix, prefix_bt, kvh, blk0 * kBlk, (blk0 + piece_n) * kBlk, quota,
+            after + g1 - g - piece_n, NewToken{-1, 0, nullptr, nullptr}, qrow,
+            [&](int c, int d, float M, float Ls, float O) {
+              const int64_t ps = slot * 16 + c;
+              p.flat_o[ps * D + d] = O;
+              if (d == 0) {
+                p.flat_m[ps] = M;
+                p.flat_l[ps] = Ls;
+              }
+            },
+            lane, wave);
         g += piece_n;
       }
     };
-    // private blocks, units [g0, g1) of the concatenated per-sequence lists
+    // private blocks, units [g0, g1) of the concatenated per-segment lists
     auto private_part = [&](int32_t g0, int32_t g1, int32_t after) {
       for (int32_t g = g0; g < g1;) {
-        // first sequence whose inclusive prefix exceeds g
-        int32_t lo = 0, hi = p.B - 1;
+        // first segment whose inclusive prefix exceeds g
+        int32_t lo = 0, hi = S - 1;
         while (lo < hi) {
           const int32_t mid = (lo + hi) >> 1;
           if (sm_cum[mid] > g) hi = mid;
           else lo = mid + 1;
         }
-        const int32_t b = lo;
-        const int32_t seg_first = b > 0 ? sm_cum[b - 1] : 0;
-        const int32_t seg_n = sm_cum[b] - seg_first;
+        const int32_t s = lo;
+        const int32_t b = s / p.n_qt;
+        const int32_t t = s - b * p.n_qt;
+        const int32_t seg_first = s > 0 ? sm_cum[s - 1] : 0;
+        const int32_t seg_n = sm_cum[s] - seg_first;
         const int32_t blk0 = g - seg_first;
         const int32_t piece_n = min(g1 - g, seg_n - blk0);
-        const int32_t L = sm_len[b];
-        const int32_t s0 = first_token(L);
+        const int32_t L = sm_len[s];
+        const int32_t s0 = first_token(L, t);
         const int32_t start = s0 + blk0 * kBlk;
-        const int32_t end = min(L, s0 + (blk0 + piece_n) * kBlk);
+        const int32_t end = min(seg_end(L, t), s0 + (blk0 + piece_n) * kBlk);
         const int64_t head_row0 = (int64_t)b * p.Hq + (int64_t)kvh * G;
         const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
         NewToken nt{-1, 0, nullptr, nullptr};
@@ -1091,7 +1119,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
             nt = NewToken{(end - 1 - start) >> 4, (end - 1) & 15, p.k_new + src, p.v_new + src};
           }
         }
-        const int64_t slot = slot_base + p.n_tiles + Wk + b;
+        const int64_t slot = slot_base + p.n_tiles + Wk + s;
         auto emit = [&](int c, int d, float M, float Ls, float O) {
           const int64_t ps = slot * 16 + c;
           p.flat_o[ps * D + d] = O;
@@ -1101,19 +1129,21 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
           }
         };
         if constexpr (MQ) {
-          // columns (query i, head g) = i * G + g of the chunk of the last nq tokens
-          const int32_t ncol = p.nq * G;
+          // columns (query q0 + i, head g) = i * G + g of query tile t of the chunk
+          const int32_t q0 = tile_q0(t);
+          const int32_t nqt = tile_nq(t);
+          const int32_t ncol = nqt * G;
           run_range<D, 16, kKvLoadPolicy, false, K8, true>(
               p, smem.tile.prefix, bt_row, kvh, start, end, quota, after + g1 - g - piece_n, nt,
               [&](int c) -> int64_t {
-                return c < ncol ? ((int64_t)b * p.nq + c / G) * p.Hq + (int64_t)kvh * G + c % G : -1;
+                return c < ncol ? ((int64_t)b * p.nq + q0 + c / G) * p.Hq + (int64_t)kvh * G + c % G : -1;
               },
-              emit, lane, wave, L - p.nq, G, window_lo(L));
+              emit, lane, wave, L - p.nq + q0, G, window_lo(L, t), nqt);
         } else {
           run_range<D, G, kKvLoadPolicy, FUSED, K8>(
               p, smem.tile.priv, bt_row, kvh, start, end, quota, after + g1 - g - piece_n, nt,
               [&](int c) -> int64_t { return c < G ? head_row0 + c : -1; }, emit, lane, wave, 0, 1,
-              window_lo(L));
+              window_lo(L, t));
         }
         g += piece_n;
       }
@@ -1134,63 +1164,90 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
 // decode: log-sum-exp reduce over partitions
 // -------------------------------------------------------------------------
 
-// One workgroup of D threads per (sequence, query head). Its partials are the
-// pieces of the head's prefix tile segment (column = its row within the tile)
-// and of its private segment, made by KV head kvh's workgroups j0 .. j1 of the
-// balanced schedule (slot segment + j of each list). Every load is issued
-// before any arithmetic: the maxima and denominators go to LDS, and thread d
-// holds output dim d of the first partials in registers; then each thread
-// merges over all partials with weights exp2(m_j - M).
-template <int D>
-__global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
-  constexpr int kR = 8;               // partials whose outputs are loaded up front
-  __shared__ float sm_m[kMaxPartitions];
-  __shared__ float sm_l[kMaxPartitions];
-  const int64_t bh = blockIdx.x;                    // row (b * nq + query) * Hq + h of out
+// Where the partials of output row bh = (b * nq + query) * Hq + h lie: the
+// pieces of its prefix tile segment (np1 of them; column = its row within the
+// tile), then those of its private segment (column = its place among the
+// segment's query tile columns), made by KV head kvh's workgroups ja .. and
+// jb .. of the balanced schedule (slot segment + j of each list).
+struct MergeRow {
+  int32_t state;       // len_state of the row's sequence
+  int32_t np1, np;     // prefix pieces; all pieces (0 unless the row is attended)
+  int64_t part1;       // partial index of the first prefix piece (slot * 16 + column)
+  int64_t part2;       // partial index of the first private piece
+};
+
+__device__ __forceinline__ MergeRow merge_row(const DecodeParams& p, int64_t bh) {
+  MergeRow m;
   const int32_t b = (int32_t)(bh / ((int64_t)p.nq * p.Hq));
   const int32_t qi = (int32_t)((bh / p.Hq) % p.nq);
   const int32_t h = (int32_t)(bh % p.Hq);
   const int32_t G = p.Hq / p.Hkv;
   const int32_t kvh = h / G;
   const int32_t hg = h % G;
-  const int d = threadIdx.x;
-  const int32_t L = p.lens[b];
-  const bool bad_len = L < p.min_len || L > p.max_context || (p.ring == 0 && L > (p.max_pages << p.p_shift));
+  m.state = len_state(p, p.lens[b]);
   const int32_t Qv = p.flat_hdr[1];
   const int32_t Qp = p.flat_hdr[2];
   const int32_t Wk = p.n_flat_wgs / p.Hkv;
   const int32_t PB = p.prefix_tokens / kBlk;
-  const int64_t slot_base = (int64_t)kvh * (p.n_tiles + p.B + 2 * Wk);
+  const int32_t S = p.B * p.n_qt;
+  const int64_t slot_base = (int64_t)kvh * (p.n_tiles + S + 2 * Wk);
   // prefix tile segment of row r = (b * nq + qi) * G + hg
   const int32_t r = (b * p.nq + qi) * G + hg;
   const int32_t rt = r / 16;
-  const int32_t ct = r % 16;
-  int32_t np1 = 0, ja = 0;
+  int32_t ja = 0;
+  m.np1 = 0;
   if (PB > 0) {
     const int32_t u0 = rt * PB;
     ja = u0 / Qp;
-    np1 = (u0 + PB - 1) / Qp - ja + 1;
+    m.np1 = (u0 + PB - 1) / Qp - ja + 1;
   }
-  // private segment
-  const int32_t prev = b > 0 ? p.flat_cum[b - 1] : 0;
-  const int32_t nblk = p.flat_cum[b] - prev;
+  m.part1 = (slot_base + rt + ja) * 16 + r % 16;
+  // private segment: query tile t = cq / 16 of the chunk, column cq % 16
+  const int32_t cq = qi * G + hg;
+  const int32_t s = b * p.n_qt + cq / 16;
+  const int32_t prev = s > 0 ? p.flat_cum[s - 1] : 0;
+  const int32_t nblk = p.flat_cum[s] - prev;
   int32_t np2 = 0, jb = 0;
   if (nblk > 0) {
     jb = prev / Qv;
     np2 = (prev + nblk - 1) / Qv - jb + 1;
   }
-  const int32_t np = bad_len ? 0 : np1 + np2;
-  auto idx = [&](int32_t j) -> int64_t {
-    return j < np1 ? (slot_base + rt + ja + j) * 16 + ct
-                   : (slot_base + p.n_tiles + Wk + b + jb + (j - np1)) * 16 + qi * G + hg;
-  };
+  m.part2 = (slot_base + p.n_tiles + Wk + s + jb) * 16 + cq % 16;
+  m.np = m.state == 1 ? m.np1 + np2 : 0;
+  return m;
+}
 
+__device__ __forceinline__ int64_t part_index(const MergeRow& m, int32_t j) {
+  return j < m.np1 ? m.part1 + (int64_t)j * 16 : m.part2 + (int64_t)(j - m.np1) * 16;
+}
+
+// The merged row: 0 for an idle slot, NaN for an invalid length or a bad page
+// met in any piece, else the normalised sum.
+__device__ __forceinline__ float merged(const MergeRow& m, float Ls, float O) {
+  if (m.state == 0) return 0.f;
+  if (m.state < 0 || Ls != Ls) return __builtin_nanf("");
+  return Ls > 0.f ? O / Ls : 0.f;
+}
+
+// One workgroup of D threads per output row. Every load is issued before any
+// arithmetic: the maxima and denominators go to LDS, and thread d holds output
+// dim d of the first partials in registers; then each thread merges over all
+// partials with weights exp2(m_j - M).
+template <int D>
+__global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
+  constexpr int kR = 8;               // partials whose outputs are loaded up front
+  __shared__ float sm_m[kMaxPartitions];
+  __shared__ float sm_l[kMaxPartitions];
+  const int64_t bh = blockIdx.x;
+  const int d = threadIdx.x;
+  const MergeRow mr = merge_row(p, bh);
+  const int32_t np = mr.np;
   const float* po = p.flat_o + d;
   float ov[kR];
 #pragma unroll
-  for (int j = 0; j < kR; ++j) ov[j] = j < np ? po[idx(j) * D] : 0.f;
+  for (int j = 0; j < kR; ++j) ov[j] = j < np ? po[part_index(mr, j) * D] : 0.f;
   for (int32_t j = d; j < np; j += D) {
-    const int64_t q = idx(j);
+    const int64_t q = part_index(mr, j);
     sm_m[j] = p.flat_m[q];
     sm_l[j] = p.flat_l[q];
   }
@@ -1210,11 +1267,9 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
   for (int32_t j = kR; j < np; ++j) {
     const float wj = fast_exp2(sm_m[j] - Ms);
     Ls = fmaf(wj, sm_l[j], Ls);
-    O = fmaf(wj, po[idx(j) * D], O);
+    O = fmaf(wj, po[part_index(mr, j) * D], O);
   }
-  float res = Ls > 0.f ? O / Ls : 0.f;
-  if (bad_len || Ls != Ls) res = __builtin_nanf("");
-  p.out[bh * D + d] = (half_t)res;
+  p.out[bh * D + d] = (half_t)merged(mr, Ls, O);
 }
 
 // The same merge with one wave per row (four rows per workgroup, lane l
@@ -1231,47 +1286,15 @@ __global__ __launch_bounds__(kThreads) void lse_reduce_wave_kernel(DecodeParams 
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t bh = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);   // row (b * nq + query) * Hq + h of out
   if (bh >= (int64_t)p.B * p.nq * p.Hq) return;                            // the whole wave
-  const int32_t b = (int32_t)(bh / ((int64_t)p.nq * p.Hq));
-  const int32_t qi = (int32_t)((bh / p.Hq) % p.nq);
-  const int32_t h = (int32_t)(bh % p.Hq);
-  const int32_t G = p.Hq / p.Hkv;
-  const int32_t kvh = h / G;
-  const int32_t hg = h % G;
-  const int32_t L = p.lens[b];
-  const bool bad_len = L < p.min_len || L > p.max_context || (p.ring == 0 && L > (p.max_pages << p.p_shift));
-  const int32_t Qv = p.flat_hdr[1];
-  const int32_t Qp = p.flat_hdr[2];
-  const int32_t Wk = p.n_flat_wgs / p.Hkv;
-  const int32_t PB = p.prefix_tokens / kBlk;
-  const int64_t slot_base = (int64_t)kvh * (p.n_tiles + p.B + 2 * Wk);
-  const int32_t r = (b * p.nq + qi) * G + hg;
-  const int32_t rt = r / 16;
-  const int32_t ct = r % 16;
-  int32_t np1 = 0, ja = 0;
-  if (PB > 0) {
-    const int32_t u0 = rt * PB;
-    ja = u0 / Qp;
-    np1 = (u0 + PB - 1) / Qp - ja + 1;
-  }
-  const int32_t prev = b > 0 ? p.flat_cum[b - 1] : 0;
-  const int32_t nblk = p.flat_cum[b] - prev;
-  int32_t np2 = 0, jb = 0;
-  if (nblk > 0) {
-    jb = prev / Qv;
-    np2 = (prev + nblk - 1) / Qv - jb + 1;
-  }
-  const int32_t np = bad_len ? 0 : np1 + np2;
-  auto idx = [&](int32_t j) -> int64_t {
-    return j < np1 ? (slot_base + rt + ja + j) * 16 + ct
-                   : (slot_base + p.n_tiles + Wk + b + jb + (j - np1)) * 16 + qi * G + hg;
-  };
+  const MergeRow mr = merge_row(p, bh);
+  const int32_t np = mr.np;
   const float* po = p.flat_o + lane;
   float mv[kR], lv[kR], ov[kR][DPL];
   auto load_batch = [&](int32_t j0) {
 #pragma unroll
     for (int k = 0; k < kR; ++k) {
       const bool live = j0 + k < np;
-      const int64_t q = live ? idx(j0 + k) : 0;
+      const int64_t q = live ? part_index(mr, j0 + k) : 0;
       mv[k] = live ? p.flat_m[q] : 0.f;
       lv[k] = live ? p.flat_l[q] : 0.f;
 #pragma unroll
@@ -1282,7 +1305,7 @@ __global__ __launch_bounds__(kThreads) void lse_reduce_wave_kernel(DecodeParams 
   float M = kNegInf();
   for (int32_t j0 = 0; j0 < np; j0 += kWave) {
     const int32_t j = j0 + lane;
-    M = fmaxf(M, j < np ? p.flat_m[idx(j)] : kNegInf());
+    M = fmaxf(M, j < np ? p.flat_m[part_index(mr, j)] : kNegInf());
   }
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) M = fmaxf(M, __shfl_xor(M, off));
@@ -1303,11 +1326,7 @@ __global__ __launch_bounds__(kThreads) void lse_reduce_wave_kernel(DecodeParams 
     }
   }
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) {
-    float res = Ls > 0.f ? O[e] / Ls : 0.f;
-    if (bad_len || Ls != Ls) res = __builtin_nanf("");
-    p.out[bh * D + lane + e * kWave] = (half_t)res;
-  }
+  for (int e = 0; e < DPL; ++e) p.out[bh * D + lane + e * kWave] = (half_t)merged(mr, Ls, O[e]);
 }
 
 // -------------------------------------------------------------------------
@@ -1328,13 +1347,13 @@ int log2_page(int32_t P) {
 
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
-// Workspace of a split call: a 256-byte header, the per-sequence prefix sums,
+// Workspace of a split call: a 256-byte header, the per-segment prefix sums,
 // then the piece partials [slots][16] (max, sum) and [slots][16][D] (output).
 struct WsLayout {
   size_t hdr_off, cum_off, fm_off, fl_off, fo_off, total;
 };
 
-WsLayout ws_layout(int64_t B, int64_t D, int64_t slots) {
+WsLayout ws_layout(int64_t segments, int64_t D, int64_t slots) {
   WsLayout w{};
   size_t at = 0;
   auto take = [&](size_t bytes) {
@@ -1343,7 +1362,7 @@ WsLayout ws_layout(int64_t B, int64_t D, int64_t slots) {
     return off;
   };
   w.hdr_off = take(3 * sizeof(int32_t));
-  w.cum_off = take(static_cast<size_t>(B) * sizeof(int32_t));
+  w.cum_off = take(static_cast<size_t>(segments) * sizeof(int32_t));
   w.fm_off = take(static_cast<size_t>(slots * 16) * sizeof(float));
   w.fl_off = take(static_cast<size_t>(slots * 16) * sizeof(float));
   w.fo_off = take(static_cast<size_t>(slots * 16 * D) * sizeof(float));
@@ -1351,44 +1370,65 @@ WsLayout ws_layout(int64_t B, int64_t D, int64_t slots) {
   return w;
 }
 
+// Split-mode workgroups: kWgsPerCu per compute unit of the current device
+// (cached per device), at most kMaxFlatWgs, which also sizes the workspace
+// query (that query needs no device).
+constexpr int32_t kMaxFlatWgs = 1024;
+constexpr int kMaxDevices = 64;
+std::atomic<int32_t> g_flat_wgs[kMaxDevices];
+
+int32_t device_flat_wgs() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return -1;
+  if (dev < kMaxDevices) {
+    const int32_t cached = g_flat_wgs[dev].load(std::memory_order_relaxed);
+    if (cached > 0) return cached;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) return -1;
+  const int32_t w = std::min(kWgsPerCu * cus, kMaxFlatWgs);
+  if (dev < kMaxDevices) g_flat_wgs[dev].store(w, std::memory_order_relaxed);
+  return w;
+}
+
 // Work decomposition of one decode call.
 struct Plan {
   bool split;
+  int32_t n_qt;            // 16-column query tiles per (sequence, KV head): ceil(nq * G / 16) for chunks, else 1
+  int32_t segments;        // private segments per KV head: B * n_qt
   int32_t n_tiles;         // 16-row query tiles per KV head reading the shared prefix
   int32_t n_flat_wgs;      // workgroups of the split schedule (a multiple of Hkv)
   int32_t min_piece;       // minimum blocks per piece
-  int64_t slots;           // piece slots: Hkv * (n_tiles + B + 2 * n_flat_wgs / Hkv)
+  int64_t slots;           // piece slots: Hkv * (n_tiles + segments + 2 * n_flat_wgs / Hkv)
   int64_t grid;
 };
 
-int make_plan(int32_t B, int32_t Hq, int32_t Hkv, int32_t max_context, int32_t partition_tokens,
-              int32_t prefix_tokens, Plan* pl, int32_t nq = 1) {
-  if (B < 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_context < 0 || partition_tokens < 0 ||
+int make_plan(int32_t B, int32_t nq, int32_t Hq, int32_t Hkv, int32_t max_context, int32_t partition_tokens,
+              int32_t prefix_tokens, int32_t flat_wgs, Plan* pl) {
+  if (B < 0 || nq < 1 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || max_context < 0 || partition_tokens < 0 ||
       partition_tokens % kBlk != 0 || prefix_tokens < 0 || prefix_tokens % kBlk != 0 || prefix_tokens > max_context)
     return PKV_ERR_INVALID_ARG;
   if (prefix_tokens > 0 && partition_tokens == 0) return PKV_ERR_INVALID_ARG;
+  const int64_t G = Hq / Hkv;
   Plan p{};
   p.split = partition_tokens > 0;
-  if (p.split && B > kMaxFlatBatch) return PKV_ERR_INVALID_ARG;
-  const int64_t rows = static_cast<int64_t>(B) * nq * (Hq / Hkv);    // query rows per KV head
+  const int64_t n_qt = nq > 1 ? (static_cast<int64_t>(nq) * G + 15) / 16 : 1;
+  const int64_t segments = static_cast<int64_t>(B) * n_qt;
+  if (p.split && segments > kMaxSegments) return PKV_ERR_INVALID_ARG;
+  p.n_qt = static_cast<int32_t>(std::min<int64_t>(n_qt, 0x7fffffff));
+  p.segments = static_cast<int32_t>(std::min<int64_t>(segments, 0x7fffffff));
+  const int64_t rows = static_cast<int64_t>(B) * nq * G;                // query rows per KV head
+  if (rows > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
   p.n_tiles = prefix_tokens > 0 ? static_cast<int32_t>((rows + 15) / 16) : 0;
-  // a whole number of workgroups per KV head, at least one
-  p.n_flat_wgs = p.split ? max(PKV_FLAT_WORKGROUPS / Hkv, 1) * Hkv : 0;
-  if (p.split && 2 * (p.n_flat_wgs / Hkv) > kMaxPartitions) return PKV_ERR_INVALID_ARG;
+  // a whole number of workgroups per KV head, at least one; a row's pieces
+  // (at most two per workgroup of its head) fit the merge kernel's LDS
+  p.n_flat_wgs = p.split ? std::min(std::max(flat_wgs / Hkv, 1), kMaxPartitions / 2) * Hkv : 0;
   p.min_piece = partition_tokens / kBlk;
-  p.slots = p.split ? static_cast<int64_t>(Hkv) * (p.n_tiles + B + 2 * (p.n_flat_wgs / Hkv)) : 0;
-  p.grid = p.split ? p.n_flat_wgs : static_cast<int64_t>(B) * Hkv;
-  if (p.grid > 0x7fffffffLL || static_cast<int64_t>(B) * Hq > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
+  p.slots = p.split ? static_cast<int64_t>(Hkv) * (p.n_tiles + segments + 2 * (p.n_flat_wgs / Hkv)) : 0;
+  p.grid = p.split ? p.n_flat_wgs : segments * Hkv;
+  if (p.grid > 0x7fffffffLL || static_cast<int64_t>(B) * nq * Hq > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
   *pl = p;
   return PKV_OK;
-}
-
-// Upper bound of Plan::slots over every Hkv that divides Hq (the workspace
-// query does not take Hkv): Hkv * n_tiles <= B * Hq / 16 + Hkv,
-// Hkv * B <= Hq * B, Hkv * (W / Hkv) <= max(W, Hkv).
-int64_t max_slots(int32_t B, int32_t Hq, bool prefix) {
-  return (prefix ? static_cast<int64_t>(B) * Hq / 16 + Hq : 0) + static_cast<int64_t>(B) * Hq +
-         2 * (static_cast<int64_t>(PKV_FLAT_WORKGROUPS) + Hq);
 }
 
 // Measurement hook: events that the next decode call made on this host thread
@@ -1444,14 +1484,14 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
       partition_tokens < 0 || prefix_tokens < 0)
     return PKV_ERR_INVALID_ARG;
   if (Hq % Hkv != 0) return PKV_ERR_INVALID_ARG;
-  if (!(scale == scale) || scale == __builtin_huge_valf() || scale == -__builtin_huge_valf())
-    return PKV_ERR_INVALID_ARG;
+  // a positive, finite softmax scale: the kernels take a block's score
+  // maximum as the maximum of its scaled scores
+  if (!(scale > 0.f) || scale == __builtin_huge_valf()) return PKV_ERR_INVALID_ARG;
   const int G = Hq / Hkv;
   if (nq < 1) return PKV_ERR_INVALID_ARG;
   if (nq > 1 && fused) return PKV_ERR_INVALID_ARG;
   if (window < 0 || (window > 0 && prefix_tokens > 0)) return PKV_ERR_INVALID_ARG;
   if (D != 64 && D != 128) return PKV_ERR_UNSUPPORTED;
-  if (static_cast<int64_t>(nq) * G > 16) return PKV_ERR_UNSUPPORTED;     // one 16-column matrix-core tile
   if (static_cast<int64_t>(B) * nq * Hq > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
   const int p_shift = log2_page(P);
   if (p_shift < 0) return PKV_ERR_UNSUPPORTED;
@@ -1462,8 +1502,16 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   // a ring of max_pages pages holds every page the windows of a chunk touch
   if (window > 0 && static_cast<int64_t>(window) + nq - 1 > (static_cast<int64_t>(max_pages) - 1) * P + 1)
     return PKV_ERR_INVALID_ARG;
+  // split workgroups for the current device; if its compute units cannot be
+  // counted, the plan takes the largest count (correct on any device: the
+  // schedule only gets finer), and a launch on a host without a device fails
+  int32_t flat_wgs = kMaxFlatWgs;
+  if (partition_tokens > 0 && B > 0) {
+    const int32_t w = device_flat_wgs();
+    if (w > 0) flat_wgs = w;
+  }
   Plan plan;
-  const int rc = make_plan(B, Hq, Hkv, max_context, partition_tokens, prefix_tokens, &plan, nq);
+  const int rc = make_plan(B, nq, Hq, Hkv, max_context, partition_tokens, prefix_tokens, flat_wgs, &plan);
   if (rc != PKV_OK) return rc;
   if (B == 0) return PKV_OK;
   if (!out || !q || !k_pool || !v_pool || !bt || !lens) return PKV_ERR_INVALID_ARG;
@@ -1503,6 +1551,8 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   // an appended token must land in a private page; a chunk of queries lies after the prefix
   prm.min_len = nq > 1 ? prefix_tokens + nq : prefix_tokens + (fused && prefix_tokens > 0 ? 1 : 0);
   prm.nq = nq;
+  prm.n_qt = plan.n_qt;
+  prm.qpt = nq > 1 ? 16 / G : 1;
   prm.ring = window > 0 ? max_pages : 0;
   prm.window = window;
   prm.n_tiles = plan.n_tiles;
@@ -1511,7 +1561,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   prm.scale_log2 = scale * kLog2e;
 
   if (plan.split) {
-    const WsLayout ws = ws_layout(B, D, plan.slots);
+    const WsLayout ws = ws_layout(plan.segments, D, plan.slots);
     if (!workspace) return PKV_ERR_INVALID_ARG;
     if (!aligned(workspace, kWsAlign)) return PKV_ERR_INVALID_ARG;
     if (workspace_bytes < ws.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
@@ -1559,14 +1609,26 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   return PKV_OK;
 }
 
-int workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context, int32_t partition_tokens,
+// The largest workspace any KV-head count allowed with Hq query heads needs
+// (the query takes no Hkv), with the most split workgroups any device gets.
+int workspace_bytes(int32_t B, int32_t nq, int32_t Hq, int32_t D, int32_t max_context, int32_t partition_tokens,
                     int32_t prefix_tokens, size_t* bytes) {
-  if (!bytes || D <= 0) return PKV_ERR_INVALID_ARG;
-  Plan plan;
-  // Hkv does not change the slot count; any divisor of Hq gives the same plan sizes
-  const int rc = make_plan(B, Hq, Hq, max_context, partition_tokens, prefix_tokens, &plan);
+  if (!bytes || D <= 0 || Hq <= 0) return PKV_ERR_INVALID_ARG;
+  size_t best = 0;
+  int rc = PKV_ERR_INVALID_ARG;
+  for (int32_t G = 1; G <= 16; G *= 2) {
+    if (Hq % G != 0) continue;
+    Plan plan;
+    const int r = make_plan(B, nq, Hq, Hq / G, max_context, partition_tokens, prefix_tokens, kMaxFlatWgs, &plan);
+    if (r != PKV_OK) {
+      if (rc != PKV_OK) rc = r;
+      continue;
+    }
+    rc = PKV_OK;
+    if (plan.split) best = std::max(best, ws_layout(plan.segments, D, plan.slots).total);
+  }
   if (rc != PKV_OK) return rc;
-  *bytes = plan.split ? ws_layout(B, D, max_slots(B, Hq, prefix_tokens > 0)).total : 0;
+  *bytes = best;
   return PKV_OK;
 }
 
@@ -1689,12 +1751,17 @@ int pkv_kv_append(const void* k_new, const void* v_new, void* k_pool, void* v_po
 
 int pkv_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t D, int32_t max_context, int32_t partition_tokens,
                                size_t* bytes) {
-  return workspace_bytes(B, Hq, D, max_context, partition_tokens, 0, bytes);
+  return workspace_bytes(B, 1, Hq, D, max_context, partition_tokens, 0, bytes);
 }
 
 int pkv_decode_workspace_bytes_shared_prefix(int32_t B, int32_t Hq, int32_t D, int32_t max_context,
                                              int32_t partition_tokens, int32_t prefix_tokens, size_t* bytes) {
-  return workspace_bytes(B, Hq, D, max_context, partition_tokens, prefix_tokens, bytes);
+  return workspace_bytes(B, 1, Hq, D, max_context, partition_tokens, prefix_tokens, bytes);
+}
+
+int pkv_decode_workspace_bytes_multi(int32_t B, int32_t n_query, int32_t Hq, int32_t D, int32_t max_context,
+                                     int32_t partition_tokens, int32_t prefix_tokens, size_t* bytes) {
+  return workspace_bytes(B, n_query, Hq, D, max_context, partition_tokens, prefix_tokens, bytes);
 }
 
 int pkv_paged_decode_attention(void* out, const void* q, const void* k_pool, const void* v_pool,

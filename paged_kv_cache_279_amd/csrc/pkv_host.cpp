@@ -124,7 +124,7 @@ const char* pkv_status_string(int status) {
   }
 }
 
-int pkv_abi_version(void) { return 1; }
+int pkv_abi_version(void) { return 2; }
 
 int pkv_alloc_create(int32_t num_pages, int32_t page_size, const int32_t* free_order,
                      pkv_allocator** out) {
@@ -358,10 +358,14 @@ int pkv_alloc_refcount(const pkv_allocator* a, int32_t page, int32_t* count) {
 }
 
 int pkv_validate_tables(const int32_t* bt, const int32_t* lens, int32_t B, int32_t max_pages, int32_t P,
-                        int32_t N, int32_t exclusive_tail, int32_t* bad_row, int32_t* bad_entry,
-                        int32_t* rule) {
+                        int32_t N, int32_t exclusive_tail, int32_t prefix_tokens, int32_t window, int32_t* bad_row,
+                        int32_t* bad_entry, int32_t* rule) {
   return guarded([&]() -> int {
-    if (B < 0 || max_pages < 0 || P <= 0 || N < 0) return PKV_ERR_INVALID_ARG;
+    if (B < 0 || max_pages < 0 || P <= 0 || N < 0 || prefix_tokens < 0 || window < 0) return PKV_ERR_INVALID_ARG;
+    if (prefix_tokens % P != 0 || (window > 0 && prefix_tokens > 0)) return PKV_ERR_INVALID_ARG;
+    // a window must fit its ring: the pages it touches are distinct entries
+    if (window > 0 && static_cast<int64_t>(window) > (static_cast<int64_t>(max_pages) - 1) * P + 1)
+      return PKV_ERR_INVALID_ARG;
     if (B > 0 && (!bt || !lens)) return PKV_ERR_INVALID_ARG;
     auto fail = [&](int32_t r, int32_t row, int32_t entry) {
       if (bad_row) *bad_row = row;
@@ -372,32 +376,62 @@ int pkv_validate_tables(const int32_t* bt, const int32_t* lens, int32_t B, int32
     if (bad_row) *bad_row = -1;
     if (bad_entry) *bad_entry = -1;
     if (rule) *rule = 0;
+    // the entries a row's tokens reach, in token order: logical pages 0 ..
+    // ceil(L / P) - 1, or under a window the ring entries (j % max_pages) of
+    // the logical pages holding tokens max(0, L - window) .. L - 1
+    auto reached = [&](int64_t L, std::vector<int32_t>& out) {
+      out.clear();
+      if (L <= 0) return;
+      const int64_t lo = window > 0 ? std::max<int64_t>(0, L - window) : 0;
+      for (int64_t j = lo / P; j <= (L - 1) / P; ++j)
+        out.push_back(static_cast<int32_t>(window > 0 ? j % max_pages : j));
+    };
     std::vector<int32_t> owners(static_cast<size_t>(N), 0);   // rows referencing each page
     std::vector<int32_t> last_owner(static_cast<size_t>(N), -1);
     std::vector<int32_t> mark(static_cast<size_t>(N), -1);     // row that last saw the page
+    std::vector<int32_t> tail(static_cast<size_t>(B), -1);     // entry of each row's last token
+    std::vector<int32_t> ent;
     for (int32_t b = 0; b < B; ++b) {
       const int64_t n = lens[b];
       if (n < 0) return fail(1, b, -1);
-      const int64_t used = pages_for(n, P);
-      if (used > max_pages) return fail(2, b, -1);
+      if (window == 0 && pages_for(n, P) > max_pages) return fail(2, b, -1);
+      reached(n, ent);
       const int32_t* row = bt + static_cast<int64_t>(b) * max_pages;
-      for (int64_t j = 0; j < used; ++j) {
+      for (const int32_t j : ent) {
         const int32_t p = row[j];
-        if (p < 0 || p >= N) return fail(3, b, static_cast<int32_t>(j));
-        if (mark[p] == b) return fail(4, b, static_cast<int32_t>(j));
+        if (p < 0 || p >= N) return fail(3, b, j);
+        if (mark[p] == b) return fail(4, b, j);
         mark[p] = b;
         if (last_owner[p] != b) {
           owners[p] += 1;
           last_owner[p] = b;
         }
       }
+      if (!ent.empty()) tail[b] = ent.back();
     }
     if (exclusive_tail) {
       for (int32_t b = 0; b < B; ++b) {
-        const int64_t used = pages_for(lens[b], P);
-        if (used == 0) continue;
-        const int32_t p = bt[static_cast<int64_t>(b) * max_pages + used - 1];
-        if (owners[p] > 1) return fail(5, b, static_cast<int32_t>(used - 1));
+        if (tail[b] < 0) continue;
+        const int32_t p = bt[static_cast<int64_t>(b) * max_pages + tail[b]];
+        if (owners[p] > 1) return fail(5, b, tail[b]);
+      }
+    }
+    if (prefix_tokens > 0) {
+      // every attended row (lens > 0) holds the shared prefix in the same pages
+      // as the first attended row; an idle row (lens == 0) may hold anything
+      const int32_t np = prefix_tokens / P;
+      int32_t first = -1;
+      for (int32_t b = 0; b < B; ++b) {
+        if (lens[b] == 0) continue;
+        if (lens[b] < prefix_tokens) return fail(7, b, -1);
+        if (first < 0) {
+          first = b;
+          continue;
+        }
+        const int32_t* row = bt + static_cast<int64_t>(b) * max_pages;
+        const int32_t* ref = bt + static_cast<int64_t>(first) * max_pages;
+        for (int32_t j = 0; j < np; ++j)
+          if (row[j] != ref[j]) return fail(6, b, j);
       }
     }
     return PKV_OK;

@@ -132,7 +132,13 @@ int main(int argc, char** argv) {
     for (auto& x : bt) x = (int32_t)(rng() % 14) - 2;
     for (auto& x : lens) x = (int32_t)(rng() % 100) - 5;
     int32_t r, e, rule;
-    pkv_validate_tables(bt.data(), lens.data(), B, W, P, N, rng() % 2, &r, &e, &rule);
+    // plain tables, shared prefixes (up to 2 pages) and rings (windows up to 70 tokens; lengths far past the ring)
+    const int mode = rng() % 3;
+    const int32_t prefix = mode == 1 ? (int32_t)(rng() % 3) * P : 0;
+    const int32_t window = mode == 2 ? (int32_t)(rng() % 70) : 0;
+    if (mode == 2)
+      for (auto& x : lens) x = (int32_t)(rng() % 400) - 5;
+    pkv_validate_tables(bt.data(), lens.data(), B, W, P, N, rng() % 2, prefix, window, &r, &e, &rule);
   }
   printf("ok\n");
   return 0;

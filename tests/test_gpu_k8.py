@@ -64,7 +64,7 @@ def random_k8_pool(rng, N, Hkv, P, D, live=None):
 
 def poison_v(v_pool, live):
     v = v_pool.copy()
-    n, hkv, p, d = v.shape
+    n, hkv, p, d = oracle.pool_dims(v)
     for page, t in zip(*np.nonzero(~live)):
         for h in range(hkv):
             oracle.write_token(v, page, h, t, np.full(d, np.nan, np.float16), "v")

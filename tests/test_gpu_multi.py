@@ -96,15 +96,25 @@ def test_multi_query_short_rows_and_single_query(part):
     check_close(one[:, 0], ref1, "multi n_query=1")
 
 
-def test_multi_query_argument_checks():
+def test_multi_query_beyond_one_tile_and_idle_rows():
+    """5 queries x G = 4 = 20 query rows span two 16-column tiles; an idle row
+    (length 0) gives zeros and reads nothing of its table row (all -1)."""
     m = pkv()
-    w = workload(3, batch=2)
-    lens = w.lens(0)
-    q = torch.zeros((w.B, 5, w.Hq, w.D), dtype=torch.float16, device="cuda")      # 5 * G(4) > 16
-    with pytest.raises(m.PkvError) as e:
-        m.paged_decode_attention_multi(q, dev(w.k_pool), dev(w.v_pool), dev(w.block_table), dev(lens),
-                                       int(lens.max()), w.scale, 512)
-    assert e.value.status == m.PKV_ERR_UNSUPPORTED
+    w = workload(3, batch=3)
+    lens = w.lens(0).copy()
+    lens[0] = 0
+    bt = w.block_table.copy()
+    bt[0] = -1
+    kp, vp = poison_unused(w, lens)
+    nq = 5
+    q = np.random.default_rng(8).standard_normal((w.B, nq, w.Hq, w.D)).astype(np.float16)
+    for part in (0, 512):
+        say("multi two tiles + idle row, part=%d" % part)
+        got = host(m.paged_decode_attention_multi(dev(q), dev(kp), dev(vp), dev(bt), dev(lens), int(lens.max()),
+                                                  w.scale, part))
+        assert np.all(got[0] == 0)
+        ref = oracle.decode_attention_multi(q, kp, vp, bt, lens, w.scale, w.P)
+        check_close(torch.from_numpy(got), ref, "multi 5 queries, part=%d" % part, rows=[1, 2])
 
 
 @pytest.mark.parametrize("batch,nq,part", [(6, 4, 512), (6, 2, 1024), (3, 3, 256), (None, 4, 1024), (5, 1, 512)])

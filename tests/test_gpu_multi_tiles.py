@@ -1,0 +1,216 @@
+"""GPU parity for chunks of queries larger than one 16-column matrix-core
+tile: n_query * (Hq / Hkv) > 16, so the query rows of a (sequence, KV head)
+span several query tiles, each streaming the sequence up to its own last
+query (the chunked prefill and many-token draft verification of pgsm §3.2).
+Checked through the C ABI against the oracle's causal chunk attention
+(``decode_attention_multi`` and its int8-key and sliding-window forms) within
+4e-3, every slot no query attends holding NaN; lengths are ragged and put
+query tiles, causal bounds and chunk starts on page edges."""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from _helpers import k8_pool, live_slots, poison
+from workloads import workload
+
+pytestmark = pytest.mark.gpu
+
+TOL = 4e-3
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+
+
+def pkv():
+    import paged_kv_cache_279_amd as m
+    m.lib()
+    return m
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    return t.cpu().numpy()
+
+
+def f16(rng, shape):
+    return rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+
+
+def check_close(got, ref, what, rows=None):
+    got64 = host(got).astype(np.float64) if isinstance(got, torch.Tensor) else got.astype(np.float64)
+    if rows is not None:
+        got64, ref = got64[rows], ref[rows]
+    assert np.all(np.isfinite(got64)), "%s: non-finite output" % what
+    err = np.abs(got64 - ref)
+    say("%s: max_abs_err=%.3e rms=%.3e" % (what, err.max(), math.sqrt(float((err ** 2).mean()))))
+    assert err.max() <= TOL, "%s: max abs error %.3e" % (what, err.max())
+
+
+def chunk_case(rng, B, Hkv, D, P, lens, prefix_pages=0):
+    """Block table (shared prefix pages first when prefix_pages > 0, then
+    private pages in a seeded permutation) and NaN-poisoned pools holding
+    exactly the tokens [0, lens[b]) of every row."""
+    npg = [max(prefix_pages, -(-int(n) // P)) for n in lens]
+    N = prefix_pages + sum(n - prefix_pages for n in npg) + 3
+    perm = rng.permutation(N).astype(np.int32)
+    bt = np.full((B, max(npg)), -1, np.int32)
+    cur = prefix_pages
+    for b in range(B):
+        bt[b, :prefix_pages] = perm[:prefix_pages]
+        bt[b, prefix_pages:npg[b]] = perm[cur:cur + npg[b] - prefix_pages]
+        cur += npg[b] - prefix_pages
+    live = live_slots(N, P, bt, lens)
+    kp = poison(f16(rng, oracle.pool_shape(N, Hkv, P, D)), live, "k")
+    vp = poison(f16(rng, oracle.pool_shape(N, Hkv, P, D)), live, "v")
+    return bt, kp, vp, live, N
+
+
+def ragged_lens(rng, B, base, P):
+    """Lengths past ``base``: the chunk's first position exactly on a page
+    start, on a page's last slot, and random."""
+    lens = base + rng.integers(0, 600, size=B)
+    lens[0] = base + 3 * P                  # first query at a page start (base is a multiple of P)
+    if B > 1:
+        lens[1] = base + 2 * P - 1          # first query on a page's last slot
+    return lens.astype(np.int32)
+
+
+@pytest.mark.parametrize("nq,prefix_pages,part", [
+    (8, 0, 0), (8, 0, 64), (8, 5, 64),
+    (64, 0, 0), (64, 0, 512), (64, 5, 128),
+    (256, 0, 0), (256, 0, 64), (256, 5, 512),
+    (33, 0, 16), (33, 3, 16),               # 33 queries: the last tile holds one query
+])
+def test_chunk_tiles_match_oracle(nq, prefix_pages, part):
+    G, Hkv, D, P = 4, 2, 128, 16
+    Hq = G * Hkv
+    B = 2 if nq >= 256 else 3
+    rng = np.random.default_rng(1000 + nq + 7 * prefix_pages + part)
+    prefix = prefix_pages * P
+    lens = ragged_lens(rng, B, prefix + nq, P)
+    bt, kp, vp, _, N = chunk_case(rng, B, Hkv, D, P, lens, prefix_pages)
+    q = f16(rng, (B, nq, Hq, D))
+    scale = 1 / math.sqrt(D)
+    say("chunk tiles nq=%d G=%d prefix=%d part=%d lens=%s" % (nq, G, prefix, part, lens.tolist()))
+    got = pkv().paged_decode_attention_multi(dev(q), dev(kp), dev(vp), dev(bt), dev(lens), int(lens.max()), scale,
+                                             part, prefix_tokens=prefix)
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention_multi(q, kp, vp, bt, lens, scale, P)
+    check_close(got, ref, "chunk tiles nq=%d prefix=%d part=%d" % (nq, prefix, part))
+
+
+@pytest.mark.parametrize("nq,G,prefix_pages,part", [(64, 4, 0, 0), (64, 4, 0, 128), (40, 4, 4, 64), (24, 2, 0, 32),
+                                                   (12, 16, 0, 64)])
+def test_chunk_tiles_int8_keys_match_oracle(nq, G, prefix_pages, part):
+    Hkv, D, P = 2, 128, 32
+    Hq = G * Hkv
+    B = 3
+    rng = np.random.default_rng(2000 + nq + G + part)
+    prefix = prefix_pages * P
+    lens = ragged_lens(rng, B, prefix + nq, P)
+    bt, _, vp, live, N = chunk_case(rng, B, Hkv, D, P, lens, prefix_pages)
+    pool8 = k8_pool(rng, N, Hkv, P, D, live)
+    q = f16(rng, (B, nq, Hq, D))
+    scale = 1 / math.sqrt(D)
+    say("chunk tiles int8 keys nq=%d G=%d prefix=%d part=%d" % (nq, G, prefix, part))
+    got = pkv().paged_decode_attention_multi_k8(dev(q), dev(pool8), dev(vp), dev(bt), dev(lens), int(lens.max()),
+                                                scale, part, prefix_tokens=prefix)
+    torch.cuda.synchronize()
+    ref = oracle.decode_attention_multi_k8(q, pool8, vp, bt, lens, scale, P)
+    check_close(got, ref, "chunk tiles int8 nq=%d G=%d prefix=%d" % (nq, G, prefix))
+
+
+@pytest.mark.parametrize("nq,G,window,part,k8", [(40, 4, 100, 0, False), (40, 4, 100, 64, False),
+                                                  (20, 8, 49, 32, True), (65, 1, 300, 0, True)])
+def test_chunk_tiles_sliding_window_match_oracle(nq, G, window, part, k8):
+    """Chunks of queries over a ring of pages: each query attends the window
+    ending at itself; the query tiles start at their own first query's
+    window."""
+    Hkv, D, P = 2, 64, 16
+    Hq = G * Hkv
+    B = 3
+    R = -(-(window + nq - 1 - 1) // P) + 2                     # window + nq - 1 <= (R - 1) P + 1
+    rng = np.random.default_rng(3000 + nq + window)
+    N = B * R + 2
+    ring = rng.permutation(N)[:B * R].reshape(B, R).astype(np.int32)
+    lens = np.array([nq + 5, R * P * 3 + 7, window + nq + P], np.int32)   # short of the window, wrapped, just past
+    lo = np.maximum(lens - nq + 1 - window, 0)
+    live = live_slots(N, P, ring, lens, lo=lo)
+    vp = poison(f16(rng, oracle.pool_shape(N, Hkv, P, D)), live, "v")
+    q = f16(rng, (B, nq, Hq, D))
+    scale = 1 / math.sqrt(D)
+    say("chunk tiles window nq=%d G=%d W=%d part=%d int8=%d" % (nq, G, window, part, k8))
+    if k8:
+        pool8 = k8_pool(rng, N, Hkv, P, D, live)
+        got = pkv().paged_decode_attention_window_multi(dev(q), dev(pool8), dev(vp), dev(ring), dev(lens), window,
+                                                        scale, part)
+        ref = oracle.decode_attention_window_multi_k8(q, pool8, vp, ring, lens, window, scale, P)
+    else:
+        kp = poison(f16(rng, oracle.pool_shape(N, Hkv, P, D)), live, "k")
+        got = pkv().paged_decode_attention_window_multi(dev(q), dev(kp), dev(vp), dev(ring), dev(lens), window,
+                                                        scale, part)
+        ref = oracle.decode_attention_window_multi(q, kp, vp, ring, lens, window, scale, P)
+    torch.cuda.synchronize()
+    check_close(got, ref, "chunk tiles window nq=%d W=%d" % (nq, window))
+
+
+@pytest.mark.parametrize("nq", [8, 256])
+def test_chunk_tiles_headline_batch(nq):
+    """The Llama-3-8B GQA batch (64 sequences, 32/8 heads, 2048 shared prefix
+    tokens) with 8 drafted tokens or a 256-token prefill chunk per sequence,
+    in the launch configuration the benchmark times; sampled sequences
+    against the oracle, every row finite."""
+    m = pkv()
+    w = workload(3)
+    prefix = w.shared_prefix_pages * w.P
+    lens = w.lens(0)
+    keep = lens >= prefix + nq
+    lens = np.where(keep, lens, 0).astype(np.int32)                 # a too-short row becomes an idle slot
+    rng = np.random.default_rng(4000 + nq)
+    q = f16(rng, (w.B, nq, w.Hq, w.D))
+    say("chunk tiles headline B=%d nq=%d rows kept %d" % (w.B, nq, int(keep.sum())))
+    got = host(m.paged_decode_attention_multi(dev(q), dev(w.k_pool), dev(w.v_pool), dev(w.block_table), dev(lens),
+                                              int(lens.max()), w.scale, w.partition_tokens, prefix_tokens=prefix))
+    assert np.all(np.isfinite(got.astype(np.float64)))
+    assert np.all(got[~keep] == 0)
+    live = np.nonzero(keep)[0]
+    sample = live[np.linspace(0, len(live) - 1, 3).astype(int)]
+    qi = np.unique(np.array([0, 1, nq // 2, nq - 1]))
+    # query i of a chunk is the single-token decode of its own prefix (the oracle's chunk definition),
+    # computed for the sampled queries only
+    ref = np.stack([oracle.decode_attention(q[sample, i], w.k_pool, w.v_pool, w.block_table[sample],
+                                            lens[sample] - nq + i + 1, w.scale, w.P) for i in qi], axis=1)
+    check_close(got[sample][:, qi], ref, "chunk tiles headline nq=%d" % nq)
+
+
+def test_chunk_tiles_segment_limit():
+    """In split mode a call holds at most 4096 (sequence, query tile)
+    segments; the unsplit path has no such limit."""
+    m = pkv()
+    B, nq, Hq, Hkv, D, P = 65, 256, 8, 2, 64, 16                   # 65 x 64 tiles at G = 4
+    lens = np.full(B, nq, np.int32)
+    bt = np.tile(np.arange(nq // P, dtype=np.int32), (B, 1))
+    pool = torch.zeros(oracle.pool_shape(nq // P, Hkv, P, D), dtype=torch.float16, device="cuda")
+    q = torch.zeros((B, nq, Hq, D), dtype=torch.float16, device="cuda")
+    with pytest.raises(m.PkvError) as e:
+        m.paged_decode_attention_multi(q, pool, pool, dev(bt), dev(lens), nq, 0.125, 64,
+                                       workspace=torch.empty(1 << 20, dtype=torch.uint8, device="cuda"))
+    assert e.value.status == m.PKV_ERR_INVALID_ARG
+    out = m.paged_decode_attention_multi(q, pool, pool, dev(bt), dev(lens), nq, 0.125, 0)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)                                      # zero values: zero output

@@ -65,8 +65,8 @@ def test_copy_on_write_decode_matches_oracle():
     prompt = 40                                     # 2.5 pages: the third page is partly filled
     a = m.PageAllocator(N, P)
     model = PageAllocatorModel(N, P)
-    kp = rng.standard_normal((N, Hkv, P, D)).astype(np.float16)
-    vp = rng.standard_normal((N, Hkv, P, D)).astype(np.float16)
+    kp = rng.standard_normal(oracle.pool_shape(N, Hkv, P, D)).astype(np.float16)
+    vp = rng.standard_normal(oracle.pool_shape(N, Hkv, P, D)).astype(np.float16)
     # sequence 0 holds the prompt; the cache keeps it; sequences 1 and 2 start from the cache
     for alloc in (a, model):
         alloc.reserve(0, prompt)

@@ -17,6 +17,7 @@ import pytest
 import torch
 
 import oracle
+from _helpers import k8_pool, live_slots, poison
 
 pytestmark = pytest.mark.gpu
 
@@ -53,41 +54,6 @@ def host(t):
 
 def f16(rng, shape):
     return rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
-
-
-def poison(pool, live, kind):
-    """NaN into every slot of an fp16 pool that `live` [N][P] does not mark."""
-    n, hkv, p, d = pool.shape
-    pages, slots = np.nonzero(~live)
-    if len(pages) == 0:
-        return pool
-    f = oracle.k_tile_offset if kind == "k" else oracle.v_tile_offset
-    off = f(slots[:, None], np.arange(d)[None, :], p, d)
-    tiles = pool.reshape(n, hkv, p * d)
-    for kvh in range(hkv):
-        tiles[pages[:, None], kvh, off] = np.nan
-    return pool
-
-
-def live_slots(N, P, table, lens, lo=None):
-    """[N][P] mask of the slots holding tokens [lo[b], lens[b]) of each row
-    (table columns taken modulo the table width, as a ring does)."""
-    live = np.zeros((N, P), dtype=bool)
-    R = table.shape[1]
-    for b in range(table.shape[0]):
-        start = 0 if lo is None else int(lo[b])
-        t = np.arange(start, max(int(lens[b]), start))
-        if len(t):
-            live[table[b, (t // P) % R], t % P] = True
-    return live
-
-
-def k8_pool(rng, N, Hkv, P, D, live):
-    codes = rng.integers(-127, 128, size=(N, Hkv, P // 16, 16 * D)).astype(np.int8).view(np.uint8)
-    scales = (np.abs(rng.standard_normal((N, Hkv, P // 16, 16))) * 0.05 + 0.005).astype(np.float32)
-    dead = ~live.reshape(N, 1, P // 16, 16)
-    scales = np.where(np.broadcast_to(dead, scales.shape), np.float32(np.nan), scales)
-    return np.ascontiguousarray(np.concatenate([codes, scales.view(np.uint8)], axis=-1))
 
 
 def make_case(i):
@@ -206,7 +172,7 @@ def run_case(c, i):
         attended = lens - 1 if fused else lens
         lo = np.maximum(lens - nq + 1 - W, 0)                        # the first query's window start
         live = live_slots(N, P, ring, attended, lo)
-        vp = poison(f16(rng, (N, Hkv, P, D)), live, "v")
+        vp = poison(f16(rng, oracle.pool_shape(N, Hkv, P, D)), live, "v")
         q = f16(rng, (B, Hq, D))
         width = max(1, -(-int(lens.max()) // P))
         logical = np.ascontiguousarray(ring[:, np.arange(width) % R])
@@ -218,7 +184,7 @@ def run_case(c, i):
                                                             scale, part)
                 ref = oracle.decode_attention_window_multi_k8(q, pool8, vp, ring, lens, W, scale, P)
             else:
-                kp = poison(f16(rng, (N, Hkv, P, D)), live, "k")
+                kp = poison(f16(rng, oracle.pool_shape(N, Hkv, P, D)), live, "k")
                 got = m.paged_decode_attention_window_multi(dev(q), dev(kp), dev(vp), dev(ring), dev(lens), W,
                                                             scale, part)
                 ref = oracle.decode_attention_window_multi(q, kp, vp, ring, lens, W, scale, P)
@@ -240,7 +206,7 @@ def run_case(c, i):
             ref = oracle.decode_attention_window_k8(q, pool8, vp, ring, lens, W, scale, P)
             check(host(got), ref, what + " R=%d W=%d" % (R, W))
             return
-        kp = poison(f16(rng, (N, Hkv, P, D)), live, "k")
+        kp = poison(f16(rng, oracle.pool_shape(N, Hkv, P, D)), live, "k")
         kd, vd = dev(kp), dev(vp)
         if fused:
             kn, vn = f16(rng, (B, Hkv, D)), f16(rng, (B, Hkv, D))
@@ -261,7 +227,7 @@ def run_case(c, i):
     live = live_slots(N, P, bt, np.maximum(attended, 0))
     if prefix:
         live[bt[0, :prefix // P], :] = True
-    vp = poison(f16(rng, (N, Hkv, P, D)), live, "v")
+    vp = poison(f16(rng, oracle.pool_shape(N, Hkv, P, D)), live, "v")
 
     if mode.startswith("k8"):
         pool8 = k8_pool(rng, N, Hkv, P, D, live)
@@ -289,7 +255,7 @@ def run_case(c, i):
         check(host(got), ref, what)
         return
 
-    kp = poison(f16(rng, (N, Hkv, P, D)), live, "k")
+    kp = poison(f16(rng, oracle.pool_shape(N, Hkv, P, D)), live, "k")
     kd, vd = dev(kp), dev(vp)
     if mode.startswith("multi"):
         q = f16(rng, (B, nq, Hq, D))

@@ -47,8 +47,8 @@ def ring_case(seed, B, Hq, Hkv, D, P, R, lens, window, extra_pages=3):
     rng = np.random.default_rng(seed)
     N = B * R + extra_pages
     ring = rng.permutation(N)[:B * R].reshape(B, R).astype(np.int32)
-    kp = rng.standard_normal((N, Hkv, P, D), dtype=np.float32).astype(np.float16)
-    vp = rng.standard_normal((N, Hkv, P, D), dtype=np.float32).astype(np.float16)
+    kp = rng.standard_normal(oracle.pool_shape(N, Hkv, P, D), dtype=np.float32).astype(np.float16)
+    vp = rng.standard_normal(oracle.pool_shape(N, Hkv, P, D), dtype=np.float32).astype(np.float16)
     q = rng.standard_normal((B, Hq, D), dtype=np.float32).astype(np.float16)
     live = np.zeros((N, P), dtype=bool)
     for b in range(B):
@@ -189,7 +189,7 @@ def test_window_k8_matches_oracle(part, fused):
     scales = (np.abs(rng.standard_normal((N, Hkv, P // 16, 16))) * 0.05 + 0.005).astype(np.float32)
     scales = np.where(np.broadcast_to(~live.reshape(N, 1, P // 16, 16), scales.shape), np.float32(np.nan), scales)
     pool8 = np.ascontiguousarray(np.concatenate([codes, scales.view(np.uint8)], axis=-1))
-    vp = rng.standard_normal((N, Hkv, P, D), dtype=np.float32).astype(np.float16)
+    vp = rng.standard_normal(oracle.pool_shape(N, Hkv, P, D), dtype=np.float32).astype(np.float16)
     pages, slots = np.nonzero(~live)
     tiles = vp.reshape(N, Hkv, P * D)
     off = orc.v_tile_offset(slots[:, None], np.arange(D)[None, :], P, D)
@@ -235,8 +235,8 @@ def test_window_chunks_match_oracle(nq, part, k8):
     for b in range(B):
         t = np.arange(lo[b], before[b])
         live[ring[b, (t // P) % R], t % P] = True
-    vp = rng.standard_normal((N, Hkv, P, D), dtype=np.float32).astype(np.float16)
-    kp = rng.standard_normal((N, Hkv, P, D), dtype=np.float32).astype(np.float16)
+    vp = rng.standard_normal(oracle.pool_shape(N, Hkv, P, D), dtype=np.float32).astype(np.float16)
+    kp = rng.standard_normal(oracle.pool_shape(N, Hkv, P, D), dtype=np.float32).astype(np.float16)
     pages, slots = np.nonzero(~live)
     for pool, f in ((kp, orc.k_tile_offset), (vp, orc.v_tile_offset)):
         tiles = pool.reshape(N, Hkv, P * D)

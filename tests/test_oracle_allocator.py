@@ -114,6 +114,17 @@ def test_validate_tables_detects_problems():
     assert validate_tables(shared, [20, 20], 16, 3, exclusive_tail=True) == []
     assert validate_tables(shared, [16, 20], 16, 3, exclusive_tail=True) == [("shared_tail_page", 0, 0)]
     assert validate_tables(shared, [16, 20], 16, 3) == []
+    # shared prefix (dpshk §4.2): every attended row holds it in the same pages; idle rows hold anything
+    pre = np.array([[-1, -1, -1], [0, 1, 2], [0, 1, 3], [0, 4, 5]], np.int32)
+    assert validate_tables(pre[:3], [0, 40, 40], 16, 6, prefix_tokens=32) == []
+    assert validate_tables(pre, [0, 40, 40, 40], 16, 6, prefix_tokens=32) == [("prefix_differs", 3, 1)]
+    assert validate_tables(pre[:3], [0, 40, 20], 16, 6, prefix_tokens=32) == [("shorter_than_prefix", 2, -1)]
+    # rings (hotelren §3.2): the entries the window reaches, in token order
+    ring = np.array([[0, 1, 2]], np.int32)
+    assert validate_tables(ring, [100], 16, 3, window=33) == []
+    assert validate_tables(np.array([[0, 1, 9]], np.int32), [100], 16, 3, window=33) == [("page_out_of_range", 0, 2)]
+    assert validate_tables(np.array([[9, 1, 2]], np.int32), [96], 16, 3, window=17) == []
+    assert validate_tables(np.array([[1, 1, 2]], np.int32), [100], 16, 3, window=33) == [("duplicate_in_row", 0, 0)]
 
 
 # ---------------------------------------------------------------------------

@@ -81,7 +81,7 @@ def test_format_is_a_bijection(D):
 
 
 def _paged_fp16_pool(rng, N, Hkv, P, D):
-    return _fp16(rng.standard_normal((N, Hkv, P, D)))
+    return _fp16(rng.standard_normal(oracle.pool_shape(N, Hkv, P, D)))
 
 
 @pytest.mark.parametrize("P,D", [(16, 64), (32, 128)])
@@ -252,6 +252,8 @@ def _check_multi_k8(fn, seed=21):
     np.testing.assert_array_equal(one[:, 0], oracle.decode_attention_k8(q[:, -1], pool8, vp, bt, lens, 0.125, P))
     short = fn(q, pool8, vp, bt, np.array([k - 1, 41], np.int32), 0.125, P)
     assert np.all(np.isnan(short[0])) and np.all(np.isfinite(short[1]))
+    idle = fn(q, pool8, vp, bt, np.array([0, 41], np.int32), 0.125, P)      # an idle batch slot
+    assert np.all(idle[0] == 0) and np.array_equal(idle[1], got[1])
 
 
 def test_multi_k8_brute_force():
@@ -259,11 +261,13 @@ def test_multi_k8_brute_force():
 
 
 @pytest.mark.parametrize("old,new", [
-    ("li = np.where(short, 0, lens64 - k + i + 1)\n        out[:, i] = decode_attention_k8",
-     "li = np.where(short, 0, lens64 - k + i)\n        out[:, i] = decode_attention_k8"),
+    ("li = np.where(lens64 < k, 0, lens64 - k + i + 1)\n        out[:, i] = decode_attention_k8",
+     "li = np.where(lens64 < k, 0, lens64 - k + i)\n        out[:, i] = decode_attention_k8"),
     ("out[:, i] = decode_attention_k8(q[:, i],", "out[:, i] = decode_attention_k8(q[:, k - 1 - i],"),
-    ("short = lens64 < k                  # the chunk would reach before token 0: the whole row is invalid\n    for i in range(k):\n        li = np.where(short, 0, lens64 - k + i + 1)\n        out[:, i] = decode_attention_k8",
-     "short = lens64 < 1                  # the chunk would reach before token 0: the whole row is invalid\n    for i in range(k):\n        li = np.where(short, 0, lens64 - k + i + 1)\n        out[:, i] = decode_attention_k8"),
+    ("short = (lens64 < k) & (lens64 != 0)\n    for i in range(k):\n        li = np.where(lens64 < k, 0, lens64 - k + i + 1)\n        out[:, i] = decode_attention_k8",
+     "short = (lens64 < 1) & (lens64 != 0)\n    for i in range(k):\n        li = np.where(lens64 < k, 0, lens64 - k + i + 1)\n        out[:, i] = decode_attention_k8"),
+    ("short = (lens64 < k) & (lens64 != 0)\n    for i in range(k):\n        li = np.where(lens64 < k, 0, lens64 - k + i + 1)\n        out[:, i] = decode_attention_k8",
+     "short = lens64 < k\n    for i in range(k):\n        li = np.where(lens64 < k, 0, lens64 - k + i + 1)\n        out[:, i] = decode_attention_k8"),
 ])
 def test_multi_k8_planted_mistake_is_caught(old, new):
     src = open(quant_k8.__file__).read()

@@ -87,3 +87,7 @@ def test_causality_within_the_chunk():
     short[0] = 2
     nanrows = oracle.decode_attention_multi(qm, kp, vp, bt, short, 0.3, P)
     assert np.all(np.isnan(nanrows[0])) and np.array_equal(nanrows[1], base[1])
+    # length 0 is an idle batch slot: zero rows, the others untouched
+    short[0] = 0
+    idle = oracle.decode_attention_multi(qm, kp, vp, bt, short, 0.3, P)
+    assert np.all(idle[0] == 0) and np.array_equal(idle[1], base[1])

@@ -96,8 +96,8 @@ def make_paged_case(rng, B, Hq, Hkv, D, P, lens, spare_pages=3, poison=True):
     N = need + spare_pages
     perm = rng.permutation(N)
     fill = np.nan if poison else 0.0
-    k_pool = np.full((N, Hkv, P, D), fill, dtype=np.float16)
-    v_pool = np.full((N, Hkv, P, D), fill, dtype=np.float16)
+    k_pool = np.full(oracle.pool_shape(N, Hkv, P, D), fill, dtype=np.float16)
+    v_pool = np.full(oracle.pool_shape(N, Hkv, P, D), fill, dtype=np.float16)
     bt = np.full((B, max_pages), -1, dtype=np.int32)
     K = []
     V = []
@@ -257,8 +257,8 @@ def test_page_size_is_invisible():
         npg = [-(-n // P) for n in lens]
         N = sum(npg) + 1
         perm = np.random.default_rng(P).permutation(N)
-        kp = np.full((N, Hkv, P, D), np.nan, np.float16)
-        vp = np.full((N, Hkv, P, D), np.nan, np.float16)
+        kp = np.full(oracle.pool_shape(N, Hkv, P, D), np.nan, np.float16)
+        vp = np.full(oracle.pool_shape(N, Hkv, P, D), np.nan, np.float16)
         bt = np.full((B, max(npg)), -1, np.int32)
         cur = 0
         for b, n in enumerate(lens):
@@ -297,7 +297,7 @@ def test_tile_layout_keeps_16_byte_runs():
 
 def test_write_then_read_token_roundtrip():
     rng = np.random.default_rng(3)
-    pool = np.zeros((3, 2, 32, 64), np.float16)
+    pool = np.zeros(oracle.pool_shape(3, 2, 32, 64), np.float16)
     vec = rng.standard_normal(64).astype(np.float16)
     for kind in ("k", "v"):
         oracle.write_token(pool, 2, 1, 17, vec, kind)

@@ -23,8 +23,8 @@ def _ring_case(rng, B, Hkv, D, P, R, lens, extra_pages=2):
     N = B * R + extra_pages
     perm = rng.permutation(N)
     ring = perm[:B * R].reshape(B, R).astype(np.int32)
-    kp = np.full((N, Hkv, P, D), np.nan, np.float16)
-    vp = np.full((N, Hkv, P, D), np.nan, np.float16)
+    kp = np.full(oracle.pool_shape(N, Hkv, P, D), np.nan, np.float16)
+    vp = np.full(oracle.pool_shape(N, Hkv, P, D), np.nan, np.float16)
     K, V = [], []
     for b in range(B):
         n = int(lens[b])
@@ -129,3 +129,5 @@ def test_window_chunks_brute_force(k, W, R):
     short = oracle.decode_attention_window_multi(q, kp, vp, ring, np.array([k - 1, 40], np.int32), W, 0.2, P)
     if k > 1:
         assert np.all(np.isnan(short[0])) and np.all(np.isfinite(short[1]))
+    idle = oracle.decode_attention_window_multi(q, kp, vp, ring, np.array([0, 40], np.int32), W, 0.2, P)
+    assert np.all(idle[0] == 0) and np.array_equal(idle[1], short[1])

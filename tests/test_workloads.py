@@ -74,4 +74,4 @@ def test_sliding_window_workload_ring():
     assert R == 257 and (R - 1) * w.P + 1 >= w.window
     assert w.N == w.B * R and sorted(w.block_table.ravel().tolist()) == list(range(w.N))
     assert w.context.min() >= w.window and w.context.max() <= 8 * w.window and w.steps == 1
-    assert w.k_pool.shape == (w.N, 8, 16, 128)
+    assert w.k_pool.shape == (w.N, 8, 1, 16 * 128)

@@ -61,8 +61,8 @@ class DecodeWorkload:
     N: int
     scale: float
     q: np.ndarray            # fp16 [B][Hq][D]
-    k_pool: np.ndarray       # fp16 [N][Hkv][P][D]
-    v_pool: np.ndarray       # fp16 [N][Hkv][P][D]
+    k_pool: np.ndarray       # fp16 storage [N][Hkv][P/16][16*D] (tile layout of the oracle)
+    v_pool: np.ndarray       # fp16 storage [N][Hkv][P/16][16*D]
     block_table: np.ndarray  # int32 [B][max_pages], -1 where unused
     context: np.ndarray      # int32 [B] tokens cached before the first step
     k_new: np.ndarray        # fp16 [steps][B][Hkv][D] (steps may be 0)
@@ -138,8 +138,8 @@ def _build(name, rng, seed, B, Hq, Hkv, D, P, context, tokens_needed, steps, sca
         bt[b, prefix_pages:prefix_pages + private_pages[b]] = perm[cursor:cursor + private_pages[b]]
         cursor += private_pages[b]
     q = _normal_fp16(seed, 1, (B, Hq, D))
-    k_pool = _normal_fp16(seed, 2, (n_pages, Hkv, P, D))
-    v_pool = _normal_fp16(seed, 3, (n_pages, Hkv, P, D))
+    k_pool = _normal_fp16(seed, 2, (n_pages, Hkv, P // 16, 16 * D))
+    v_pool = _normal_fp16(seed, 3, (n_pages, Hkv, P // 16, 16 * D))
     k_new = _normal_fp16(seed, 4, (steps, B, Hkv, D))
     v_new = _normal_fp16(seed, 5, (steps, B, Hkv, D))
     return DecodeWorkload(name=name, B=B, Hq=Hq, Hkv=Hkv, D=D, P=P, N=n_pages, scale=scale,
@@ -163,8 +163,8 @@ def workload(number, page_size=None, seed=None, batch=None):
         perm = rng.permutation(n_pages).astype(np.int32)
         bt = np.stack([perm[16 * b:16 * b + 16] for b in range(B)]).astype(np.int32)
         q = _normal_fp16(seed, 1, (B, Hq, D))
-        k_pool = _normal_fp16(seed, 2, (n_pages, Hkv, P, D))
-        v_pool = _normal_fp16(seed, 3, (n_pages, Hkv, P, D))
+        k_pool = _normal_fp16(seed, 2, (n_pages, Hkv, P // 16, 16 * D))
+        v_pool = _normal_fp16(seed, 3, (n_pages, Hkv, P // 16, 16 * D))
         empty = np.zeros((0, B, Hkv, D), dtype=np.float16)
         return DecodeWorkload("tiny", B, Hq, Hkv, D, P, n_pages, 1.0 / math.sqrt(D), q, k_pool, v_pool,
                               bt, context.astype(np.int32), empty, empty.copy(), perm=perm)
@@ -200,8 +200,8 @@ def workload(number, page_size=None, seed=None, batch=None):
         perm = rng.permutation(n_pages).astype(np.int32)
         ring = perm.reshape(B, R).copy()
         q = _normal_fp16(seed, 1, (B, 32, 128))
-        k_pool = _normal_fp16(seed, 2, (n_pages, 8, P, 128))
-        v_pool = _normal_fp16(seed, 3, (n_pages, 8, P, 128))
+        k_pool = _normal_fp16(seed, 2, (n_pages, 8, P // 16, 16 * 128))
+        v_pool = _normal_fp16(seed, 3, (n_pages, 8, P // 16, 16 * 128))
         k_new = _normal_fp16(seed, 4, (1, B, 8, 128))
         v_new = _normal_fp16(seed, 5, (1, B, 8, 128))
         return DecodeWorkload("sliding-window-4096", B, 32, 8, 128, P, n_pages, 1.0 / math.sqrt(128), q, k_pool,
