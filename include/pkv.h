@@ -72,7 +72,8 @@ typedef enum pkv_status {
   PKV_ERR_HIP = 5,                  /* a kernel launch failed */
   PKV_ERR_INVALID_TABLE = 6,        /* pkv_validate_tables found a bad entry */
   PKV_ERR_NOT_FOUND = 7,            /* pkv_alloc_cache_lookup: no entry under the key */
-  PKV_ERR_HOST_MEMORY = 8           /* the host allocator's own bookkeeping could not grow */
+  PKV_ERR_HOST_MEMORY = 8,          /* the host allocator's own bookkeeping could not grow */
+  PKV_ERR_SCRATCH_LIMIT = 9         /* a call needs more than the fixed scratch of the no-allocation entry */
 } pkv_status;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -290,6 +291,36 @@ int pkv_paged_decode_attention_shared_prefix(void* out, const void* q, const voi
                                              int32_t Hkv, int32_t D, int32_t P, int32_t N, int32_t max_context,
                                              float scale, int32_t partition_tokens, int32_t prefix_tokens,
                                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * pkv_paged_decode_attention_shared_prefix_noalloc -- for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): pkv_paged_decode_attention_shared_prefix
+ * without a workspace argument. The split path's partials and per-segment
+ * prefix sums go to a fixed array of pkv_noalloc_scratch_bytes() (32 MiB)
+ * that the library holds in every GPU it runs on until the process ends; its
+ * device address is looked up on the first call on each device. The call
+ * allocates nothing (no hipMalloc, no library allocation); the caller passes
+ * the inputs and the output as for the workspace entry point, with the same
+ * result bit for bit (same kernels, same schedule).
+ * The array keeps the last call's contents; no part of it needs clearing
+ * (every word a call reads was written earlier in the same call). Calls on
+ * one GPU share the array, so calls that overlap in time on one GPU (other
+ * streams, other host threads) race: order them on one stream.
+ * Errors: as pkv_paged_decode_attention_shared_prefix, with
+ * PKV_ERR_SCRATCH_LIMIT (nothing launched) when the split path needs more
+ * than the fixed array (the Llama-3-8B GQA batch of 64 sequences needs about
+ * 14 MB); PKV_ERR_HIP if the array's address cannot be found.
+ */
+int pkv_paged_decode_attention_shared_prefix_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                                                     void* k_pool, void* v_pool, const int32_t* block_table,
+                                                     int32_t max_pages, const int32_t* lens, int32_t B, int32_t Hq,
+                                                     int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                                                     int32_t max_context, float scale, int32_t partition_tokens,
+                                                     int32_t prefix_tokens, void* stream);
+
+/* Bytes of the fixed scratch array of the no-allocation entry point. */
+size_t pkv_noalloc_scratch_bytes(void);
 
 /*
  * pkv_paged_decode_attention_multi -- attention for a chunk of the last

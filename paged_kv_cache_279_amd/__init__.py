@@ -15,6 +15,7 @@ from .binding import (  # noqa: F401
     PKV_ERR_INVALID_TABLE,
     PKV_ERR_NOT_FOUND,
     PKV_ERR_HOST_MEMORY,
+    PKV_ERR_SCRATCH_LIMIT,
     PkvError,
     PageAllocator,
     append_paged_decode_attention,
@@ -34,6 +35,8 @@ from .binding import (  # noqa: F401
     paged_decode_attention_multi,
     paged_decode_attention_multi_k8,
     paged_decode_attention_shared_prefix,
+    paged_decode_attention_shared_prefix_noalloc,
+    noalloc_scratch_bytes,
     paged_decode_attention_window,
     paged_decode_attention_window_multi,
     paged_decode_attention_window_k8,

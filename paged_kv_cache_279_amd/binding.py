@@ -26,6 +26,7 @@ PKV_ERR_HIP = 5
 PKV_ERR_INVALID_TABLE = 6
 PKV_ERR_NOT_FOUND = 7
 PKV_ERR_HOST_MEMORY = 8
+PKV_ERR_SCRATCH_LIMIT = 9
 
 _i32 = ctypes.c_int32
 _vp = ctypes.c_void_p
@@ -78,6 +79,10 @@ _SIGNATURES = {
     "pkv_paged_decode_attention_shared_prefix": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _i32,
                                                                 _i32, _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
                                                                 _i32, _i32, _vp, ctypes.c_size_t, _vp]),
+    "pkv_paged_decode_attention_shared_prefix_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp,
+                                                                        _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                                                        ctypes.c_float, _i32, _i32, _vp]),
+    "pkv_noalloc_scratch_bytes": (ctypes.c_size_t, []),
     "pkv_alloc_create": (ctypes.c_int, [_i32, _i32, _ip, ctypes.POINTER(_vp)]),
     "pkv_alloc_destroy": (None, [_vp]),
     "pkv_alloc_reserve": (ctypes.c_int, [_vp, _i32, _i32, _ip, _i32, _ip]),
@@ -276,6 +281,42 @@ def kv_append_chunk(k_new, v_new, k_pool, v_pool, block_table, pos, stream=None)
                                    _dev_ptr(pos, torch.int32, "pos"), B, int(k_new.shape[1]), Hkv, D, P, N,
                                    _stream(stream))
     _check(rc, "pkv_kv_append_chunk")
+
+
+def paged_decode_attention_shared_prefix_noalloc(q, k_pool, v_pool, block_table, lens, max_context, scale,
+                                                 partition_tokens, prefix_tokens, out, k_new=None, v_new=None,
+                                                 stream=None):
+    """pkv_paged_decode_attention_shared_prefix_noalloc: the shared-prefix call with the split
+    partials in the library's fixed scratch array; ``out`` (fp16 [B][Hq][D]) must be given --
+    nothing is allocated."""
+    B, Hq, D = q.shape
+    N, Hkv, P, _ = _f16_pool(k_pool, "k_pool", int(D))
+    _, max_pages = block_table.shape
+    if tuple(v_pool.shape) != tuple(k_pool.shape) or block_table.shape[0] != B or tuple(lens.shape) != (B,):
+        raise ValueError("shape mismatch")
+    if out is None or tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be given, [B][Hq][D]")
+    if (k_new is None) != (v_new is None):
+        raise ValueError("give both k_new and v_new, or neither")
+    if k_new is not None:
+        if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+            raise ValueError("k_new/v_new must be [B][Hkv][D]")
+        kn, vn = _dev_ptr(k_new, torch.float16, "k_new"), _dev_ptr(v_new, torch.float16, "v_new")
+    else:
+        kn, vn = ctypes.c_void_p(0), ctypes.c_void_p(0)
+    rc = lib().pkv_paged_decode_attention_shared_prefix_noalloc(
+        _dev_ptr(out, torch.float16, "out"), _dev_ptr(q, torch.float16, "q"), kn, vn,
+        _dev_ptr(k_pool, torch.float16, "k_pool"), _dev_ptr(v_pool, torch.float16, "v_pool"),
+        _dev_ptr(block_table, torch.int32, "block_table"), max_pages, _dev_ptr(lens, torch.int32, "lens"),
+        B, Hq, Hkv, D, P, N, int(max_context), float(scale), int(partition_tokens), int(prefix_tokens),
+        _stream(stream))
+    _check(rc, "pkv_paged_decode_attention_shared_prefix_noalloc")
+    return out
+
+
+def noalloc_scratch_bytes():
+    """pkv_noalloc_scratch_bytes: size of the no-allocation entry point's fixed scratch array."""
+    return int(lib().pkv_noalloc_scratch_bytes())
 
 
 def paged_decode_attention_multi(q, k_pool, v_pool, block_table, lens, max_context, scale, partition_tokens=0,

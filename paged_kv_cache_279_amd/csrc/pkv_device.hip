@@ -40,6 +40,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 #include <vector>
 
 #include "pkv.h"
@@ -1475,7 +1476,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
                   const int32_t* lens, int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t P, int32_t N,
                   int32_t max_context, float scale, int32_t partition_tokens, int32_t prefix_tokens,
                   void* workspace, size_t workspace_bytes, void* stream, bool fused, bool k8 = false,
-                  int32_t nq = 1, int32_t window = 0) {
+                  int32_t nq = 1, int32_t window = 0, int too_small = PKV_ERR_WORKSPACE_TOO_SMALL) {
   // an armed measurement hook belongs to this call, whatever it returns
   t_prof_call[0] = t_prof_armed[0];
   t_prof_call[1] = t_prof_armed[1];
@@ -1564,7 +1565,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
     const WsLayout ws = ws_layout(plan.segments, D, plan.slots);
     if (!workspace) return PKV_ERR_INVALID_ARG;
     if (!aligned(workspace, kWsAlign)) return PKV_ERR_INVALID_ARG;
-    if (workspace_bytes < ws.total) return PKV_ERR_WORKSPACE_TOO_SMALL;
+    if (workspace_bytes < ws.total) return too_small;
     char* base = static_cast<char*>(workspace);
     prm.flat_hdr = reinterpret_cast<int32_t*>(base + ws.hdr_off);
     prm.flat_cum = reinterpret_cast<int32_t*>(base + ws.cum_off);
@@ -1606,6 +1607,35 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
     }
     if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   }
+  return PKV_OK;
+}
+
+// Scratch of the entry point that allocates nothing: the split path's
+// partials and prefix sums in a fixed device array instead of a caller
+// workspace. Each GPU the library runs on holds its own copy until the
+// process ends. Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in): its device address is looked up once per
+// device with that device current and kept.
+constexpr size_t kScratchBytes = size_t{32} << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return PKV_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return PKV_ERR_UNSUPPORTED;
+  void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return PKV_ERR_HIP;
+      g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
   return PKV_OK;
 }
 
@@ -1941,5 +1971,27 @@ int pkv_paged_decode_attention_shared_prefix(void* out, const void* q, const voi
                        Hkv, D, P, N, max_context, scale, partition_tokens, prefix_tokens, workspace, workspace_bytes,
                        stream, fused);
 }
+
+int pkv_paged_decode_attention_shared_prefix_noalloc(void* out, const void* q, const void* k_new, const void* v_new,
+                                                     void* k_pool, void* v_pool, const int32_t* block_table,
+                                                     int32_t max_pages, const int32_t* lens, int32_t B, int32_t Hq,
+                                                     int32_t Hkv, int32_t D, int32_t P, int32_t N,
+                                                     int32_t max_context, float scale, int32_t partition_tokens,
+                                                     int32_t prefix_tokens, void* stream) {
+  if ((k_new == nullptr) != (v_new == nullptr)) return PKV_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  if (partition_tokens > 0 && B > 0) {
+    const int rc = scratch_address(&ws);
+    if (rc != PKV_OK) return rc;
+    ws_bytes = kScratchBytes;
+  }
+  const bool fused = k_new != nullptr;
+  return decode_common(out, q, k_new, v_new, k_pool, v_pool, k_pool, v_pool, block_table, max_pages, lens, B, Hq,
+                       Hkv, D, P, N, max_context, scale, partition_tokens, prefix_tokens, ws, ws_bytes, stream, fused,
+                       false, 1, 0, PKV_ERR_SCRATCH_LIMIT);
+}
+
+size_t pkv_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 }  // extern "C"

@@ -120,6 +120,7 @@ const char* pkv_status_string(int status) {
     case PKV_ERR_INVALID_TABLE: return "PKV_ERR_INVALID_TABLE";
     case PKV_ERR_NOT_FOUND: return "PKV_ERR_NOT_FOUND";
     case PKV_ERR_HOST_MEMORY: return "PKV_ERR_HOST_MEMORY";
+    case PKV_ERR_SCRATCH_LIMIT: return "PKV_ERR_SCRATCH_LIMIT";
     default: return "PKV_ERR_UNKNOWN";
   }
 }
