@@ -454,6 +454,9 @@ def main():
     layer_step(0, 0)
     torch.cuda.synchronize()
     got = out.cpu().numpy().astype(np.float64)
+    # the split schedule's header (private blocks per KV head, then the private
+    # and prefix blocks per workgroup piece) as the partition kernel left it
+    sched = workspace[:12].view(torch.int32).cpu().numpy().tolist() if part > 0 else None
     sample = np.linspace(0, B - 1, min(B, args.check_sequences)).astype(int)
     if KQ > 1:
         got = out_mq.cpu().numpy().astype(np.float64)
@@ -639,18 +642,27 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f16",
         "data": "synthetic",
         "config": {
             "workload": w.name,
             "batch": B, "q_heads": Hq, "kv_heads": Hkv, "head_dim": D, "page_size": P,
             "kv_dtype": "k int8 + fp32 scale per token and head, v f16" if k8 else "f16", "accumulate": "f32",
+            "arithmetic": "matrix-core products on f16 operands (q, K, V and the softmax weights P rounded to f16; int8 "
+                          "key codes widened to f16 exactly) with f32 accumulation; softmax statistics and the "
+                          "log-sum-exp merge in f32; f16 output",
             "mean_context": float(np.mean(w.context + KQ * (args.warmup + 1 + (args.steps - 1) / 2))),
             "queries_per_sequence": KQ,
             "window_tokens": W or None,
             "ring_pages": max_pages if W else None,
             "shared_prefix_tokens": prefix_pages * P,
             "partition_tokens": part,
+            "split_schedule": None if sched is None else {
+                "private_blocks_per_kv_head": sched[0],
+                "private_piece_blocks": sched[1], "private_piece_tokens": sched[1] * 16,
+                "prefix_piece_blocks": sched[2] if prefix_tokens else None,
+                "note": "partition_tokens is the minimum piece; each workgroup takes one piece of this many "
+                        "16-token blocks from each work list (pieces may cross sequence boundaries)"},
             "layers_per_step": R,
             "append": "fused" if fused else "separate",
             "launch": "eager" if graph is None else "hip graph per step (%d layer calls)" % R,

@@ -217,8 +217,11 @@ int pkv_paged_decode_attention(void* out, const void* q, const void* k_pool, con
  * pkv_paged_decode_attention(...): the new token is part of the context it
  * attends to (hotelren §3.1: write the new K/V at the end, then attend). The
  * wave that streams the block holding the new token takes its K/V from k_new /
- * v_new into registers, uses them there and writes them to the pool, saving
- * a launch per step.
+ * v_new into registers and uses them there, saving a launch per step. The
+ * pool write itself goes to the merge launch that follows in split mode
+ * (stores issued while every compute unit streams reads cost microseconds)
+ * and to the streaming wave when unsplit; either way it is done when the
+ * call's work on the stream is.
  * lens[b] >= 1 is the context after the append; lens[b] == 0 writes a zero
  * row and appends nothing. Arguments as in the two calls above.
  */
@@ -458,7 +461,7 @@ int pkv_paged_decode_attention_multi_shared_prefix(void* out, const void* q, con
  * block is one token's D keys of one KV head, with its own fp32 scale: appends
  * never rewrite older tokens (pgsm §4.3), so a page-wide scale would have to
  * clip later tokens. Per token and KV head: scale = amax / 127 and
- * code = rint(k / scale) (IEEE fp32, half to even; amax == 0 gives scale 0,
+ * code = rint(k * (127 / amax)) (IEEE fp32, half to even; amax == 0 gives scale 0,
  * codes 0); the dequantised key is code * scale.
  *
  * int8-key pool: bytes [N][Hkv][P / 16][16 * D + 64]. A 16-token sub-block holds

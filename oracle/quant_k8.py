@@ -13,10 +13,12 @@ block nor the rounding, so this library reads them as follows:
   fp32 scale. Appends write a token once and never touch older tokens
   (pgsm §4.3), so a scale shared by a whole page would have to be fixed before
   the page's later tokens exist (clipping them) or rewritten with them;
-* symmetric int8: ``scale = amax / 127`` and ``code = rint(k / scale)`` with
-  round-half-to-even, both in IEEE fp32 arithmetic (the kernel's precision:
-  where a float decides an integer, both sides decide it the same way);
-  ``amax == 0`` gives scale 0 and all-zero codes;
+* symmetric int8: ``scale = amax / 127`` and ``code = rint(k * (127 / amax))``
+  with round-half-to-even, in IEEE fp32 arithmetic (the kernel's precision:
+  where a float decides an integer, both sides decide it the same way); the
+  reciprocal ``127 / amax`` is rounded to fp32 once per token, so a kernel
+  needs one division per token rather than one per element; ``amax == 0``
+  gives scale 0 and all-zero codes;
 * the dequantised key is ``code * scale``; attention is then computed exactly
   as for fp16 keys (``decode_attention``), in fp64.
 
@@ -65,16 +67,18 @@ def k8_scale_offset(u, head_dim):
 def quantize_k(vec):
     """Symmetric int8 codes and the fp32 scale of one token's key vector.
 
-    ``scale = amax / 127`` and ``code = rint(k / scale)`` (half to even) in IEEE
-    fp32, so that a kernel doing the same fp32 operations reaches the same
-    codes; ``amax == 0`` gives scale 0 and zero codes.
+    ``scale = amax / 127`` and ``code = rint(k * inv)`` (half to even) with
+    ``inv = 127 / amax``, each operation in IEEE fp32, so that a kernel doing
+    the same fp32 operations reaches the same codes; ``amax == 0`` gives scale
+    0 and zero codes.
     """
     k = np.asarray(vec).astype(np.float32)
     amax = np.float32(np.abs(k).max()) if k.size else np.float32(0.0)
     if amax == 0:
         return np.zeros(k.shape, np.int8), np.float32(0.0)
     scale = np.float32(amax / np.float32(127.0))
-    codes = np.rint(k / scale)
+    inv = np.float32(np.float32(127.0) / amax)
+    codes = np.rint(k * inv)
     return np.clip(codes, -127, 127).astype(np.int8), scale
 
 

@@ -61,7 +61,7 @@ constexpr int kBlk = 16;                   // tokens per block (= one sub-block)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr size_t kWsAlign = 256;
 constexpr int32_t kMaxPartitions = 1024;   // partial slots per (sequence, head) (reduce kernel LDS)
-constexpr uint32_t kWaveMergeRows = 4096;  // output rows from which the one-wave-per-row merge runs
+constexpr uint32_t kWaveMergeRows = 2048;  // output rows from which the one-wave-per-row merge runs
 // work segments per split call (one per sequence, or per sequence and 16-column
 // query tile for chunks of queries): their block prefix sums sit in LDS
 constexpr int32_t kMaxSegments = 4096;
@@ -109,6 +109,8 @@ struct DecodeParams {
   int32_t window;            // sliding window: tokens attended (the last `window`)
   int32_t n_tiles;           // 16-row query tiles per KV head that read the prefix (0 = none)
   int32_t n_flat_wgs;        // workgroups of the balanced split schedule
+  int32_t write_new;         // the partition kernel writes the appended token (unsplit); else the merge launch does
+  int32_t append_wgs;        // leading workgroups of the merge launch that write the appended tokens (split calls)
   int32_t min_piece;         // minimum blocks per piece
   int32_t* flat_hdr;         // [3]: private blocks per KV head, private and prefix units per workgroup
   int32_t* flat_cum;         // [B * n_qt]: inclusive prefix sums of private blocks per segment
@@ -316,22 +318,53 @@ __global__ __launch_bounds__(kPatchMax) void table_patch_kernel(int32_t* __restr
   if (i < patch.n) bt[(int64_t)patch.row[i] * max_pages + patch.col[i]] = patch.page[i];
 }
 
-// One workgroup of D threads per (b, kvh): quantises the new token's key to
-// int8 with its own fp32 scale (scale = amax / 127, code = rint(k / scale),
-// IEEE fp32, half to even; amax = 0 gives scale 0 and zero codes) and writes
-// codes and scale into the int8-key sub-block, the value into the fp16 V tile.
+// Quantise one token's key to int8 with its own fp32 scale (scale = amax /
+// 127, code = rint(k * (127 / amax)), IEEE fp32, half to even; amax = 0 gives
+// scale 0 and zero codes) and write codes and scale into the int8-key
+// sub-block of token slot t of `page`, the value into the fp16 V tile.
+// Called by every thread of a workgroup of at least D threads (threads tid <
+// D hold dim tid; the others only join the barrier); k_src / v_src are the
+// token's D keys and values.
+template <int D>
+__device__ __forceinline__ void write_token_k8(const half_t* k_src, const half_t* v_src, uint8_t* k8, half_t* v_pool,
+                                               int32_t page, int32_t kvh, int32_t Hkv, int32_t p_shift, int32_t t,
+                                               int tid) {
+  __shared__ float sm_max[D / kWave];
+  const float kv = tid < D ? (float)k_src[tid] : 0.f;
+  float m = fabsf(kv);
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (tid < D && (tid & (kWave - 1)) == 0) sm_max[tid / kWave] = m;
+  __syncthreads();
+  float amax = sm_max[0];
+#pragma unroll
+  for (int w = 1; w < D / kWave; ++w) amax = fmaxf(amax, sm_max[w]);
+  if (tid >= D) return;
+  const float qs = amax / 127.0f;
+  const float inv = 127.0f / amax;
+  int32_t code = 0;
+  if (amax > 0.f) code = max(-127, min(127, (int32_t)rintf(kv * inv)));
+  const int32_t u = t & 15;
+  const int64_t sub = ((((int64_t)page * Hkv + kvh) << (p_shift - 4)) + ((t & ((1 << p_shift) - 1)) >> 4)) *
+                      (kBlk * D + 64);
+  const int d = tid;
+  const int32_t cofs = ((d / 64) * 64 + ((d / 8) % 4) * 16 + u) * 16 + ((d / 32) % 2) * 8 + d % 8;
+  k8[sub + cofs] = (uint8_t)(int8_t)code;
+  if (d == 0) *reinterpret_cast<float*>(k8 + sub + kBlk * D + 4 * u) = amax > 0.f ? qs : 0.f;
+  const int64_t vsub = ((((int64_t)page * Hkv + kvh) * D) << p_shift) + (int64_t)((t & ((1 << p_shift) - 1)) >> 4) * (kBlk * D);
+  v_pool[vsub + v_sub_off<D>(u, d)] = v_src[d];
+}
+
+// One workgroup of D threads per (b, token of the chunk, kvh): the int8-key append.
 template <int D>
 __global__ __launch_bounds__(D) void kv_append_k8_kernel(const half_t* __restrict__ k_new,
                                                          const half_t* __restrict__ v_new, uint8_t* __restrict__ k8,
                                                          half_t* __restrict__ v_pool, const int32_t* __restrict__ bt,
                                                          int32_t max_pages, const int32_t* __restrict__ pos,
                                                          int32_t Hkv, int32_t p_shift, int32_t N, int32_t n_tokens) {
-  __shared__ float sm_max[D / kWave];
   // workgroup (sequence b, token i of its chunk, KV head): token i goes to position pos[b] + i
   const int32_t kvh = blockIdx.x % Hkv;
   const int32_t bi = blockIdx.x / Hkv;
   const int32_t b = bi / n_tokens;
-  const int d = threadIdx.x;
   const int32_t p0 = pos[b];
   if (p0 < 0 || p0 > 0x7fffffff - n_tokens) return;
   const int32_t t = p0 + bi % n_tokens;
@@ -339,25 +372,7 @@ __global__ __launch_bounds__(D) void kv_append_k8_kernel(const half_t* __restric
   const int32_t page = bt[(int64_t)b * max_pages + (t >> p_shift)];
   if (page < 0 || page >= N) return;
   const int64_t src = ((int64_t)bi * Hkv + kvh) * D;
-  const float kv = (float)k_new[src + d];
-  float m = fabsf(kv);
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if ((d & (kWave - 1)) == 0) sm_max[d / kWave] = m;
-  __syncthreads();
-  float amax = sm_max[0];
-#pragma unroll
-  for (int w = 1; w < D / kWave; ++w) amax = fmaxf(amax, sm_max[w]);
-  const float qs = amax / 127.0f;
-  int32_t code = 0;
-  if (amax > 0.f) code = max(-127, min(127, (int32_t)rintf(kv / qs)));
-  const int32_t u = t & 15;
-  const int64_t sub = ((((int64_t)page * Hkv + kvh) << (p_shift - 4)) + ((t & ((1 << p_shift) - 1)) >> 4)) *
-                      (kBlk * D + 64);
-  const int32_t cofs = ((d / 64) * 64 + ((d / 8) % 4) * 16 + u) * 16 + ((d / 32) % 2) * 8 + d % 8;
-  k8[sub + cofs] = (uint8_t)(int8_t)code;
-  if (d == 0) *reinterpret_cast<float*>(k8 + sub + kBlk * D + 4 * u) = amax > 0.f ? qs : 0.f;
-  const int64_t vsub = ((((int64_t)page * Hkv + kvh) * D) << p_shift) + (int64_t)((t & ((1 << p_shift) - 1)) >> 4) * (kBlk * D);
-  v_pool[vsub + v_sub_off<D>(u, d)] = v_new[src + d];
+  write_token_k8<D>(k_new + src, v_new + src, k8, v_pool, page, kvh, Hkv, p_shift, t, threadIdx.x);
 }
 
 // -------------------------------------------------------------------------
@@ -464,45 +479,32 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     kb = k0;
   };
 
-  // appended token: K slice of lane (col, quad) for row u = col, and the two V
-  // values of lane (col, quad = u / 4) per 32 dims (dims 32 j + col, + 16)
-  uint4 kn[KL];
-  uint32_t vn[KL];
-  uint2 kc[KL];                        // int8 keys: the lane's 8 codes per 32 dims of the new token
-  float kq = 0.f;                      // int8 keys: the new token's scale
-  int64_t new_off = -1;                // element offset of the token's block (valid page), else -1
-  int64_t new_sub8 = -1;               // int8 keys: byte offset of the token's sub-block
-  if constexpr (kAppend) {
-    if (nt.blk >= 0) {
-#pragma unroll
-      for (int j = 0; j < KL; ++j) {
-        kn[j] = *reinterpret_cast<const uint4*>(nt.k + 32 * j + 8 * quad);
-        const uint32_t lo = reinterpret_cast<const uint16_t*>(nt.v)[32 * j + col];
-        const uint32_t hi = reinterpret_cast<const uint16_t*>(nt.v)[32 * j + 16 + col];
-        vn[j] = lo | (hi << 16);
-      }
-    }
-  }
+  // The appended token (kAppend, nt.blk >= 0) sits in the range's last block.
+  // The wave that streams that block (its owner) takes it first: it loads the
+  // block and the token's K and V operand slices, puts its first loop blocks
+  // in flight, then quantises the key (int8 keys), patches the block's
+  // registers, writes the token to the pool (unsplit calls) and consumes the
+  // block. The streaming loop then covers the other blocks and carries no
+  // append work or registers.
+  const bool owns_new = kAppend && nt.blk >= 0 && nt.blk >= first && (nt.blk - first) % stride == 0;
+  const int32_t nloop = (kAppend && nt.blk >= 0) ? nblocks - 1 : nblocks;   // blocks of the streaming loop
+  int32_t new_pid = -1;                // page id of the token's block, read as the block is loaded
 
   // Loads go through buffer descriptors built per 16-token block (base = the
   // block's sub-block, size 16 * D halves). Past the last block the size is 0:
   // the loads return zeros without touching memory, so the prefetch below is
   // unconditional and the compiler keeps exactly kDepth blocks in flight.
   // k counts this wave's blocks: block first + k * stride.
-  auto load_block = [&](int32_t k, uint4 kr[KL], uint4 vr[KL]) {
-    if (k - kb >= kWave) fetch_pages(k);
+  auto load_block = [&](int32_t k, int32_t limit, uint4 kr[KL], uint4 vr[KL]) {
+    if (k - kb >= kWave || k < kb) fetch_pages(k);
     const int32_t blk = first + k * stride;
-    const bool live = blk < nblocks;
+    const bool live = blk < limit;
     const int32_t t0 = start + (live ? blk : 0) * kBlk;
     const int32_t pid = __builtin_amdgcn_readlane(pg, k - kb);
     const int32_t page = pid < 0 ? 0 : pid;                        // stay in bounds
     const int64_t off = ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)(t0 & pmask) * D;
     if constexpr (kAppend) {
-      if (live && blk == nt.blk && pid >= 0) {
-        new_off = off;
-        if constexpr (kK8)
-          new_sub8 = ((((int64_t)page * p.Hkv + kvh) << (p.p_shift - 4)) + ((t0 & pmask) >> 4)) * kSub8;
-      }
+      if (blk == nt.blk) new_pid = pid;
     }
     const int32_t bytes = live ? kBlk * D * 2 : 0;
     if constexpr (kK8) {
@@ -531,92 +533,6 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
 
   auto consume = [&](int32_t blk, uint4 kr[KL], uint4 vr[KL]) {
     const int32_t t0 = start + blk * kBlk;
-    if constexpr (kAppend) {
-      if (blk == nt.blk) {
-        // K: row u sits in lanes col == u; V: row u is half u % 4 of each
-        // 4-half group in lanes quad == u / 4
-        const bool kl = col == nt.u;
-        const bool vl = quad == (nt.u >> 2);
-        const uint32_t sh = (nt.u & 1) * 16;
-        const uint32_t keep = ~(0xFFFFu << sh);
-        if constexpr (kK8) {
-          // codes into the lane's 16-byte run of each 64 dims, scale into slot u % 4 of the scale run
-#pragma unroll
-          for (int j = 0; j < KL; ++j) {
-            if (kl) {
-              if (j & 1) {
-                kr[j / 2].z = kc[j].x;
-                kr[j / 2].w = kc[j].y;
-              } else {
-                kr[j / 2].x = kc[j].x;
-                kr[j / 2].y = kc[j].y;
-              }
-            }
-          }
-          if (vl) {
-            const uint32_t qb32 = __builtin_bit_cast(uint32_t, kq);
-            switch (nt.u & 3) {
-              case 0: kr[D / 64].x = qb32; break;
-              case 1: kr[D / 64].y = qb32; break;
-              case 2: kr[D / 64].z = qb32; break;
-              default: kr[D / 64].w = qb32; break;
-            }
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < KL; ++j) {
-          if constexpr (!kK8) {
-            if (kl) kr[j] = kn[j];
-          }
-          const uint32_t lo = (vn[j] & 0xFFFFu) << sh;
-          const uint32_t hi = (vn[j] >> 16) << sh;
-          if (vl) {
-            if (nt.u & 2) {
-              vr[j].y = (vr[j].y & keep) | lo;
-              vr[j].w = (vr[j].w & keep) | hi;
-            } else {
-              vr[j].x = (vr[j].x & keep) | lo;
-              vr[j].z = (vr[j].z & keep) | hi;
-            }
-          }
-        }
-        if (new_off >= 0) {
-          const int32_t bytes = kBlk * D * 2;
-          const __amdgpu_buffer_rsrc_t vws =
-              __builtin_amdgcn_make_buffer_rsrc((void*)(p.v_pool_w + new_off), (short)0, bytes, kBufferFlags);
-          const int32_t hoff = (nt.u & 3) * 2;
-          if constexpr (kK8) {
-            const __amdgpu_buffer_rsrc_t kws =
-                __builtin_amdgcn_make_buffer_rsrc((void*)(p.k8_w + new_sub8), (short)0, kSub8, kBufferFlags);
-#pragma unroll
-            for (int j = 0; j < KL; ++j) {
-              if (kl) {
-                const int32_t o = (j / 2) * 1024 + lane * 16 + (j & 1) * 8;
-                __builtin_amdgcn_raw_buffer_store_b32(kc[j].x, kws, o, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b32(kc[j].y, kws, o + 4, 0, 0);
-              }
-            }
-            if (kl && quad == 0)
-              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, kq), kws, kBlk * D + 4 * nt.u, 0, 0);
-          }
-#pragma unroll
-          for (int j = 0; j < KL; ++j) {
-            if constexpr (!kK8) {
-              if (kl) {
-                const __amdgpu_buffer_rsrc_t kws =
-                    __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_pool_w + new_off), (short)0, bytes, kBufferFlags);
-                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, kn[j]), kws, lane * 16 + j * 1024,
-                                                       0, 0);
-              }
-            }
-            if (vl) {
-              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(vn[j] & 0xFFFFu), vws, lane * 16 + j * 1024 + hoff, 0, 0);
-              __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(vn[j] >> 16), vws, lane * 16 + j * 1024 + 8 + hoff, 0, 0);
-            }
-          }
-        }
-      }
-    }
     // scores of tokens 4 quad + i for query row col
     float4_t s = {0.f, 0.f, 0.f, 0.f};
     if constexpr (kK8) {
@@ -704,7 +620,9 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     // every token alike (with fp32 weights in the denominator a dominant token
     // whose weight is not exactly 1 would bias the output by ~2^-11 |v|).
     const half4_t pa = {(half_t)pr[0], (half_t)pr[1], (half_t)pr[2], (half_t)pr[3]};
-    st.l_part += ((float)pa[0] + (float)pa[1]) + ((float)pa[2] + (float)pa[3]);
+    const half2_t ones = {(half_t)1.0f, (half_t)1.0f};
+    st.l_part = __builtin_amdgcn_fdot2(half2_t{pa[0], pa[1]}, ones, st.l_part, false);
+    st.l_part = __builtin_amdgcn_fdot2(half2_t{pa[2], pa[3]}, ones, st.l_part, false);
 #pragma unroll
     for (int j = 0; j < KL; ++j) {
       st.o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, lo4(vr[j]), st.o[2 * j], 0, 0, 0);
@@ -712,21 +630,16 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     }
   };
 
-  // software pipeline over a ring of kDepth + 1 block buffers: while block i is
-  // consumed, the next kDepth blocks of this wave are in flight. The scheduling
-  // barriers keep the compiler from sinking a prefetch below the first use of
-  // the current block.
-  uint4 kr[kDepth + 1][KL], vr[kDepth + 1][KL];
-#pragma unroll
-  for (int r = 0; r < kDepth; ++r) load_block(r, kr[r], vr[r]);
-  if constexpr (kAppend && kK8) {
-    // Quantise the new key once the first blocks' loads are in flight (it
-    // waits for the token's own loads; done before them, it would hold back
-    // the whole pipeline). As the append kernel does: the 4 quads of a
-    // column hold all D dims between them, so two shuffles give amax; then
-    // scale = amax / 127 and code = rint(k / scale) in IEEE fp32.
-    __builtin_amdgcn_sched_barrier(0);
-    if (nt.blk >= 0) {
+  // The appended token's block, when this wave owns it: rebuild the token's
+  // operand registers from the compact ones, quantise (int8 keys), patch the
+  // block's registers, write the token to the pool, then consume the block.
+  auto append_epilogue = [&](uint4 (&ekr)[KL], uint4 (&evr)[KL], const uint4 (&kn)[KL], const uint32_t (&vn)[KL]) {
+    // int8 keys: the 4 quads of a column hold all D dims between them, so two
+    // shuffles give amax; then scale = amax / 127 and code = rint(k * (127 /
+    // amax)) in IEEE fp32, as the append kernel does (bit-identical codes)
+    uint2 kc[KL];
+    float kq = 0.f;
+    if constexpr (kK8) {
       float amax = 0.f;
 #pragma unroll
       for (int j = 0; j < KL; ++j) {
@@ -737,6 +650,7 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
       amax = fmaxf(amax, __shfl_xor(amax, 16));
       amax = fmaxf(amax, __shfl_xor(amax, 32));
       const float qs = amax / 127.0f;
+      const float inv = 127.0f / amax;
       kq = amax > 0.f ? qs : 0.f;
 #pragma unroll
       for (int j = 0; j < KL; ++j) {
@@ -745,21 +659,148 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           int32_t c = 0;
-          if (amax > 0.f) c = max(-127, min(127, (int32_t)rintf((float)h[e] / qs)));
+          if (amax > 0.f) c = max(-127, min(127, (int32_t)rintf((float)h[e] * inv)));
           w[e / 4] |= ((uint32_t)c & 0xFFu) << (8 * (e % 4));
         }
         kc[j] = make_uint2(w[0], w[1]);
       }
     }
+    // patch the token into the block's registers. K: row u sits in lanes
+    // col == u; V: row u is half u % 4 of each 4-half group in lanes
+    // quad == u / 4
+    const bool kl = col == nt.u;
+    const bool vl = quad == (nt.u >> 2);
+    const uint32_t sh = (nt.u & 1) * 16;
+    const uint32_t keep = ~(0xFFFFu << sh);
+    if constexpr (kK8) {
+      // codes into the lane's 16-byte run of each 64 dims, scale into slot u % 4 of the scale run
+#pragma unroll
+      for (int j = 0; j < KL; ++j) {
+        if (kl) {
+          if (j & 1) {
+            ekr[j / 2].z = kc[j].x;
+            ekr[j / 2].w = kc[j].y;
+          } else {
+            ekr[j / 2].x = kc[j].x;
+            ekr[j / 2].y = kc[j].y;
+          }
+        }
+      }
+      if (vl) {
+        const uint32_t qb32 = __builtin_bit_cast(uint32_t, kq);
+        switch (nt.u & 3) {
+          case 0: ekr[D / 64].x = qb32; break;
+          case 1: ekr[D / 64].y = qb32; break;
+          case 2: ekr[D / 64].z = qb32; break;
+          default: ekr[D / 64].w = qb32; break;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+      if constexpr (!kK8) {
+        if (kl) ekr[j] = kn[j];
+      }
+      const uint32_t lo = (vn[j] & 0xFFFFu) << sh;
+      const uint32_t hi = (vn[j] >> 16) << sh;
+      if (vl) {
+        if (nt.u & 2) {
+          evr[j].y = (evr[j].y & keep) | lo;
+          evr[j].w = (evr[j].w & keep) | hi;
+        } else {
+          evr[j].x = (evr[j].x & keep) | lo;
+          evr[j].z = (evr[j].z & keep) | hi;
+        }
+      }
+    }
+    // write the token to the pool from the patched registers (a bad page id
+    // writes nothing: the row is NaN). In split calls the merge launch writes
+    // it instead: stores issued while every CU streams reads cost several
+    // microseconds, while the latency-bound merge leaves memory idle.
+    if (new_pid >= 0 && p.write_new) {
+      const int32_t t0 = start + nt.blk * kBlk;
+      const int64_t off = ((int64_t)new_pid * p.Hkv + kvh) * tile_elems + (int64_t)(t0 & pmask) * D;
+      const int32_t bytes = kBlk * D * 2;
+      const __amdgpu_buffer_rsrc_t vws =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(p.v_pool_w + off), (short)0, bytes, kBufferFlags);
+      const int32_t hoff = (nt.u & 3) * 2;
+      if constexpr (kK8) {
+        const int64_t sub8 = ((((int64_t)new_pid * p.Hkv + kvh) << (p.p_shift - 4)) + ((t0 & pmask) >> 4)) * kSub8;
+        const __amdgpu_buffer_rsrc_t kws =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(p.k8_w + sub8), (short)0, kSub8, kBufferFlags);
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+          if (kl) {
+            const int32_t o = (j / 2) * 1024 + lane * 16 + (j & 1) * 8;
+            __builtin_amdgcn_raw_buffer_store_b32(kc[j].x, kws, o, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(kc[j].y, kws, o + 4, 0, 0);
+          }
+        }
+        if (kl && quad == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, kq), kws, kBlk * D + 4 * nt.u, 0, 0);
+      } else {
+        const __amdgpu_buffer_rsrc_t kws =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(p.k_pool_w + off), (short)0, bytes, kBufferFlags);
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+          if (kl)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u32_t, kn[j]), kws, lane * 16 + j * 1024, 0,
+                                                   0);
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < KL; ++j) {
+        if (vl) {
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(vn[j] & 0xFFFFu), vws, lane * 16 + j * 1024 + hoff, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(vn[j] >> 16), vws, lane * 16 + j * 1024 + 8 + hoff, 0, 0);
+        }
+      }
+    }
+    consume(nt.blk, ekr, evr);
+  };
+
+  // software pipeline over a ring of kDepth + 1 block buffers: while block i is
+  // consumed, the next kDepth blocks of this wave are in flight. The scheduling
+  // barriers keep the compiler from sinking a prefetch below the first use of
+  // the current block.
+  uint4 kr[kDepth + 1][KL], vr[kDepth + 1][KL];
+  bool primed = false;
+  if constexpr (kAppend) {
+    if (owns_new) {
+      // the token's operand slices: K of lane (col, quad) = dims 32 j + 8 quad
+      // .. + 8 (row u = col), the two V values of lane (col, quad) = dims
+      // 32 j + col and 32 j + 16 + col (rows 4 quad .. + 3 hold u in one quad)
+      uint4 kn[KL];
+      uint32_t vn[KL];
+#pragma unroll
+      for (int j = 0; j < KL; ++j) {
+        kn[j] = *reinterpret_cast<const uint4*>(nt.k + 32 * j + 8 * quad);
+        const uint32_t lo = reinterpret_cast<const uint16_t*>(nt.v)[32 * j + col];
+        const uint32_t hi = reinterpret_cast<const uint16_t*>(nt.v)[32 * j + 16 + col];
+        vn[j] = lo | (hi << 16);
+      }
+      uint4 ekr[KL], evr[KL];
+      fetch_pages(0);
+      load_block((nt.blk - first) / stride, nblocks, ekr, evr);
+#pragma unroll
+      for (int r = 0; r < kDepth; ++r) load_block(r, nloop, kr[r], vr[r]);
+      __builtin_amdgcn_sched_barrier(0);
+      append_epilogue(ekr, evr, kn, vn);
+      primed = true;
+    }
+  }
+  if (!primed) {
+#pragma unroll
+    for (int r = 0; r < kDepth; ++r) load_block(r, nloop, kr[r], vr[r]);
   }
   int32_t k = 0;
   while (true) {
 #pragma unroll
     for (int r = 0; r <= kDepth; ++r) {
       const int32_t blk = first + k * stride;
-      if (blk >= nblocks) return;
+      if (blk >= nloop) return;
       if (quota > 0) set_priority(after + nblocks - blk, quota);
-      load_block(k + kDepth, kr[(r + kDepth) % (kDepth + 1)], vr[(r + kDepth) % (kDepth + 1)]);
+      load_block(k + kDepth, nloop, kr[(r + kDepth) % (kDepth + 1)], vr[(r + kDepth) % (kDepth + 1)]);
       __builtin_amdgcn_sched_barrier(0);
       consume(blk, kr[r], vr[r]);
       ++k;
@@ -1165,6 +1206,31 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
 // decode: log-sum-exp reduce over partitions
 // -------------------------------------------------------------------------
 
+// Workgroup i of the merge launch's append part writes the appended token of
+// (sequence i / Hkv, KV head i % Hkv) into the pools, as the append kernels do
+// (the partition kernel took it from k_new / v_new in registers): only for an
+// attended row whose token slot has a page, as the partition kernel attends it.
+template <int D>
+__device__ __forceinline__ void merge_launch_append(const DecodeParams& p, int32_t i) {
+  const int32_t b = i / p.Hkv;
+  const int32_t kvh = i % p.Hkv;
+  const int32_t L = p.lens[b];
+  if (len_state(p, L) != 1) return;
+  const int32_t t = L - 1;
+  int32_t entry = t >> p.p_shift;
+  if (p.ring > 0) entry %= p.ring;
+  const int32_t page = p.bt[(int64_t)b * p.max_pages + entry];
+  if (page < 0 || page >= p.N) return;
+  const int64_t src = ((int64_t)b * p.Hkv + kvh) * D;
+  if (p.k8_w) {
+    write_token_k8<D>(p.k_new + src, p.v_new + src, p.k8_w, p.v_pool_w, page, kvh, p.Hkv, p.p_shift, t, threadIdx.x);
+  } else if (threadIdx.x < D) {
+    const int64_t tile = (((int64_t)page * p.Hkv + kvh) * D) << p.p_shift;
+    const int64_t sub = tile + (int64_t)((t & ((1 << p.p_shift) - 1)) >> 4) * (kBlk * D);
+    store_token<D>(p.k_pool_w + sub, p.v_pool_w + sub, t & 15, p.k_new + src, p.v_new + src, threadIdx.x);
+  }
+}
+
 // Where the partials of output row bh = (b * nq + query) * Hq + h lie: the
 // pieces of its prefix tile segment (np1 of them; column = its row within the
 // tile), then those of its private segment (column = its place among the
@@ -1239,7 +1305,11 @@ __global__ __launch_bounds__(D) void lse_reduce_kernel(DecodeParams p) {
   constexpr int kR = 8;               // partials whose outputs are loaded up front
   __shared__ float sm_m[kMaxPartitions];
   __shared__ float sm_l[kMaxPartitions];
-  const int64_t bh = blockIdx.x;
+  if ((int32_t)blockIdx.x < p.append_wgs) {          // the appended tokens (split calls with k_new)
+    merge_launch_append<D>(p, blockIdx.x);
+    return;
+  }
+  const int64_t bh = (int64_t)blockIdx.x - p.append_wgs;
   const int d = threadIdx.x;
   const MergeRow mr = merge_row(p, bh);
   const int32_t np = mr.np;
@@ -1284,8 +1354,12 @@ __global__ __launch_bounds__(kThreads) void lse_reduce_wave_kernel(DecodeParams 
   constexpr int kR = 8;               // partials loaded per batch
   constexpr int DPL = D / kWave;      // output dims per lane
   static_assert(D % kWave == 0, "D is a multiple of the wave size");
+  if ((int32_t)blockIdx.x < p.append_wgs) {          // the appended tokens (split calls with k_new)
+    merge_launch_append<D>(p, blockIdx.x);
+    return;
+  }
   const int lane = threadIdx.x & (kWave - 1);
-  const int64_t bh = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);   // row (b * nq + query) * Hq + h of out
+  const int64_t bh = ((int64_t)blockIdx.x - p.append_wgs) * kWaves + (threadIdx.x >> 6);   // row (b * nq + query) * Hq + h of out
   if (bh >= (int64_t)p.B * p.nq * p.Hq) return;                            // the whole wave
   const MergeRow mr = merge_row(p, bh);
   const int32_t np = mr.np;
@@ -1558,6 +1632,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   prm.window = window;
   prm.n_tiles = plan.n_tiles;
   prm.n_flat_wgs = plan.n_flat_wgs;
+  prm.write_new = plan.split ? 0 : 1;
   prm.min_piece = plan.min_piece;
   prm.scale_log2 = scale * kLog2e;
 
@@ -1596,14 +1671,17 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   }
   if (plan.split) {
     const uint32_t rows = static_cast<uint32_t>(static_cast<int64_t>(B) * nq * Hq);
+    // a fused append's tokens are written by one more workgroup each
+    const uint32_t appends = fused ? static_cast<uint32_t>(B) * Hkv : 0;
     if (rows >= kWaveMergeRows) {
       const uint32_t wgs = (rows + kWaves - 1) / kWaves;        // one wave per row
-      if (D == 64) hipLaunchKernelGGL(lse_reduce_wave_kernel<64>, dim3(wgs), dim3(kThreads), 0, s, prm);
-      else hipLaunchKernelGGL(lse_reduce_wave_kernel<128>, dim3(wgs), dim3(kThreads), 0, s, prm);
-    } else if (D == 64) {
-      hipLaunchKernelGGL(lse_reduce_kernel<64>, dim3(rows), dim3(64), 0, s, prm);
+      prm.append_wgs = appends;
+      if (D == 64) hipLaunchKernelGGL(lse_reduce_wave_kernel<64>, dim3(wgs + appends), dim3(kThreads), 0, s, prm);
+      else hipLaunchKernelGGL(lse_reduce_wave_kernel<128>, dim3(wgs + appends), dim3(kThreads), 0, s, prm);
     } else {
-      hipLaunchKernelGGL(lse_reduce_kernel<128>, dim3(rows), dim3(128), 0, s, prm);
+      prm.append_wgs = appends;
+      if (D == 64) hipLaunchKernelGGL(lse_reduce_kernel<64>, dim3(rows + appends), dim3(64), 0, s, prm);
+      else hipLaunchKernelGGL(lse_reduce_kernel<128>, dim3(rows + appends), dim3(128), 0, s, prm);
     }
     if (hipGetLastError() != hipSuccess) return PKV_ERR_HIP;
   }

@@ -56,9 +56,10 @@ def _check_quantiser(mod):
         assert scale == np.float32(np.float32(amax) / np.float32(127))
         assert codes.dtype == np.int8 and np.abs(codes.astype(int)).max() == 127
         assert np.abs(codes.astype(int)).max() <= 127
-        # half a step, plus the fp32 rounding of k / scale (|k / scale| <= 127, so <= 127 * 2^-24 steps)
+        # half a step, plus the fp32 roundings of scale, 127 / amax and k * inv (each <= 2^-24
+        # relative, on |k| / scale <= 127 steps)
         err = np.abs(kf - codes.astype(np.float64) * float(scale))
-        assert err.max() <= float(scale) * (0.5 + 127 * 2.0 ** -24)
+        assert err.max() <= float(scale) * (0.5 + 127 * 3 * 2.0 ** -24)
 
 
 def test_quantiser_pins():
@@ -183,7 +184,8 @@ def test_append_k8_touches_one_token_per_head():
 # ---------------------------------------------------------------------------
 
 K8_MUTANTS = [
-    ("codes = np.rint(k / scale)", "codes = np.trunc(k / scale)"),                    # truncation
+    ("codes = np.rint(k * inv)", "codes = np.trunc(k * inv)"),                        # truncation
+    ("inv = np.float32(np.float32(127.0) / amax)", "inv = np.float32(np.float32(128.0) / amax)"),
     ("scale = np.float32(amax / np.float32(127.0))", "scale = np.float32(amax / np.float32(128.0))"),
     ("return codes.view(np.int8).astype(np.float64)", "return codes.astype(np.float64)"),   # unsigned codes
     ("return codes.view(np.int8).astype(np.float64) * scales.astype(np.float64)[:, None]",
