@@ -450,6 +450,10 @@ def main():
         host_t["upload"] += time.perf_counter() - t1
 
     # ---- parity check: step 0, layer 0, sampled sequences, against the oracle
+    if KQ > 1:
+        # the pools before the call (pages past the workload's pool are drawn on the device): the oracle
+        # appends the chunk itself
+        k_init, v_init = k_pools[0].cpu().numpy(), v_pools[0].cpu().numpy()
     host_step(0)
     layer_step(0, 0)
     torch.cuda.synchronize()
@@ -463,15 +467,28 @@ def main():
         kp0, vp0 = w.k_pool, w.v_pool
         bt0 = bt_np[:, :]
         kn0, vn0 = knew_mq[0].cpu().numpy(), vnew_mq[0].cpu().numpy()
-        kpool_full = k_pools[0].cpu().numpy()            # pages beyond the workload's pool were drawn on device
-        vpool_full = v_pools[0].cpu().numpy()
-        append = oracle.kv_append_k8 if k8 else oracle.kv_append
-        for i in range(KQ):
-            kpool_full, vpool_full = append(kpool_full, vpool_full, kn0[:, i], vn0[:, i], bt0,
-                                            (w.context + i).astype(np.int32), P)
-        chunk = oracle.decode_attention_multi_k8 if k8 else oracle.decode_attention_multi
-        ref = chunk(q_mq.cpu().numpy()[sample], kpool_full, vpool_full, bt0[sample],
-                    (w.context + KQ).astype(np.int32)[sample], scale, P)
+        # token i of sequence b goes to position context[b] + i (the oracle's token writes, in place on
+        # one copy of the pools; int8 keys quantised by the oracle's quantiser)
+        kpool_full, vpool_full = k_init.copy(), v_init.copy()
+        for b in range(B):
+            for i in range(KQ):
+                page, off = oracle.token_slot(bt0[b], int(w.context[b]) + i, P)
+                for h in range(Hkv):
+                    if k8:
+                        codes, sc = oracle.quantize_k(kn0[b, i, h])
+                        oracle.k8_write_token(kpool_full, page, h, off, codes, sc, D)
+                    else:
+                        oracle.write_token(kpool_full, page, h, off, kn0[b, i, h], "k")
+                    oracle.write_token(vpool_full, page, h, off, vn0[b, i, h], "v")
+        # query i of a chunk is the single-token decode of its own prefix (the oracle's chunk
+        # definition); long chunks are checked on the first, second, middle and last queries
+        qi = np.arange(KQ) if KQ <= 8 else np.unique(np.array([0, 1, KQ // 2, KQ - 1]))
+        one = oracle.decode_attention_k8 if k8 else oracle.decode_attention
+        qh = q_mq.cpu().numpy()[sample]
+        lens0 = (w.context + KQ).astype(np.int32)[sample]
+        ref = np.stack([one(qh[:, i], kpool_full, vpool_full, bt0[sample], lens0 - KQ + i + 1, scale, P) for i in qi],
+                       axis=1)
+        got = got[:, qi]
     elif W:
         logical = logical_table(w.block_table, int(w.lens(0).max()), P)
         if k8:
