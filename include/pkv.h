@@ -249,12 +249,12 @@ int pkv_decode_workspace_bytes_shared_prefix(int32_t B, int32_t Hq, int32_t D, i
  * pkv_decode_workspace_bytes_multi -- workspace size for the chunked calls
  * (pkv_paged_decode_attention_multi, _multi_shared_prefix, _multi_k8,
  * _window_multi, _window_multi_k8) with n_query queries per sequence: one
- * private segment per sequence and 16-column query tile (chunks of pgsm
- * §3.2's draft verification and chunked prefill), one prefix segment per 16
- * chunk rows of a KV head when prefix_tokens > 0. n_query == 1 gives the
- * single-query sizes. Errors: PKV_ERR_INVALID_ARG (as
- * pkv_decode_workspace_bytes_shared_prefix; n_query < 1; more than 4096
- * segments for every allowed Hkv).
+ * private segment per sequence and group of up to four 16-column query tiles
+ * (chunks of pgsm §3.2's draft verification and chunked prefill), one prefix
+ * segment per group of up to four 16-row tiles of a KV head's chunk rows when
+ * prefix_tokens > 0. n_query == 1 gives the single-query sizes. Errors:
+ * PKV_ERR_INVALID_ARG (as pkv_decode_workspace_bytes_shared_prefix;
+ * n_query < 1; more than 4096 segments for every allowed Hkv).
  */
 int pkv_decode_workspace_bytes_multi(int32_t B, int32_t n_query, int32_t Hq, int32_t D, int32_t max_context,
                                      int32_t partition_tokens, int32_t prefix_tokens, size_t* bytes);
@@ -340,9 +340,11 @@ size_t pkv_noalloc_scratch_bytes(void);
  *   q            : fp16 [B][n_query][Hq][D] device, read.
  *   n_query      : >= 1. The n_query * (Hq / Hkv) query rows of a (sequence,
  *                  KV head) are cut into 16-column matrix-core tiles of 16 /
- *                  (Hq / Hkv) consecutive queries; each tile streams the
- *                  sequence's tokens up to its last query. In split mode
- *                  B * ceil(n_query * (Hq / Hkv) / 16) <= 4096.
+ *                  (Hq / Hkv) consecutive queries, and the tiles into groups
+ *                  of up to four; the waves of a group's tiles stream the
+ *                  sequence's tokens up to the group's last query together
+ *                  (one read from memory, the others from the L2). In split
+ *                  mode B * ceil(ceil(n_query * (Hq / Hkv) / 16) / 4) <= 4096.
  *   lens[b]      : tokens in the cache including the whole chunk; a row with
  *                  0 < lens[b] < n_query (or beyond max_context / the table)
  *                  is NaN; lens[b] == 0 gives zero rows.

@@ -75,6 +75,9 @@ constexpr int32_t kWindowMaxLen = 0x7fffffff - 64;
 constexpr float kRescaleSlack = 8.0f;
 // Blocks each wave keeps in flight ahead of the one it is consuming.
 constexpr int kDepth = 2;
+// Tile groups staged through LDS: blocks whose chunks each thread keeps in
+// flight ahead of the block being staged.
+constexpr int kLdsDepth = 4;
 // Word 3 of a raw gfx9 buffer descriptor (32-bit data format, no swizzle).
 constexpr int32_t kBufferFlags = 0x00020000;
 // Cache policy of the K/V loads: 2 = non-temporal (private pages are streamed
@@ -98,6 +101,7 @@ struct DecodeParams {
   const int32_t* lens;       // [B]
   int32_t max_pages;
   int32_t B, Hq, Hkv, N;
+  int32_t g_shift;           // log2(Hq / Hkv)
   int32_t p_shift;           // log2(P)
   int32_t max_context;
   int32_t prefix_tokens;     // shared leading tokens (0 = none), multiple of P
@@ -105,20 +109,43 @@ struct DecodeParams {
   int32_t nq;                // queries per sequence (1 = decode; > 1: the chunk of the last nq tokens)
   int32_t n_qt;              // 16-column query tiles per (sequence, KV head): ceil(nq * G / 16) for chunks, else 1
   int32_t qpt;               // queries per query tile (16 / G for chunks)
+  int32_t tw;                // query tiles per group (1, 2 or 4): a group's tiles share one stream of the blocks
+  int32_t tw_shift;          // log2(tw)
+  int32_t n_grp;             // query tile groups per (sequence, KV head): ceil(n_qt / tw)
   int32_t ring;              // sliding window: pages per sequence in its ring (logical page j -> entry j % ring)
   int32_t window;            // sliding window: tokens attended (the last `window`)
-  int32_t n_tiles;           // 16-row query tiles per KV head that read the prefix (0 = none)
+  int32_t n_ptiles;          // 16-row query tiles per KV head that read the prefix (0 = none)
+  int32_t ptw;               // prefix tiles per prefix group (1, 2 or 4; one stream of the prefix blocks each)
+  int32_t ptw_shift;         // log2(ptw)
+  int32_t n_pgrp;            // prefix groups per KV head: ceil(n_ptiles / ptw)
   int32_t n_flat_wgs;        // workgroups of the balanced split schedule
   int32_t write_new;         // the partition kernel writes the appended token (unsplit); else the merge launch does
   int32_t append_wgs;        // leading workgroups of the merge launch that write the appended tokens (split calls)
-  int32_t min_piece;         // minimum blocks per piece
+  int32_t min_piece_p;       // minimum blocks per piece of the prefix list
+  int32_t min_piece_v;       // minimum blocks per piece of the private list
+  int64_t priv_col0;         // first partial column of the private pieces
+  int32_t pslots;            // prefix piece slots per KV head: n_pgrp + n_flat_wgs / Hkv
+  int32_t vslots;            // private piece slots per KV head: B n_grp + n_flat_wgs / Hkv
   int32_t* flat_hdr;         // [3]: private blocks per KV head, private and prefix units per workgroup
-  int32_t* flat_cum;         // [B * n_qt]: inclusive prefix sums of private blocks per segment
-  float* flat_m;             // [slots][16]: piece partials, base-2 scaled score max
-  float* flat_l;             // [slots][16]: softmax denominators
-  float* flat_o;             // [slots][16][D]: unnormalised outputs
+  int32_t* flat_cum;         // [B * n_grp]: inclusive prefix sums of private blocks per segment
+  float* flat_m;             // [columns]: piece partials, base-2 scaled score max
+  float* flat_l;             // [columns]: softmax denominators
+  float* flat_o;             // [columns][D]: unnormalised outputs
   float scale_log2;          // scale * log2(e)
 };
+
+// Partial columns of the split schedule. KV head kvh's prefix pieces own
+// slots [0, n_pgrp + Wk) of 16 ptw columns each, its private pieces slots
+// [0, S + Wk) of 16 tw columns each (S = B n_grp segments); the piece of
+// (segment s, workgroup j) takes slot s + j of its list, and tile tl of a
+// group writes columns 16 tl .. 16 tl + 15 of the slot.
+__device__ __forceinline__ int64_t prefix_col(const DecodeParams& p, int32_t kvh, int32_t slot, int32_t tl, int32_t c) {
+  return ((int64_t)kvh * p.pslots + slot) * (16 * p.ptw) + 16 * tl + c;
+}
+
+__device__ __forceinline__ int64_t priv_col(const DecodeParams& p, int32_t kvh, int32_t slot, int32_t tl, int32_t c) {
+  return p.priv_col0 + ((int64_t)kvh * p.vslots + slot) * (16 * p.tw) + 16 * tl + c;
+}
 
 __device__ __forceinline__ float kNegInf() { return -__builtin_huge_valf(); }
 
@@ -133,6 +160,15 @@ __device__ __forceinline__ int len_state(const DecodeParams& p, int32_t L) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Workgroup barrier that orders LDS accesses only: the global loads a wave
+// has in flight stay in flight across it (a full __syncthreads would wait for
+// them and drain every prefetch).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 __device__ __forceinline__ half8_t as_h8(const uint4& v) { return __builtin_bit_cast(half8_t, v); }
 
@@ -440,13 +476,21 @@ __device__ __forceinline__ void set_priority(int32_t remaining, int32_t quota) {
 // other loads, patches them into the block's registers before use, and writes
 // them to the pool from there. No other wave reads that row, so the write
 // needs no ordering against the loads.
-template <int D, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ>
+//
+// kLds: the workgroup streams the range once for all its waves (first = 0,
+// stride = 1, a tile group's waves each consuming every block for its own
+// tile): thread t loads 16-byte chunk t of each block's K and V bytes,
+// kLdsDepth blocks ahead, and stores it to one of two block slots in `ring`
+// (LDS); after a barrier every wave reads its operands from there. A wave with
+// active == false only loads and stages.
+template <int D, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ, bool kLds = false>
 __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32_t* bt_row, int32_t kvh,
                                               int32_t start, int32_t end, int32_t first, int32_t stride,
                                               int32_t quota, int32_t after, const NewToken& nt,
                                               int32_t clim, int32_t clim_min, int32_t clo, int32_t clo_max,
                                               int32_t win_lo,
-                                              const half8_t (&qb)[D / 32], WaveState<D>& st, int lane) {
+                                              const half8_t (&qb)[D / 32], WaveState<D>& st, int lane,
+                                              char* ring = nullptr, bool active = true) {
   constexpr int KL = D / 32;           // 16-byte loads per lane per block, for K and for V
   constexpr int NT = D / 16;           // 16-dim output tiles
   const int quad = lane >> 4;          // MFMA k-group: tokens 4 quad .. 4 quad + 3
@@ -531,9 +575,8 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
       vr[j] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, lane * 16 + j * 1024, 0, kPolicy));
   };
 
-  auto consume = [&](int32_t blk, uint4 kr[KL], uint4 vr[KL]) {
-    const int32_t t0 = start + blk * kBlk;
-    // scores of tokens 4 quad + i for query row col
+  // scores of tokens 4 quad + i of a block for query row col
+  auto scores = [&](const uint4* kr) -> float4_t {
     float4_t s = {0.f, 0.f, 0.f, 0.f};
     if constexpr (kK8) {
 #pragma unroll
@@ -551,6 +594,13 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
 #pragma unroll
       for (int j = 0; j < KL; ++j) s = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(kr[j]), qb[j], s, 0, 0, 0);
     }
+    return s;
+  };
+
+  // block blk's scores s: masks, the online-softmax update of state ws and
+  // the P.V product
+  auto update = [&](int32_t blk, float4_t s, uint4* vr, WaveState<D>& ws) {
+    const int32_t t0 = start + blk * kBlk;
     if (t0 < win_lo) {
       // sliding window: tokens before its start get masked scores and zeroed values (never 0 * NaN)
       const int32_t tq = t0 + 4 * quad;
@@ -593,25 +643,25 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     }
     float bm = col_max4(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])));
     bm *= c;                            // block max of column col, base-2 units (c > 0)
-    if (__builtin_amdgcn_ballot_w64(bm > st.m_ref + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(st.m_ref, bm);
-      float alpha = fast_exp2(st.m_ref - m_new);               // 0 on the first block
+    if (__builtin_amdgcn_ballot_w64(bm > ws.m_ref + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(ws.m_ref, bm);
+      float alpha = fast_exp2(ws.m_ref - m_new);               // 0 on the first block
       if constexpr (kMQ) {
         // a causally masked column may have seen no token yet: -inf - -inf
         if (m_new == kNegInf()) alpha = 1.f;
       }
-      st.l_part *= alpha;
+      ws.l_part *= alpha;
       // output row 4 quad + i belongs to column 4 quad + i, whose alpha sits in lane 4 quad + i
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float a = __shfl(alpha, 4 * quad + i);
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) st.o[nt][i] *= a;
+        for (int nt = 0; nt < NT; ++nt) ws.o[nt][i] *= a;
       }
-      st.m_ref = m_new;
+      ws.m_ref = m_new;
     }
     float pr[4];
-    float mref = st.m_ref;
+    float mref = ws.m_ref;
     if constexpr (kMQ) mref = mref == kNegInf() ? 0.f : mref;   // all its scores are -inf then: p = 0
 #pragma unroll
     for (int i = 0; i < 4; ++i) pr[i] = fast_exp2(fmaf(s[i], c, -mref));
@@ -621,14 +671,16 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     // whose weight is not exactly 1 would bias the output by ~2^-11 |v|).
     const half4_t pa = {(half_t)pr[0], (half_t)pr[1], (half_t)pr[2], (half_t)pr[3]};
     const half2_t ones = {(half_t)1.0f, (half_t)1.0f};
-    st.l_part = __builtin_amdgcn_fdot2(half2_t{pa[0], pa[1]}, ones, st.l_part, false);
-    st.l_part = __builtin_amdgcn_fdot2(half2_t{pa[2], pa[3]}, ones, st.l_part, false);
+    ws.l_part = __builtin_amdgcn_fdot2(half2_t{pa[0], pa[1]}, ones, ws.l_part, false);
+    ws.l_part = __builtin_amdgcn_fdot2(half2_t{pa[2], pa[3]}, ones, ws.l_part, false);
 #pragma unroll
     for (int j = 0; j < KL; ++j) {
-      st.o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, lo4(vr[j]), st.o[2 * j], 0, 0, 0);
-      st.o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, hi4(vr[j]), st.o[2 * j + 1], 0, 0, 0);
+      ws.o[2 * j] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, lo4(vr[j]), ws.o[2 * j], 0, 0, 0);
+      ws.o[2 * j + 1] = __builtin_amdgcn_mfma_f32_16x16x16f16(pa, hi4(vr[j]), ws.o[2 * j + 1], 0, 0, 0);
     }
   };
+
+  auto consume = [&](int32_t blk, uint4 kr[KL], uint4 vr[KL]) { update(blk, scores(kr), vr, st); };
 
   // The appended token's block, when this wave owns it: rebuild the token's
   // operand registers from the compact ones, quantise (int8 keys), patch the
@@ -759,6 +811,90 @@ __device__ __forceinline__ void stream_blocks(const DecodeParams& p, const int32
     consume(nt.blk, ekr, evr);
   };
 
+  if constexpr (kLds) {
+    static_assert(!kAppend, "staged ranges carry no appended token");
+    // block bytes: K (fp16 tile rows, or int8 codes then the 16 fp32 scales), then V
+    constexpr int32_t kKb = kK8 ? kSub8 : kBlk * D * 2;
+    constexpr int32_t kVb = kBlk * D * 2;
+    constexpr int32_t kSlot = kKb + kVb;
+    static_assert(kKb <= kThreads * 16 && kVb <= kThreads * 16, "one chunk of K and of V per thread");
+    const int32_t tid = (int32_t)threadIdx.x;
+    const bool has_k = tid * 16 < kKb;
+    const bool has_v = tid * 16 < kVb;
+    auto issue = [&](int32_t k, uint4& ck, uint4& cv) {
+      if (k - kb >= kWave || k < kb) fetch_pages(k);
+      const bool live = k < nblocks;
+      const int32_t t0 = start + (live ? k : 0) * kBlk;
+      const int32_t pid = __builtin_amdgcn_readlane(pg, k - kb);
+      const int32_t page = pid < 0 ? 0 : pid;                       // stay in bounds
+      const int64_t off = ((int64_t)page * p.Hkv + kvh) * tile_elems + (int64_t)(t0 & pmask) * D;
+      const void* kbase;
+      if constexpr (kK8) {
+        const int64_t sub = (((int64_t)page * p.Hkv + kvh) << (p.p_shift - 4)) + ((t0 & pmask) >> 4);
+        kbase = p.k8 + sub * kSub8;
+      } else {
+        kbase = p.k_pool + off;
+      }
+      const __amdgpu_buffer_rsrc_t krs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, live ? kKb : 0, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t vrs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)(p.v_pool + off), (short)0, live ? kVb : 0, kBufferFlags);
+      // every lane loads (a select would zero the registers first and wait
+      // for every load in flight); a lane without a chunk reads past the end
+      // of the descriptor, which returns zeros without touching memory
+      ck = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(krs, has_k ? tid * 16 : kKb, 0, kPolicy));
+      cv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(vrs, has_v ? tid * 16 : kVb, 0, kPolicy));
+    };
+    auto stage = [&](int32_t slot, const uint4& ck, const uint4& cv) {
+      char* base = ring + slot * kSlot;
+      if (has_k) *reinterpret_cast<uint4*>(base + tid * 16) = ck;
+      if (has_v) *reinterpret_cast<uint4*>(base + kKb + tid * 16) = cv;
+    };
+    auto read_block = [&](int32_t slot, uint4 (&kr)[KL], uint4 (&vr)[KL]) {
+      const char* base = ring + slot * kSlot;
+      if constexpr (kK8) {
+#pragma unroll
+        for (int j = 0; j < D / 64; ++j) kr[j] = *reinterpret_cast<const uint4*>(base + lane * 16 + j * 1024);
+        kr[D / 64] = *reinterpret_cast<const uint4*>(base + kBlk * D + quad * 16);
+      } else {
+#pragma unroll
+        for (int j = 0; j < KL; ++j) kr[j] = *reinterpret_cast<const uint4*>(base + lane * 16 + j * 1024);
+      }
+#pragma unroll
+      for (int j = 0; j < KL; ++j) vr[j] = *reinterpret_cast<const uint4*>(base + kKb + lane * 16 + j * 1024);
+    };
+    uint4 sk[kLdsDepth], sv[kLdsDepth];      // block b's chunks sit in sk/sv[b % kLdsDepth] while in flight
+#pragma unroll
+    for (int r = 0; r < kLdsDepth; ++r) issue(r, sk[r], sv[r]);
+    stage(0, sk[0], sv[0]);
+    issue(kLdsDepth, sk[0], sv[0]);
+    // iterations padded to a multiple of kLdsDepth (the register slots stay
+    // compile-time indices); the padding only passes barriers
+    const int32_t n_iter = (nblocks + kLdsDepth - 1) / kLdsDepth * kLdsDepth;
+    for (int32_t i0 = 0; i0 < n_iter; i0 += kLdsDepth) {
+#pragma unroll
+      for (int r = 0; r < kLdsDepth; ++r) {
+        const int32_t i = i0 + r;
+        if (quota > 0 && i < nblocks) set_priority(after + nblocks - i, quota);
+        // block i is in slot i & 1 for everyone; every wave is done with block i - 1, whose slot takes block i + 1
+        lds_barrier();
+        // unconditional, so that the count of loads issued after any block's
+        // is the same on every path and only that block's loads are waited
+        // for (past the last block: zeros into the slot no one reads next)
+        const int rn = (r + 1) % kLdsDepth;
+        stage((i + 1) & 1, sk[rn], sv[rn]);
+        issue(i + 1 + kLdsDepth, sk[rn], sv[rn]);
+        if (active && i < nblocks) {
+          uint4 kr[KL], vr[KL];
+          read_block(i & 1, kr, vr);
+          consume(i, kr, vr);
+        }
+      }
+    }
+    lds_barrier();                         // every wave is done with the ring (the caller reuses the LDS)
+    return;
+  }
+
   // software pipeline over a ring of kDepth + 1 block buffers: while block i is
   // consumed, the next kDepth blocks of this wave are in flight. The scheduling
   // barriers keep the compiler from sinking a prefetch below the first use of
@@ -842,25 +978,42 @@ struct KernelShared {
 
 // The 4 waves of a workgroup stream tokens [start, end) of KV head kvh through
 // block-table row bt_row (wave w takes blocks w, w + 4, ...), for NC query
-// rows: column c < NC reads q row qrow(c) (< 0: no row, zero query). The
+// rows: column c < NC reads q row qrow(0, c) (< 0: no row, zero query). The
 // waves merge through LDS and every (column c, dim d) goes to
-// emit(c, d, M, Ls, O): the column's base-2 score max, softmax denominator
+// emit(0, c, d, M, Ls, O): the column's base-2 score max, softmax denominator
 // and unnormalised output. Callers must be workgroup-uniform.
 // kMQ: column c is query c / g of a tile of mq_n queries of a chunk (g = mq_g
 // heads per query); query i of the tile sits at position mq_last0 + i and may
 // see tokens up to there (with a sliding window, the window ending there).
-template <int D, int NC, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ = false, class RowFn,
+// kGrp: the range serves ntl (1 to 4) query tiles of NC = 16 columns at once,
+// tile tl reading rows qrow(tl, c) and emitting through emit(tl, ...). For 2
+// to 4 tiles the workgroup reads each block once into LDS and wave tl
+// consumes every block for tile tl (waves past the last tile only load); a
+// single tile is streamed as above. With kMQ the group's mq_n queries start
+// at mq_last0, p.qpt queries per tile.
+template <int D, int NC, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ = false, bool kGrp = false, class RowFn,
           class EmitFn>
 __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>& sh, const int32_t* bt_row,
                                           int32_t kvh, int32_t start, int32_t end, int32_t quota, int32_t after,
                                           const NewToken& nt, RowFn qrow, EmitFn emit, int lane, int wave,
-                                          int32_t mq_last0 = 0, int32_t mq_g = 1, int32_t lo = 0, int32_t mq_n = 0) {
+                                          int32_t mq_last0 = 0, int32_t mq_g = 1, int32_t lo = 0, int32_t mq_n = 0,
+                                          int32_t ntl = 1) {
   constexpr int KL = D / 32;
   constexpr int NT = D / 16;
+  static_assert(!kGrp || NC == 16, "tile groups are of 16-column tiles");
   const int col = lane & 15;
   const int quad = lane >> 4;
+  // two ring slots of a staged range (K and V bytes of a block each) fit the merge area
+  static_assert(!kGrp || sizeof(WgShared<D, NC>) >= 2 * ((kK8 ? kBlk * D + 64 : kBlk * D * 2) + kBlk * D * 2),
+                "LDS ring");
+  // waves per tile, this wave's tile and its place among the tile's waves: a
+  // group of 2 to 4 tiles is staged through LDS, one wave per tile (the other
+  // waves only load); a single tile keeps the 4 waves splitting its blocks
+  const int wpt = kGrp ? (ntl >= 2 ? 1 : kWaves) : kWaves;
+  const int tl = kGrp ? wave / wpt : 0;
+  const bool active = !kGrp || tl < ntl;
   // B operand of the score MFMA: lane (column col, quad) holds q[row][32 j + 8 quad .. + 8]
-  const int64_t row = col < NC ? qrow(col) : -1;
+  const int64_t row = active && col < NC ? qrow(tl, col) : -1;
   half8_t qb[KL];
 #pragma unroll
   for (int j = 0; j < KL; ++j) {
@@ -872,17 +1025,25 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
   init_state<D>(st);
   int32_t clim = 0x7fffffff;
   int32_t clo = 0, clo_max = 0;
+  int32_t t_last0 = mq_last0;                    // position of this wave's tile's first query
   if constexpr (kMQ) {
-    // query qi sits at mq_last0 + qi; with a window it sees window tokens ending there
+    // query qi of the wave's tile sits at t_last0 + qi; with a window it sees window tokens ending there
+    const int32_t t_n = kGrp ? min(p.qpt, mq_n - tl * p.qpt) : mq_n;
+    if constexpr (kGrp) t_last0 = mq_last0 + tl * p.qpt;
     const int32_t qi = col / mq_g;
-    clim = qi < mq_n ? mq_last0 + qi : 0x7fffffff;
+    clim = qi < t_n ? t_last0 + qi : 0x7fffffff;
     if (p.window > 0) {
-      clo = qi < mq_n ? max(0, mq_last0 + qi + 1 - p.window) : 0;
-      clo_max = max(0, mq_last0 + mq_n - p.window);
+      clo = qi < t_n ? max(0, t_last0 + qi + 1 - p.window) : 0;
+      clo_max = max(0, t_last0 + t_n - p.window);
     }
   }
-  stream_blocks<D, kPolicy, kAppend, kK8, kMQ>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, nt,
-                                                     clim, mq_last0, clo, clo_max, lo, qb, st, lane);
+  if (kGrp && ntl >= 2)
+    stream_blocks<D, kPolicy, kAppend, kK8, kMQ, kGrp>(p, bt_row, kvh, start, end, 0, 1, quota, after, nt, clim,
+                                                       t_last0, clo, clo_max, lo, qb, st, lane,
+                                                       reinterpret_cast<char*>(&sh), active);
+  else
+    stream_blocks<D, kPolicy, kAppend, kK8, kMQ>(p, bt_row, kvh, start, end, wave, kWaves, quota, after, nt, clim,
+                                                 t_last0, clo, clo_max, lo, qb, st, lane);
   // per-column denominators of this wave: sum the 4 quads of column col
   st.l_part += __shfl_xor(st.l_part, 16);
   st.l_part += __shfl_xor(st.l_part, 32);
@@ -901,21 +1062,27 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
     }
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < NC * D; i += kThreads) {
-    const int c = i / D;
+  const int n_out = (kGrp ? ntl : 1) * NC * D;
+  for (int i = threadIdx.x; i < n_out; i += kThreads) {
+    const int ot = kGrp ? i / (NC * D) : 0;      // tile of this output, merged over its team's waves
+    const int c = (i / D) % NC;
     const int d = i % D;
-    float M = sh.m[0][c];
+    const int w0 = ot * wpt;
+    float M = sh.m[w0][c];
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) M = fmaxf(M, sh.m[w][c]);
+    for (int w = 1; w < kWaves; ++w)
+      if (!kGrp || w < wpt) M = fmaxf(M, sh.m[w0 + w][c]);
     const float Ms = M == kNegInf() ? 0.f : M;
     float Ls = 0.f, O = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float wt = fast_exp2(sh.m[w][c] - Ms);
-      Ls = fmaf(wt, sh.l[w][c], Ls);
-      O = fmaf(wt, sh.o[w][c][d], O);
+      if (!kGrp || w < wpt) {
+        const float wt = fast_exp2(sh.m[w0 + w][c] - Ms);
+        Ls = fmaf(wt, sh.l[w0 + w][c], Ls);
+        O = fmaf(wt, sh.o[w0 + w][c][d], O);
+      }
     }
-    emit(c, d, M, Ls, O);
+    emit(ot, c, d, M, Ls, O);
   }
   // the LDS is reused by the caller's next range
   __syncthreads();
@@ -923,18 +1090,19 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
 
 // Unsplit (partition_tokens == 0): workgroup (KV head, sequence) over the
 // whole context; columns are the G heads of the group (zero-padded to 16);
-// fp16 output. A chunk of queries: workgroup (KV head, query tile,
-// sequence), the tile's queries and heads as columns.
+// fp16 output. A chunk of queries: workgroup (KV head, query tile group,
+// sequence), each tile's queries and heads as the columns of its waves.
 //
 // Split: a balanced schedule per KV head over two work lists,
-//   prefix:  [tile 0: PB blocks] ... [tile NT-1: PB blocks]
+//   prefix:  [group 0: PB blocks] ... [group NP-1: PB blocks]
 //   private: [segment 0 blocks] ... [segment S-1 blocks]
 // A prefix segment is the PB = prefix_tokens / 16 shared blocks read for one
-// tile of 16 query rows (row r = sequence r / G, head kvh * G + r % G: a full
-// 16-column MFMA tile, the shared pages read once for all 16); a private
-// segment is a sequence's own blocks after the prefix, read for its G heads
-// (for a chunk of queries, segment b * n_qt + t is sequence b's blocks up to
-// the last query of its query tile t, read for that tile's columns).
+// group of ptw tiles of 16 query rows (row r = sequence r / G, head kvh * G +
+// r % G: full 16-column MFMA tiles, the shared pages read once for all their
+// rows); a private segment is a sequence's own blocks after the prefix, read
+// for its G heads (for a chunk of queries, segment b * n_grp + gq is sequence
+// b's blocks up to the last query of its tile group gq, read for the columns
+// of the group's tiles).
 // Workgroup w serves KV head w % Hkv (under round-robin dispatch an XCD keeps
 // to the same heads, so their shared pages stay in its L2); its index j =
 // w / Hkv among the head's Wk = W / Hkv workgroups selects units
@@ -942,48 +1110,56 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
 // list, Qx = max(ceil(list length / Wk), minimum piece). Every workgroup thus
 // gets the same mix of L2-resident prefix reads and HBM-bound private reads;
 // pieces cross segment boundaries. The piece of (segment s, workgroup j)
-// writes slot kvh * (NT + S + 2 Wk) + s + j, private segments numbered after
-// NT + Wk: walking a list in order increases s or j (or both) by one each
-// step, so the slots are distinct; each slot holds 16 columns.
-template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ>
+// writes slot s + j of its list (prefix_col, priv_col): walking a list in
+// order increases s or j (or both) by one each step, so the slots are
+// distinct.
+template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ, bool GRP>
 __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodeParams p) {
   static_assert(!MQ || !FUSED, "chunks of queries: no fused append");
+  static_assert(MQ || !GRP, "tile groups are for chunks of queries");
   static_assert(D % 32 == 0 && G >= 1 && G <= 16, "shape");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   __shared__ KernelShared<D, G> smem;
 
   if constexpr (!SPLIT && MQ) {
-    // query tile t of a chunk of nq queries: columns (query q0 + i, head g) = i * G + g
+    // query tile group gq of a chunk of nq queries: tiles gq tw .. of qpt
+    // queries each, columns (query q0 + i, head g) = i * G + g of each tile
     const int32_t kvh = blockIdx.x % p.Hkv;
-    const int32_t bt_i = blockIdx.x / p.Hkv;
-    const int32_t t = bt_i % p.n_qt;
-    const int32_t b = bt_i / p.n_qt;
+    const int32_t bg = blockIdx.x / p.Hkv;
+    const int32_t gq = bg % p.n_grp;
+    const int32_t b = bg / p.n_grp;
     const int32_t L = p.lens[b];
     const int ls = len_state(p, L);
-    const int32_t q0 = t * p.qpt;
-    const int32_t nqt = min(p.nq - q0, p.qpt);
-    const int32_t ncol = nqt * G;
-    auto row = [&](int c) -> int64_t { return ((int64_t)b * p.nq + q0 + c / G) * p.Hq + (int64_t)kvh * G + c % G; };
+    const int32_t q0 = gq * p.tw * p.qpt;            // the group's first query
+    const int32_t nqg = min(p.nq - q0, p.tw * p.qpt);
+    const int32_t ntl = (nqg + p.qpt - 1) / p.qpt;
+    auto row = [&](int32_t qi, int32_t g) -> int64_t {
+      return ((int64_t)b * p.nq + q0 + qi) * p.Hq + (int64_t)kvh * G + g;
+    };
     if (ls != 1) {
       const half_t fill = ls == 0 ? (half_t)0.0f : (half_t)__builtin_nanf("");
-      for (int i = threadIdx.x; i < ncol * D; i += kThreads) p.out[row(i / D) * D + i % D] = fill;
+      for (int i = threadIdx.x; i < nqg * G * D; i += kThreads) p.out[row(i / (G * D), (i / D) % G) * D + i % D] = fill;
       return;
     }
     const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
-    const int32_t pos0 = L - p.nq + q0;            // position of the tile's first query
+    const int32_t pos0 = L - p.nq + q0;            // position of the group's first query
     // sliding window: from the block holding the first query's window start
     const int32_t lo = p.window > 0 ? max(0, pos0 + 1 - p.window) : 0;
-    run_range<D, 16, kKvLoadPolicy, false, K8, true>(
-        p, smem.tile.prefix, bt_row, kvh, lo & ~(kBlk - 1), pos0 + nqt, 0, 0, NewToken{-1, 0, nullptr, nullptr},
-        [&](int c) -> int64_t { return c < ncol ? row(c) : -1; },
-        [&](int c, int d, float, float Ls, float O) {
-          if (c < ncol) {
+    run_range<D, 16, kKvLoadPolicy, false, K8, true, GRP>(
+        p, smem.tile.prefix, bt_row, kvh, lo & ~(kBlk - 1), pos0 + nqg, 0, 0, NewToken{-1, 0, nullptr, nullptr},
+        [&](int tl, int c) -> int64_t {
+          const int32_t qi = tl * p.qpt + c / G;
+          return c < p.qpt * G && qi < nqg ? row(qi, c % G) : -1;
+        },
+        [&](int tl, int c, int d, float, float Ls, float O) {
+          const int32_t qi = tl * p.qpt + c / G;
+          if (c < p.qpt * G && qi < nqg) {
             const float r = Ls > 0.f ? O / Ls : (Ls == 0.f ? 0.f : __builtin_nanf(""));
-            p.out[row(c) * D + d] = (half_t)(Ls != Ls ? __builtin_nanf("") : r);
+            p.out[row(qi, c % G) * D + d] = (half_t)(Ls != Ls ? __builtin_nanf("") : r);
           }
         },
-        lane, wave, pos0, G, lo, nqt);
+        lane, wave, pos0, G, lo, nqg, ntl);
   } else if constexpr (!SPLIT) {
     WgShared<D, G>& sh = smem.tile.priv;
     const int32_t kvh = blockIdx.x % p.Hkv;
@@ -1006,8 +1182,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
       nt = NewToken{(L - 1 - s0) >> 4, (L - 1) & 15, p.k_new + src, p.v_new + src};
     }
     run_range<D, G, kKvLoadPolicy, FUSED, K8>(
-        p, sh, bt_row, kvh, s0, L, 0, 0, nt, [&](int c) -> int64_t { return head_row0 + c; },
-        [&](int c, int d, float, float Ls, float O) {
+        p, sh, bt_row, kvh, s0, L, 0, 0, nt, [&](int, int c) -> int64_t { return head_row0 + c; },
+        [&](int, int c, int d, float, float Ls, float O) {
           const float r = Ls > 0.f ? O / Ls : (Ls == 0.f ? 0.f : __builtin_nanf(""));
           p.out[(head_row0 + c) * D + d] = (half_t)(Ls != Ls ? __builtin_nanf("") : r);
         },
@@ -1016,35 +1192,35 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
     int32_t* sm_cum = smem.cum;
     int32_t* sm_len = smem.len;
     const int32_t wg = blockIdx.x;
-    const int32_t S = p.B * p.n_qt;                   // private segments
+    const int32_t S = p.B * p.n_grp;                  // private segments
     const int32_t per = (S + kThreads - 1) / kThreads;
     const int32_t s_first = threadIdx.x * per;
-    // queries of tile t of a chunk (a single query: tile 0, one query)
-    auto tile_q0 = [&](int32_t t) -> int32_t { return MQ ? t * p.qpt : 0; };
-    auto tile_nq = [&](int32_t t) -> int32_t { return MQ ? min(p.nq - t * p.qpt, p.qpt) : 1; };
-    // window start of the first query of tile t, and the first streamed
+    // queries of tile group gq of a chunk (a single query: group 0, one query)
+    auto grp_q0 = [&](int32_t gq) -> int32_t { return MQ ? gq * p.tw * p.qpt : 0; };
+    auto grp_nq = [&](int32_t gq) -> int32_t { return MQ ? min(p.nq - gq * p.tw * p.qpt, p.tw * p.qpt) : 1; };
+    // window start of the first query of group gq, and the first streamed
     // token: after the shared prefix, or the 16-aligned block holding the
     // window start
-    auto window_lo = [&](int32_t L, int32_t t) -> int32_t {
-      return p.window > 0 ? max(0, L - p.nq + tile_q0(t) + 1 - p.window) : 0;
+    auto window_lo = [&](int32_t L, int32_t gq) -> int32_t {
+      return p.window > 0 ? max(0, L - p.nq + grp_q0(gq) + 1 - p.window) : 0;
     };
-    auto first_token = [&](int32_t L, int32_t t) -> int32_t {
-      return p.window > 0 ? window_lo(L, t) & ~(kBlk - 1) : p.prefix_tokens;
+    auto first_token = [&](int32_t L, int32_t gq) -> int32_t {
+      return p.window > 0 ? window_lo(L, gq) & ~(kBlk - 1) : p.prefix_tokens;
     };
-    // one past the last token segment (b, t) attends: its tile's last query
-    auto seg_end = [&](int32_t L, int32_t t) -> int32_t { return L - p.nq + tile_q0(t) + tile_nq(t); };
+    // one past the last token segment (b, gq) attends: its group's last query
+    auto seg_end = [&](int32_t L, int32_t gq) -> int32_t { return L - p.nq + grp_q0(gq) + grp_nq(gq); };
     int32_t local = 0;
     int32_t first_live = 0x7fffffff;                  // first attended sequence (shared prefix page ids)
     for (int32_t i = 0; i < per; ++i) {
       const int32_t s = s_first + i;
       if (s < S) {
-        const int32_t b = s / p.n_qt;
-        const int32_t t = s - b * p.n_qt;
+        const int32_t b = s / p.n_grp;
+        const int32_t gq = s - b * p.n_grp;
         const int32_t L = p.lens[b];
         sm_len[s] = L;
         int32_t nb = 0;
         if (len_state(p, L) == 1) {
-          nb = (seg_end(L, t) - first_token(L, t) + kBlk - 1) / kBlk;
+          nb = (seg_end(L, gq) - first_token(L, gq) + kBlk - 1) / kBlk;
           first_live = min(first_live, b);
         }
         sm_cum[s] = nb;
@@ -1078,11 +1254,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
     if (prefix_row == 0x7fffffff) prefix_row = 0;
     __syncthreads();
     const int32_t NB = sm_cum[S - 1];                 // private blocks per KV head
-    const int32_t PB = p.prefix_tokens / kBlk;        // prefix blocks per tile
-    const int32_t NTP = p.n_tiles * PB;               // prefix units per KV head
+    const int32_t PB = p.prefix_tokens / kBlk;        // prefix blocks per prefix group
+    const int32_t NTP = p.n_pgrp * PB;                // prefix units per KV head
     const int32_t Wk = p.n_flat_wgs / p.Hkv;          // workgroups per KV head
-    const int32_t Qv = max(max((NB + Wk - 1) / Wk, p.min_piece), 1);
-    const int32_t Qp = max(max((NTP + Wk - 1) / Wk, p.min_piece), 1);
+    const int32_t Qv = max(max((NB + Wk - 1) / Wk, p.min_piece_v), 1);
+    const int32_t Qp = max(max((NTP + Wk - 1) / Wk, p.min_piece_p), 1);
     if (wg == 0) {
       // the reduce kernel locates the pieces from these
       if (threadIdx.x == 0) {
@@ -1094,39 +1270,47 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
     }
     const int32_t kvh = wg % p.Hkv;
     const int32_t jw = wg / p.Hkv;
-    const int64_t slot_base = (int64_t)kvh * (p.n_tiles + S + 2 * Wk) + jw;
     const int32_t gp0 = min(jw * Qp, NTP), gp1 = min(gp0 + Qp, NTP);
     const int32_t gv0 = min(jw * Qv, NB), gv1 = min(gv0 + Qv, NB);
     const int32_t quota = (gp1 - gp0) + (gv1 - gv0);
     // the prefix pages are the same in every attended row of the table: read
     // them from the first such row (an idle slot's row may hold anything)
     const int32_t* prefix_bt = p.bt + (int64_t)prefix_row * p.max_pages;
+    auto put = [&](int64_t col, int d, float M, float Ls, float O) {
+      p.flat_o[col * D + d] = O;
+      if (d == 0) {
+        p.flat_m[col] = M;
+        p.flat_l[col] = Ls;
+      }
+    };
 
-    // shared prefix, units [g0, g1): 16 query rows of tile rt per piece
+    // shared prefix, units [g0, g1): the 16-row query tiles of prefix group
+    // pg (ptw of them, the last group possibly fewer) per piece
     auto prefix_part = [&](int32_t g0, int32_t g1, int32_t after) {
       for (int32_t g = g0; g < g1;) {
-        const int32_t rt = g / PB;
-        const int32_t blk0 = g - rt * PB;
+        const int32_t pg = g / PB;
+        const int32_t blk0 = g - pg * PB;
         const int32_t piece_n = min(g1 - g, PB - blk0);
         // row r = (sequence * nq + query) * G + head in group: q row (r / G) * Hq + kvh * G + r % G
         const int32_t rows = p.B * p.nq * G;
-        auto qrow = [&](int c) -> int64_t {
-          const int32_t r = rt * 16 + c;
+        auto qrow = [&](int tl, int c) -> int64_t {
+          const int32_t r = (pg * p.ptw + tl) * 16 + c;
           return r < rows ? (int64_t)(r / G) * p.Hq + (int64_t)kvh * G + r % G : -1;
         };
-        const int64_t slot = slot_base + rt;
-        run_range<D, 16, kPrefixLoadPolicy, false, K8>(
-            p, smem.tile.prefix, prefix_bt, kvh, blk0 * kBlk, (blk0 + piece_n) * kBlk, quota,
-            after + g1 - g - piece_n, NewToken{-1, 0, nullptr, nullptr}, qrow,
-            [&](int c, int d, float M, float Ls, float O) {
-              const int64_t ps = slot * 16 + c;
-              p.flat_o[ps * D + d] = O;
-              if (d == 0) {
-                p.flat_m[ps] = M;
-                p.flat_l[ps] = Ls;
-              }
-            },
-            lane, wave);
+        const int32_t slot = pg + jw;
+        auto emit = [&](int tl, int c, int d, float M, float Ls, float O) {
+          put(prefix_col(p, kvh, slot, tl, c), d, M, Ls, O);
+        };
+        if constexpr (GRP) {
+          run_range<D, 16, kPrefixLoadPolicy, false, K8, false, true>(
+              p, smem.tile.prefix, prefix_bt, kvh, blk0 * kBlk, (blk0 + piece_n) * kBlk, quota,
+              after + g1 - g - piece_n, NewToken{-1, 0, nullptr, nullptr}, qrow, emit, lane, wave, 0, 1, 0, 0,
+              min(p.ptw, p.n_ptiles - pg * p.ptw));
+        } else {
+          run_range<D, 16, kPrefixLoadPolicy, false, K8>(
+              p, smem.tile.prefix, prefix_bt, kvh, blk0 * kBlk, (blk0 + piece_n) * kBlk, quota,
+              after + g1 - g - piece_n, NewToken{-1, 0, nullptr, nullptr}, qrow, emit, lane, wave);
+        }
         g += piece_n;
       }
     };
@@ -1141,16 +1325,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
           else lo = mid + 1;
         }
         const int32_t s = lo;
-        const int32_t b = s / p.n_qt;
-        const int32_t t = s - b * p.n_qt;
+        const int32_t b = s / p.n_grp;
+        const int32_t gq = s - b * p.n_grp;
         const int32_t seg_first = s > 0 ? sm_cum[s - 1] : 0;
         const int32_t seg_n = sm_cum[s] - seg_first;
         const int32_t blk0 = g - seg_first;
         const int32_t piece_n = min(g1 - g, seg_n - blk0);
         const int32_t L = sm_len[s];
-        const int32_t s0 = first_token(L, t);
+        const int32_t s0 = first_token(L, gq);
         const int32_t start = s0 + blk0 * kBlk;
-        const int32_t end = min(seg_end(L, t), s0 + (blk0 + piece_n) * kBlk);
+        const int32_t end = min(seg_end(L, gq), s0 + (blk0 + piece_n) * kBlk);
         const int64_t head_row0 = (int64_t)b * p.Hq + (int64_t)kvh * G;
         const int32_t* bt_row = p.bt + (int64_t)b * p.max_pages;
         NewToken nt{-1, 0, nullptr, nullptr};
@@ -1161,31 +1345,27 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
             nt = NewToken{(end - 1 - start) >> 4, (end - 1) & 15, p.k_new + src, p.v_new + src};
           }
         }
-        const int64_t slot = slot_base + p.n_tiles + Wk + s;
-        auto emit = [&](int c, int d, float M, float Ls, float O) {
-          const int64_t ps = slot * 16 + c;
-          p.flat_o[ps * D + d] = O;
-          if (d == 0) {
-            p.flat_m[ps] = M;
-            p.flat_l[ps] = Ls;
-          }
+        const int32_t slot = s + jw;
+        auto emit = [&](int tl, int c, int d, float M, float Ls, float O) {
+          put(priv_col(p, kvh, slot, tl, c), d, M, Ls, O);
         };
         if constexpr (MQ) {
-          // columns (query q0 + i, head g) = i * G + g of query tile t of the chunk
-          const int32_t q0 = tile_q0(t);
-          const int32_t nqt = tile_nq(t);
-          const int32_t ncol = nqt * G;
-          run_range<D, 16, kKvLoadPolicy, false, K8, true>(
+          // tiles of qpt queries from the group's first query q0; columns
+          // (query q0 + tl qpt + i, head g) = i * G + g of tile tl
+          const int32_t q0 = grp_q0(gq);
+          const int32_t nqg = grp_nq(gq);
+          run_range<D, 16, kKvLoadPolicy, false, K8, true, GRP>(
               p, smem.tile.prefix, bt_row, kvh, start, end, quota, after + g1 - g - piece_n, nt,
-              [&](int c) -> int64_t {
-                return c < ncol ? ((int64_t)b * p.nq + q0 + c / G) * p.Hq + (int64_t)kvh * G + c % G : -1;
+              [&](int tl, int c) -> int64_t {
+                const int32_t qi = tl * p.qpt + c / G;
+                return qi < nqg ? ((int64_t)b * p.nq + q0 + qi) * p.Hq + (int64_t)kvh * G + c % G : -1;
               },
-              emit, lane, wave, L - p.nq + q0, G, window_lo(L, t), nqt);
+              emit, lane, wave, L - p.nq + q0, G, window_lo(L, gq), nqg, (nqg + p.qpt - 1) / p.qpt);
         } else {
           run_range<D, G, kKvLoadPolicy, FUSED, K8>(
               p, smem.tile.priv, bt_row, kvh, start, end, quota, after + g1 - g - piece_n, nt,
-              [&](int c) -> int64_t { return c < G ? head_row0 + c : -1; }, emit, lane, wave, 0, 1,
-              window_lo(L, t));
+              [&](int, int c) -> int64_t { return c < G ? head_row0 + c : -1; }, emit, lane, wave, 0, 1,
+              window_lo(L, gq));
         }
         g += piece_n;
       }
@@ -1232,60 +1412,63 @@ __device__ __forceinline__ void merge_launch_append(const DecodeParams& p, int32
 }
 
 // Where the partials of output row bh = (b * nq + query) * Hq + h lie: the
-// pieces of its prefix tile segment (np1 of them; column = its row within the
-// tile), then those of its private segment (column = its place among the
-// segment's query tile columns), made by KV head kvh's workgroups ja .. and
-// jb .. of the balanced schedule (slot segment + j of each list).
+// pieces of its prefix group segment (np1 of them, 16 ptw columns apart), then
+// those of its private segment (16 tw columns apart), made by KV head kvh's
+// workgroups ja .. and jb .. of the balanced schedule (slot segment + j of
+// each list; the row's tile within the group and its column within the tile
+// fix the column within the slot).
 struct MergeRow {
   int32_t state;       // len_state of the row's sequence
   int32_t np1, np;     // prefix pieces; all pieces (0 unless the row is attended)
-  int64_t part1;       // partial index of the first prefix piece (slot * 16 + column)
-  int64_t part2;       // partial index of the first private piece
+  int32_t step1, step2;  // columns between consecutive pieces of the two lists
+  int64_t part1;       // partial column of the first prefix piece
+  int64_t part2;       // partial column of the first private piece
 };
 
-__device__ __forceinline__ MergeRow merge_row(const DecodeParams& p, int64_t bh) {
+__device__ __forceinline__ MergeRow merge_row(const DecodeParams& p, int64_t bh64) {
   MergeRow m;
-  const int32_t b = (int32_t)(bh / ((int64_t)p.nq * p.Hq));
-  const int32_t qi = (int32_t)((bh / p.Hq) % p.nq);
-  const int32_t h = (int32_t)(bh % p.Hq);
-  const int32_t G = p.Hq / p.Hkv;
-  const int32_t kvh = h / G;
-  const int32_t hg = h % G;
-  m.state = len_state(p, p.lens[b]);
-  const int32_t Qv = p.flat_hdr[1];
-  const int32_t Qp = p.flat_hdr[2];
-  const int32_t Wk = p.n_flat_wgs / p.Hkv;
-  const int32_t PB = p.prefix_tokens / kBlk;
-  const int32_t S = p.B * p.n_qt;
-  const int64_t slot_base = (int64_t)kvh * (p.n_tiles + S + 2 * Wk);
-  // prefix tile segment of row r = (b * nq + qi) * G + hg
+  // indices first (B nq Hq < 2^31, checked at the call: 32-bit arithmetic),
+  // then the four loads the row's pieces depend on, issued together and
+  // without branches between them
+  const uint32_t bh = (uint32_t)bh64;
+  const uint32_t bq = bh / (uint32_t)p.Hq;
+  const int32_t h = (int32_t)(bh - bq * (uint32_t)p.Hq);
+  const int32_t b = (int32_t)(bq / (uint32_t)p.nq);
+  const int32_t qi = (int32_t)(bq - (uint32_t)b * (uint32_t)p.nq);
+  const int32_t G = 1 << p.g_shift;
+  const int32_t kvh = h >> p.g_shift;
+  const int32_t hg = h & (G - 1);
+  // prefix tile rt of row r = (b * nq + qi) * G + hg, in prefix group rt / ptw
   const int32_t r = (b * p.nq + qi) * G + hg;
   const int32_t rt = r / 16;
-  int32_t ja = 0;
-  m.np1 = 0;
-  if (PB > 0) {
-    const int32_t u0 = rt * PB;
-    ja = u0 / Qp;
-    m.np1 = (u0 + PB - 1) / Qp - ja + 1;
-  }
-  m.part1 = (slot_base + rt + ja) * 16 + r % 16;
-  // private segment: query tile t = cq / 16 of the chunk, column cq % 16
+  const int32_t pg = rt >> p.ptw_shift;
+  // private segment: query tile t = cq / 16 of the chunk in group t / tw, column cq % 16
   const int32_t cq = qi * G + hg;
-  const int32_t s = b * p.n_qt + cq / 16;
-  const int32_t prev = s > 0 ? p.flat_cum[s - 1] : 0;
-  const int32_t nblk = p.flat_cum[s] - prev;
-  int32_t np2 = 0, jb = 0;
-  if (nblk > 0) {
-    jb = prev / Qv;
-    np2 = (prev + nblk - 1) / Qv - jb + 1;
-  }
-  m.part2 = (slot_base + p.n_tiles + Wk + s + jb) * 16 + cq % 16;
+  const int32_t t = cq / 16;
+  const int32_t s = b * p.n_grp + (t >> p.tw_shift);
+  const int32_t L = p.lens[b];
+  const int32_t Qv = p.flat_hdr[1];
+  const int32_t Qp = p.flat_hdr[2];
+  const int32_t prev = p.flat_cum[s > 0 ? s - 1 : 0] & (s > 0 ? -1 : 0);
+  const int32_t cum = p.flat_cum[s];
+  m.state = len_state(p, L);
+  const int32_t PB = p.prefix_tokens / kBlk;
+  const int32_t u0 = pg * PB;
+  const int32_t ja = u0 / Qp;
+  m.np1 = PB > 0 ? (u0 + PB - 1) / Qp - ja + 1 : 0;
+  m.step1 = 16 * p.ptw;
+  m.part1 = prefix_col(p, kvh, pg + ja, rt & (p.ptw - 1), r % 16);
+  const int32_t nblk = cum - prev;
+  const int32_t jb = prev / Qv;
+  const int32_t np2 = nblk > 0 ? (prev + nblk - 1) / Qv - jb + 1 : 0;
+  m.step2 = 16 * p.tw;
+  m.part2 = priv_col(p, kvh, s + jb, t & (p.tw - 1), cq % 16);
   m.np = m.state == 1 ? m.np1 + np2 : 0;
   return m;
 }
 
 __device__ __forceinline__ int64_t part_index(const MergeRow& m, int32_t j) {
-  return j < m.np1 ? m.part1 + (int64_t)j * 16 : m.part2 + (int64_t)(j - m.np1) * 16;
+  return j < m.np1 ? m.part1 + (int64_t)j * m.step1 : m.part2 + (int64_t)(j - m.np1) * m.step2;
 }
 
 // The merged row: 0 for an idle slot, NaN for an invalid length or a bad page
@@ -1423,12 +1606,12 @@ int log2_page(int32_t P) {
 size_t align_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 // Workspace of a split call: a 256-byte header, the per-segment prefix sums,
-// then the piece partials [slots][16] (max, sum) and [slots][16][D] (output).
+// then the piece partials [columns] (max, sum) and [columns][D] (output).
 struct WsLayout {
   size_t hdr_off, cum_off, fm_off, fl_off, fo_off, total;
 };
 
-WsLayout ws_layout(int64_t segments, int64_t D, int64_t slots) {
+WsLayout ws_layout(int64_t segments, int64_t D, int64_t cols) {
   WsLayout w{};
   size_t at = 0;
   auto take = [&](size_t bytes) {
@@ -1438,9 +1621,9 @@ WsLayout ws_layout(int64_t segments, int64_t D, int64_t slots) {
   };
   w.hdr_off = take(3 * sizeof(int32_t));
   w.cum_off = take(static_cast<size_t>(segments) * sizeof(int32_t));
-  w.fm_off = take(static_cast<size_t>(slots * 16) * sizeof(float));
-  w.fl_off = take(static_cast<size_t>(slots * 16) * sizeof(float));
-  w.fo_off = take(static_cast<size_t>(slots * 16 * D) * sizeof(float));
+  w.fm_off = take(static_cast<size_t>(cols) * sizeof(float));
+  w.fl_off = take(static_cast<size_t>(cols) * sizeof(float));
+  w.fo_off = take(static_cast<size_t>(cols * D) * sizeof(float));
   w.total = at;
   return w;
 }
@@ -1470,13 +1653,29 @@ int32_t device_flat_wgs() {
 struct Plan {
   bool split;
   int32_t n_qt;            // 16-column query tiles per (sequence, KV head): ceil(nq * G / 16) for chunks, else 1
-  int32_t segments;        // private segments per KV head: B * n_qt
-  int32_t n_tiles;         // 16-row query tiles per KV head reading the shared prefix
+  int32_t tw;              // query tiles per group (one stream of the blocks for all of them)
+  int32_t n_grp;           // tile groups per (sequence, KV head): ceil(n_qt / tw)
+  int32_t segments;        // private segments per KV head: B * n_grp
+  int32_t n_ptiles;        // 16-row query tiles per KV head reading the shared prefix
+  int32_t ptw;             // prefix tiles per prefix group
+  int32_t n_pgrp;          // prefix groups per KV head
   int32_t n_flat_wgs;      // workgroups of the split schedule (a multiple of Hkv)
-  int32_t min_piece;       // minimum blocks per piece
-  int64_t slots;           // piece slots: Hkv * (n_tiles + segments + 2 * n_flat_wgs / Hkv)
+  int32_t min_piece_p;     // minimum blocks per piece: prefix list
+  int32_t min_piece_v;     // minimum blocks per piece: private list
+  int64_t priv_col0;       // first partial column of the private list
+  int64_t cols;            // partial columns: Hkv ((n_pgrp + Wk) 16 ptw + (segments + Wk) 16 tw)
   int64_t grid;
 };
+
+// Query tiles per group: chunks of queries stream a sequence's blocks once
+// for up to 4 tiles (staged through LDS, one wave per tile); a single tile
+// (single-token decode: the G heads) keeps the workgroup's 4 waves splitting
+// its blocks.
+constexpr int32_t kMaxTileGroup = 4;
+
+// Tiles per group for n tiles: 1, 2 or 4 (a power of two; 3 tiles form one
+// group of 4 slots, its fourth wave idle).
+int32_t tile_group(int64_t n) { return n >= 3 ? kMaxTileGroup : (n == 2 ? 2 : 1); }
 
 int make_plan(int32_t B, int32_t nq, int32_t Hq, int32_t Hkv, int32_t max_context, int32_t partition_tokens,
               int32_t prefix_tokens, int32_t flat_wgs, Plan* pl) {
@@ -1488,18 +1687,35 @@ int make_plan(int32_t B, int32_t nq, int32_t Hq, int32_t Hkv, int32_t max_contex
   Plan p{};
   p.split = partition_tokens > 0;
   const int64_t n_qt = nq > 1 ? (static_cast<int64_t>(nq) * G + 15) / 16 : 1;
-  const int64_t segments = static_cast<int64_t>(B) * n_qt;
+  p.tw = nq > 1 ? tile_group(n_qt) : 1;
+  const int64_t n_grp = (n_qt + p.tw - 1) / p.tw;
+  const int64_t segments = static_cast<int64_t>(B) * n_grp;
   if (p.split && segments > kMaxSegments) return PKV_ERR_INVALID_ARG;
   p.n_qt = static_cast<int32_t>(std::min<int64_t>(n_qt, 0x7fffffff));
+  p.n_grp = static_cast<int32_t>(std::min<int64_t>(n_grp, 0x7fffffff));
   p.segments = static_cast<int32_t>(std::min<int64_t>(segments, 0x7fffffff));
   const int64_t rows = static_cast<int64_t>(B) * nq * G;                // query rows per KV head
   if (rows > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
-  p.n_tiles = prefix_tokens > 0 ? static_cast<int32_t>((rows + 15) / 16) : 0;
+  const int64_t n_ptiles = prefix_tokens > 0 ? (rows + 15) / 16 : 0;
+  p.n_ptiles = static_cast<int32_t>(n_ptiles);
+  // prefix tiles are grouped (staged through LDS) only for chunks that
+  // span several query tiles: the prefix pages sit in the L2, where the
+  // 4-way split of a single tile streams them faster per tile than a staged
+  // group, which pays off only once many tiles re-read them
+  p.ptw = n_qt >= 2 ? tile_group(n_ptiles) : 1;
+  p.n_pgrp = static_cast<int32_t>((n_ptiles + p.ptw - 1) / p.ptw);
   // a whole number of workgroups per KV head, at least one; a row's pieces
   // (at most two per workgroup of its head) fit the merge kernel's LDS
   p.n_flat_wgs = p.split ? std::min(std::max(flat_wgs / Hkv, 1), kMaxPartitions / 2) * Hkv : 0;
-  p.min_piece = partition_tokens / kBlk;
-  p.slots = p.split ? static_cast<int64_t>(Hkv) * (p.n_tiles + segments + 2 * (p.n_flat_wgs / Hkv)) : 0;
+  const int64_t Wk = p.n_flat_wgs / Hkv;
+  // partition_tokens is the minimum work of a piece, in blocks of one
+  // workgroup's 4-way split: a block of a staged group of 2 to 4 tiles costs
+  // every wave a whole block, 4 times as much
+  const int32_t min_piece = partition_tokens / kBlk;
+  p.min_piece_p = p.ptw >= 2 ? (min_piece + kWaves - 1) / kWaves : min_piece;
+  p.min_piece_v = p.tw >= 2 ? (min_piece + kWaves - 1) / kWaves : min_piece;
+  p.priv_col0 = p.split ? static_cast<int64_t>(Hkv) * (p.n_pgrp + Wk) * 16 * p.ptw : 0;
+  p.cols = p.split ? p.priv_col0 + static_cast<int64_t>(Hkv) * (segments + Wk) * 16 * p.tw : 0;
   p.grid = p.split ? p.n_flat_wgs : segments * Hkv;
   if (p.grid > 0x7fffffffLL || static_cast<int64_t>(B) * nq * Hq > 0x7fffffffLL) return PKV_ERR_INVALID_ARG;
   *pl = p;
@@ -1512,9 +1728,9 @@ int make_plan(int32_t B, int32_t nq, int32_t Hq, int32_t Hkv, int32_t max_contex
 thread_local hipEvent_t t_prof_armed[2] = {nullptr, nullptr};
 thread_local hipEvent_t t_prof_call[2] = {nullptr, nullptr};
 
-template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ>
+template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ, bool GRP>
 hipError_t launch_partition(const DecodeParams& p, hipStream_t stream, int64_t grid) {
-  const void* fn = reinterpret_cast<const void*>(&decode_partition_kernel<D, G, SPLIT, FUSED, K8, MQ>);
+  const void* fn = reinterpret_cast<const void*>(&decode_partition_kernel<D, G, SPLIT, FUSED, K8, MQ, GRP>);
   if (t_prof_call[0] || t_prof_call[1]) {
     // the start and stop of this kernel alone go into the caller's events
     DecodeParams arg = p;
@@ -1523,26 +1739,26 @@ hipError_t launch_partition(const DecodeParams& p, hipStream_t stream, int64_t g
                                             t_prof_call[0], t_prof_call[1], 0);
     return e != hipSuccess ? e : hipGetLastError();
   }
-  hipLaunchKernelGGL((decode_partition_kernel<D, G, SPLIT, FUSED, K8, MQ>), dim3(static_cast<uint32_t>(grid)),
+  hipLaunchKernelGGL((decode_partition_kernel<D, G, SPLIT, FUSED, K8, MQ, GRP>), dim3(static_cast<uint32_t>(grid)),
                      dim3(kThreads), 0, stream, p);
   return hipGetLastError();
 }
 
-template <int D, bool SPLIT, bool FUSED, bool K8, bool MQ = false>
+template <int D, bool SPLIT, bool FUSED, bool K8, bool MQ = false, bool GRP = false>
 hipError_t dispatch_g(int G, const DecodeParams& p, hipStream_t s, int64_t grid) {
   switch (G) {
-    case 1: return launch_partition<D, 1, SPLIT, FUSED, K8, MQ>(p, s, grid);
-    case 2: return launch_partition<D, 2, SPLIT, FUSED, K8, MQ>(p, s, grid);
-    case 4: return launch_partition<D, 4, SPLIT, FUSED, K8, MQ>(p, s, grid);
-    case 8: return launch_partition<D, 8, SPLIT, FUSED, K8, MQ>(p, s, grid);
-    default: return launch_partition<D, 16, SPLIT, FUSED, K8, MQ>(p, s, grid);
+    case 1: return launch_partition<D, 1, SPLIT, FUSED, K8, MQ, GRP>(p, s, grid);
+    case 2: return launch_partition<D, 2, SPLIT, FUSED, K8, MQ, GRP>(p, s, grid);
+    case 4: return launch_partition<D, 4, SPLIT, FUSED, K8, MQ, GRP>(p, s, grid);
+    case 8: return launch_partition<D, 8, SPLIT, FUSED, K8, MQ, GRP>(p, s, grid);
+    default: return launch_partition<D, 16, SPLIT, FUSED, K8, MQ, GRP>(p, s, grid);
   }
 }
 
-template <bool SPLIT, bool FUSED, bool K8, bool MQ = false>
+template <bool SPLIT, bool FUSED, bool K8, bool MQ = false, bool GRP = false>
 hipError_t dispatch_d(int D, int G, const DecodeParams& p, hipStream_t s, int64_t grid) {
-  return D == 64 ? dispatch_g<64, SPLIT, FUSED, K8, MQ>(G, p, s, grid)
-                 : dispatch_g<128, SPLIT, FUSED, K8, MQ>(G, p, s, grid);
+  return D == 64 ? dispatch_g<64, SPLIT, FUSED, K8, MQ, GRP>(G, p, s, grid)
+                 : dispatch_g<128, SPLIT, FUSED, K8, MQ, GRP>(G, p, s, grid);
 }
 
 int decode_common(void* out, const void* q, const void* k_new, const void* v_new, const void* k_pool,
@@ -1621,6 +1837,7 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   prm.Hkv = Hkv;
   prm.N = N;
   prm.p_shift = p_shift;
+  prm.g_shift = G == 1 ? 0 : G == 2 ? 1 : G == 4 ? 2 : G == 8 ? 3 : 4;
   prm.max_context = max_context;
   prm.prefix_tokens = prefix_tokens;
   // an appended token must land in a private page; a chunk of queries lies after the prefix
@@ -1628,16 +1845,26 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   prm.nq = nq;
   prm.n_qt = plan.n_qt;
   prm.qpt = nq > 1 ? 16 / G : 1;
+  prm.tw = plan.tw;
+  prm.tw_shift = plan.tw == 4 ? 2 : plan.tw - 1;
+  prm.n_grp = plan.n_grp;
   prm.ring = window > 0 ? max_pages : 0;
   prm.window = window;
-  prm.n_tiles = plan.n_tiles;
+  prm.n_ptiles = plan.n_ptiles;
+  prm.ptw = plan.ptw;
+  prm.ptw_shift = plan.ptw == 4 ? 2 : plan.ptw - 1;
+  prm.n_pgrp = plan.n_pgrp;
+  prm.priv_col0 = plan.priv_col0;
+  prm.pslots = plan.n_pgrp + plan.n_flat_wgs / Hkv;
+  prm.vslots = plan.segments + plan.n_flat_wgs / Hkv;
   prm.n_flat_wgs = plan.n_flat_wgs;
   prm.write_new = plan.split ? 0 : 1;
-  prm.min_piece = plan.min_piece;
+  prm.min_piece_p = plan.min_piece_p;
+  prm.min_piece_v = plan.min_piece_v;
   prm.scale_log2 = scale * kLog2e;
 
   if (plan.split) {
-    const WsLayout ws = ws_layout(plan.segments, D, plan.slots);
+    const WsLayout ws = ws_layout(plan.segments, D, plan.cols);
     if (!workspace) return PKV_ERR_INVALID_ARG;
     if (!aligned(workspace, kWsAlign)) return PKV_ERR_INVALID_ARG;
     if (workspace_bytes < ws.total) return too_small;
@@ -1653,9 +1880,18 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   const int64_t grid = plan.grid;
   hipError_t e = hipSuccess;
   if (grid > 0) {
-    if (nq > 1 && k8)
+    // chunks spanning one query tile (and ungrouped prefix tiles) take the
+    // kernels without the staged tile-group path
+    const bool grp = plan.tw > 1 || plan.ptw > 1;
+    if (nq > 1 && k8 && grp)
+      e = plan.split ? dispatch_d<true, false, true, true, true>(D, G, prm, s, grid)
+                     : dispatch_d<false, false, true, true, true>(D, G, prm, s, grid);
+    else if (nq > 1 && k8)
       e = plan.split ? dispatch_d<true, false, true, true>(D, G, prm, s, grid)
                      : dispatch_d<false, false, true, true>(D, G, prm, s, grid);
+    else if (nq > 1 && grp)
+      e = plan.split ? dispatch_d<true, false, false, true, true>(D, G, prm, s, grid)
+                     : dispatch_d<false, false, false, true, true>(D, G, prm, s, grid);
     else if (nq > 1)
       e = plan.split ? dispatch_d<true, false, false, true>(D, G, prm, s, grid)
                      : dispatch_d<false, false, false, true>(D, G, prm, s, grid);
@@ -1733,7 +1969,7 @@ int workspace_bytes(int32_t B, int32_t nq, int32_t Hq, int32_t D, int32_t max_co
       continue;
     }
     rc = PKV_OK;
-    if (plan.split) best = std::max(best, ws_layout(plan.segments, D, plan.slots).total);
+    if (plan.split) best = std::max(best, ws_layout(plan.segments, D, plan.cols).total);
   }
   if (rc != PKV_OK) return rc;
   *bytes = best;

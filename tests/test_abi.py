@@ -119,7 +119,7 @@ def test_workspace_size(pkv):
         pkv.decode_workspace_bytes(5000, 32, 128, 32768, 512)        # split path holds at most 4096 sequences
     with pytest.raises(pkv.PkvError):
         pkv.decode_workspace_bytes(4, 32, 128, 2000, 0, prefix_tokens=1024)   # prefix needs the split path
-    # chunks of queries: one private segment per sequence and 16-column query tile
+    # chunks of queries: one private segment per sequence and group of up to four 16-column query tiles
     assert pkv.decode_workspace_bytes_multi(4, 1, 32, 128, 32768, 512) == n
     assert pkv.decode_workspace_bytes_multi(4, 1, 32, 128, 32768, 512, 2048) == m
     k256 = pkv.decode_workspace_bytes_multi(64, 256, 32, 128, 32768, 512)
@@ -128,7 +128,9 @@ def test_workspace_size(pkv):
     with pytest.raises(pkv.PkvError):
         pkv.decode_workspace_bytes_multi(64, 0, 32, 128, 32768, 512)
     with pytest.raises(pkv.PkvError):
-        pkv.decode_workspace_bytes_multi(4096, 64, 32, 128, 32768, 512)     # > 4096 segments for every Hkv
+        pkv.decode_workspace_bytes_multi(4097, 64, 32, 128, 32768, 512)     # > 4096 segments for every Hkv
+    # segments are (sequence, group of up to 4 query tiles): 4096 sequences of 64 queries fit at G = 1
+    assert pkv.decode_workspace_bytes_multi(4096, 64, 32, 128, 32768, 512) > 0
 
 
 # ---------------------------------------------------------------------------

@@ -199,10 +199,11 @@ def test_chunk_tiles_headline_batch(nq):
 
 
 def test_chunk_tiles_segment_limit():
-    """In split mode a call holds at most 4096 (sequence, query tile)
-    segments; the unsplit path has no such limit."""
+    """In split mode a call holds at most 4096 (sequence, query tile group)
+    segments, a group being up to 4 tiles of 16 columns that stream the
+    sequence together; the unsplit path has no such limit."""
     m = pkv()
-    B, nq, Hq, Hkv, D, P = 65, 256, 8, 2, 64, 16                   # 65 x 64 tiles at G = 4
+    B, nq, Hq, Hkv, D, P = 257, 256, 8, 2, 64, 16                  # 257 x 16 groups of 4 tiles at G = 4
     lens = np.full(B, nq, np.int32)
     bt = np.tile(np.arange(nq // P, dtype=np.int32), (B, 1))
     pool = torch.zeros(oracle.pool_shape(nq // P, Hkv, P, D), dtype=torch.float16, device="cuda")
@@ -211,6 +212,7 @@ def test_chunk_tiles_segment_limit():
         m.paged_decode_attention_multi(q, pool, pool, dev(bt), dev(lens), nq, 0.125, 64,
                                        workspace=torch.empty(1 << 20, dtype=torch.uint8, device="cuda"))
     assert e.value.status == m.PKV_ERR_INVALID_ARG
+    ok = m.paged_decode_attention_multi(q[:256], pool, pool, dev(bt[:256]), dev(lens[:256]), nq, 0.125, 64)
     out = m.paged_decode_attention_multi(q, pool, pool, dev(bt), dev(lens), nq, 0.125, 0)
     torch.cuda.synchronize()
-    assert torch.all(out == 0)                                      # zero values: zero output
+    assert torch.all(ok == 0) and torch.all(out == 0)               # zero values: zero output
