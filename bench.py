@@ -505,8 +505,15 @@ def main():
     else:
         kp0, vp0 = oracle.kv_append(w.k_pool, w.v_pool, w.k_new[0], w.v_new[0], w.block_table, w.pos(0), P)
         ref = oracle.decode_attention(w.q[sample], kp0, vp0, w.block_table[sample], w.lens(0)[sample], scale, P)
-    max_err = float(np.abs(got[sample] - ref).max())
-    log("parity (layer 0, step 0, %d sequences): max_abs_err=%.3e" % (len(sample), max_err))
+    err = np.abs(got[sample].astype(np.float64) - ref)
+    max_err = float(err.max())
+    # the worst element beside half a step of the fp16 output grid at its
+    # value: what rounding the exact result to fp16 alone leaves there
+    worst = np.unravel_index(int(np.argmax(err)), err.shape)
+    worst_ref = float(ref[worst])
+    worst_half_step = float(np.spacing(np.float16(abs(worst_ref)))) / 2
+    log("parity (layer 0, step 0, %d sequences): max_abs_err=%.3e at an output of %.3f (half an fp16 step there: %.3e)"
+        % (len(sample), max_err, worst_ref, worst_half_step))
     if not max_err <= 4e-3:
         raise SystemExit("parity check failed: %.3e" % max_err)
     # the check ran step 0 on layer 0 already; restore its pools so every layer starts alike
@@ -694,6 +701,8 @@ def main():
             "kv_gbps": round(kv_per_call / (ms_per_layer / 1e3) / 1e9, 1),
             "kv_frac_of_peak": round(kv_per_call / (ms_per_layer / 1e3) / 1e9 / PEAK_HBM_GBPS, 4),
             "parity_max_abs_err": max_err,
+            "parity_worst_output": round(worst_ref, 5),
+            "parity_worst_fp16_half_step": worst_half_step,
             "working_set_gb": round(mem_gb, 2),
             "wall_s": round(wall, 3),
             "git": git_sha(),
