@@ -62,8 +62,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr size_t kWsAlign = 256;
 constexpr int32_t kMaxPartitions = 1024;   // partial slots per (sequence, head) (reduce kernel LDS)
 constexpr uint32_t kWaveMergeRows = 2048;  // output rows from which the one-wave-per-row merge runs
-// work segments per split call (one per sequence, or per sequence and 16-column
-// query tile for chunks of queries): their block prefix sums sit in LDS
+// work segments per split call (one per sequence, or per sequence and group of
+// query tiles for chunks of queries): their block prefix sums sit in LDS
 constexpr int32_t kMaxSegments = 4096;
 // Split-mode workgroups per compute unit: two stream side by side (<= 256 VGPRs each)
 constexpr int kWgsPerCu = 2;
@@ -961,9 +961,11 @@ struct WgShared {
   float l[kWaves][NC];
 };
 
-// LDS of the partition kernel: the merge area of one range (16 columns for a
-// prefix tile or a tile of a chunk of queries, G for a private segment; one at
-// a time) and the per-segment block prefix sums of the split schedule.
+// LDS of the partition kernel: the merge area of one range (16 columns per
+// wave for prefix tiles and tiles of a chunk of queries, G for a private
+// segment; one range at a time; a staged tile group's two-block ring aliases
+// it while the range streams) and the per-segment block prefix sums of the
+// split schedule.
 template <int D, int G>
 struct KernelShared {
   union {
