@@ -95,6 +95,7 @@ def ragged_lens(rng, B, base, P):
     (64, 0, 0), (64, 0, 512), (64, 5, 128),
     (256, 0, 0), (256, 0, 64), (256, 5, 512),
     (33, 0, 16), (33, 3, 16),               # 33 queries: the last tile holds one query
+    (20, 2, 32), (20, 0, 0),                # 15 prefix tiles (a last prefix group of 3), private groups of 4 and 1
 ])
 def test_chunk_tiles_match_oracle(nq, prefix_pages, part):
     G, Hkv, D, P = 4, 2, 128, 16
