@@ -966,14 +966,16 @@ struct WgShared {
 // segment; one range at a time; a staged tile group's two-block ring aliases
 // it while the range streams) and the per-segment block prefix sums of the
 // split schedule.
-template <int D, int G>
+template <int D, int G, bool GRP>
 struct KernelShared {
   union {
     WgShared<D, 16> prefix;
     WgShared<D, G> priv;
   } tile;
   int32_t cum[kMaxSegments];     // inclusive prefix sums of private blocks per segment
-  int32_t len[kMaxSegments];     // the length of each segment's sequence
+  // the length of each segment's sequence (tile-group kernels re-read the
+  // lengths instead, so that three workgroups fit a compute unit's LDS)
+  int32_t len[GRP ? 1 : kMaxSegments];
   int32_t wsum[kWaves];
   int32_t wmin[kWaves];
 };
@@ -988,11 +990,10 @@ struct KernelShared {
 // heads per query); query i of the tile sits at position mq_last0 + i and may
 // see tokens up to there (with a sliding window, the window ending there).
 // kGrp: the range serves ntl (1 to 4) query tiles of NC = 16 columns at once,
-// tile tl reading rows qrow(tl, c) and emitting through emit(tl, ...). For 2
-// to 4 tiles the workgroup reads each block once into LDS and wave tl
-// consumes every block for tile tl (waves past the last tile only load); a
-// single tile is streamed as above. With kMQ the group's mq_n queries start
-// at mq_last0, p.qpt queries per tile.
+// tile tl reading rows qrow(tl, c) and emitting through emit(tl, ...): the
+// workgroup reads each block once into LDS and wave tl consumes every block
+// for tile tl (waves past the last tile only load). With kMQ the group's
+// mq_n queries start at mq_last0, p.qpt queries per tile.
 template <int D, int NC, int32_t kPolicy, bool kAppend, bool kK8, bool kMQ = false, bool kGrp = false, class RowFn,
           class EmitFn>
 __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>& sh, const int32_t* bt_row,
@@ -1008,10 +1009,11 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
   // two ring slots of a staged range (K and V bytes of a block each) fit the merge area
   static_assert(!kGrp || sizeof(WgShared<D, NC>) >= 2 * ((kK8 ? kBlk * D + 64 : kBlk * D * 2) + kBlk * D * 2),
                 "LDS ring");
-  // waves per tile, this wave's tile and its place among the tile's waves: a
-  // group of 2 to 4 tiles is staged through LDS, one wave per tile (the other
-  // waves only load); a single tile keeps the 4 waves splitting its blocks
-  const int wpt = kGrp ? (ntl >= 2 ? 1 : kWaves) : kWaves;
+  // waves per tile and this wave's tile: a group is staged through LDS, one
+  // wave per tile (the other waves only load; a group of one tile, the tail
+  // of a chunk, has one wave computing); ungrouped ranges keep the 4 waves
+  // splitting the blocks
+  const int wpt = kGrp ? 1 : kWaves;
   const int tl = kGrp ? wave / wpt : 0;
   const bool active = !kGrp || tl < ntl;
   // B operand of the score MFMA: lane (column col, quad) holds q[row][32 j + 8 quad .. + 8]
@@ -1039,8 +1041,8 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
       clo_max = max(0, t_last0 + t_n - p.window);
     }
   }
-  if (kGrp && ntl >= 2)
-    stream_blocks<D, kPolicy, kAppend, kK8, kMQ, kGrp>(p, bt_row, kvh, start, end, 0, 1, quota, after, nt, clim,
+  if constexpr (kGrp)
+    stream_blocks<D, kPolicy, kAppend, kK8, kMQ, true>(p, bt_row, kvh, start, end, 0, 1, quota, after, nt, clim,
                                                        t_last0, clo, clo_max, lo, qb, st, lane,
                                                        reinterpret_cast<char*>(&sh), active);
   else
@@ -1116,13 +1118,13 @@ __device__ __forceinline__ void run_range(const DecodeParams& p, WgShared<D, NC>
 // order increases s or j (or both) by one each step, so the slots are
 // distinct.
 template <int D, int G, bool SPLIT, bool FUSED, bool K8, bool MQ, bool GRP>
-__global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kThreads, GRP ? 3 : 2) void decode_partition_kernel(DecodeParams p) {
   static_assert(!MQ || !FUSED, "chunks of queries: no fused append");
   static_assert(MQ || !GRP, "tile groups are for chunks of queries");
   static_assert(D % 32 == 0 && G >= 1 && G <= 16, "shape");
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  __shared__ KernelShared<D, G> smem;
+  __shared__ KernelShared<D, G, GRP> smem;
 
   if constexpr (!SPLIT && MQ) {
     // query tile group gq of a chunk of nq queries: tiles gq tw .. of qpt
@@ -1219,7 +1221,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
         const int32_t b = s / p.n_grp;
         const int32_t gq = s - b * p.n_grp;
         const int32_t L = p.lens[b];
-        sm_len[s] = L;
+        if constexpr (!GRP) sm_len[s] = L;
         int32_t nb = 0;
         if (len_state(p, L) == 1) {
           nb = (seg_end(L, gq) - first_token(L, gq) + kBlk - 1) / kBlk;
@@ -1333,7 +1335,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_partition_kernel(DecodePar
         const int32_t seg_n = sm_cum[s] - seg_first;
         const int32_t blk0 = g - seg_first;
         const int32_t piece_n = min(g1 - g, seg_n - blk0);
-        const int32_t L = sm_len[s];
+        const int32_t L = GRP ? p.lens[b] : sm_len[s];
         const int32_t s0 = first_token(L, gq);
         const int32_t start = s0 + blk0 * kBlk;
         const int32_t end = min(seg_end(L, gq), s0 + (blk0 + piece_n) * kBlk);
