@@ -109,11 +109,10 @@ struct DecodeParams {
   int32_t prefix_tokens;     // shared leading tokens (0 = none), multiple of P
   int32_t min_len;           // a positive length below this is invalid (NaN rows)
   int32_t nq;                // queries per sequence (1 = decode; > 1: the chunk of the last nq tokens)
-  int32_t n_qt;              // 16-column query tiles per (sequence, KV head): ceil(nq * G / 16) for chunks, else 1
   int32_t qpt;               // queries per query tile (16 / G for chunks)
   int32_t tw;                // query tiles per group (1, 2 or 4): a group's tiles share one stream of the blocks
   int32_t tw_shift;          // log2(tw)
-  int32_t n_grp;             // query tile groups per (sequence, KV head): ceil(n_qt / tw)
+  int32_t n_grp;             // query tile groups per (sequence, KV head): ceil(ceil(nq * G / 16) / tw)
   int32_t ring;              // sliding window: pages per sequence in its ring (logical page j -> entry j % ring)
   int32_t window;            // sliding window: tokens attended (the last `window`)
   int32_t n_ptiles;          // 16-row query tiles per KV head that read the prefix (0 = none)
@@ -1658,9 +1657,8 @@ int32_t device_flat_wgs() {
 // Work decomposition of one decode call.
 struct Plan {
   bool split;
-  int32_t n_qt;            // 16-column query tiles per (sequence, KV head): ceil(nq * G / 16) for chunks, else 1
   int32_t tw;              // query tiles per group (one stream of the blocks for all of them)
-  int32_t n_grp;           // tile groups per (sequence, KV head): ceil(n_qt / tw)
+  int32_t n_grp;           // tile groups per (sequence, KV head): ceil(ceil(nq * G / 16) / tw)
   int32_t segments;        // private segments per KV head: B * n_grp
   int32_t n_ptiles;        // 16-row query tiles per KV head reading the shared prefix
   int32_t ptw;             // prefix tiles per prefix group
@@ -1697,7 +1695,6 @@ int make_plan(int32_t B, int32_t nq, int32_t Hq, int32_t Hkv, int32_t max_contex
   const int64_t n_grp = (n_qt + p.tw - 1) / p.tw;
   const int64_t segments = static_cast<int64_t>(B) * n_grp;
   if (p.split && segments > kMaxSegments) return PKV_ERR_INVALID_ARG;
-  p.n_qt = static_cast<int32_t>(std::min<int64_t>(n_qt, 0x7fffffff));
   p.n_grp = static_cast<int32_t>(std::min<int64_t>(n_grp, 0x7fffffff));
   p.segments = static_cast<int32_t>(std::min<int64_t>(segments, 0x7fffffff));
   const int64_t rows = static_cast<int64_t>(B) * nq * G;                // query rows per KV head
@@ -1849,7 +1846,6 @@ int decode_common(void* out, const void* q, const void* k_new, const void* v_new
   // an appended token must land in a private page; a chunk of queries lies after the prefix
   prm.min_len = nq > 1 ? prefix_tokens + nq : prefix_tokens + (fused && prefix_tokens > 0 ? 1 : 0);
   prm.nq = nq;
-  prm.n_qt = plan.n_qt;
   prm.qpt = nq > 1 ? 16 / G : 1;
   prm.tw = plan.tw;
   prm.tw_shift = plan.tw == 4 ? 2 : plan.tw - 1;
