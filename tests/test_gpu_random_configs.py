@@ -22,7 +22,7 @@ from _helpers import k8_pool, live_slots, poison
 pytestmark = pytest.mark.gpu
 
 TOL = 4e-3
-N_CASES = 220
+N_CASES = 1000
 MODES = ["decode", "fused", "prefix", "prefix_fused", "k8", "k8_fused", "k8_prefix", "multi", "multi_prefix",
          "window", "window_fused", "k8_multi", "k8_multi_prefix", "k8_window", "k8_window_fused", "window_multi",
          "k8_window_multi"]
